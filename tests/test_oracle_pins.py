@@ -1,0 +1,428 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle.
+
+Each test names what it pins: a closed form, an exhaustive enumeration, a
+library routine on a special case, a hand-derived example (tests/golden/)
+or brute force on tiny inputs.  Sources are cited by page title and part:
+  [LG] LiquidGEMM, Pith review of arXiv 2509.01229 ("What carries the
+       argument"; referee summary; major comment 3 = paper Sec. 4 Eq. 7;
+       minor comment 2 = Eq. 10; circularity audit = Eq. 11/12).
+  [FQ] FireQ, arXiv 2505.20839, abstract.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+
+# ----------------------------------------------------------------- P1 ------
+def _all_valid_triples():
+    m = np.arange(-128, 128).reshape(-1, 1, 1)
+    s = np.arange(0, 256).reshape(1, -1, 1)
+    q = np.arange(0, 16).reshape(1, 1, -1)
+    val = m + q * s
+    ok = (val >= -128) & (val <= 127)
+    mm, ss, qq = np.broadcast_arrays(m, s, q)
+    return mm[ok], ss[ok], qq[ok]
+
+
+def test_p1_identity_exhaustive():
+    """[LG] Eq. 12: (q*s + a) XOR 0x80 with a = 128 + m equals the affine
+    dequantisation m + q*s, with no carry out of the UINT8 byte, for every
+    (m, s, q) whose value is an INT8."""
+    m, s, q = _all_valid_triples()
+    n = m.size
+    assert n == 176198  # count of valid triples (independent enumeration)
+    codes = q.astype(np.uint8).reshape(n, 1)
+    su8 = s.astype(np.uint8).reshape(n, 1)
+    au8 = (128 + m).astype(np.uint8).reshape(n, 1)
+    dec = oracle.lqq_decode(codes, su8, au8, 1, check_carry=True)
+    np.testing.assert_array_equal(dec.reshape(-1).astype(np.int64), m + q * s)
+
+
+def test_p1_carry_is_reported():
+    """Outside the INT8 range the byte would carry; the oracle must say so."""
+    codes = np.array([[15]], np.uint8)
+    with pytest.raises(AssertionError):
+        oracle.lqq_decode(codes, np.array([[17]], np.uint8),
+                          np.array([[1]], np.uint8), 1, check_carry=True)
+
+
+def test_p1_swar_lanes_carry_free():
+    """Four codes per 32-bit word, multiplied and offset as two 16-bit lanes
+    (each holding two code bytes), give the four scalar decodes: the byte
+    lanes never carry into each other when every q*s + a <= 255."""
+    rng = np.random.default_rng(5)
+    m, s, q = _all_valid_triples()
+    idx = rng.integers(0, m.size, size=(20000,))
+    for i0 in range(0, 20000, 4000):
+        sel = idx[i0:i0 + 4000]
+        # one (m, s) per word, four codes whose values stay in range
+        mm, ss = m[sel], s[sel]
+        qmax = np.where(ss > 0, (127 - mm) // np.maximum(ss, 1), 15)
+        qmax = np.minimum(qmax, 15)
+        qs = rng.integers(0, qmax[:, None] + 1, size=(sel.size, 4))
+        word = (qs[:, 0] | (qs[:, 1] << 8) | (qs[:, 2] << 16) | (qs[:, 3] << 24))
+        a = 128 + mm
+        lo = (word & 0xFFFF) * ss + (a | (a << 8))
+        hi = ((word >> 16) & 0xFFFF) * ss + (a | (a << 8))
+        res = ((lo & 0xFFFF) | ((hi & 0xFFFF) << 16)) ^ 0x80808080
+        got = np.stack([((res >> (8 * j)) & 0xFF) for j in range(4)], 1)
+        got = np.where(got > 127, got - 256, got)
+        np.testing.assert_array_equal(got, mm[:, None] + qs * ss[:, None])
+
+
+# ----------------------------------------------------------------- P2 ------
+def _exhaustive_groups(lo, hi, g=64):
+    """Groups covering every (m, M, Q) with lo <= m <= Q <= M <= hi."""
+    rows = []
+    per = g - 2
+    for m in range(lo, hi + 1):
+        for M in range(m, hi + 1):
+            vals = np.arange(m, M + 1)
+            for c0 in range(0, vals.size, per):
+                chunk = vals[c0:c0 + per]
+                row = np.full(g, m, np.int64)
+                row[1] = M
+                row[2:2 + chunk.size] = chunk
+                rows.append(row)
+    return np.asarray(rows, np.int8)
+
+
+@pytest.fixture(scope="module")
+def groups_127():
+    return _exhaustive_groups(-127, 127)
+
+
+def test_p2_quantizer_bounds_full_range(groups_127):
+    """[LG] major comment 3 / minor comment 2: integer scale, nearest
+    rounding.  Exhaustive over -127 <= m <= Q <= M <= 127:
+      * s is the least integer >= 1 with R/s <= 15;
+      * a = 128 + m;
+      * every decoded value is an INT8 that never exceeds 127 (no wrap);
+      * unsaturated codes are the nearest grid point (ties upward);
+      * saturated codes sit below Q by less than one step."""
+    Q = groups_127
+    codes, s, a, nsat = oracle.lqq_encode(Q, 64)
+    s = s[:, 0].astype(np.int64)
+    a = a[:, 0].astype(np.int64)
+    Qi = Q.astype(np.int64)
+    m, M = Qi.min(1), Qi.max(1)
+    R = M - m
+    assert np.all(R <= 15 * s)
+    assert np.all((s == 1) | (R > 15 * (s - 1)))
+    np.testing.assert_array_equal(a, 128 + m)
+    dec = oracle.lqq_decode(codes, s.astype(np.uint8)[:, None],
+                            a.astype(np.uint8)[:, None], 64).astype(np.int64)
+    q = codes.astype(np.int64)
+    np.testing.assert_array_equal(dec, m[:, None] + q * s[:, None])
+    assert dec.max() <= 127 and dec.min() >= -127
+    # nearest grid point, ties upward, unless lowered by the saturation
+    err = Qi - dec
+    cap = (127 - m) // s
+    sat = q == cap[:, None]
+    near = (2 * np.abs(err) < s[:, None]) | (2 * err == -s[:, None])
+    unsat_ok = near | sat
+    assert np.all(unsat_ok)
+    assert np.all(err[sat] < s[:, None].repeat(64, 1)[sat])
+    assert np.all(err[~sat] <= s[:, None].repeat(64, 1)[~sat] // 2)
+    assert nsat > 0  # the full +-127 range does need the saturation
+
+
+def test_p2_protective_range_needs_no_saturation():
+    """[LG] circularity audit / Eq. 11: on [-119, 119] the multiply-add stays
+    in UINT8 by construction: scale <= 16 (the review's number) and the
+    saturation never fires."""
+    Q = _exhaustive_groups(-119, 119)
+    codes, s, a, nsat = oracle.lqq_encode(Q, 64)
+    assert int(s.max()) == 16
+    assert nsat == 0
+    dec = oracle.lqq_decode(codes, s, a, 64)
+    assert np.abs(dec.astype(np.int64) - Q.astype(np.int64)).max() <= 8
+
+
+def test_golden_lqq_examples(golden_dir):
+    """Hand-derived groups from the page's definitions."""
+    path = os.path.join(golden_dir, "lqq_examples.txt")
+    n_cases = 0
+    for line in open(path):
+        if not line.strip() or line.startswith("#"):
+            continue
+        vals, s, a, codes, dec, nsat = [f.split() for f in line.split("|")]
+        v = np.array([int(t) for t in vals], np.int64)
+        # pad to a group of 64 by repeating the first value, which is the
+        # group minimum in every example (code 0, never saturated)
+        g = np.full(64, v[0], np.int64)
+        g[:v.size] = v
+        c, ss, aa, ns = oracle.lqq_encode(g.astype(np.int8).reshape(1, 64), 64)
+        assert int(ss[0, 0]) == int(s[0]), line
+        assert int(aa[0, 0]) == int(a[0]), line
+        assert list(c[0, :v.size]) == [int(t) for t in codes], line
+        d = oracle.lqq_decode(c, ss, aa, 64)
+        assert list(d[0, :v.size]) == [int(t) for t in dec], line
+        assert v[0] == v.min(), line
+        assert ns == int(nsat[0]), line
+        n_cases += 1
+    assert n_cases == 7
+
+
+# ----------------------------------------------------------------- P3 ------
+def test_p3_lossless_when_range_fits_4_bits():
+    """If every group spans at most 15, s = 1 and the decode returns Q
+    exactly, so the W4A8 GEMM is the plain INT8 GEMM (numpy int64 matmul)."""
+    rng = np.random.default_rng(11)
+    N, K, M, g = 48, 384, 7, 64
+    base = rng.integers(-127, 113, size=(N, K // g, 1))
+    Q = (base + rng.integers(0, 16, size=(N, K // g, g))).reshape(N, K)
+    Q = Q.astype(np.int8)
+    codes, s, a, nsat = oracle.lqq_encode(Q, g)
+    assert np.all(s == 1) and nsat == 0
+    dec = oracle.lqq_decode(codes, s, a, g)
+    np.testing.assert_array_equal(dec, Q)
+    X = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    acc = oracle.gemm_i32(X, dec)
+    np.testing.assert_array_equal(acc, X.astype(np.int64) @ Q.astype(np.int64).T)
+
+
+# ----------------------------------------------------------------- P4 ------
+def test_p4_bruteforce_tiny_gemm_and_epilogue():
+    """Tiny shapes: the int32 GEMM of the decoded weights equals an fp64
+    matmul exactly (all values < 2^53) and a pure-Python triple loop; the
+    fp16 epilogue equals numpy's float64 -> float16 rounding of the fp64
+    product acc * sx * sw."""
+    for (M, N, K, g, seed) in [(3, 16, 128, 64, 1), (8, 32, 256, 128, 2),
+                               (5, 16, 256, 64, 3)]:
+        W = wl.gen_weights(N, K, seed)
+        X = wl.gen_activations(M, K, seed + 10, seed + 20)
+        pk = oracle.w4a8_pack(W, g)
+        X8, sx = oracle.quant_sym_rows(X, 127)
+        acc, y, yd = oracle.w4a8_gemm(X8, sx, pk, g)
+        dec = oracle.lqq_decode(pk["codes"], pk["s_u8"], pk["a_u8"], g)
+        ref = X8.astype(np.float64) @ dec.astype(np.float64).T
+        np.testing.assert_array_equal(acc.astype(np.float64), ref)
+        for (mi, ni) in [(0, 0), (M - 1, N - 1), (M // 2, 3)]:
+            s_ = sum(int(X8[mi, k]) * int(dec[ni, k]) for k in range(K))
+            assert acc[mi, ni] == s_
+        v = acc.astype(np.float64) * sx.astype(np.float64)[:, None] * \
+            pk["sw"].astype(np.float64)[None, :]
+        np.testing.assert_array_equal(yd, v)
+        np.testing.assert_array_equal(y, v.astype(np.float16).view(np.uint16))
+
+
+def test_gemm_i32_matches_numpy_random():
+    """Library routine on random operands (integer matmul, exact)."""
+    rng = np.random.default_rng(3)
+    X = rng.integers(-127, 128, size=(9, 640)).astype(np.int8)
+    W = rng.integers(-128, 128, size=(33, 640)).astype(np.int8)
+    np.testing.assert_array_equal(oracle.gemm_i32(X, W),
+                                  X.astype(np.int64) @ W.astype(np.int64).T)
+
+
+# ------------------------------------------------------- fp16 / bf16 -------
+def test_round_f16_matches_numpy():
+    """numpy converts float64 to float16 with one nearest-even rounding."""
+    rng = np.random.default_rng(7)
+    v = np.concatenate([
+        rng.standard_normal(20000) * 10.0 ** rng.integers(-9, 6, 20000),
+        [0.0, -0.0, 65504.0, 65519.99, 65520.0, -65520.0, 1e6, 2.0 ** -24,
+         2.0 ** -25, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 - 2.0 ** -25],
+    ])
+    # exact ties between neighbouring halves
+    h = rng.integers(0, 0x7BFF, 5000).astype(np.uint16).view(np.float16)
+    h2 = (h.view(np.uint16) + 1).view(np.float16)
+    ties = (h.astype(np.float64) + h2.astype(np.float64)) / 2
+    v = np.concatenate([v, ties, -ties])
+    np.testing.assert_array_equal(oracle.round_f16(v),
+                                  v.astype(np.float16).view(np.uint16))
+
+
+def _bf16_value(bits):
+    return (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def test_round_bf16_nearest_even():
+    """bfloat16 rounding: the result is a bfloat16 value, it is the nearer of
+    the two bfloat16 neighbours of v (found by truncating the float32 bit
+    pattern), and exact midpoints go to the even pattern."""
+    rng = np.random.default_rng(8)
+    v = rng.standard_normal(50000) * 10.0 ** rng.integers(-6, 6, 50000)
+    out = oracle.round_bf16(v)
+    r = _bf16_value(out)
+    # neighbours: truncate toward zero at float32 then at bfloat16
+    f = np.abs(v).astype(np.float32)
+    # float32 rounding may cross a bfloat16 boundary, so take a +-1 window
+    t = (f.view(np.uint32) >> 16).astype(np.int64)
+    cands = np.stack([t - 1, t, t + 1, t + 2], 1)
+    cv = _bf16_value(cands.astype(np.uint16)) * np.sign(v)[:, None]
+    dist = np.abs(cv - v[:, None])
+    best = dist.min(1)
+    assert np.all(np.abs(r - v) == best)
+    # midpoints
+    b = rng.integers(0x3800, 0x4700, 5000).astype(np.uint16)
+    lo, hi = _bf16_value(b), _bf16_value(b + 1)
+    mid = (lo + hi) / 2
+    got = oracle.round_bf16(mid)
+    want = np.where(b % 2 == 0, b, b + 1).astype(np.uint16)
+    np.testing.assert_array_equal(got, want)
+
+
+# ------------------------------------------------------------ e4m3 ---------
+def test_e4m3_decode_table():
+    """OCP 8-bit float E4M3 ("fn": no infinities) definition points."""
+    b = np.arange(256, dtype=np.uint8)
+    v = oracle.e4m3_decode(b)
+    assert v[0x00] == 0.0 and np.signbit(v[0x80])
+    assert v[0x01] == 2.0 ** -9 and v[0x07] == 7 * 2.0 ** -9
+    assert v[0x08] == 2.0 ** -6
+    assert v[0x30] == 0.5 and v[0x38] == 1.0 and v[0x40] == 2.0
+    assert v[0x44] == 3.0 and v[0x4E] == 7.0 and v[0x77] == 240.0
+    assert v[0x7E] == 448.0 and v[0xFE] == -448.0
+    assert np.isnan(v[0x7F]) and np.isnan(v[0xFF])
+    assert np.sum(np.isnan(v)) == 2
+    pos = v[:0x7F]
+    assert np.all(np.diff(pos) > 0)
+    np.testing.assert_array_equal(v[0x80:0xFF], -pos)
+
+
+def test_e4m3_encode_nearest_even_saturating():
+    b = np.arange(0x7F, dtype=np.uint8)
+    vals = oracle.e4m3_decode(b)
+    # every finite value round-trips, with sign
+    np.testing.assert_array_equal(oracle.e4m3_encode(vals.astype(np.float32)), b)
+    np.testing.assert_array_equal(oracle.e4m3_encode(-vals.astype(np.float32)),
+                                  b | 0x80)
+    # midpoints go to the even code
+    mids = ((vals[:-1] + vals[1:]) / 2).astype(np.float32)
+    assert np.all(mids.astype(np.float64) == (vals[:-1] + vals[1:]) / 2)
+    got = oracle.e4m3_encode(mids)
+    want = np.where(b[:-1] % 2 == 0, b[:-1], b[:-1] + 1)
+    np.testing.assert_array_equal(got, want)
+    # brute force nearest on random values, saturation above 448
+    rng = np.random.default_rng(9)
+    x = (rng.standard_normal(20000) * 10.0 ** rng.integers(-4, 3, 20000))
+    x = x.astype(np.float32)
+    got = oracle.e4m3_decode(oracle.e4m3_encode(x))
+    d = np.abs(np.abs(x.astype(np.float64))[:, None] - vals[None, :])
+    assert np.all(np.abs(np.abs(got) - np.abs(x)) == d.min(1))
+    big = np.array([448.0, 460.0, 1e4, -1e30], np.float32)
+    np.testing.assert_array_equal(oracle.e4m3_encode(big), [0x7E, 0x7E, 0x7E, 0xFE])
+    assert oracle.e4m3_encode(np.array([np.nan], np.float32))[0] == 0x7F
+
+
+def test_quant_rows_e4m3_scale():
+    """[FQ] abstract (FP8 activations): the largest magnitude maps to 448."""
+    x = wl.gen_activations(6, 512, 1, 2)
+    q, s = oracle.quant_rows_e4m3(x)
+    np.testing.assert_array_equal(s, (np.abs(x).max(1) / np.float32(448)).astype(np.float32))
+    dec = oracle.e4m3_decode(q)
+    assert np.all(np.abs(dec).max(1) == 448.0)
+    rel = np.abs(dec * s[:, None] - x) / np.maximum(np.abs(x), 1e-3)
+    assert np.median(rel) < 0.04
+
+
+# ------------------------------------------------------ per-row quant ------
+def test_quant_sym_rows_properties():
+    rng = np.random.default_rng(12)
+    # exact integers times a power of two come back exactly
+    k = rng.integers(-127, 128, size=(5, 300)).astype(np.float32)
+    k[:, 0] = 127
+    q, s = oracle.quant_sym_rows(k * np.float32(2.0 ** -5), 127)
+    np.testing.assert_array_equal(s, np.float32(2.0 ** -5))
+    np.testing.assert_array_equal(q, k.astype(np.int8))
+    # ties round to even: values at (j + 1/2) * scale with scale = 1
+    t = np.array([[127.0, 0.5, 1.5, 2.5, -0.5, -1.5, 126.5, -126.5]], np.float32)
+    q, s = oracle.quant_sym_rows(t, 127)
+    assert s[0] == 1.0
+    assert list(q[0]) == [127, 0, 2, 2, 0, -2, 126, -126]
+    # all-zero row -> scale 1 and zero codes; sign symmetry; the max hits qmax
+    x = wl.gen_weights(4, 256, 3)
+    x[2] = 0
+    q, s = oracle.quant_sym_rows(x, 119)
+    assert s[2] == 1.0 and np.all(q[2] == 0)
+    qn, sn = oracle.quant_sym_rows(-x, 119)
+    np.testing.assert_array_equal(qn, -q)
+    for r in (0, 1, 3):
+        assert np.abs(q[r]).max() == 119
+        err = np.abs(x[r].astype(np.float64) - q[r] * np.float64(s[r]))
+        assert err.max() <= 0.5 * s[r] * (1 + 1e-6)
+
+
+def test_int4_sign_magnitude():
+    """INT4 per-channel weights of the FP8 variant ([FQ] abstract)."""
+    v = np.arange(-7, 8, dtype=np.int8)
+    c = oracle.int4_sm_codes(v)
+    assert list(c) == [15, 14, 13, 12, 11, 10, 9, 0, 1, 2, 3, 4, 5, 6, 7]
+    np.testing.assert_array_equal(oracle.int4_sm_values(c), v)
+    pk = oracle.w4fp8_pack(wl.gen_weights(32, 256, 4))
+    assert np.abs(pk["q"]).max() == 7
+
+
+# ------------------------------------------------------------ layout -------
+def test_pack_layout_golden(golden_dir):
+    path = os.path.join(golden_dir, "pack_layout.txt")
+    n = 0
+    for line in open(path):
+        if not line.strip() or line.startswith("#"):
+            continue
+        N, K, r, k, byte, hi = map(int, line.split())
+        codes = np.zeros((N, K), np.uint8)
+        codes[r, k] = 0xA
+        wq = oracle.pack_nibbles(codes)
+        nz = np.nonzero(wq)[0]
+        assert list(nz) == [byte], line
+        assert wq[byte] == (0xA << (4 * hi)), line
+        n += 1
+    assert n == 11
+
+
+def test_pack_layout_bijective():
+    rng = np.random.default_rng(4)
+    N, K = 48, 384
+    codes = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    wq = oracle.pack_nibbles(codes)
+    np.testing.assert_array_equal(oracle.unpack_nibbles(wq, N, K), codes)
+    # every nibble of the output is written exactly once
+    seen = []
+    for idx in rng.choice(N * K, 300, replace=False):
+        one = np.zeros(N * K, np.uint8)
+        one[idx] = 1
+        wq1 = oracle.pack_nibbles(one.reshape(N, K))
+        pos = np.nonzero(wq1)[0]
+        assert pos.size == 1 and wq1[pos[0]] in (0x01, 0x10)
+        seen.append(2 * int(pos[0]) + (wq1[pos[0]] == 0x10))
+    assert len(set(seen)) == 300
+
+
+# ------------------------------------------------------- FP8 variant -------
+def test_p6_fp8_reference_exact_special_case():
+    """FP8 e4m3 holds small integers exactly; with unit scales the FP8
+    reference equals the integer GEMM (numpy int64 matmul), and on random
+    FP8 data the unscaled sum equals an fp64 matmul of the decoded values."""
+    rng = np.random.default_rng(13)
+    M, N, K = 6, 32, 256
+    xi = rng.integers(-16, 17, size=(M, K)).astype(np.float32)
+    X8 = oracle.e4m3_encode(xi)
+    np.testing.assert_array_equal(oracle.e4m3_decode(X8), xi)
+    qi = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    ref, pre = oracle.w4fp8_ref(X8, np.ones(M, np.float32), qi, np.ones(N, np.float32))
+    want = xi.astype(np.int64) @ qi.astype(np.int64).T
+    np.testing.assert_array_equal(ref, want.astype(np.float64))
+    x = wl.gen_activations(M, K, 5, 6)
+    X8, sx = oracle.quant_rows_e4m3(x)
+    sw = rng.random(N).astype(np.float32)
+    ref, pre = oracle.w4fp8_ref(X8, sx, qi, sw)
+    np.testing.assert_array_equal(pre, oracle.e4m3_decode(X8) @ qi.astype(np.float64).T)
+    np.testing.assert_allclose(ref, pre * sx[:, None].astype(np.float64) *
+                               sw[None, :].astype(np.float64), rtol=1e-15)
+
+
+def test_generator_deterministic():
+    a = wl.gen_weights(64, 128, 7)
+    b = wl.gen_weights(64, 128, 7)
+    np.testing.assert_array_equal(a, b)
+    x = wl.gen_activations(4, 1000, 1, 2)
+    ch = wl.outlier_channels(1000, 2)
+    assert ch.size == 10 and np.unique(ch).size == 10
+    assert abs(float(a.std()) - 0.02) < 0.002
