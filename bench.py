@@ -1,0 +1,242 @@
+"""Benchmark: W4A8 GEMM TOPS and weight-stream GB/s on the Llama-2-70B linear
+shapes (N=28672,K=8192 and N=8192,K=28672; group 128) for M in
+{1, 16, 128, 1024, 4096}, on one MI355X.
+
+One step = the ten W4A8 GEMMs of that sweep (fp16 output, fused epilogue),
+inputs resident in HBM.  Each GEMM slot owns a distinct copy of its packed
+weights (10 x 121 MB), so a slot's weights are evicted from the 256 MB
+Infinity Cache by the others before they are read again.
+
+Prints one JSON line.  `value` = whole-step TOPS (sum of 2*M*N*K over the
+step / step time).  Per-slot kernel times come from HIP events recorded on
+the stream the kernels run on.  `cpu_baseline` times the CPU oracle (decode
++ int32 GEMM + epilogue) on a bounded sample of the same sweep.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = ("W4A8 GEMM TOPS + weight-stream GB/s at Llama-7B/70B linear shapes, "
+          "M=1..4096")
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
+FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
+CFG = 3
+MS = (1, 16, 128, 1024, 4096)
+
+
+def weight_bytes(N, K, g):
+    return N * K // 2 + 2 * N * (K // g)
+
+
+def algo_bytes(M, N, K, g):
+    """Weights + scales + X + sx + Y (fp16): what the method must move."""
+    return weight_bytes(N, K, g) + 4 * N + M * K + 4 * M + 2 * M * N
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--only", default="", help="run one slot, e.g. upgate:M4096")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-fp8", action="store_true")
+    p.add_argument("--cpu-sample-cols", type=int, default=256)
+    return p.parse_args()
+
+
+def cpu_baseline(slots_desc, ncols):
+    """Oracle (test infrastructure) timed on the host cores: identity decode,
+    int32 GEMM and fp16 epilogue for every slot of the sweep, restricted to
+    `ncols` output channels per slot; scaled to the full step."""
+    import numpy as np
+    import oracle
+    import workloads as wl
+    total_ops_full = 0.0
+    t_scaled = 0.0
+    per_pair = {}
+    for (tag, M, N, K, g, pair) in slots_desc:
+        if pair not in per_pair:
+            # numpy draws row-major: a smaller draw with the same seed is
+            # exactly the leading rows of the full matrices the GPU uses
+            W = wl.gen_weights(ncols, K, wl.seed_w(CFG, pair))
+            X = wl.gen_activations(max(MS), K, wl.seed_x(CFG, max(MS)),
+                                   wl.seed_outliers(CFG))
+            X8_all, sx_all = oracle.quant_sym_rows(X, 127)
+            per_pair[pair] = (oracle.w4a8_pack(W, g), X8_all, sx_all)
+        pk, X8_all, sx_all = per_pair[pair]
+        X8, sx = X8_all[:M], sx_all[:M]
+        t0 = time.perf_counter()
+        oracle.w4a8_gemm(X8, sx, pk, g)
+        dt = time.perf_counter() - t0
+        t_scaled += dt * (N / ncols)
+        total_ops_full += 2.0 * M * N * K
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
+    return {"value": total_ops_full / t_scaled / 1e12, "unit": "TOPS", "cores": threads,
+            "kind": "oracle",
+            "sample": f"each of the 10 GEMMs of the sweep on {ncols} of its N output "
+                      f"channels (decode + int32 GEMM + fp16 epilogue), time scaled by "
+                      f"N/{ncols}; {t_scaled:.1f} s projected for one full step"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
+              "multi-GPU runs are not part of this library", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import w4a8_quantized_gemm_amd as w4
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    pairs = wl.nk_pairs(CFG)           # [(28672, 8192), (8192, 28672)]
+    tags = {pairs[0]: "upgate", pairs[1]: "down"}
+    g = 128
+
+    # ---- inputs: packed weights (one copy per slot), activations per shape
+    slots = []
+    for pi, (N, K) in enumerate(pairs):
+        Wf = torch.from_numpy(wl.gen_weights(N, K, wl.seed_w(CFG, pi))).to(dev)
+        pk = w4.pack(Wf, group=g)
+        del Wf
+        Xf = torch.from_numpy(wl.gen_activations(max(MS), K, wl.seed_x(CFG, max(MS)),
+                                                 wl.seed_outliers(CFG))).to(dev)
+        Xq, sx = w4.quant_act(Xf)
+        del Xf
+        for M in MS:
+            name = f"{tags[(N, K)]}:M{M}"
+            if args.only and args.only != name:
+                continue
+            copy = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in pk.items()}
+            Y = torch.empty((M, N), dtype=torch.float16, device=dev)
+            slots.append({"name": name, "M": M, "N": N, "K": K, "pair": pi, "pk": copy,
+                          "X": Xq[:M], "sx": sx[:M], "Y": Y})
+        del pk
+    torch.cuda.synchronize()
+    if not slots:
+        print(f"unknown slot {args.only}", file=sys.stderr)
+        sys.exit(2)
+
+    def step(evs=None):
+        for i, s in enumerate(slots):
+            if evs is not None:
+                evs[i][0].record(stream)
+            w4.gemm(s["X"], s["sx"], s["pk"], out=s["Y"])
+            if evs is not None:
+                evs[i][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
+            for _ in slots] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+
+    sweep = []
+    total_ops = 0.0
+    kern_ms_sum = 0.0
+    for i, s in enumerate(slots):
+        times = np.array([evs[k][i][0].elapsed_time(evs[k][i][1]) for k in range(args.steps)])
+        us = float(np.mean(times) * 1e3)
+        M, N, K = s["M"], s["N"], s["K"]
+        ops = 2.0 * M * N * K
+        total_ops += ops
+        kern_ms_sum += us / 1e3
+        wgbs = weight_bytes(N, K, g) / (us * 1e-6) / 1e9
+        sweep.append({"slot": s["name"], "M": M, "N": N, "K": K, "group": g,
+                      "us_mean": round(us, 2), "us_min": round(float(times.min() * 1e3), 2),
+                      "tops": round(ops / (us * 1e-6) / 1e12, 2),
+                      "weight_stream_gbs": round(wgbs, 1),
+                      "hbm_frac_algo": round(algo_bytes(M, N, K, g) / (us * 1e-6) / 1e9
+                                             / HBM_PEAK_GBS, 4),
+                      "mfma_frac": round(ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4)})
+
+    value = total_ops / (ms_per_step * 1e-3) / 1e12
+
+    def roof(slot_name, bound):
+        e = next((x for x in sweep if x["slot"] == slot_name), None)
+        if e is None:
+            return None
+        if bound == "mfma":
+            a = 2.0 * e["M"] * e["N"] * e["K"] / (e["us_mean"] * 1e-6) / 1e12
+            return {"bound": "mfma", "achieved": round(a, 2), "peak": INT8_PEAK_TOPS,
+                    "unit": "TFLOP/s", "frac": round(a / INT8_PEAK_TOPS, 4),
+                    "traffic": None, "kernel_slot": slot_name,
+                    "us_per_launch": e["us_mean"]}
+        a = algo_bytes(e["M"], e["N"], e["K"], g) / (e["us_mean"] * 1e-6) / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel_slot": slot_name,
+                "us_per_launch": e["us_mean"]}
+
+    # dominant kernel: the slot with the largest share of the step
+    dom = max(sweep, key=lambda e: e["us_mean"])
+    dom_bound = "mfma" if dom["M"] >= 1024 else "hbm"
+    out = {
+        "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "llama2-70b linear sweep (W4A8, group 128)",
+                   "shapes_NK": [list(p) for p in pairs], "M": list(MS),
+                   "slots": [s["name"] for s in slots], "out": "fp16",
+                   "weights_per_slot_MB": round(weight_bytes(*pairs[0], g) / 1e6, 1),
+                   "parallelism": "single GPU"},
+        "roofline": roof(dom["slot"], dom_bound),
+        "roofline_decode": roof("upgate:M16", "hbm") or roof("down:M16", "hbm"),
+        "kernel_ms_per_step": round(kern_ms_sum, 4),
+        "sweep": sweep,
+    }
+
+    # ---- FP8 variant (INT4 weights x e4m3 activations), reported alongside
+    if not args.no_fp8 and not args.only:
+        sh = wl.CONFIGS[4].shapes[0]
+        Wf = torch.from_numpy(wl.gen_weights(sh.N, sh.K, wl.seed_w(4))).to(dev)
+        pk8 = w4.pack(Wf, mode=w4.PACK_INT4_SYM)
+        del Wf
+        Xf = torch.from_numpy(wl.gen_activations(sh.M, sh.K, wl.seed_x(4),
+                                                 wl.seed_outliers(4))).to(dev)
+        X8, sx8 = w4.quant_act_fp8(Xf)
+        Yb = torch.empty((sh.M, sh.N), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            w4.gemm_fp8(X8, sx8, pk8, out=Yb)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record(stream)
+        for _ in range(reps):
+            w4.gemm_fp8(X8, sx8, pk8, out=Yb)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+        tf = 2.0 * sh.M * sh.N * sh.K / (us * 1e-6) / 1e12
+        out["variant_fp8"] = {"workload": "int4-fp8 2048x8192x8192, bf16 out",
+                              "us": round(us, 2), "tflops": round(tf, 2),
+                              "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4)}
+
+    if not args.no_cpu_baseline and not args.only:
+        desc = [(s["name"], s["M"], s["N"], s["K"], g, s["pair"]) for s in slots]
+        out["cpu_baseline"] = cpu_baseline(desc, args.cpu_sample_cols)
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,129 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry
+point include/w4a8.h declares, and rejects bad arguments on the host before
+any HIP call (pointers below are fake addresses that are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a8.h")
+
+w4 = pytest.importorskip("w4a8_quantized_gemm_amd")
+lib = w4.lib
+
+OK, NULL, SHAPE, ALIGN, WS, UNSUP, HIP = range(7)
+A = 0x10000  # a 16-byte-aligned fake device address, never dereferenced
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return set(re.findall(r"^\s*(?:w4a8_status_t|size_t|int|const char\*)\s+(\w+)\s*\(",
+                          text, re.M))
+
+
+def test_exports_match_header():
+    names = declared_functions()
+    assert names == set(w4.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_layout_version_and_strings():
+    assert lib.w4a8_layout_version() == 1
+    for s in range(7):
+        assert lib.w4a8_status_str(s)
+    assert lib.w4a8_status_str(99) == b"unknown status"
+    assert lib.w4a8_workspace_size(16, 4096, 4096, 0) == 0
+
+
+def pack(W=A, N=32, K=256, g=64, qmax=127, mode=0, wq=A, s=A, a=A, sw=A):
+    return lib.w4a8_pack(W, N, K, g, qmax, mode, wq, s, a, sw, None)
+
+
+def test_pack_validation():
+    assert pack(W=None) == NULL
+    assert pack(wq=None) == NULL
+    assert pack(s=None) == NULL
+    assert pack(mode=1, s=None, a=None, g=0, qmax=0) != NULL  # INT4: s/a unused
+    assert pack(N=0, W=None, wq=None) == OK  # empty: pointers not read
+    assert pack(mode=7) == UNSUP
+    assert pack(K=200) == SHAPE
+    assert pack(K=0) == SHAPE
+    assert pack(N=24) == SHAPE
+    assert pack(N=-16) == SHAPE
+    assert pack(g=32) == SHAPE
+    assert pack(qmax=0) == SHAPE
+    assert pack(qmax=128) == SHAPE
+    assert pack(W=A + 4) == ALIGN
+    assert pack(wq=A + 8) == ALIGN
+    assert pack(N=0) == OK  # empty problem, nothing launched
+
+
+def gemm(X=A, sx=A, wq=A, s=A, a=A, sw=A, Y=A, out=0, M=16, N=32, K=256, g=64,
+         splitk=0, ws=None, wsb=0):
+    return lib.w4a8_gemm(X, sx, wq, s, a, sw, Y, out, M, N, K, g, splitk, ws, wsb, None)
+
+
+def test_gemm_validation():
+    assert gemm(X=None) == NULL
+    assert gemm(Y=None) == NULL
+    assert gemm(sx=None) == NULL
+    assert gemm(sx=None, sw=None, out=1, M=0) == OK  # int32 output needs no scales
+    assert gemm(out=5) == UNSUP
+    assert gemm(M=-1) == SHAPE
+    assert gemm(K=192) == SHAPE
+    assert gemm(N=40) == SHAPE
+    assert gemm(g=256) == SHAPE
+    assert gemm(splitk=3) == SHAPE
+    assert gemm(splitk=4, K=256) == SHAPE  # more slices than K tiles
+    assert gemm(splitk=32, K=8192) == SHAPE
+    assert gemm(X=A + 1) == ALIGN
+    assert gemm(Y=A + 2) == ALIGN
+    assert gemm(sx=A + 2) == ALIGN
+    assert gemm(M=0) == OK
+    assert gemm(N=0) == OK
+    assert gemm(M=0, X=None, Y=None) == OK  # empty: pointers not read
+    assert gemm(M=0, K=100) == SHAPE
+
+
+def fp8(X=A, sx=A, wq=A, sw=A, Y=A, out=0, M=16, N=32, K=256, splitk=0):
+    return lib.w4fp8_gemm(X, sx, wq, sw, Y, out, M, N, K, splitk, None, 0, None)
+
+
+def test_fp8_gemm_validation():
+    assert fp8(X=None) == NULL
+    assert fp8(sw=None) == NULL
+    assert fp8(out=2) == UNSUP
+    assert fp8(K=100) == SHAPE
+    assert fp8(N=8) == SHAPE
+    assert fp8(wq=A + 4) == ALIGN
+    assert fp8(M=0) == OK
+
+
+def test_quant_act_validation():
+    f = lib.w4a8_quant_act
+    g = lib.w4fp8_quant_act
+    for fn in (f, g):
+        assert fn(None, 4, 64, A, A, None) == NULL
+        assert fn(A, 4, 60, A, A, None) == SHAPE
+        assert fn(A, -1, 64, A, A, None) == SHAPE
+        assert fn(A + 4, 4, 64, A, A, None) == ALIGN
+        assert fn(A, 0, 64, A, A, None) == OK
+
+
+def test_valid_call_without_gpu_reports_hip_error():
+    """A call that passes validation reaches the HIP runtime; with no GPU
+    the device query fails and the status is W4A8_ERR_HIP, not a crash."""
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    st = gemm()
+    assert st in (HIP, UNSUP)
+    if st == HIP:
+        assert lib.w4a8_last_hip_error() != 0

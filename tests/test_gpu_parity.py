@@ -1,0 +1,254 @@
+"""GPU parity: the HIP path against the CPU oracle on the same seeded inputs.
+
+Bars: bit-exact for packed bytes, codes, scales and int32 accumulators;
+fp16 output within 1 ulp of the oracle's once-rounded double result; FP8
+variant within relative Frobenius error 1e-3 of the double reference (the
+float32 output), and of the bfloat16-rounded double reference (the bfloat16
+output).  Small cases run against the full oracle; the Llama-shaped
+workloads run in the launch configuration the benchmark uses and are
+checked on sampled rows and columns (the oracle quantises per row, so a row
+sample is computed exactly as in the full problem).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import w4a8_quantized_gemm_amd as w4  # noqa: E402  (must load: no fallback)
+
+DEV = "cuda:0"
+
+
+def to_dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+def poison(shape, dtype):
+    t = torch.empty(shape, dtype=dtype, device=DEV)
+    t.view(torch.uint8).fill_(0xAB)
+    return t
+
+
+def f16_ulp_diff(a_bits, b_bits):
+    def ordered(u):
+        u = u.astype(np.int64)
+        mag = u & 0x7FFF
+        return np.where(u & 0x8000, -mag, mag)
+    return np.abs(ordered(a_bits) - ordered(b_bits))
+
+
+def rel_fro(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def bf16_bits_of(t):
+    return host(t.view(torch.int16)).view(np.uint16)
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------ packing ------
+@pytest.mark.parametrize("N,K,g,qmax", [(256, 512, 64, 127), (48, 384, 64, 119),
+                                        (64, 1024, 128, 127), (4096, 4096, 64, 127)])
+def test_pack_lqq_parity(N, K, g, qmax):
+    say(f"pack lqq N={N} K={K} g={g} qmax={qmax}")
+    W = wl.gen_weights(N, K, 100 + N)
+    W[3] = 0.0  # all-zero channel
+    ref = oracle.w4a8_pack(W, g, qmax)
+    pk = w4.pack(to_dev(W), group=g, qmax=qmax)
+    np.testing.assert_array_equal(host(pk["sw"]), ref["sw"])
+    np.testing.assert_array_equal(host(pk["s_u8"]), ref["s_u8"])
+    np.testing.assert_array_equal(host(pk["a_u8"]), ref["a_u8"])
+    np.testing.assert_array_equal(host(pk["wq"]), ref["wq"])
+
+
+@pytest.mark.parametrize("N,K", [(256, 512), (96, 1024)])
+def test_pack_int4_parity(N, K):
+    say(f"pack int4 N={N} K={K}")
+    W = wl.gen_weights(N, K, 200 + N)
+    ref = oracle.w4fp8_pack(W)
+    pk = w4.pack(to_dev(W), mode=w4.PACK_INT4_SYM)
+    np.testing.assert_array_equal(host(pk["sw"]), ref["sw"])
+    np.testing.assert_array_equal(host(pk["wq"]), ref["wq"])
+
+
+# ------------------------------------------------- activation quant --------
+@pytest.mark.parametrize("M,K", [(1, 512), (16, 4096), (33, 1024)])
+def test_quant_act_parity(M, K):
+    say(f"quant act M={M} K={K}")
+    X = wl.gen_activations(M, K, 300 + M, 301)
+    if M > 2:
+        X[1] = 0.0
+    q8, s8 = oracle.quant_sym_rows(X, 127)
+    Xq, sx = w4.quant_act(to_dev(X))
+    np.testing.assert_array_equal(host(sx), s8)
+    np.testing.assert_array_equal(host(Xq), q8)
+    qf, sf = oracle.quant_rows_e4m3(X)
+    Xf, sxf = w4.quant_act_fp8(to_dev(X))
+    np.testing.assert_array_equal(host(sxf), sf)
+    np.testing.assert_array_equal(host(Xf), qf)
+
+
+# ------------------------------------------------------- W4A8 GEMM ---------
+def _small_problem(M, N, K, g, seed):
+    W = wl.gen_weights(N, K, seed)
+    X = wl.gen_activations(M, K, seed + 1, seed + 2)
+    pk_ref = oracle.w4a8_pack(W, g)
+    X8, sx = oracle.quant_sym_rows(X, 127)
+    acc, y, _ = oracle.w4a8_gemm(X8, sx, pk_ref, g)
+    pk = {"wq": to_dev(pk_ref["wq"]), "s_u8": to_dev(pk_ref["s_u8"]),
+          "a_u8": to_dev(pk_ref["a_u8"]), "sw": to_dev(pk_ref["sw"]),
+          "N": N, "K": K, "group": g}
+    return to_dev(X8), to_dev(sx), pk, acc, y
+
+
+@pytest.mark.parametrize("M", list(range(1, 18)) + [33, 100])
+@pytest.mark.parametrize("N,K,g", [(96, 640, 64), (80, 512, 128)])
+def test_w4a8_gemm_parity(M, N, K, g):
+    say(f"w4a8 gemm M={M} N={N} K={K} g={g}")
+    X8, sx, pk, acc, y = _small_problem(M, N, K, g, 1000 + M)
+    Yi = poison((M, N), torch.int32)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, out=Yi)
+    np.testing.assert_array_equal(host(Yi), acc)
+    Yh = poison((M, N), torch.float16)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_F16, out=Yh)
+    d = f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y)
+    assert d.max() <= 1
+
+
+def test_splitk_invariance_and_determinism():
+    say("w4a8 split-K sweep M=16 N=256 K=2048")
+    X8, sx, pk, acc, _ = _small_problem(16, 256, 2048, 64, 77)
+    outs = []
+    for sk in (1, 2, 4, 8, 16, 0, 0):
+        Y = poison((16, 256), torch.int32)
+        w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, splitk=sk, out=Y)
+        outs.append(host(Y))
+    for o in outs:
+        np.testing.assert_array_equal(o, acc)
+
+
+def test_empty_problem_touches_nothing():
+    X8, sx, pk, acc, _ = _small_problem(4, 32, 256, 64, 5)
+    Y = poison((4, 32), torch.float16)
+    w4.gemm(X8[:0], sx[:0], pk, out=Y[:0])
+    assert np.all(host(Y.view(torch.uint8)) == 0xAB)
+
+
+# ------------------------------------------------------ W4FP8 GEMM ---------
+@pytest.mark.parametrize("M", [1, 16, 37])
+def test_w4fp8_gemm_parity(M):
+    N, K = 96, 1024
+    say(f"w4fp8 gemm M={M} N={N} K={K}")
+    W = wl.gen_weights(N, K, 400 + M)
+    X = wl.gen_activations(M, K, 401 + M, 402)
+    pk_ref = oracle.w4fp8_pack(W)
+    X8, sx = oracle.quant_rows_e4m3(X)
+    ref, _ = oracle.w4fp8_ref(X8, sx, pk_ref["q"], pk_ref["sw"])
+    pk = {"wq": to_dev(pk_ref["wq"]), "sw": to_dev(pk_ref["sw"]), "N": N, "K": K}
+    Yf = poison((M, N), torch.float32)
+    w4.gemm_fp8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F32, out=Yf)
+    err = rel_fro(host(Yf), ref)
+    say(f"  f32 vs fp64 rel fro {err:.3e}")
+    assert err <= 1e-3
+    Yb = poison((M, N), torch.bfloat16)
+    w4.gemm_fp8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_BF16, out=Yb)
+    got = bf16_bits_of(Yb)
+    want = oracle.round_bf16(ref)
+    gv = (got.astype(np.uint32) << 16).view(np.float32)
+    wv = (want.astype(np.uint32) << 16).view(np.float32)
+    err_b = rel_fro(gv, wv)
+    say(f"  bf16 vs bf16(fp64) rel fro {err_b:.3e}; vs fp64 {rel_fro(gv, ref):.3e}")
+    assert err_b <= 1e-3
+
+
+# ------------------------------------------- Llama-shaped workloads --------
+_FULL = [(1, sh) for sh in wl.CONFIGS[1].shapes] + \
+        [(2, sh) for sh in wl.CONFIGS[2].shapes] + \
+        [(3, sh) for sh in wl.CONFIGS[3].shapes]
+
+_packed_cache = {}
+
+
+def _device_packed(cfg, sh):
+    key = (cfg, sh.N, sh.K, sh.group)
+    if key not in _packed_cache:
+        _packed_cache.clear()
+        pair = wl.nk_pairs(cfg).index((sh.N, sh.K))
+        W = wl.gen_weights(sh.N, sh.K, wl.seed_w(cfg, pair))
+        pk = w4.pack(to_dev(W), group=sh.group)
+        torch.cuda.synchronize()
+        _packed_cache[key] = (W, pk)
+    return _packed_cache[key]
+
+
+@pytest.mark.parametrize("cfg,sh", _FULL, ids=[s.name for _, s in _FULL])
+def test_llama_shapes_sampled(cfg, sh):
+    say(f"full-size {sh.name}: M={sh.M} N={sh.N} K={sh.K} g={sh.group}")
+    W, pk = _device_packed(cfg, sh)
+    X = wl.gen_activations(sh.M, sh.K, wl.seed_x(cfg, sh.M), wl.seed_outliers(cfg))
+    Xq, sx = w4.quant_act(to_dev(X))
+    Yh = w4.gemm(Xq, sx, pk, out_type=w4.OUT_F16)
+    Yi = w4.gemm(Xq, sx, pk, out_type=w4.OUT_I32)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(sh.M * 7 + sh.N)
+    nsel = np.sort(rng.choice(sh.N, 48, replace=False))
+    msel = np.arange(sh.M) if sh.M <= 16 else np.sort(rng.choice(sh.M, 12, replace=False))
+    # weights: oracle packing of the sampled channels vs the device's bytes
+    ref = oracle.w4a8_pack(W[nsel], sh.group)
+    codes_dev = oracle.unpack_nibbles(host(pk["wq"]), sh.N, sh.K)[nsel]
+    np.testing.assert_array_equal(codes_dev, ref["codes"])
+    np.testing.assert_array_equal(host(pk["s_u8"])[nsel], ref["s_u8"])
+    np.testing.assert_array_equal(host(pk["a_u8"])[nsel], ref["a_u8"])
+    np.testing.assert_array_equal(host(pk["sw"])[nsel], ref["sw"])
+    # activations: sampled tokens
+    X8, sx8 = oracle.quant_sym_rows(X[msel], 127)
+    np.testing.assert_array_equal(host(Xq)[msel], X8)
+    np.testing.assert_array_equal(host(sx)[msel], sx8)
+    # GEMM on the sample
+    acc, y, _ = oracle.w4a8_gemm(X8, sx8, ref, sh.group)
+    np.testing.assert_array_equal(host(Yi)[np.ix_(msel, nsel)], acc)
+    yh = host(Yh.view(torch.int16)).view(np.uint16)[np.ix_(msel, nsel)]
+    assert f16_ulp_diff(yh, y).max() <= 1
+
+
+def test_fp8_variant_full_size_sampled():
+    sh = wl.CONFIGS[4].shapes[0]
+    say(f"full-size {sh.name}: M={sh.M} N={sh.N} K={sh.K}")
+    W = wl.gen_weights(sh.N, sh.K, wl.seed_w(4))
+    X = wl.gen_activations(sh.M, sh.K, wl.seed_x(4), wl.seed_outliers(4))
+    pk = w4.pack(to_dev(W), mode=w4.PACK_INT4_SYM)
+    Xq, sx = w4.quant_act_fp8(to_dev(X))
+    Yf = w4.gemm_fp8(Xq, sx, pk, out_type=w4.OUT_F32)
+    Yb = w4.gemm_fp8(Xq, sx, pk, out_type=w4.OUT_BF16)
+    rng = np.random.default_rng(4)
+    nsel = np.sort(rng.choice(sh.N, 64, replace=False))
+    msel = np.sort(rng.choice(sh.M, 24, replace=False))
+    ref_pk = oracle.w4fp8_pack(W[nsel])
+    codes_dev = oracle.unpack_nibbles(host(pk["wq"]), sh.N, sh.K)[nsel]
+    np.testing.assert_array_equal(codes_dev, ref_pk["codes"])
+    X8, sx8 = oracle.quant_rows_e4m3(X[msel])
+    np.testing.assert_array_equal(host(Xq)[msel], X8)
+    ref, _ = oracle.w4fp8_ref(X8, sx8, ref_pk["q"], ref_pk["sw"])
+    err = rel_fro(host(Yf)[np.ix_(msel, nsel)], ref)
+    gv = (bf16_bits_of(Yb)[np.ix_(msel, nsel)].astype(np.uint32) << 16).view(np.float32)
+    wv = (oracle.round_bf16(ref).astype(np.uint32) << 16).view(np.float32)
+    err_b = rel_fro(gv, wv)
+    say(f"  f32 rel fro {err:.3e}  bf16 vs bf16(ref) {err_b:.3e}  bf16 vs ref {rel_fro(gv, ref):.3e}")
+    assert err <= 1e-3 and err_b <= 1e-3

@@ -1,0 +1,196 @@
+"""Python binding of libw4a8.so (W4A8 / W4FP8 GEMM for MI355X, gfx950).
+
+Argument marshalling only: every step runs in the HIP kernels of the shared
+library.  torch is used for device memory and the current stream.  If the
+library is not built, importing this package raises ImportError -- there is
+no fallback path.
+
+The C entry points are available unchanged as ``lib.<name>``; the helpers
+below take torch tensors, check dtypes/devices/contiguity, and raise
+``W4A8Error`` on a non-OK status.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libw4a8.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with "
+        "`python w4a8_quantized_gemm_amd/build.py` (hipcc, gfx950)")
+
+# torch carries its own HIP runtime (same soname as the system one).  The
+# library must bind to that runtime, since the device pointers and streams it
+# receives belong to it: load torch first so the dynamic linker reuses it.
+import torch  # noqa: E402,F401
+
+lib = ctypes.CDLL(LIB_PATH)
+
+W4A8_OK = 0
+STATUS_NAMES = {0: "W4A8_OK", 1: "W4A8_ERR_NULL_PTR", 2: "W4A8_ERR_SHAPE",
+                3: "W4A8_ERR_ALIGNMENT", 4: "W4A8_ERR_WORKSPACE",
+                5: "W4A8_ERR_UNSUPPORTED", 6: "W4A8_ERR_HIP"}
+PACK_LQQ, PACK_INT4_SYM = 0, 1
+OUT_F16, OUT_I32 = 0, 1
+OUT_BF16, OUT_F32 = 0, 1
+LAYOUT_VERSION = 1
+
+EXPORTS = ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act",
+           "w4a8_workspace_size", "w4a8_gemm", "w4fp8_gemm",
+           "w4a8_status_str", "w4a8_last_hip_error", "w4a8_layout_version")
+
+_P, _I, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+lib.w4a8_pack.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
+lib.w4a8_quant_act.argtypes = [_P, _I, _I, _P, _P, _P]
+lib.w4fp8_quant_act.argtypes = [_P, _I, _I, _P, _P, _P]
+lib.w4a8_workspace_size.argtypes = [_I, _I, _I, _I]
+lib.w4a8_workspace_size.restype = _Z
+lib.w4a8_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]
+lib.w4fp8_gemm.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]
+lib.w4a8_status_str.argtypes = [_I]
+lib.w4a8_status_str.restype = ctypes.c_char_p
+lib.w4a8_last_hip_error.restype = _I
+lib.w4a8_layout_version.restype = _I
+for _n in ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act", "w4a8_gemm", "w4fp8_gemm"):
+    getattr(lib, _n).restype = _I
+
+assert lib.w4a8_layout_version() == LAYOUT_VERSION
+
+
+class W4A8Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = lib.w4a8_status_str(status).decode()
+        extra = ""
+        if status == 6:
+            extra = f" (hipError {lib.w4a8_last_hip_error()})"
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {msg}{extra}")
+
+
+def _check(status: int, where: str):
+    if status != W4A8_OK:
+        raise W4A8Error(status, where)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(t, dtype, name):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU device")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ------------------------------------------------------------------ API ----
+
+def pack(W, group: int = 64, qmax: int = 127, mode: int = PACK_LQQ, stream=None):
+    """w4a8_pack on a float32 [N][K] device tensor.
+
+    Returns a dict with wq (uint8 [N*K/2]), sw (float32 [N]) and, in LQQ
+    mode, s_u8 / a_u8 (uint8 [N][K/group])."""
+    torch = _torch()
+    _need(W, torch.float32, "W")
+    N, K = W.shape
+    dev = W.device
+    wq = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+    sw = torch.empty(N, dtype=torch.float32, device=dev)
+    out = {"wq": wq, "sw": sw, "N": N, "K": K, "mode": mode}
+    s_u8 = a_u8 = None
+    if mode == PACK_LQQ:
+        s_u8 = torch.empty((N, K // group), dtype=torch.uint8, device=dev)
+        a_u8 = torch.empty((N, K // group), dtype=torch.uint8, device=dev)
+        out.update(s_u8=s_u8, a_u8=a_u8, group=group)
+    _check(lib.w4a8_pack(_ptr(W), N, K, group, qmax, mode, _ptr(wq), _ptr(s_u8),
+                         _ptr(a_u8), _ptr(sw), _stream(stream)), "w4a8_pack")
+    return out
+
+
+def quant_act(X, stream=None):
+    """Per-token INT8: (Xq int8 [M][K], sx float32 [M])."""
+    torch = _torch()
+    _need(X, torch.float32, "X")
+    M, K = X.shape
+    Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
+    sx = torch.empty(M, dtype=torch.float32, device=X.device)
+    _check(lib.w4a8_quant_act(_ptr(X), M, K, _ptr(Xq), _ptr(sx), _stream(stream)),
+           "w4a8_quant_act")
+    return Xq, sx
+
+
+def quant_act_fp8(X, stream=None):
+    """Per-token e4m3: (Xq uint8 [M][K], sx float32 [M])."""
+    torch = _torch()
+    _need(X, torch.float32, "X")
+    M, K = X.shape
+    Xq = torch.empty((M, K), dtype=torch.uint8, device=X.device)
+    sx = torch.empty(M, dtype=torch.float32, device=X.device)
+    _check(lib.w4fp8_quant_act(_ptr(X), M, K, _ptr(Xq), _ptr(sx), _stream(stream)),
+           "w4fp8_quant_act")
+    return Xq, sx
+
+
+def workspace_size(M: int, N: int, K: int, splitk: int = 0) -> int:
+    return int(lib.w4a8_workspace_size(M, N, K, splitk))
+
+
+def gemm(Xq, sx, packed, out_type: int = OUT_F16, splitk: int = 0, out=None,
+         workspace=None, stream=None):
+    """w4a8_gemm: Y [M][N] float16 (OUT_F16) or int32 (OUT_I32)."""
+    torch = _torch()
+    _need(Xq, torch.int8, "Xq")
+    M, K = Xq.shape
+    N = packed["N"]
+    if packed["K"] != K:
+        raise ValueError("K of X and of the packed weights differ")
+    if out_type == OUT_F16:
+        _need(sx, torch.float32, "sx")
+    ydt = torch.float16 if out_type == OUT_F16 else torch.int32
+    Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
+    _need(Y, ydt, "out")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.w4a8_gemm(_ptr(Xq), _ptr(sx), _ptr(packed["wq"]), _ptr(packed["s_u8"]),
+                         _ptr(packed["a_u8"]), _ptr(packed["sw"]), _ptr(Y), out_type, M, N,
+                         K, packed["group"], splitk, _ptr(workspace), ws_bytes,
+                         _stream(stream)), "w4a8_gemm")
+    return Y
+
+
+def gemm_fp8(Xq, sx, packed, out_type: int = OUT_BF16, splitk: int = 0, out=None,
+             workspace=None, stream=None):
+    """w4fp8_gemm: Y [M][N] bfloat16 (OUT_BF16) or float32 (OUT_F32)."""
+    torch = _torch()
+    _need(Xq, torch.uint8, "Xq")
+    _need(sx, torch.float32, "sx")
+    M, K = Xq.shape
+    N = packed["N"]
+    if packed["K"] != K:
+        raise ValueError("K of X and of the packed weights differ")
+    ydt = torch.bfloat16 if out_type == OUT_BF16 else torch.float32
+    Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
+    _need(Y, ydt, "out")
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.w4fp8_gemm(_ptr(Xq), _ptr(sx), _ptr(packed["wq"]), _ptr(packed["sw"]),
+                          _ptr(Y), out_type, M, N, K, splitk, _ptr(workspace), ws_bytes,
+                          _stream(stream)), "w4fp8_gemm")
+    return Y

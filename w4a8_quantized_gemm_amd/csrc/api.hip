@@ -1,0 +1,178 @@
+// C ABI of libw4a8 (declared in include/w4a8.h): argument validation on the
+// host, then kernel dispatch on the caller's stream.  Validation makes no
+// HIP call, so every error path below can be exercised without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "launch.h"
+#include "w4a8.h"
+
+#define W4A8_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+w4a8_status_t hip_status(hipError_t e) {
+    if (e == hipSuccess) return W4A8_OK;
+    g_last_hip_error = (int)e;
+    return W4A8_ERR_HIP;
+}
+
+// Per-device cache: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_arch_ok[64];
+
+w4a8_status_t check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e);
+    if (dev < 0 || dev >= 64) return W4A8_ERR_UNSUPPORTED;
+    int c = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (c == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return hip_status(e);
+        c = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+        g_arch_ok[dev].store(c, std::memory_order_relaxed);
+    }
+    return c == 1 ? W4A8_OK : W4A8_ERR_UNSUPPORTED;
+}
+
+bool valid_nk(int N, int K) { return N >= 0 && K > 0 && K % 128 == 0 && N % 16 == 0; }
+bool valid_group(int g) { return g == 64 || g == 128; }
+
+int k_tiles(int K) { return K / 128; }
+
+// Split of K across the waves of one workgroup, and weight tiles per wave.
+// Aim: enough waves in flight to cover HBM latency on 256 CUs without
+// shrinking each wave's K range below a few tiles.
+w4a8::StreamCfg choose_stream(int M, int N, int K, int splitk) {
+    w4a8::StreamCfg c;
+    const int mt = (M + 15) / 16;
+    c.nt_per_wave = (N % 32 == 0) ? 2 : 1;
+    const long long wgs = (long long)(N / (16 * c.nt_per_wave)) * mt;
+    if (splitk > 0) {
+        c.ks = splitk;
+    } else {
+        const long long target_waves = 256LL * 24;
+        int ks = 1;
+        while (ks < 16 && wgs * ks < target_waves && k_tiles(K) / (ks * 2) >= 4) ks *= 2;
+        c.ks = ks;
+    }
+    return c;
+}
+
+bool valid_splitk(int splitk, int K) {
+    if (splitk == 0) return true;
+    if (splitk != 1 && splitk != 2 && splitk != 4 && splitk != 8 && splitk != 16) return false;
+    return splitk <= k_tiles(K);
+}
+
+}  // namespace
+
+W4A8_EXPORT const char* w4a8_status_str(w4a8_status_t s) {
+    switch (s) {
+        case W4A8_OK: return "ok";
+        case W4A8_ERR_NULL_PTR: return "a required pointer is NULL";
+        case W4A8_ERR_SHAPE: return "invalid shape, group, qmax or split factor";
+        case W4A8_ERR_ALIGNMENT: return "a device pointer is not 16-byte aligned";
+        case W4A8_ERR_WORKSPACE: return "workspace is smaller than w4a8_workspace_size()";
+        case W4A8_ERR_UNSUPPORTED: return "unsupported device, mode or output type";
+        case W4A8_ERR_HIP: return "HIP runtime error (see w4a8_last_hip_error)";
+    }
+    return "unknown status";
+}
+
+W4A8_EXPORT int w4a8_last_hip_error(void) { return g_last_hip_error; }
+
+W4A8_EXPORT int w4a8_layout_version(void) { return W4A8_LAYOUT_VERSION; }
+
+W4A8_EXPORT size_t w4a8_workspace_size(int M, int N, int K, int splitk) {
+    (void)M; (void)N; (void)K; (void)splitk;
+    return 0;
+}
+
+W4A8_EXPORT w4a8_status_t w4a8_pack(const float* W, int N, int K, int group, int qmax_i8,
+                                    int mode, uint8_t* wq, uint8_t* s_u8, uint8_t* a_u8,
+                                    float* sw, hipStream_t stream) {
+    if (mode != W4A8_PACK_LQQ && mode != W4A8_PACK_INT4_SYM) return W4A8_ERR_UNSUPPORTED;
+    if (!valid_nk(N, K)) return W4A8_ERR_SHAPE;
+    if (mode == W4A8_PACK_LQQ && (!valid_group(group) || qmax_i8 < 1 || qmax_i8 > 127))
+        return W4A8_ERR_SHAPE;
+    if (N == 0) return W4A8_OK;  // nothing to read or write
+    if (!W || !wq || !sw) return W4A8_ERR_NULL_PTR;
+    if (mode == W4A8_PACK_LQQ && (!s_u8 || !a_u8)) return W4A8_ERR_NULL_PTR;
+    if (!aligned16(W) || !aligned16(wq) || !aligned4(sw)) return W4A8_ERR_ALIGNMENT;
+    w4a8_status_t d = check_device();
+    if (d != W4A8_OK) return d;
+    if (mode == W4A8_PACK_LQQ)
+        return hip_status(w4a8::launch_pack_lqq(W, N, K, group, qmax_i8, wq, s_u8, a_u8, sw, stream));
+    return hip_status(w4a8::launch_pack_int4(W, N, K, wq, sw, stream));
+}
+
+W4A8_EXPORT w4a8_status_t w4a8_quant_act(const float* X, int M, int K, int8_t* Xq, float* sx,
+                                         hipStream_t stream) {
+    if (M < 0 || K <= 0 || K % 16 != 0) return W4A8_ERR_SHAPE;
+    if (M == 0) return W4A8_OK;  // nothing to read or write
+    if (!X || !Xq || !sx) return W4A8_ERR_NULL_PTR;
+    if (!aligned16(X) || !aligned16(Xq) || !aligned4(sx)) return W4A8_ERR_ALIGNMENT;
+    w4a8_status_t d = check_device();
+    if (d != W4A8_OK) return d;
+    return hip_status(w4a8::launch_act_int8(X, M, K, Xq, sx, stream));
+}
+
+W4A8_EXPORT w4a8_status_t w4fp8_quant_act(const float* X, int M, int K, uint8_t* Xq, float* sx,
+                                          hipStream_t stream) {
+    if (M < 0 || K <= 0 || K % 16 != 0) return W4A8_ERR_SHAPE;
+    if (M == 0) return W4A8_OK;  // nothing to read or write
+    if (!X || !Xq || !sx) return W4A8_ERR_NULL_PTR;
+    if (!aligned16(X) || !aligned16(Xq) || !aligned4(sx)) return W4A8_ERR_ALIGNMENT;
+    w4a8_status_t d = check_device();
+    if (d != W4A8_OK) return d;
+    return hip_status(w4a8::launch_act_e4m3(X, M, K, Xq, sx, stream));
+}
+
+W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint8_t* wq,
+                                    const uint8_t* s_u8, const uint8_t* a_u8, const float* sw,
+                                    void* Y, int out_type, int M, int N, int K, int group,
+                                    int splitk, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    if (out_type != W4A8_OUT_F16 && out_type != W4A8_OUT_I32) return W4A8_ERR_UNSUPPORTED;
+    if (M < 0 || !valid_nk(N, K) || !valid_group(group) || !valid_splitk(splitk, K))
+        return W4A8_ERR_SHAPE;
+    if (M == 0 || N == 0) return W4A8_OK;  // nothing to read or write
+    if (!X || !wq || !s_u8 || !a_u8 || !Y) return W4A8_ERR_NULL_PTR;
+    if (out_type == W4A8_OUT_F16 && (!sx || !sw)) return W4A8_ERR_NULL_PTR;
+    if (!aligned16(X) || !aligned16(wq) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
+    if ((sx && !aligned4(sx)) || (sw && !aligned4(sw))) return W4A8_ERR_ALIGNMENT;
+    if (workspace_bytes < w4a8_workspace_size(M, N, K, splitk)) return W4A8_ERR_WORKSPACE;
+    (void)workspace;
+    w4a8_status_t d = check_device();
+    if (d != W4A8_OK) return d;
+    return hip_status(w4a8::launch_w4a8_stream(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
+                                               group, choose_stream(M, N, K, splitk), stream));
+}
+
+W4A8_EXPORT w4a8_status_t w4fp8_gemm(const uint8_t* X_e4m3, const float* sx, const uint8_t* wq,
+                                     const float* sw, void* Y, int out_type, int M, int N, int K,
+                                     int splitk, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+    if (out_type != W4FP8_OUT_BF16 && out_type != W4FP8_OUT_F32) return W4A8_ERR_UNSUPPORTED;
+    if (M < 0 || !valid_nk(N, K) || !valid_splitk(splitk, K)) return W4A8_ERR_SHAPE;
+    if (M == 0 || N == 0) return W4A8_OK;  // nothing to read or write
+    if (!X_e4m3 || !sx || !wq || !sw || !Y) return W4A8_ERR_NULL_PTR;
+    if (!aligned16(X_e4m3) || !aligned16(wq) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
+    if (!aligned4(sx) || !aligned4(sw)) return W4A8_ERR_ALIGNMENT;
+    if (workspace_bytes < w4a8_workspace_size(M, N, K, splitk)) return W4A8_ERR_WORKSPACE;
+    (void)workspace;
+    w4a8_status_t d = check_device();
+    if (d != W4A8_OK) return d;
+    return hip_status(w4a8::launch_w4fp8_stream(X_e4m3, sx, wq, sw, Y, out_type, M, N, K,
+                                                choose_stream(M, N, K, splitk), stream));
+}

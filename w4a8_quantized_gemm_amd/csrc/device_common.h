@@ -1,0 +1,81 @@
+// Device helpers shared by the gfx950 kernels of libw4a8.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kTileN = 16;     // rows of one packed tile
+constexpr int kTileK = 128;    // K columns of one packed tile
+constexpr int kTileBytes = 1024;
+
+// 16-byte global load through the vector memory path.
+__device__ __forceinline__ v4i load16(const void* p) {
+    return *reinterpret_cast<const v4i*>(p);
+}
+
+// LiquidQuant dequantisation of four codes held one per byte of `c`
+// (LiquidGEMM, Pith review of arXiv 2509.01229, "What carries the
+// argument" / paper Eq. 12): byte = (q*s + a) XOR 0x80.  The multiply-add
+// runs as two 16-bit lanes, each holding two code bytes; the byte lanes
+// cannot carry because every q*s + a <= 255.  `s2` = s in both 16-bit
+// halves, `a4` = a in all four bytes.
+__device__ __forceinline__ unsigned lqq_dequant4(unsigned c, u16x2 s2, u16x2 a4) {
+    u16x2 v = __builtin_bit_cast(u16x2, c);
+    v = v * s2 + a4;
+    return __builtin_bit_cast(unsigned, v) ^ 0x80808080u;
+}
+
+// Dequantise the 8 codes of one packed dword into 8 INT8 bytes in K order:
+// .x = columns +0..+3 (low nibbles), .y = columns +4..+7 (high nibbles).
+__device__ __forceinline__ void lqq_dequant8(unsigned w, u16x2 s2, u16x2 a4,
+                                             unsigned& lo, unsigned& hi) {
+    lo = lqq_dequant4(w & 0x0F0F0F0Fu, s2, a4);
+    hi = lqq_dequant4((w >> 4) & 0x0F0F0F0Fu, s2, a4);
+}
+
+// Sign-magnitude INT4 (bit 3 sign, bits 0..2 magnitude) to OCP e4m3 for
+// the four codes in the low nibbles of the bytes of `c` (high nibbles of
+// `c` must be the sign bits' neighbours of nothing: callers mask first).
+// Magnitudes 0..7 map exactly: 0, 1.0, 2.0, 3.0, 4.0, 5.0, 6.0, 7.0 ->
+// 0x00 0x38 0x40 0x44 0x48 0x4A 0x4C 0x4E.  The byte lookup is one
+// v_perm_b32 over the 8-byte table {lut_hi, lut_lo}.
+constexpr unsigned kE4m3LutLo = 0x44403800u;  // bytes for 3,2,1,0
+constexpr unsigned kE4m3LutHi = 0x4E4C4A48u;  // bytes for 7,6,5,4
+
+__device__ __forceinline__ unsigned int4_to_e4m3_lo(unsigned w) {
+    // low nibbles: magnitude bits 0..2, sign bit 3 -> e4m3 sign bit 7
+    unsigned mag = w & 0x07070707u;
+    unsigned e = __builtin_amdgcn_perm(kE4m3LutHi, kE4m3LutLo, mag);
+    return e | ((w << 4) & 0x80808080u);
+}
+
+__device__ __forceinline__ unsigned int4_to_e4m3_hi(unsigned w) {
+    // high nibbles: magnitude bits 4..6, sign bit 7 is already in place
+    unsigned mag = (w >> 4) & 0x07070707u;
+    unsigned e = __builtin_amdgcn_perm(kE4m3LutHi, kE4m3LutLo, mag);
+    return e | (w & 0x80808080u);
+}
+
+// float -> IEEE binary16 bits, nearest-even (hardware conversion).
+__device__ __forceinline__ unsigned short f32_to_f16_bits(float v) {
+    _Float16 h = (_Float16)v;
+    return __builtin_bit_cast(unsigned short, h);
+}
+
+// float -> bfloat16 bits, nearest-even on the float32 bit pattern.
+__device__ __forceinline__ unsigned short f32_to_bf16_bits(float v) {
+    unsigned u = __builtin_bit_cast(unsigned, v);
+    if ((u & 0x7F800000u) == 0x7F800000u) {  // inf / nan
+        return (unsigned short)((u >> 16) | ((u & 0xFFFFu) ? 0x40u : 0u));
+    }
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (unsigned short)(u >> 16);
+}
+
+}  // namespace w4a8

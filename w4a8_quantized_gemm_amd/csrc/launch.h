@@ -1,0 +1,33 @@
+// Internal host-side launchers of libw4a8 (not part of the C ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a8 {
+
+hipError_t launch_pack_lqq(const float* W, int N, int K, int group, int qmax, uint8_t* wq,
+                           uint8_t* s_u8, uint8_t* a_u8, float* sw, hipStream_t st);
+hipError_t launch_pack_int4(const float* W, int N, int K, uint8_t* wq, float* sw,
+                            hipStream_t st);
+hipError_t launch_act_int8(const float* X, int M, int K, int8_t* Xq, float* sx,
+                           hipStream_t st);
+hipError_t launch_act_e4m3(const float* X, int M, int K, uint8_t* Xq, float* sx,
+                           hipStream_t st);
+
+// Streamed-tile GEMMs: one workgroup per (16*nt_per_wave rows of N, 16 rows
+// of M); `ks` waves split K and reduce in LDS.
+struct StreamCfg {
+    int nt_per_wave;  // 16-row weight tiles per wave (1, 2 or 4)
+    int ks;           // waves per workgroup splitting K (1..16)
+};
+
+hipError_t launch_w4a8_stream(const int8_t* X, const float* sx, const uint8_t* wq,
+                              const uint8_t* s_u8, const uint8_t* a_u8, const float* sw,
+                              void* Y, int out_type, int M, int N, int K, int group,
+                              StreamCfg cfg, hipStream_t st);
+
+hipError_t launch_w4fp8_stream(const uint8_t* X, const float* sx, const uint8_t* wq,
+                               const float* sw, void* Y, int out_type, int M, int N, int K,
+                               StreamCfg cfg, hipStream_t st);
+
+}  // namespace w4a8

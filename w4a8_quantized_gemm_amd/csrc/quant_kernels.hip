@@ -1,0 +1,227 @@
+// Quantisation kernels for gfx950: offline weight packing (LiquidQuant and
+// INT4 sign-magnitude) and per-token activation quantisation (INT8, e4m3).
+//
+// Sources: LiquidGEMM, Pith review of arXiv 2509.01229 (referee summary:
+// per-channel INT8 then per-group UINT4 in the UINT8 domain; "What carries
+// the argument": offset a = 2^7 + min; major comment 3: integer scale,
+// Sec. 4 Eq. 7; minor comment 2: nearest rounding, Eq. 10).  FireQ, arXiv
+// 2505.20839, abstract (INT4 weights with channel-wise scales, FP8
+// activations).
+//
+// Every float step that decides an integer (scale division, quotient,
+// rounding) is done in float32 with correctly rounded division and
+// round-half-even, so the codes are a deterministic function of the input.
+#include "device_common.h"
+#include "launch.h"
+
+namespace w4a8 {
+
+// ---------------------------------------------------------------------------
+// Row max |x| reduced by one workgroup of 256 threads, then scale =
+// max / qmax (a row whose scale is not positive gets scale 1).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float block_absmax_256(const float* row, int K) {
+    float m = 0.0f;
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+    for (int i = threadIdx.x; i < K / 4; i += 256) {
+        float4 v = r4[i];
+        m = fmaxf(m, fmaxf(fmaxf(fabsf(v.x), fabsf(v.y)), fmaxf(fabsf(v.z), fabsf(v.w))));
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    __shared__ float part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    __syncthreads();
+    return m;
+}
+
+__device__ __forceinline__ float scale_of(float amax, float qmax) {
+    float s = __fdiv_rn(amax, qmax);
+    return (s > 0.0f) ? s : 1.0f;
+}
+
+__device__ __forceinline__ int quant_sym(float x, float s, float qmax) {
+    float v = __builtin_rintf(__fdiv_rn(x, s));
+    v = fminf(fmaxf(v, -qmax), qmax);
+    return (int)v;
+}
+
+// Per-row scale (weights: per output channel).
+__global__ __launch_bounds__(256) void row_scale_kernel(const float* __restrict__ W, int K,
+                                                        float qmax, float* __restrict__ sw) {
+    const float* row = W + (size_t)blockIdx.x * K;
+    float amax = block_absmax_256(row, K);
+    if (threadIdx.x == 0) sw[blockIdx.x] = scale_of(amax, qmax);
+}
+
+// Byte offset of packed dword d of lane (G, r) in tile (nt, kt).
+__device__ __forceinline__ size_t packed_dword_offset(int nt, int kt, int KT, int G, int r, int d) {
+    return ((size_t)nt * KT + kt) * kTileBytes + (size_t)(16 * G + r) * 16 + 4 * d;
+}
+
+// LiquidQuant second level.  One thread per (row n, group j): a first pass
+// finds min/max of the INT8 values of its group, a second pass writes the
+// UINT4 codes (as whole packed dwords: 8 consecutive columns) plus s_u8/a_u8.
+__global__ __launch_bounds__(256) void lqq_group_kernel(const float* __restrict__ W,
+                                                        const float* __restrict__ sw, int N, int K,
+                                                        int group, float qmax,
+                                                        uint8_t* __restrict__ wq,
+                                                        uint8_t* __restrict__ s_u8,
+                                                        uint8_t* __restrict__ a_u8) {
+    const int groups = K / group;
+    const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (tid >= (long long)N * groups) return;
+    const int n = (int)(tid / groups);
+    const int j = (int)(tid % groups);
+    const float s_ch = sw[n];
+    const float* w = W + (size_t)n * K + (size_t)j * group;
+    int mn = 127, mx = -128;
+    for (int t = 0; t < group; ++t) {
+        int q = quant_sym(w[t], s_ch, qmax);
+        mn = min(mn, q);
+        mx = max(mx, q);
+    }
+    const int R = mx - mn;
+    int s = (R + 14) / 15;
+    s = s < 1 ? 1 : s;
+    const int a = 128 + mn;
+    const int cap = (127 - mn) / s;
+    s_u8[(size_t)n * groups + j] = (uint8_t)s;
+    a_u8[(size_t)n * groups + j] = (uint8_t)a;
+    const int KT = K / kTileK, nt = n / kTileN, r = n % kTileN;
+    for (int c8 = 0; c8 < group; c8 += 8) {
+        unsigned word = 0;
+        for (int e = 0; e < 8; ++e) {
+            int u = quant_sym(w[c8 + e], s_ch, qmax) - mn;
+            int q = (2 * u + s) / (2 * s);
+            q = min(q, cap);
+            q = min(q, 15);
+            // column +e -> byte (e & 3), low nibble for e < 4, high for e >= 4
+            word |= (unsigned)q << (8 * (e & 3) + 4 * (e >> 2));
+        }
+        const int k = j * group + c8;
+        const int kt = k / kTileK, kk = k % kTileK;
+        size_t off = packed_dword_offset(nt, kt, KT, kk / 32, r, (kk % 32) / 8);
+        *reinterpret_cast<unsigned*>(wq + off) = word;
+    }
+}
+
+// INT4 symmetric sign-magnitude nibbles.  One thread per packed dword
+// (8 consecutive columns of one row).
+__global__ __launch_bounds__(256) void int4_pack_kernel(const float* __restrict__ W,
+                                                        const float* __restrict__ sw, int N, int K,
+                                                        uint8_t* __restrict__ wq) {
+    const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const long long per_row = K / 8;
+    if (tid >= (long long)N * per_row) return;
+    const int n = (int)(tid / per_row);
+    const int k = (int)(tid % per_row) * 8;
+    const float s_ch = sw[n];
+    const float* w = W + (size_t)n * K + k;
+    unsigned word = 0;
+    for (int e = 0; e < 8; ++e) {
+        int q = quant_sym(w[e], s_ch, 7.0f);
+        unsigned c = q < 0 ? (0x8u | (unsigned)(-q)) : (unsigned)q;
+        word |= c << (8 * (e & 3) + 4 * (e >> 2));
+    }
+    const int KT = K / kTileK, nt = n / kTileN, r = n % kTileN;
+    const int kt = k / kTileK, kk = k % kTileK;
+    size_t off = packed_dword_offset(nt, kt, KT, kk / 32, r, (kk % 32) / 8);
+    *reinterpret_cast<unsigned*>(wq + off) = word;
+}
+
+// ---------------------------------------------------------------------------
+// Per-token activation quantisation: one workgroup per row.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void act_int8_kernel(const float* __restrict__ X, int K,
+                                                       int8_t* __restrict__ Xq,
+                                                       float* __restrict__ sx) {
+    const float* row = X + (size_t)blockIdx.x * K;
+    const float s = scale_of(block_absmax_256(row, K), 127.0f);
+    if (threadIdx.x == 0) sx[blockIdx.x] = s;
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+    unsigned* out = reinterpret_cast<unsigned*>(Xq + (size_t)blockIdx.x * K);
+    for (int i = threadIdx.x; i < K / 4; i += 256) {
+        float4 v = r4[i];
+        unsigned b0 = (unsigned)(quant_sym(v.x, s, 127.0f) & 0xFF);
+        unsigned b1 = (unsigned)(quant_sym(v.y, s, 127.0f) & 0xFF);
+        unsigned b2 = (unsigned)(quant_sym(v.z, s, 127.0f) & 0xFF);
+        unsigned b3 = (unsigned)(quant_sym(v.w, s, 127.0f) & 0xFF);
+        out[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    }
+}
+
+// float32 -> OCP e4m3 ("fn"), nearest-even, saturating to +-448, sign kept.
+// Normal inputs: the significand is rounded to 3 fraction bits at the
+// input's own binade (2^(e-3) quantum); below 2^-6 the fixed subnormal
+// quantum 2^-9 applies.  A carry out of the significand moves to the next
+// binade through the plain addition of the exponent and mantissa fields.
+__device__ __forceinline__ unsigned f32_to_e4m3(float x) {
+    unsigned u = __builtin_bit_cast(unsigned, x);
+    unsigned sign = (u >> 24) & 0x80u;
+    float a = fabsf(x);
+    if (a != a) return 0x7Fu;
+    if (a >= 448.0f) return sign | 0x7Eu;
+    if (a < 0.015625f) {  // 2^-6
+        unsigned m = (unsigned)__builtin_rintf(a * 512.0f);  // exact scaling by 2^9
+        return sign | m;  // m == 8 is exactly the smallest normal, code 0x08
+    }
+    int e = (int)((u >> 23) & 0xFFu) - 127;         // -6 .. 8
+    float t = __builtin_ldexpf(a, 3 - e);            // in [8, 16), exact
+    unsigned mi = (unsigned)__builtin_rintf(t);      // 8 .. 16
+    unsigned code = (unsigned)((e + 7) << 3) + (mi - 8u);
+    if (code > 0x7Eu) code = 0x7Eu;
+    return sign | code;
+}
+
+__global__ __launch_bounds__(256) void act_e4m3_kernel(const float* __restrict__ X, int K,
+                                                       uint8_t* __restrict__ Xq,
+                                                       float* __restrict__ sx) {
+    const float* row = X + (size_t)blockIdx.x * K;
+    const float s = scale_of(block_absmax_256(row, K), 448.0f);
+    if (threadIdx.x == 0) sx[blockIdx.x] = s;
+    const float4* r4 = reinterpret_cast<const float4*>(row);
+    unsigned* out = reinterpret_cast<unsigned*>(Xq + (size_t)blockIdx.x * K);
+    for (int i = threadIdx.x; i < K / 4; i += 256) {
+        float4 v = r4[i];
+        unsigned b0 = f32_to_e4m3(__fdiv_rn(v.x, s));
+        unsigned b1 = f32_to_e4m3(__fdiv_rn(v.y, s));
+        unsigned b2 = f32_to_e4m3(__fdiv_rn(v.z, s));
+        unsigned b3 = f32_to_e4m3(__fdiv_rn(v.w, s));
+        out[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    }
+}
+
+// ----------------------------------------------------------- launchers ----
+hipError_t launch_pack_lqq(const float* W, int N, int K, int group, int qmax, uint8_t* wq,
+                           uint8_t* s_u8, uint8_t* a_u8, float* sw, hipStream_t st) {
+    hipLaunchKernelGGL(row_scale_kernel, dim3(N), dim3(256), 0, st, W, K, (float)qmax, sw);
+    long long threads = (long long)N * (K / group);
+    unsigned blocks = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL(lqq_group_kernel, dim3(blocks), dim3(256), 0, st, W, sw, N, K, group,
+                       (float)qmax, wq, s_u8, a_u8);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_int4(const float* W, int N, int K, uint8_t* wq, float* sw,
+                            hipStream_t st) {
+    hipLaunchKernelGGL(row_scale_kernel, dim3(N), dim3(256), 0, st, W, K, 7.0f, sw);
+    long long threads = (long long)N * (K / 8);
+    unsigned blocks = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL(int4_pack_kernel, dim3(blocks), dim3(256), 0, st, W, sw, N, K, wq);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_int8(const float* X, int M, int K, int8_t* Xq, float* sx, hipStream_t st) {
+    hipLaunchKernelGGL(act_int8_kernel, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
+    return hipGetLastError();
+}
+
+hipError_t launch_act_e4m3(const float* X, int M, int K, uint8_t* Xq, float* sx,
+                           hipStream_t st) {
+    hipLaunchKernelGGL(act_e4m3_kernel, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
+    return hipGetLastError();
+}
+
+}  // namespace w4a8
