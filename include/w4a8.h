@@ -133,9 +133,12 @@ size_t w4a8_workspace_size(int M, int N, int K, int splitk);
  *   out_type W4A8_OUT_I32: Y[m][n] = acc[m][n] (sx, sw may be NULL)
  * X: int8 [M][K] per-token quantised; wq, s_u8, a_u8, sw from w4a8_pack
  * (LQQ mode, same N, K, group); Y: fp16 or int32 [M][N].
- * splitk: number of K-slices reduced per output tile (0 = automatic,
- * otherwise 1, 2, 4, 8 or 16 and at most K/128).  The int32 result does not
- * depend on it.
+ * Kernel choice is a function of the shape: M >= 64 with N % 256 == 0 runs
+ * the matrix-core tile kernel (128- or 256-row workgroup tiles); otherwise
+ * the streamed-tile kernel runs, with `splitk` K-slices per output tile.
+ * splitk: 0 = automatic; 1, 2, 4, 8 or 16 (at most K/128) forces the
+ * streamed-tile kernel with that split.  The int32 result depends on
+ * neither choice.
  */
 w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint8_t* wq,
                         const uint8_t* s_u8, const uint8_t* a_u8,

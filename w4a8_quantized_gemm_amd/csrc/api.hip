@@ -68,6 +68,18 @@ w4a8::StreamCfg choose_stream(int M, int N, int K, int splitk) {
     return c;
 }
 
+// Kernel choice (a pure function of the shape, so tests can reach both):
+// the matrix-core tile kernel takes M >= 64 when N is a multiple of its
+// 256-channel workgroup tile; smaller M streams weight tiles per 16 rows.
+bool use_mfma_tiles(int M, int N) { return M >= 64 && N % 256 == 0; }
+
+// 256-row tiles halve the per-weight dequantisation cost; fall back to 128
+// rows when 256 would leave the 256 CUs with fewer workgroups than CUs.
+int choose_mt(int M, int N) {
+    const long long t256 = (long long)(N / 256) * ((M + 255) / 256);
+    return (M > 128 && t256 >= 256) ? 256 : 128;
+}
+
 bool valid_splitk(int splitk, int K) {
     if (splitk == 0) return true;
     if (splitk != 1 && splitk != 2 && splitk != 4 && splitk != 8 && splitk != 16) return false;
@@ -155,6 +167,9 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint
     (void)workspace;
     w4a8_status_t d = check_device();
     if (d != W4A8_OK) return d;
+    if (splitk == 0 && use_mfma_tiles(M, N))
+        return hip_status(w4a8::launch_w4a8_mfma(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
+                                                 group, choose_mt(M, N), stream));
     return hip_status(w4a8::launch_w4a8_stream(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
                                                group, choose_stream(M, N, K, splitk), stream));
 }

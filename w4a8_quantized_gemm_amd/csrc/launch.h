@@ -26,6 +26,12 @@ hipError_t launch_w4a8_stream(const int8_t* X, const float* sx, const uint8_t* w
                               void* Y, int out_type, int M, int N, int K, int group,
                               StreamCfg cfg, hipStream_t st);
 
+// Matrix-core tile kernel for large M: N % 256 == 0, mt = 128 or 256 rows.
+hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
+                            const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
+                            int out_type, int M, int N, int K, int group, int mt,
+                            hipStream_t st);
+
 hipError_t launch_w4fp8_stream(const uint8_t* X, const float* sx, const uint8_t* wq,
                                const float* sw, void* Y, int out_type, int M, int N, int K,
                                StreamCfg cfg, hipStream_t st);
