@@ -29,7 +29,7 @@
  *   - M = 0 or N = 0 is a valid empty problem: once the sizes and modes are
  *     valid the call returns W4A8_OK without checking pointers (nothing is
  *     read or written) and launches nothing.
- *   - Shape constraints: K a positive multiple of 128, N a multiple of 16,
+ *   - Shape constraints: K a positive multiple of 128, N a multiple of 64,
  *     group in {64, 128}; every device pointer 16-byte aligned.
  *
  * Packed 4-bit weight layout (W4A8_LAYOUT_VERSION 1), wq = N*K/2 bytes:
@@ -42,8 +42,13 @@
  *   holds column 32G+8d+b in the low nibble and column 32G+8d+4+b in the
  *   high nibble.  One 16-byte load by one lane thus carries 32 weights of one
  *   output channel: two K-steps of the INT8 matrix core, one of the FP8 one.
- * Per-group parameters (LiquidQuant mode) are row-major: s_u8[N][K/group],
- * a_u8[N][K/group].  Scales: sw[N], sx[M] float32.
+ * Per-group parameters (LiquidQuant mode), s_u8 and a_u8, N*K/group bytes
+ * each, in "panel" order: output channels are taken in panels of 64
+ * (p = n/64); the parameters of panel p and group j (columns
+ * j*group .. j*group+group-1) are the 64 bytes at offset 64*(p*(K/group) + j),
+ * and channel n sits at byte 4*(n%16) + (n%64)/16 of them.  A lane that
+ * handles row r of the four 16-row tiles of a panel thus reads the
+ * parameters of all four with one 4-byte load.  Scales: sw[N], sx[M] float32.
  */
 #ifndef W4A8_H
 #define W4A8_H
@@ -59,7 +64,7 @@ extern "C" {
 typedef enum {
     W4A8_OK = 0,
     W4A8_ERR_NULL_PTR = 1,    /* a required pointer is NULL                     */
-    W4A8_ERR_SHAPE = 2,       /* negative size, K % 128, N % 16, group, qmax     */
+    W4A8_ERR_SHAPE = 2,       /* negative size, K % 128, N % 64, group, qmax     */
     W4A8_ERR_ALIGNMENT = 3,   /* a device pointer is not 16-byte aligned         */
     W4A8_ERR_WORKSPACE = 4,   /* workspace smaller than w4a8_workspace_size()    */
     W4A8_ERR_UNSUPPORTED = 5, /* device is not gfx950, or a bad mode/flag value  */
@@ -93,7 +98,7 @@ enum { W4FP8_OUT_BF16 = 0, W4FP8_OUT_F32 = 1 };
  *   nibbles (bit 3 = sign, bits 0..2 = |q|).  group, qmax_i8, s_u8, a_u8
  *   are ignored and may be 0 / NULL.
  * W: float32 [N][K].  Outputs: wq [N*K/2] (layout above), s_u8 and a_u8
- * [N][K/group], sw [N].
+ * [N*K/group] (panel order above), sw [N].
  */
 w4a8_status_t w4a8_pack(const float* W, int N, int K, int group, int qmax_i8,
                         int mode, uint8_t* wq, uint8_t* s_u8, uint8_t* a_u8,

@@ -58,6 +58,8 @@ def _declare(L):
         "orc_lqq_decode": ([_P, _P, _P, _I, _I, _I, _P], ctypes.c_int64),
         "orc_pack_nibbles": ([_P, _I, _I, _P], None),
         "orc_unpack_nibbles": ([_P, _I, _I, _P], None),
+        "orc_params_to_panels": ([_P, _I, _I, _P], None),
+        "orc_params_from_panels": ([_P, _I, _I, _P], None),
         "orc_gemm_i32": ([_P, _P, _I, _I, _I, _P], None),
         "orc_round_f16": ([_P, _I, _P], None),
         "orc_round_bf16": ([_P, _I, _P], None),
@@ -138,6 +140,25 @@ def unpack_nibbles(wq, N: int, K: int):
     codes = np.empty((N, K), np.uint8)
     lib().orc_unpack_nibbles(_p(wq), N, K, _p(codes))
     return codes
+
+
+def params_to_panels(p):
+    """Row-major [N][K/g] group parameters -> the library's panel order."""
+    p = _c(p, np.uint8)
+    N, groups = p.shape
+    assert N % 64 == 0
+    out = np.empty(N * groups, np.uint8)
+    lib().orc_params_to_panels(_p(p), N, groups, _p(out))
+    return out
+
+
+def params_from_panels(panels, N: int, groups: int):
+    """The library's panel order -> row-major [N][groups]."""
+    panels = _c(panels, np.uint8).reshape(-1)
+    assert panels.size == N * groups and N % 64 == 0
+    out = np.empty((N, groups), np.uint8)
+    lib().orc_params_from_panels(_p(panels), N, groups, _p(out))
+    return out
 
 
 def gemm_i32(X, W):
@@ -236,8 +257,12 @@ def w4a8_pack(W, group: int, qmax: int = 127):
     """Offline LiquidQuant of float32 W[N][K]: per-channel INT8, then LQQ."""
     Q, sw = quant_sym_rows(W, qmax)
     codes, s, a, nsat = lqq_encode(Q, group)
-    return {"Q": Q, "sw": sw, "codes": codes, "s_u8": s, "a_u8": a,
-            "nsat": nsat, "wq": pack_nibbles(codes)}
+    out = {"Q": Q, "sw": sw, "codes": codes, "s_u8": s, "a_u8": a,
+           "nsat": nsat, "wq": pack_nibbles(codes)}
+    if W.shape[0] % 64 == 0:  # the device format (panel order)
+        out["s_panels"] = params_to_panels(s)
+        out["a_panels"] = params_to_panels(a)
+    return out
 
 
 def w4fp8_pack(W):

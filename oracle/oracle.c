@@ -177,7 +177,30 @@ ORC_API void orc_pack_nibbles(const uint8_t* codes, int64_t N, int64_t K,
     }
 }
 
-/* Inverse of the layout above, used by tests to read device-packed bytes. */
+/* Per-group parameter order (panel order): the row-major [N][K/g] array of
+ * s (or a) bytes is rewritten so that panel p = n/64 and group j occupy the
+ * 64 bytes at 64*(p*(K/g) + j), channel n at byte 4*(n%16) + (n%64)/16. */
+ORC_API void orc_params_to_panels(const uint8_t* rowmajor, int64_t N,
+                                  int64_t groups, uint8_t* panels) {
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < groups; ++j) {
+            int64_t p = n / 64;
+            int64_t off = 64 * (p * groups + j) + 4 * (n % 16) + (n % 64) / 16;
+            panels[off] = rowmajor[n * groups + j];
+        }
+    }
+}
+
+/* Inverse of the panel order (tests read device-written parameters). */
+ORC_API void orc_params_from_panels(const uint8_t* panels, int64_t N,
+                                    int64_t groups, uint8_t* rowmajor) {
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t j = 0; j < groups; ++j)
+            rowmajor[n * groups + j] =
+                panels[64 * ((n / 64) * groups + j) + 4 * (n % 16) + (n % 64) / 16];
+}
+
+/* Inverse of the nibble layout, used by tests to read device-packed bytes. */
 ORC_API void orc_unpack_nibbles(const uint8_t* wq, int64_t N, int64_t K,
                                 uint8_t* codes) {
     int64_t KT = K / 128;

@@ -39,7 +39,7 @@ def test_layout_version_and_strings():
     assert lib.w4a8_workspace_size(16, 4096, 4096, 0) == 0
 
 
-def pack(W=A, N=32, K=256, g=64, qmax=127, mode=0, wq=A, s=A, a=A, sw=A):
+def pack(W=A, N=64, K=256, g=64, qmax=127, mode=0, wq=A, s=A, a=A, sw=A):
     return lib.w4a8_pack(W, N, K, g, qmax, mode, wq, s, a, sw, None)
 
 
@@ -62,7 +62,7 @@ def test_pack_validation():
     assert pack(N=0) == OK  # empty problem, nothing launched
 
 
-def gemm(X=A, sx=A, wq=A, s=A, a=A, sw=A, Y=A, out=0, M=16, N=32, K=256, g=64,
+def gemm(X=A, sx=A, wq=A, s=A, a=A, sw=A, Y=A, out=0, M=16, N=64, K=256, g=64,
          splitk=0, ws=None, wsb=0):
     return lib.w4a8_gemm(X, sx, wq, s, a, sw, Y, out, M, N, K, g, splitk, ws, wsb, None)
 
@@ -76,6 +76,7 @@ def test_gemm_validation():
     assert gemm(M=-1) == SHAPE
     assert gemm(K=192) == SHAPE
     assert gemm(N=40) == SHAPE
+    assert gemm(N=48) == SHAPE  # N must be a multiple of 64
     assert gemm(g=256) == SHAPE
     assert gemm(splitk=3) == SHAPE
     assert gemm(splitk=4, K=256) == SHAPE  # more slices than K tiles
@@ -89,7 +90,7 @@ def test_gemm_validation():
     assert gemm(M=0, K=100) == SHAPE
 
 
-def fp8(X=A, sx=A, wq=A, sw=A, Y=A, out=0, M=16, N=32, K=256, splitk=0):
+def fp8(X=A, sx=A, wq=A, sw=A, Y=A, out=0, M=16, N=64, K=256, splitk=0):
     return lib.w4fp8_gemm(X, sx, wq, sw, Y, out, M, N, K, splitk, None, 0, None)
 
 

@@ -377,6 +377,33 @@ def test_pack_layout_golden(golden_dir):
     assert n == 11
 
 
+def test_param_panels_golden(golden_dir):
+    path = os.path.join(golden_dir, "param_panels.txt")
+    n_ok = 0
+    for line in open(path):
+        if not line.strip() or line.startswith("#"):
+            continue
+        N, G, n, j, byte = map(int, line.split())
+        p = np.zeros((N, G), np.uint8)
+        p[n, j] = 0x5A
+        out = oracle.params_to_panels(p)
+        assert list(np.nonzero(out)[0]) == [byte], line
+        n_ok += 1
+    assert n_ok == 9
+
+
+def test_param_panels_bijective():
+    rng = np.random.default_rng(21)
+    p = rng.integers(0, 256, size=(192, 5)).astype(np.uint8)
+    out = oracle.params_to_panels(p)
+    assert sorted(out.tolist()) == sorted(p.reshape(-1).tolist())
+    np.testing.assert_array_equal(oracle.params_from_panels(out, 192, 5), p)
+    idx = np.arange(192 * 5, dtype=np.int64).reshape(192, 5)
+    # positions are a permutation: tag every entry with a distinct id
+    ids = oracle.params_to_panels((idx % 251).astype(np.uint8))
+    assert ids.size == 960
+
+
 def test_pack_layout_bijective():
     rng = np.random.default_rng(4)
     N, K = 48, 384

@@ -108,7 +108,7 @@ def pack(W, group: int = 64, qmax: int = 127, mode: int = PACK_LQQ, stream=None)
     """w4a8_pack on a float32 [N][K] device tensor.
 
     Returns a dict with wq (uint8 [N*K/2]), sw (float32 [N]) and, in LQQ
-    mode, s_u8 / a_u8 (uint8 [N][K/group])."""
+    mode, s_u8 / a_u8 (uint8 [N*K/group], panel order of include/w4a8.h)."""
     torch = _torch()
     _need(W, torch.float32, "W")
     N, K = W.shape
@@ -118,8 +118,8 @@ def pack(W, group: int = 64, qmax: int = 127, mode: int = PACK_LQQ, stream=None)
     out = {"wq": wq, "sw": sw, "N": N, "K": K, "mode": mode}
     s_u8 = a_u8 = None
     if mode == PACK_LQQ:
-        s_u8 = torch.empty((N, K // group), dtype=torch.uint8, device=dev)
-        a_u8 = torch.empty((N, K // group), dtype=torch.uint8, device=dev)
+        s_u8 = torch.empty(N * K // group, dtype=torch.uint8, device=dev)
+        a_u8 = torch.empty(N * K // group, dtype=torch.uint8, device=dev)
         out.update(s_u8=s_u8, a_u8=a_u8, group=group)
     _check(lib.w4a8_pack(_ptr(W), N, K, group, qmax, mode, _ptr(wq), _ptr(s_u8),
                          _ptr(a_u8), _ptr(sw), _stream(stream)), "w4a8_pack")

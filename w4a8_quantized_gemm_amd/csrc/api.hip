@@ -44,7 +44,7 @@ w4a8_status_t check_device() {
     return c == 1 ? W4A8_OK : W4A8_ERR_UNSUPPORTED;
 }
 
-bool valid_nk(int N, int K) { return N >= 0 && K > 0 && K % 128 == 0 && N % 16 == 0; }
+bool valid_nk(int N, int K) { return N >= 0 && K > 0 && K % 128 == 0 && N % 64 == 0; }
 bool valid_group(int g) { return g == 64 || g == 128; }
 
 int k_tiles(int K) { return K / 128; }
@@ -55,7 +55,7 @@ int k_tiles(int K) { return K / 128; }
 w4a8::StreamCfg choose_stream(int M, int N, int K, int splitk) {
     w4a8::StreamCfg c;
     const int mt = (M + 15) / 16;
-    c.nt_per_wave = (N % 32 == 0) ? 2 : 1;
+    c.nt_per_wave = 2;  // N % 64 == 0
     const long long wgs = (long long)(N / (16 * c.nt_per_wave)) * mt;
     if (splitk > 0) {
         c.ks = splitk;
@@ -71,7 +71,9 @@ w4a8::StreamCfg choose_stream(int M, int N, int K, int splitk) {
 // Kernel choice (a pure function of the shape, so tests can reach both):
 // the matrix-core tile kernel takes M >= 64 when N is a multiple of its
 // 256-channel workgroup tile; smaller M streams weight tiles per 16 rows.
-bool use_mfma_tiles(int M, int N) { return M >= 64 && N % 256 == 0; }
+bool use_mfma_tiles(int M, int N, int K) {
+    return M >= 64 && N % 256 == 0 && (long long)M * K < (1LL << 32);
+}
 
 // 256-row tiles halve the per-weight dequantisation cost; fall back to 128
 // rows when 256 would leave the 256 CUs with fewer workgroups than CUs.
@@ -167,7 +169,7 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint
     (void)workspace;
     w4a8_status_t d = check_device();
     if (d != W4A8_OK) return d;
-    if (splitk == 0 && use_mfma_tiles(M, N))
+    if (splitk == 0 && use_mfma_tiles(M, N, K))
         return hip_status(w4a8::launch_w4a8_mfma(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
                                                  group, choose_mt(M, N), stream));
     return hip_status(w4a8::launch_w4a8_stream(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,

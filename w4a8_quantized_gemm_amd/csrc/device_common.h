@@ -31,6 +31,24 @@ __device__ __forceinline__ unsigned lqq_dequant4(unsigned c, u16x2 s2, u16x2 a4)
     return __builtin_bit_cast(unsigned, v) ^ 0x80808080u;
 }
 
+// Byte offset of the group parameters (s_u8 / a_u8, panel order) of output
+// channel n, group j: panels of 64 channels, 64 bytes per (panel, group),
+// channel n at 4*(n%16) + (n%64)/16.
+__device__ __forceinline__ size_t param_offset(int n, int j, int groups) {
+    return (size_t)64 * ((size_t)(n >> 6) * groups + j) + 4 * (n & 15) + ((n & 63) >> 4);
+}
+
+// From the 4 parameter bytes of one panel row (tile b in byte b): the scale
+// of tile b in both 16-bit halves, and its offset in all four bytes.
+// v_perm_b32 selector 0x0C yields a zero byte.
+__device__ __forceinline__ u16x2 scale_pair(unsigned sdw, int b) {
+    const unsigned sel = (unsigned)b | 0x0C00u | ((unsigned)b << 16) | 0x0C000000u;
+    return __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(0u, sdw, sel));
+}
+__device__ __forceinline__ u16x2 offset_quad(unsigned adw, int b) {
+    return __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(0u, adw, (unsigned)b * 0x01010101u));
+}
+
 // Dequantise the 8 codes of one packed dword into 8 INT8 bytes in K order:
 // .x = columns +0..+3 (low nibbles), .y = columns +4..+7 (high nibbles).
 __device__ __forceinline__ void lqq_dequant8(unsigned w, u16x2 s2, u16x2 a4,

@@ -57,7 +57,7 @@ __global__ __launch_bounds__(1024) void w4a8_stream_kernel(
         for (int t = 0; t < NTW; ++t) {
             const int nt = nt0 + t;
             const v4i w = load16(wlane + ((size_t)nt * KT + kt) * kTileBytes);
-            const size_t gi = (size_t)(nt * kTileN + r) * groups + j;
+            const size_t gi = param_offset(nt * kTileN + r, j, groups);
             const unsigned s = s_u8[gi], a = a_u8[gi];
             const u16x2 s2 = u16x2{(unsigned short)s, (unsigned short)s};
             const unsigned short aa = (unsigned short)(a * 0x101u);

@@ -87,8 +87,8 @@ __global__ __launch_bounds__(256) void lqq_group_kernel(const float* __restrict_
     s = s < 1 ? 1 : s;
     const int a = 128 + mn;
     const int cap = (127 - mn) / s;
-    s_u8[(size_t)n * groups + j] = (uint8_t)s;
-    a_u8[(size_t)n * groups + j] = (uint8_t)a;
+    s_u8[param_offset(n, j, groups)] = (uint8_t)s;
+    a_u8[param_offset(n, j, groups)] = (uint8_t)a;
     const int KT = K / kTileK, nt = n / kTileN, r = n % kTileN;
     for (int c8 = 0; c8 < group; c8 += 8) {
         unsigned word = 0;
