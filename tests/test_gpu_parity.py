@@ -163,6 +163,21 @@ def test_mfma_tiles_full_grid():
     np.testing.assert_array_equal(host(Yi), acc)
 
 
+# 256-row tiles need at least 256 workgroups: M x N = 4096 x 4096 and more.
+# K = 384 gives an odd number of K-steps (the unrolled loop's tail step).
+@pytest.mark.parametrize("M,N,K,g", [(4000, 4096, 384, 128), (4096, 4096, 512, 64)])
+def test_mfma256_tiles(M, N, K, g):
+    say(f"w4a8 mfma256 gemm M={M} N={N} K={K} g={g}")
+    X8, sx, pk, acc, y = _small_problem(M, N, K, g, 41 + K)
+    Yi = poison((M, N), torch.int32)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, out=Yi)
+    np.testing.assert_array_equal(host(Yi), acc)
+    Yh = poison((M, N), torch.float16)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_F16, out=Yh)
+    d = f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y)
+    assert d.max() <= 1
+
+
 def test_splitk_invariance_and_determinism():
     say("w4a8 split-K sweep M=16 N=256 K=2048")
     X8, sx, pk, acc, _ = _small_problem(16, 256, 2048, 64, 77)

@@ -24,6 +24,8 @@
 // With 128-row tiles two workgroups share a CU, so one's barrier and
 // dequantisation phases overlap the other's matrix-core phase.
 // Epilogue: Y = fp16((float(acc) * sx[m]) * sw[n]) or the raw int32.
+#include <utility>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -66,6 +68,72 @@ __device__ __forceinline__ void dequant_half(const WStep& ws, int h, v4i (&B)[4]
 // allocator cannot split the accumulators between register files.
 __device__ __forceinline__ void mfma_i8_acc(v4i& acc, const v4i& a, const v4i& b) {
     asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Same instruction, volatile: keeps its place relative to the one-instruction
+// dequantisation steps interleaved with it below.
+__device__ __forceinline__ void mfma_i8_acc_v(v4i& acc, const v4i& a, const v4i& b) {
+    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Dequantisation of the next K-step's four tiles as 120 single-instruction
+// steps, so that one can follow each matrix-core instruction of the current
+// step and run on the vector ALU while the matrix core is busy.
+//   steps 30b + 0, 1:   scale pair / offset quad of tile b (v_perm_b32)
+//   steps 30b + 2 + 7d + e, dword d of tile b, e = 0..6:
+//     lo = w & 0x0F0F0F0F; t = w >> 4; hi = t & 0x0F0F0F0F;
+//     lo = lo*s + a; hi = hi*s + a   (two 16-bit lanes, v_pk_mad_u16);
+//     lo ^= 0x80808080; hi ^= 0x80808080
+// Results land in B[b][d/2] components 2(d%2), 2(d%2)+1.
+struct DequantPipe {
+    unsigned s2[4], a4[4];
+    unsigned lo, t, hi;
+};
+
+template <int OP>
+__device__ __forceinline__ void dq_step(DequantPipe& p, const WStep& w, v4i (&B)[4][2]) {
+    constexpr int b = OP / 30, q = OP % 30;
+    if constexpr (q == 0) {
+        constexpr unsigned sel = (unsigned)b | 0x0C00u | ((unsigned)b << 16) | 0x0C000000u;
+        asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.s2[b]) : "v"(w.sdw), "s"(sel));
+    } else if constexpr (q == 1) {
+        constexpr unsigned sel = (unsigned)b * 0x01010101u;
+        asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.a4[b]) : "v"(w.adw), "s"(sel));
+    } else {
+        constexpr int d = (q - 2) / 7, e = (q - 2) % 7;
+        const unsigned wd = (unsigned)w.w[b][d];
+        if constexpr (e == 0) {
+            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(p.lo) : "v"(wd));
+        } else if constexpr (e == 1) {
+            asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(p.t) : "v"(wd));
+        } else if constexpr (e == 2) {
+            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(p.hi) : "v"(p.t));
+        } else if constexpr (e == 3) {
+            asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
+                         : "=v"(p.lo) : "v"(p.lo), "v"(p.s2[b]), "v"(p.a4[b]));
+        } else if constexpr (e == 4) {
+            asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
+                         : "=v"(p.hi) : "v"(p.hi), "v"(p.s2[b]), "v"(p.a4[b]));
+        } else if constexpr (e == 5) {
+            unsigned x;
+            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(p.lo));
+            B[b][d >> 1][2 * (d & 1)] = (int)x;
+        } else {
+            unsigned x;
+            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(p.hi));
+            B[b][d >> 1][2 * (d & 1) + 1] = (int)x;
+        }
+    }
+}
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 // Wait states between the last accumulation and the first read of the
@@ -225,6 +293,292 @@ __global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4a8_mfma_kernel(
     }
 }
 
+// 256-row variant (one workgroup per CU), built on v_mfma_i32_32x32x32_i8:
+// half as many matrix-core instructions per K-step as the 16x16 form, so
+// each one leaves a 32-cycle shadow for the dequantisation, LDS and memory
+// instructions of the same wave.
+//   wave tile 256 x 64 = 8 row blocks x 2 channel blocks of 32 x 32;
+//   B operand of lane (c = lane % 32, h = lane / 32): packed tile row c % 16
+//     of tile 2*cb + c/16, slots 2h and 2h+1 (K columns 64h .. 64h+63 of
+//     the 128-column step); instruction i (0..3) consumes columns
+//     64h + 16i .. +15, and the A operand (X row, same columns) matches;
+//   every global load is a buffer load (SGPR step offset, no per-load
+//     address arithmetic) issued two K-steps ahead; X rows past M fall
+//     outside the buffer and read as zero;
+//   the next step's weights are dequantised in single-instruction steps
+//     interleaved with this step's matrix-core instructions;
+//   the epilogue scales in registers, transposes through LDS and writes
+//     whole 128-byte row segments.
+namespace {
+
+__device__ __forceinline__ void mfma32_i8_acc(v16i& acc, const v4i& a, const v4i& b) {
+    asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ unsigned buf_load4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// Raw weights of one K-step for one lane: w[cb][e] = slot 2h+e of the
+// lane's row in tile 2cb + c/16; parameter dwords of the lane's panel row.
+struct WStep32 {
+    v4i w[2][2];
+    unsigned sdw, adw;
+};
+
+// 116 single-instruction dequantisation steps for the operands of one
+// K-step: for cb in {0,1}: 2 parameter extractions, then 8 dwords
+// (e, d) x 7 instructions.  Dword d of slot e feeds instruction
+// i = 2e + d/2, components 2(d%2) and 2(d%2)+1.
+struct DequantPipe32 {
+    unsigned s2[2], a4[2];
+    unsigned lo, t, hi;
+};
+
+template <int OP>
+__device__ __forceinline__ void dq32_step(DequantPipe32& p, const WStep32& w, int tb,
+                                          v4i (&B)[2][4]) {
+    constexpr int cb = OP / 58, q = OP % 58;
+    if constexpr (q == 0) {
+        const unsigned b = (unsigned)(2 * cb + tb);
+        const unsigned sel = b | 0x0C00u | (b << 16) | 0x0C000000u;
+        asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.s2[cb]) : "v"(w.sdw), "v"(sel));
+    } else if constexpr (q == 1) {
+        const unsigned b = (unsigned)(2 * cb + tb);
+        asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.a4[cb]) : "v"(w.adw), "v"(b * 0x01010101u));
+    } else {
+        constexpr int u = (q - 2) / 7, e = u / 4, d = u % 4, st = (q - 2) % 7;
+        constexpr int i = 2 * e + d / 2, comp = 2 * (d % 2);
+        const unsigned wd = (unsigned)w.w[cb][e][d];
+        if constexpr (st == 0) {
+            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(p.lo) : "v"(wd));
+        } else if constexpr (st == 1) {
+            asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(p.t) : "v"(wd));
+        } else if constexpr (st == 2) {
+            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(p.hi) : "v"(p.t));
+        } else if constexpr (st == 3) {
+            asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
+                         : "=v"(p.lo) : "v"(p.lo), "v"(p.s2[cb]), "v"(p.a4[cb]));
+        } else if constexpr (st == 4) {
+            asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
+                         : "=v"(p.hi) : "v"(p.hi), "v"(p.s2[cb]), "v"(p.a4[cb]));
+        } else if constexpr (st == 5) {
+            unsigned x;
+            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(p.lo));
+            B[cb][i][comp] = (int)x;
+        } else {
+            unsigned x;
+            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(p.hi));
+            B[cb][i][comp + 1] = (int)x;
+        }
+    }
+}
+
+// Non-interleaved form (prologue).
+__device__ __forceinline__ void dq32_all(const WStep32& w, int tb, v4i (&B)[2][4]) {
+    DequantPipe32 p;
+    static_for<116>([&](auto oc) { dq32_step<decltype(oc)::value>(p, w, tb, B); });
+}
+
+__device__ __forceinline__ void mfma32_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+}  // namespace
+
+template <int OUT, int GROUP>
+__global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
+    const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
+    const uint8_t* __restrict__ s_u8, const uint8_t* __restrict__ a_u8,
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, int tiles_n,
+    int tiles_m) {
+    constexpr int MT = 256;
+    constexpr int RB = 8;          // 32-row blocks per wave
+    constexpr int CPT = 8;         // 16-byte X chunks per thread per K-step
+    __shared__ __attribute__((aligned(1024))) uint8_t xs0[MT * 128];
+    __shared__ __attribute__((aligned(1024))) uint8_t xs1[MT * 128];
+    __shared__ float sxs[MT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int c = lane & 31, h = lane >> 5;
+    const int tb = c >> 4, r = c & 15;
+
+    const int nwg = tiles_n * tiles_m;
+    const int bid = blockIdx.x;
+    int lin = bid;
+    if ((nwg & 7) == 0) lin = (bid & 7) * (nwg >> 3) + (bid >> 3);
+    const int tm = lin % tiles_m;
+    const int tn = lin / tiles_m;
+    const int m0 = tm * MT;
+    const int n0 = tn * kNT + wave * kColsPerWave;
+    const int KT = K / kTileK;
+    const int groups = K / GROUP;
+
+    // ---- X: chunk p of this thread is row (tid>>3) + 32p, 16-byte column
+    // tid & 7, stored in LDS slot col ^ xswz(row & 15) (row & 15 is the same
+    // for all p).  Buffer offsets: rows >= M lie past the end -> zeros.
+    const __amdgpu_buffer_rsrc_t xr_rsrc = buf_rsrc(X, (unsigned)M * (unsigned)K);
+    const int xrow0 = tid >> 3, xcol = tid & 7;
+    const unsigned xvoff = (unsigned)(m0 + xrow0) * (unsigned)K + (unsigned)(xcol * 16);
+    const unsigned xrowstep = 32u * (unsigned)K;
+    const int xlds0 = xrow0 * 128 + ((xcol ^ xswz(xrow0 & 15)) * 16);
+    auto load_x = [&](int kt, v4i (&xr)[CPT]) {
+#pragma unroll
+        for (int p = 0; p < CPT; ++p)
+            xr[p] = buf_load16(xr_rsrc, xvoff + (unsigned)p * xrowstep, (unsigned)(kt * kTileK));
+    };
+    auto store_x = [&](const v4i (&xr)[CPT], uint8_t* dst) {
+#pragma unroll
+        for (int p = 0; p < CPT; ++p) *reinterpret_cast<v4i*>(dst + xlds0 + p * 4096) = xr[p];
+    };
+    // A operand (row block rb, instruction i): row 32rb + c, column 4h + i.
+    int aoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) aoff[i] = c * 128 + (((4 * h + i) ^ xswz(r)) * 16);
+
+    // ---- weights of this wave: tiles nt0 .. nt0+3 (one parameter panel)
+    const int nt0 = n0 / kTileN;
+    const __amdgpu_buffer_rsrc_t w_rsrc = buf_rsrc(wq, (unsigned)((size_t)N * K / 2));
+    const __amdgpu_buffer_rsrc_t s_rsrc = buf_rsrc(s_u8, (unsigned)((size_t)N * K / GROUP));
+    const __amdgpu_buffer_rsrc_t a_rsrc = buf_rsrc(a_u8, (unsigned)((size_t)N * K / GROUP));
+    const unsigned wvoff = (unsigned)(tb * KT) * kTileBytes + (unsigned)(32 * h + r) * 16u;
+    const unsigned pvoff = 4u * (unsigned)r + (GROUP == 64 ? 64u * (unsigned)h : 0u);
+    const unsigned ppanel = 64u * (unsigned)(n0 >> 6) * (unsigned)groups;
+    auto load_w = [&](int kt, WStep32& ws) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+                ws.w[cb][e] = buf_load16(
+                    w_rsrc, wvoff,
+                    (unsigned)(((nt0 + 2 * cb) * KT + kt) * kTileBytes + e * 256));
+        const unsigned jo = 64u * (unsigned)(kt * (kTileK / GROUP));
+        ws.sdw = buf_load4(s_rsrc, pvoff, ppanel + jo);
+        ws.adw = buf_load4(a_rsrc, pvoff, ppanel + jo);
+    };
+
+    v16i acc[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        acc[rb][0] = v16i{};
+        acc[rb][1] = v16i{};
+    }
+
+    v4i xa[CPT], xb[CPT];
+    WStep32 wa, wb;
+    v4i Ba[2][4], Bb[2][4];
+    const int k1 = min(1, KT - 1);
+    load_x(0, xa);
+    load_w(0, wa);
+    load_x(k1, xb);
+    load_w(k1, wb);
+    store_x(xa, xs0);
+    dq32_all(wa, tb, Ba);
+
+    // One K-step.  Entering: LDS `cur` = X(kt); Bcur = W(kt) operands;
+    // xst = X(kt+1), wdq = raw W(kt+1) (loaded one step ago).  xld / wld
+    // receive step kt+2 (index clamped to the last step; extra loads are
+    // never consumed).
+    auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, v4i (&xst)[CPT], v4i (&xld)[CPT],
+                    WStep32& wdq, WStep32& wld, v4i (&Bcur)[2][4], v4i (&Bnxt)[2][4]) {
+        __syncthreads();
+        const int k2 = min(kt + 2, KT - 1);
+        load_x(k2, xld);
+        load_w(k2, wld);
+        constexpr int kRing = 4;
+        auto read_a = [&](int s) {  // s = 8i + rb
+            return *reinterpret_cast<const v4i*>(cur + (s & 7) * 4096 + aoff[s >> 3]);
+        };
+        v4i Ar[kRing];
+#pragma unroll
+        for (int d = 0; d < kRing; ++d) Ar[d] = read_a(d);
+        DequantPipe32 dp;
+        static_for<4 * RB>([&](auto sc) {
+            constexpr int sI = decltype(sc)::value;
+            constexpr int i = sI / RB, rb = sI % RB;
+            const v4i a = Ar[sI % kRing];
+            if constexpr (sI + kRing < 4 * RB) Ar[sI % kRing] = read_a(sI + kRing);
+            static_for<2>([&](auto cc) {
+                constexpr int cb = decltype(cc)::value;
+                mfma32_i8_acc(acc[rb][cb], a, Bcur[cb][i]);
+                constexpr int op0 = 4 * sI + 2 * cb;  // 128 slots, 116 steps
+                if constexpr (op0 < 116) dq32_step<op0>(dp, wdq, tb, Bnxt);
+                if constexpr (op0 + 1 < 116) dq32_step<op0 + 1>(dp, wdq, tb, Bnxt);
+            });
+        });
+        store_x(xst, nxt);
+    };
+
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+        step(kt, xs0, xs1, xb, xa, wb, wa, Ba, Bb);
+        step(kt + 1, xs1, xs0, xa, xb, wa, wb, Bb, Ba);
+    }
+    if (kt < KT) step(kt, xs0, xs1, xb, xa, wb, wa, Ba, Bb);
+
+    mfma32_drain();
+    __syncthreads();  // all waves done with the X buffers
+
+    // ---- epilogue.  Accumulator (rb, cb) register v of lane (c, g = h):
+    // row 32rb + 8(v/4) + 4g + (v%4), channel n0 + 32cb + c.  Scaled values
+    // go to a per-wave LDS block [32 rows][64 channels], then each row is
+    // written as whole 16-byte pieces.
+    if (OUT == 0) {
+        sxs[tid] = (m0 + tid < M) ? sx[m0 + tid] : 0.0f;
+    }
+    const float sw0 = (OUT == 0) ? sw[n0 + c] : 0.0f;
+    const float sw1 = (OUT == 0) ? sw[n0 + 32 + c] : 0.0f;
+    __syncthreads();
+    constexpr int EB = (OUT == 1) ? 4 : 2;            // output element bytes
+    constexpr int ROWB = 64 * EB;                      // bytes per staged row
+    uint8_t* stage = xs0 + wave * (32 * ROWB);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = 8 * (v >> 2) + 4 * h + (v & 3);
+                const int col = 32 * cb + c;
+                if (OUT == 1) {
+                    *reinterpret_cast<int*>(stage + row * ROWB + col * 4) = acc[rb][cb][v];
+                } else {
+                    const float y = ((float)acc[rb][cb][v] * sxs[32 * rb + row]) * (cb ? sw1 : sw0);
+                    *reinterpret_cast<unsigned short*>(stage + row * ROWB + col * 2) =
+                        f32_to_f16_bits(y);
+                }
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+        __builtin_amdgcn_wave_barrier();
+        constexpr int PIECES = 32 * ROWB / 16;       // 16-byte pieces per block
+        constexpr int PPR = ROWB / 16;               // pieces per row
+#pragma unroll
+        for (int u = 0; u < PIECES / 64; ++u) {
+            const int q = lane + 64 * u;
+            const int row = q / PPR, piece = q % PPR;
+            const int m = m0 + 32 * rb + row;
+            const v4i val = *reinterpret_cast<const v4i*>(stage + row * ROWB + piece * 16);
+            if (m < M)
+                *reinterpret_cast<v4i*>(reinterpret_cast<uint8_t*>(Y) +
+                                        ((size_t)m * N + n0) * EB + piece * 16) = val;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
 template <int MT>
 static hipError_t launch_mt(const int8_t* X, const float* sx, const uint8_t* wq,
                             const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
@@ -247,7 +601,19 @@ hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
                             hipStream_t st) {
     if (mt == 128)
         return launch_mt<128>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, st);
-    return launch_mt<256>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, st);
+    const int tiles_n = N / kNT;
+    const int tiles_m = (M + 255) / 256;
+    dim3 grid(tiles_n * tiles_m), block(256);
+#define W4A8_L256(O, G)                                                                         \
+    hipLaunchKernelGGL((w4a8_mfma256_kernel<O, G>), grid, block, 0, st, X, sx, wq, s_u8, a_u8, \
+                       sw, Y, M, N, K, tiles_n, tiles_m)
+    if (out_type == 1) {
+        if (group == 64) W4A8_L256(1, 64); else W4A8_L256(1, 128);
+    } else {
+        if (group == 64) W4A8_L256(0, 64); else W4A8_L256(0, 128);
+    }
+#undef W4A8_L256
+    return hipGetLastError();
 }
 
 }  // namespace w4a8
