@@ -333,58 +333,64 @@ struct WStep32 {
     unsigned sdw, adw;
 };
 
-// 116 single-instruction dequantisation steps for the operands of one
-// K-step: for cb in {0,1}: 2 parameter extractions, then 8 dwords
-// (e, d) x 7 instructions.  Dword d of slot e feeds instruction
-// i = 2e + d/2, components 2(d%2) and 2(d%2)+1.
-struct DequantPipe32 {
+// Scale pair / offset quad of the lane's tiles for one K-step.
+struct WParams {
     unsigned s2[2], a4[2];
-    unsigned lo, t, hi;
 };
 
-template <int OP>
-__device__ __forceinline__ void dq32_step(DequantPipe32& p, const WStep32& w, int tb,
-                                          v4i (&B)[2][4]) {
-    constexpr int cb = OP / 58, q = OP % 58;
-    if constexpr (q == 0) {
+__device__ __forceinline__ void wparams(const WStep32& w, int tb, WParams& p) {
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb) {
         const unsigned b = (unsigned)(2 * cb + tb);
         const unsigned sel = b | 0x0C00u | (b << 16) | 0x0C000000u;
         asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.s2[cb]) : "v"(w.sdw), "v"(sel));
-    } else if constexpr (q == 1) {
-        const unsigned b = (unsigned)(2 * cb + tb);
         asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.a4[cb]) : "v"(w.adw), "v"(b * 0x01010101u));
-    } else {
-        constexpr int u = (q - 2) / 7, e = u / 4, d = u % 4, st = (q - 2) % 7;
-        constexpr int i = 2 * e + d / 2, comp = 2 * (d % 2);
-        const unsigned wd = (unsigned)w.w[cb][e][d];
-        if constexpr (st == 0) {
-            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(p.lo) : "v"(wd));
-        } else if constexpr (st == 1) {
-            asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(p.t) : "v"(wd));
-        } else if constexpr (st == 2) {
-            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(p.hi) : "v"(p.t));
-        } else if constexpr (st == 3) {
-            asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
-                         : "=v"(p.lo) : "v"(p.lo), "v"(p.s2[cb]), "v"(p.a4[cb]));
-        } else if constexpr (st == 4) {
-            asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
-                         : "=v"(p.hi) : "v"(p.hi), "v"(p.s2[cb]), "v"(p.a4[cb]));
-        } else if constexpr (st == 5) {
-            unsigned x;
-            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(p.lo));
-            B[cb][i][comp] = (int)x;
-        } else {
-            unsigned x;
-            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(p.hi));
-            B[cb][i][comp + 1] = (int)x;
-        }
     }
 }
 
-// Non-interleaved form (prologue).
-__device__ __forceinline__ void dq32_all(const WStep32& w, int tb, v4i (&B)[2][4]) {
-    DequantPipe32 p;
-    static_for<116>([&](auto oc) { dq32_step<decltype(oc)::value>(p, w, tb, B); });
+// Operands of instruction i (K columns 64h + 16i .. +15 of the lane) come
+// from dwords d = 2(i%2), 2(i%2)+1 of slot e = i/2.  Producing B[*][i] is 28
+// single-instruction steps: for cb in {0,1}, for the two dwords:
+//   lo = w & 0x0F0F0F0F; t = w >> 4; hi = t & 0x0F0F0F0F;
+//   lo = lo*s + a; hi = hi*s + a   (v_pk_mad_u16, two codes per 16-bit lane);
+//   B = lo ^ 0x80808080, hi ^ 0x80808080   (LiquidQuant decode)
+struct DqTmp {
+    unsigned lo, t, hi;
+};
+
+template <int I, int OP>
+__device__ __forceinline__ void dq_group_step(DqTmp& tmp, const WStep32& w, const WParams& p,
+                                              v4i (&B)[2][4]) {
+    constexpr int cb = OP / 14, q = OP % 14, dd = q / 7, st = q % 7;
+    constexpr int e = I / 2, d = 2 * (I % 2) + dd;
+    const unsigned wd = (unsigned)w.w[cb][e][d];
+    if constexpr (st == 0) {
+        asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.lo) : "v"(wd));
+    } else if constexpr (st == 1) {
+        asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(tmp.t) : "v"(wd));
+    } else if constexpr (st == 2) {
+        asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.hi) : "v"(tmp.t));
+    } else if constexpr (st == 3) {
+        asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
+                     : "=v"(tmp.lo) : "v"(tmp.lo), "v"(p.s2[cb]), "v"(p.a4[cb]));
+    } else if constexpr (st == 4) {
+        asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
+                     : "=v"(tmp.hi) : "v"(tmp.hi), "v"(p.s2[cb]), "v"(p.a4[cb]));
+    } else if constexpr (st == 5) {
+        unsigned x;
+        asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(tmp.lo));
+        B[cb][I][2 * dd] = (int)x;
+    } else {
+        unsigned x;
+        asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(tmp.hi));
+        B[cb][I][2 * dd + 1] = (int)x;
+    }
+}
+
+template <int I>
+__device__ __forceinline__ void dq_group_all(const WStep32& w, const WParams& p, v4i (&B)[2][4]) {
+    DqTmp tmp;
+    static_for<28>([&](auto oc) { dq_group_step<I, decltype(oc)::value>(tmp, w, p, B); });
 }
 
 __device__ __forceinline__ void mfma32_drain() {
@@ -427,21 +433,12 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
 
     // ---- X: chunk p of this thread is row (tid>>3) + 32p, 16-byte column
     // tid & 7, stored in LDS slot col ^ xswz(row & 15) (row & 15 is the same
-    // for all p).  Buffer offsets: rows >= M lie past the end -> zeros.
+    // for all p).  Rows >= M lie past the end of the buffer and read as 0.
     const __amdgpu_buffer_rsrc_t xr_rsrc = buf_rsrc(X, (unsigned)M * (unsigned)K);
     const int xrow0 = tid >> 3, xcol = tid & 7;
     const unsigned xvoff = (unsigned)(m0 + xrow0) * (unsigned)K + (unsigned)(xcol * 16);
     const unsigned xrowstep = 32u * (unsigned)K;
     const int xlds0 = xrow0 * 128 + ((xcol ^ xswz(xrow0 & 15)) * 16);
-    auto load_x = [&](int kt, v4i (&xr)[CPT]) {
-#pragma unroll
-        for (int p = 0; p < CPT; ++p)
-            xr[p] = buf_load16(xr_rsrc, xvoff + (unsigned)p * xrowstep, (unsigned)(kt * kTileK));
-    };
-    auto store_x = [&](const v4i (&xr)[CPT], uint8_t* dst) {
-#pragma unroll
-        for (int p = 0; p < CPT; ++p) *reinterpret_cast<v4i*>(dst + xlds0 + p * 4096) = xr[p];
-    };
     // A operand (row block rb, instruction i): row 32rb + c, column 4h + i.
     int aoff[4];
 #pragma unroll
@@ -455,17 +452,19 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
     const unsigned wvoff = (unsigned)(tb * KT) * kTileBytes + (unsigned)(32 * h + r) * 16u;
     const unsigned pvoff = 4u * (unsigned)r + (GROUP == 64 ? 64u * (unsigned)h : 0u);
     const unsigned ppanel = 64u * (unsigned)(n0 >> 6) * (unsigned)groups;
-    auto load_w = [&](int kt, WStep32& ws) {
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-                ws.w[cb][e] = buf_load16(
-                    w_rsrc, wvoff,
-                    (unsigned)(((nt0 + 2 * cb) * KT + kt) * kTileBytes + e * 256));
-        const unsigned jo = 64u * (unsigned)(kt * (kTileK / GROUP));
-        ws.sdw = buf_load4(s_rsrc, pvoff, ppanel + jo);
-        ws.adw = buf_load4(a_rsrc, pvoff, ppanel + jo);
+    auto w_load = [&](int kt, int part, WStep32& ws) {  // part 0..5
+        if (part < 4) {
+            const int cb = part >> 1, e = part & 1;
+            ws.w[cb][e] = buf_load16(w_rsrc, wvoff,
+                                     (unsigned)(((nt0 + 2 * cb) * KT + kt) * kTileBytes + e * 256));
+        } else {
+            const unsigned jo = ppanel + 64u * (unsigned)(kt * (kTileK / GROUP));
+            if (part == 4) ws.sdw = buf_load4(s_rsrc, pvoff, jo);
+            else ws.adw = buf_load4(a_rsrc, pvoff, jo);
+        }
+    };
+    auto x_load = [&](int kt, int p) {
+        return buf_load16(xr_rsrc, xvoff + (unsigned)p * xrowstep, (unsigned)(kt * kTileK));
     };
 
     v16i acc[RB][2];
@@ -475,73 +474,103 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
         acc[rb][1] = v16i{};
     }
 
-    v4i xa[CPT], xb[CPT];
-    WStep32 wa, wb;
-    v4i Ba[2][4], Bb[2][4];
+    // ---- prologue: X(0) -> LDS xs0, X(1) staged; W(0) dequantised fully,
+    // W(1) raw; A ring primed with step 0's first four operands.
+    v4i xe[CPT], xo[CPT];   // X staging for even / odd steps (X(kt) in set kt%2)
+    WStep32 we, wo;         // raw weights for even / odd steps
+    WParams pp;             // parameters of the raw set being dequantised
+    v4i B[2][4];
+    v4i ring[8];
     const int k1 = min(1, KT - 1);
-    load_x(0, xa);
-    load_w(0, wa);
-    load_x(k1, xb);
-    load_w(k1, wb);
-    store_x(xa, xs0);
-    dq32_all(wa, tb, Ba);
-
-    // One K-step.  Entering: LDS `cur` = X(kt); Bcur = W(kt) operands;
-    // xst = X(kt+1), wdq = raw W(kt+1) (loaded one step ago).  xld / wld
-    // receive step kt+2 (index clamped to the last step; extra loads are
-    // never consumed).
-    auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, v4i (&xst)[CPT], v4i (&xld)[CPT],
-                    WStep32& wdq, WStep32& wld, v4i (&Bcur)[2][4], v4i (&Bnxt)[2][4]) {
-        __syncthreads();
-        const int k2 = min(kt + 2, KT - 1);
-        load_x(k2, xld);
-        load_w(k2, wld);
-        constexpr int kRing = 4;
-        auto read_a = [&](int s) {  // s = 8i + rb
-            return *reinterpret_cast<const v4i*>(cur + (s & 7) * 4096 + aoff[s >> 3]);
-        };
-        v4i Ar[kRing];
 #pragma unroll
-        for (int d = 0; d < kRing; ++d) Ar[d] = read_a(d);
-        DequantPipe32 dp;
-        static_for<4 * RB>([&](auto sc) {
-            constexpr int sI = decltype(sc)::value;
-            constexpr int i = sI / RB, rb = sI % RB;
-            const v4i a = Ar[sI % kRing];
-            if constexpr (sI + kRing < 4 * RB) Ar[sI % kRing] = read_a(sI + kRing);
-            static_for<2>([&](auto cc) {
-                constexpr int cb = decltype(cc)::value;
-                mfma32_i8_acc(acc[rb][cb], a, Bcur[cb][i]);
-                constexpr int op0 = 4 * sI + 2 * cb;  // 128 slots, 116 steps
-                if constexpr (op0 < 116) dq32_step<op0>(dp, wdq, tb, Bnxt);
-                if constexpr (op0 + 1 < 116) dq32_step<op0 + 1>(dp, wdq, tb, Bnxt);
-            });
+    for (int p = 0; p < CPT; ++p) xe[p] = x_load(0, p);
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) xo[p] = x_load(k1, p);
+#pragma unroll
+    for (int part = 0; part < 6; ++part) w_load(0, part, we);
+#pragma unroll
+    for (int part = 0; part < 6; ++part) w_load(k1, part, wo);
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) *reinterpret_cast<v4i*>(xs0 + xlds0 + p * 4096) = xe[p];
+    wparams(we, tb, pp);
+    dq_group_all<0>(we, pp, B);
+    dq_group_all<1>(we, pp, B);
+    dq_group_all<2>(we, pp, B);
+    dq_group_all<3>(we, pp, B);
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 4; ++q) ring[q] = *reinterpret_cast<const v4i*>(xs0 + q * 4096 + aoff[0]);
+
+    // ---- one K-step, 64 matrix-core slots.  Slot s: instruction i = s/16,
+    // row block rb = (s/2)%8, channel block cb = s%2.  Entering step kt:
+    // LDS `cur` = X(kt); ring holds A for slots 0..7; B[*][0..2] = W(kt)
+    // operands and B[*][3] is produced in slots 0..15 from `wcur` (raw W(kt),
+    // parameters pp); `xnx` = X(kt+1) staged; `wnx` = raw W(kt+1).
+    //   slots 0..7    X(kt+2) -> xcur (the set that held X(kt))
+    //   slots 16..21  W(kt+2) -> wcur (done with it after slot 15)
+    //   slots 16..63  B[*][i-1] for step kt+1 from wnx, i = 1..3
+    //   slots 52..59  X(kt+1) -> LDS `nxt`
+    //   after slot 59: barrier, then step kt+1's first four A reads, then
+    //   slots 60..63 (their operands were read before the barrier).
+    auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, v4i (&xcur)[CPT],
+                    v4i (&xnx)[CPT], WStep32& wcur, WStep32& wnx) {
+        const int k2 = min(kt + 2, KT - 1);
+        DqTmp tmp;
+        auto read_a = [&](const uint8_t* buf, int sI) {  // sI = 8i + rb
+            return *reinterpret_cast<const v4i*>(buf + (sI & 7) * 4096 + aoff[sI >> 3]);
+        };
+        static_for<64>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            constexpr int sI = s / 2, i = sI / 8, rb = sI % 8, cb = s % 2;
+            if constexpr (s == 60) {
+                __syncthreads();
+#pragma unroll
+                for (int q = 0; q < 4; ++q) ring[q] = read_a(nxt, q);
+            }
+            mfma32_i8_acc(acc[rb][cb], ring[sI % 8], B[cb][i]);
+            if constexpr (cb == 1 && sI + 4 < 32) ring[(sI + 4) % 8] = read_a(cur, sI + 4);
+            if constexpr (s < 8) xcur[s] = x_load(k2, s);
+            if constexpr (s >= 16 && s < 22) w_load(k2, s - 16, wcur);
+            if constexpr (s >= 52 && s < 60)
+                *reinterpret_cast<v4i*>(nxt + xlds0 + (s - 52) * 4096) = xnx[s - 52];
+            // dequantisation: 28 steps per 16 slots, 2 per slot (the
+            // parameter extraction for wnx takes slot 16's pair)
+            if constexpr (s < 16) {
+                constexpr int o0 = 2 * s;
+                if constexpr (o0 < 28) dq_group_step<3, o0>(tmp, wcur, pp, B);
+                if constexpr (o0 + 1 < 28) dq_group_step<3, o0 + 1>(tmp, wcur, pp, B);
+            } else if constexpr (s == 16) {
+                wparams(wnx, tb, pp);
+            } else {
+                constexpr int g = s / 16;            // producing B[*][g-1]
+                constexpr int o0 = 2 * (s % 16) - (g == 1 ? 2 : 0);
+                if constexpr (o0 >= 0 && o0 < 28) dq_group_step<g - 1, o0>(tmp, wnx, pp, B);
+                if constexpr (o0 + 1 >= 0 && o0 + 1 < 28)
+                    dq_group_step<g - 1, o0 + 1>(tmp, wnx, pp, B);
+            }
         });
-        store_x(xst, nxt);
     };
 
     int kt = 0;
     for (; kt + 1 < KT; kt += 2) {
-        step(kt, xs0, xs1, xb, xa, wb, wa, Ba, Bb);
-        step(kt + 1, xs1, xs0, xa, xb, wa, wb, Bb, Ba);
+        step(kt, xs0, xs1, xe, xo, we, wo);
+        step(kt + 1, xs1, xs0, xo, xe, wo, we);
     }
-    if (kt < KT) step(kt, xs0, xs1, xb, xa, wb, wa, Ba, Bb);
+    if (kt < KT) step(kt, xs0, xs1, xe, xo, we, wo);
 
     mfma32_drain();
     __syncthreads();  // all waves done with the X buffers
 
-    // ---- epilogue.  Accumulator (rb, cb) register v of lane (c, g = h):
-    // row 32rb + 8(v/4) + 4g + (v%4), channel n0 + 32cb + c.  Scaled values
-    // go to a per-wave LDS block [32 rows][64 channels], then each row is
+    // ---- epilogue.  Accumulator (rb, cb) register v of lane (c, h): row
+    // 32rb + 8(v/4) + 4h + (v%4), channel n0 + 32cb + c.  Scaled values go
+    // to a per-wave LDS block [32 rows][64 channels]; each row is then
     // written as whole 16-byte pieces.
-    if (OUT == 0) {
-        sxs[tid] = (m0 + tid < M) ? sx[m0 + tid] : 0.0f;
-    }
+    if (OUT == 0) sxs[tid] = (m0 + tid < M) ? sx[m0 + tid] : 0.0f;
     const float sw0 = (OUT == 0) ? sw[n0 + c] : 0.0f;
     const float sw1 = (OUT == 0) ? sw[n0 + 32 + c] : 0.0f;
     __syncthreads();
-    constexpr int EB = (OUT == 1) ? 4 : 2;            // output element bytes
-    constexpr int ROWB = 64 * EB;                      // bytes per staged row
+    constexpr int EB = (OUT == 1) ? 4 : 2;   // output element bytes
+    constexpr int ROWB = 64 * EB;             // bytes per staged row
     uint8_t* stage = xs0 + wave * (32 * ROWB);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
@@ -562,8 +591,8 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
         __builtin_amdgcn_wave_barrier();
-        constexpr int PIECES = 32 * ROWB / 16;       // 16-byte pieces per block
-        constexpr int PPR = ROWB / 16;               // pieces per row
+        constexpr int PIECES = 32 * ROWB / 16;  // 16-byte pieces per block
+        constexpr int PPR = ROWB / 16;          // pieces per row
 #pragma unroll
         for (int u = 0; u < PIECES / 64; ++u) {
             const int q = lane + 64 * u;
