@@ -123,10 +123,14 @@ w4a8_status_t w4fp8_quant_act(const float* X, int M, int K, uint8_t* Xq,
                               float* sx, hipStream_t stream);
 
 /*
- * Bytes of device workspace w4a8_gemm / w4fp8_gemm need for this problem
- * and split factor (0 = the one the library would choose).  The current
- * kernels reduce their split-K partial sums on chip and need none: the
- * function returns 0, and workspace may be NULL.
+ * Bytes of device workspace w4a8_gemm needs for this problem: when the
+ * matrix-core kernel has too few output tiles to fill the GPU it splits K
+ * across workgroups, writes int32 partial tiles (splits x M x N x 4 bytes)
+ * and sums them in split order in a second kernel (exact and deterministic).
+ * Returns 0 when no split is used, when splitk != 0 (streamed kernel, which
+ * reduces on chip) and for w4fp8_gemm.  The workspace is scratch: its
+ * contents on entry are ignored and undefined on return; calls that share a
+ * workspace must be ordered on one stream.
  */
 size_t w4a8_workspace_size(int M, int N, int K, int splitk);
 

@@ -178,6 +178,33 @@ def test_mfma256_tiles(M, N, K, g):
     assert d.max() <= 1
 
 
+# Few output tiles -> the matrix-core kernel splits K across workgroups and
+# reduces int32 partials in a second kernel (8 splits here).
+@pytest.mark.parametrize("M,N,K,g", [(128, 512, 4096, 128), (100, 256, 2048, 64)])
+def test_mfma_split_k(M, N, K, g):
+    say(f"w4a8 mfma split-K gemm M={M} N={N} K={K} g={g} ws={w4.workspace_size(M, N, K)}")
+    assert w4.workspace_size(M, N, K) > 0
+    X8, sx, pk, acc, y = _small_problem(M, N, K, g, 51 + M)
+    Yi = poison((M, N), torch.int32)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, out=Yi)
+    np.testing.assert_array_equal(host(Yi), acc)
+    Yh = poison((M, N), torch.float16)
+    ws = poison((w4.workspace_size(M, N, K),), torch.uint8)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_F16, out=Yh, workspace=ws)
+    d = f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y)
+    assert d.max() <= 1
+
+
+def test_workspace_too_small_is_rejected():
+    M, N, K = 128, 512, 4096
+    X8, sx, pk, acc, y = _small_problem(M, N, K, 128, 3)
+    need = w4.workspace_size(M, N, K)
+    small = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(w4.W4A8Error) as ei:
+        w4.gemm(X8, sx, pk, workspace=small)
+    assert ei.value.status == 4
+
+
 def test_splitk_invariance_and_determinism():
     say("w4a8 split-K sweep M=16 N=256 K=2048")
     X8, sx, pk, acc, _ = _small_problem(16, 256, 2048, 64, 77)

@@ -156,7 +156,10 @@ def workspace_size(M: int, N: int, K: int, splitk: int = 0) -> int:
 
 def gemm(Xq, sx, packed, out_type: int = OUT_F16, splitk: int = 0, out=None,
          workspace=None, stream=None):
-    """w4a8_gemm: Y [M][N] float16 (OUT_F16) or int32 (OUT_I32)."""
+    """w4a8_gemm: Y [M][N] float16 (OUT_F16) or int32 (OUT_I32).
+
+    `workspace` (uint8 device tensor of at least workspace_size() bytes) is
+    allocated here when not given and the shape needs one."""
     torch = _torch()
     _need(Xq, torch.int8, "Xq")
     M, K = Xq.shape
@@ -168,6 +171,10 @@ def gemm(Xq, sx, packed, out_type: int = OUT_F16, splitk: int = 0, out=None,
     ydt = torch.float16 if out_type == OUT_F16 else torch.int32
     Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
     _need(Y, ydt, "out")
+    if workspace is None:
+        need = workspace_size(M, N, K, splitk)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=Xq.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.w4a8_gemm(_ptr(Xq), _ptr(sx), _ptr(packed["wq"]), _ptr(packed["s_u8"]),
                          _ptr(packed["a_u8"]), _ptr(packed["sw"]), _ptr(Y), out_type, M, N,

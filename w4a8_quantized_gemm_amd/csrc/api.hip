@@ -75,13 +75,6 @@ bool use_mfma_tiles(int M, int N, int K) {
     return M >= 64 && N % 256 == 0 && (long long)M * K < (1LL << 32);
 }
 
-// 256-row tiles halve the per-weight dequantisation cost; fall back to 128
-// rows when 256 would leave the 256 CUs with fewer workgroups than CUs.
-int choose_mt(int M, int N) {
-    const long long t256 = (long long)(N / 256) * ((M + 255) / 256);
-    return (M > 128 && t256 >= 256) ? 256 : 128;
-}
-
 bool valid_splitk(int splitk, int K) {
     if (splitk == 0) return true;
     if (splitk != 1 && splitk != 2 && splitk != 4 && splitk != 8 && splitk != 16) return false;
@@ -108,8 +101,9 @@ W4A8_EXPORT int w4a8_last_hip_error(void) { return g_last_hip_error; }
 W4A8_EXPORT int w4a8_layout_version(void) { return W4A8_LAYOUT_VERSION; }
 
 W4A8_EXPORT size_t w4a8_workspace_size(int M, int N, int K, int splitk) {
-    (void)M; (void)N; (void)K; (void)splitk;
-    return 0;
+    if (M <= 0 || !valid_nk(N, K) || N == 0 || splitk != 0) return 0;
+    if (!use_mfma_tiles(M, N, K)) return 0;
+    return w4a8::plan_w4a8_mfma(M, N, K).workspace;
 }
 
 W4A8_EXPORT w4a8_status_t w4a8_pack(const float* W, int N, int K, int group, int qmax_i8,
@@ -165,13 +159,16 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint
     if (out_type == W4A8_OUT_F16 && (!sx || !sw)) return W4A8_ERR_NULL_PTR;
     if (!aligned16(X) || !aligned16(wq) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
     if ((sx && !aligned4(sx)) || (sw && !aligned4(sw))) return W4A8_ERR_ALIGNMENT;
-    if (workspace_bytes < w4a8_workspace_size(M, N, K, splitk)) return W4A8_ERR_WORKSPACE;
-    (void)workspace;
+    const size_t need = w4a8_workspace_size(M, N, K, splitk);
+    if (workspace_bytes < need) return W4A8_ERR_WORKSPACE;
+    if (need > 0 && !workspace) return W4A8_ERR_NULL_PTR;
+    if (need > 0 && !aligned16(workspace)) return W4A8_ERR_ALIGNMENT;
     w4a8_status_t d = check_device();
     if (d != W4A8_OK) return d;
     if (splitk == 0 && use_mfma_tiles(M, N, K))
         return hip_status(w4a8::launch_w4a8_mfma(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
-                                                 group, choose_mt(M, N), stream));
+                                                 group, w4a8::plan_w4a8_mfma(M, N, K), workspace,
+                                                 stream));
     return hip_status(w4a8::launch_w4a8_stream(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
                                                group, choose_stream(M, N, K, splitk), stream));
 }

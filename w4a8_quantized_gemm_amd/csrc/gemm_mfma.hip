@@ -146,153 +146,6 @@ __device__ __forceinline__ void mfma_drain() {
 
 }  // namespace
 
-template <int MT, int OUT>
-__global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4a8_mfma_kernel(
-    const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
-    const uint8_t* __restrict__ s_u8, const uint8_t* __restrict__ a_u8,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, int group,
-    int tiles_n, int tiles_m) {
-    constexpr int MB = MT / 16;          // 16-row blocks per wave
-    constexpr int CPT = MT * 8 / 256;    // 16-byte X chunks per thread per K-step
-    __shared__ __attribute__((aligned(1024))) uint8_t xs[2][MT * 128];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    const int r = lane & 15, G = lane >> 4;
-
-    // Workgroup -> tile.  Workgroups are dealt round-robin to the 8 XCDs;
-    // regroup so each XCD walks a contiguous run of tiles, with the M tiles
-    // of one channel panel adjacent (the weight panel stays in that L2).
-    const int nwg = tiles_n * tiles_m;
-    const int bid = blockIdx.x;
-    int lin = bid;
-    if ((nwg & 7) == 0) lin = (bid & 7) * (nwg >> 3) + (bid >> 3);
-    const int tm = lin % tiles_m;
-    const int tn = lin / tiles_m;
-    const int m0 = tm * MT;
-    const int n0 = tn * kNT + wave * kColsPerWave;
-
-    const int KT = K / kTileK;
-    const int groups = K / group;
-
-    // ---- X staging: chunk c = tid + 256p is row c/8, 16-byte column c%8;
-    // it is stored in LDS slot (c%8) ^ xswz(row).  Rows past M re-read row
-    // M-1: their products land in accumulator rows that are never stored.
-    unsigned xoff[CPT];   // byte offsets into X (M*K < 2^32 is checked on the host)
-    int xlds[CPT];        // LDS byte offsets within a buffer
-#pragma unroll
-    for (int p = 0; p < CPT; ++p) {
-        const int c = tid + 256 * p;
-        const int row = c >> 3, col16 = c & 7;
-        const int m = min(m0 + row, M - 1);
-        xoff[p] = (unsigned)m * (unsigned)K + (unsigned)(col16 * 16);
-        xlds[p] = row * 128 + ((col16 ^ xswz(row & 15)) * 16);
-    }
-    v4i xr[CPT];
-    auto load_x = [&](int kt) {
-#pragma unroll
-        for (int p = 0; p < CPT; ++p) xr[p] = load16(X + xoff[p] + (unsigned)(kt * kTileK));
-    };
-    auto store_x = [&](uint8_t* dst) {
-#pragma unroll
-        for (int p = 0; p < CPT; ++p) *reinterpret_cast<v4i*>(dst + xlds[p]) = xr[p];
-    };
-    // A operand of row block i, half h: row 16i + r, column 2G + h.
-    const int aoff0 = r * 128 + (((2 * G) ^ xswz(r)) * 16);
-    const int aoff1 = r * 128 + (((2 * G + 1) ^ xswz(r)) * 16);
-
-    // ---- weights: the wave's 64 channels are one parameter panel.
-    const int nt0 = n0 / kTileN;
-    const uint8_t* wpanel = wq + (size_t)nt0 * KT * kTileBytes;   // wave-uniform
-    const unsigned wlane = (unsigned)lane * 16u;
-    const size_t ppanel = (size_t)64 * (size_t)(n0 >> 6) * groups;  // wave-uniform
-    const unsigned plane = 4u * (unsigned)r;
-    auto load_w = [&](int kt, WStep& ws) {
-        const int j = (kt * kTileK + 32 * G) / group;
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-            ws.w[b] = load16(wpanel + ((size_t)b * KT + kt) * kTileBytes + wlane);
-        const size_t po = ppanel + (size_t)64 * j + plane;
-        ws.sdw = *reinterpret_cast<const unsigned*>(s_u8 + po);
-        ws.adw = *reinterpret_cast<const unsigned*>(a_u8 + po);
-    };
-
-    v4i acc[MB][4];
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int b = 0; b < 4; ++b) acc[i][b] = v4i{0, 0, 0, 0};
-
-    WStep wn;
-    v4i B[4][2];
-    load_x(0);
-    load_w(0, wn);
-    store_x(&xs[0][0]);
-    dequant_half(wn, 0, B);
-    dequant_half(wn, 1, B);
-    __syncthreads();
-
-    // The loop body is branch-free: the prefetch index is clamped to the
-    // last step (the extra loads are never consumed).
-    for (int kt = 0; kt < KT; ++kt) {
-        const int buf = kt & 1;
-        const int kn = min(kt + 1, KT - 1);
-        load_x(kn);
-        load_w(kn, wn);
-        const uint8_t* xb = &xs[buf][0];
-
-        // A operands stream through a ring of kRing registers, each read
-        // kRing row blocks before its use (half 0 then half 1).
-        constexpr int kRing = 4;
-        auto read_a = [&](int j) {
-            const int h = j / MB, i = j % MB;
-            return *reinterpret_cast<const v4i*>(xb + i * 2048 + (h ? aoff1 : aoff0));
-        };
-        v4i Ar[kRing];
-#pragma unroll
-        for (int d = 0; d < kRing; ++d) Ar[d] = read_a(d);
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-#pragma unroll
-            for (int i = 0; i < MB; ++i) {
-                const int j = h * MB + i;
-                const v4i a = Ar[j % kRing];
-                if (j + kRing < 2 * MB) Ar[j % kRing] = read_a(j + kRing);
-#pragma unroll
-                for (int b = 0; b < 4; ++b) mfma_i8_acc(acc[i][b], a, B[b][h]);
-            }
-        }
-        store_x(&xs[buf ^ 1][0]);
-        dequant_half(wn, 0, B);
-        dequant_half(wn, 1, B);
-        __syncthreads();
-    }
-
-    mfma_drain();
-
-    // ---- epilogue: lane holds rows m0 + 16i + 4G + v, channel n0 + 16b + r
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const int n = n0 + 16 * b + r;
-        const float swn = (OUT == 1) ? 0.0f : sw[n];
-#pragma unroll
-        for (int i = 0; i < MB; ++i) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int m = m0 + 16 * i + 4 * G + v;
-                if (m >= M) continue;
-                if (OUT == 1) {
-                    reinterpret_cast<int*>(Y)[(size_t)m * N + n] = acc[i][b][v];
-                } else {
-                    const float y = ((float)acc[i][b][v] * sx[m]) * swn;
-                    reinterpret_cast<unsigned short*>(Y)[(size_t)m * N + n] = f32_to_f16_bits(y);
-                }
-            }
-        }
-    }
-}
-
 // 256-row variant (one workgroup per CU), built on v_mfma_i32_32x32x32_i8:
 // half as many matrix-core instructions per K-step as the 16x16 form, so
 // each one leaves a 32-cycle shadow for the dequantisation, LDS and memory
@@ -344,6 +197,18 @@ __device__ __forceinline__ void wparams(const WStep32& w, int tb, WParams& p) {
         const unsigned b = (unsigned)(2 * cb + tb);
         const unsigned sel = b | 0x0C00u | (b << 16) | 0x0C000000u;
         asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.s2[cb]) : "v"(w.sdw), "v"(sel));
+        asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.a4[cb]) : "v"(w.adw), "v"(b * 0x01010101u));
+    }
+}
+
+template <int K_>
+__device__ __forceinline__ void wparam_step(const WStep32& w, int tb, WParams& p) {
+    constexpr int cb = K_ / 2;
+    const unsigned b = (unsigned)(2 * cb + tb);
+    if constexpr (K_ % 2 == 0) {
+        const unsigned sel = b | 0x0C00u | (b << 16) | 0x0C000000u;
+        asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.s2[cb]) : "v"(w.sdw), "v"(sel));
+    } else {
         asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.a4[cb]) : "v"(w.adw), "v"(b * 0x01010101u));
     }
 }
@@ -401,15 +266,17 @@ __device__ __forceinline__ void mfma32_drain() {
 
 }  // namespace
 
-template <int OUT, int GROUP>
-__global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
+template <int MT, int OUT, int GROUP, bool PARTIAL>
+__global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ s_u8, const uint8_t* __restrict__ a_u8,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, int tiles_n,
-    int tiles_m) {
-    constexpr int MT = 256;
-    constexpr int RB = 8;          // 32-row blocks per wave
-    constexpr int CPT = 8;         // 16-byte X chunks per thread per K-step
+    const float* __restrict__ sw, void* __restrict__ Y, int* __restrict__ part, int M, int N,
+    int K, int tiles_n, int tiles_m, int splits) {
+    constexpr int RB = MT / 32;        // 32-row blocks per wave
+    constexpr int CPT = MT / 32;       // 16-byte X chunks per thread per K-step
+    constexpr int SLOTS = 8 * RB;      // matrix-core instructions per wave per K-step
+    constexpr int GS = SLOTS / 4;      // slots per instruction group i
+    constexpr int DQ = (32 + GS - 1) / GS;  // dequantisation steps per slot
     __shared__ __attribute__((aligned(1024))) uint8_t xs0[MT * 128];
     __shared__ __attribute__((aligned(1024))) uint8_t xs1[MT * 128];
     __shared__ float sxs[MT];
@@ -420,15 +287,23 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
     const int c = lane & 31, h = lane >> 5;
     const int tb = c >> 4, r = c & 15;
 
-    const int nwg = tiles_n * tiles_m;
+    // Workgroup -> (tile, K split).  Workgroups are dealt round-robin to the
+    // 8 XCDs; regroup so each XCD walks a contiguous run, with the M tiles of
+    // one channel panel adjacent (the weight panel stays in that L2).
+    const int ntiles = tiles_n * tiles_m;
+    const int nwg = ntiles * splits;
     const int bid = blockIdx.x;
     int lin = bid;
     if ((nwg & 7) == 0) lin = (bid & 7) * (nwg >> 3) + (bid >> 3);
-    const int tm = lin % tiles_m;
-    const int tn = lin / tiles_m;
+    const int ks = lin / ntiles;
+    const int tile = lin % ntiles;
+    const int tm = tile % tiles_m;
+    const int tn = tile / tiles_m;
     const int m0 = tm * MT;
     const int n0 = tn * kNT + wave * kColsPerWave;
-    const int KT = K / kTileK;
+    const int KTall = K / kTileK;
+    const int kt0 = (int)((long long)KTall * ks / splits);
+    const int KT = (int)((long long)KTall * (ks + 1) / splits) - kt0;  // >= 1
     const int groups = K / GROUP;
 
     // ---- X: chunk p of this thread is row (tid>>3) + 32p, 16-byte column
@@ -436,7 +311,8 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
     // for all p).  Rows >= M lie past the end of the buffer and read as 0.
     const __amdgpu_buffer_rsrc_t xr_rsrc = buf_rsrc(X, (unsigned)M * (unsigned)K);
     const int xrow0 = tid >> 3, xcol = tid & 7;
-    const unsigned xvoff = (unsigned)(m0 + xrow0) * (unsigned)K + (unsigned)(xcol * 16);
+    const unsigned xvoff =
+        (unsigned)(m0 + xrow0) * (unsigned)K + (unsigned)(xcol * 16) + (unsigned)(kt0 * kTileK);
     const unsigned xrowstep = 32u * (unsigned)K;
     const int xlds0 = xrow0 * 128 + ((xcol ^ xswz(xrow0 & 15)) * 16);
     // A operand (row block rb, instruction i): row 32rb + c, column 4h + i.
@@ -449,17 +325,18 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
     const __amdgpu_buffer_rsrc_t w_rsrc = buf_rsrc(wq, (unsigned)((size_t)N * K / 2));
     const __amdgpu_buffer_rsrc_t s_rsrc = buf_rsrc(s_u8, (unsigned)((size_t)N * K / GROUP));
     const __amdgpu_buffer_rsrc_t a_rsrc = buf_rsrc(a_u8, (unsigned)((size_t)N * K / GROUP));
-    const unsigned wvoff = (unsigned)(tb * KT) * kTileBytes + (unsigned)(32 * h + r) * 16u;
+    const unsigned wvoff = (unsigned)(tb * KTall) * kTileBytes + (unsigned)(32 * h + r) * 16u;
     const unsigned pvoff = 4u * (unsigned)r + (GROUP == 64 ? 64u * (unsigned)h : 0u);
     const unsigned ppanel = 64u * (unsigned)(n0 >> 6) * (unsigned)groups;
-    auto w_load = [&](int kt, int part, WStep32& ws) {  // part 0..5
-        if (part < 4) {
-            const int cb = part >> 1, e = part & 1;
-            ws.w[cb][e] = buf_load16(w_rsrc, wvoff,
-                                     (unsigned)(((nt0 + 2 * cb) * KT + kt) * kTileBytes + e * 256));
+    auto w_load = [&](int kt, int part_i, WStep32& ws) {  // part_i 0..5
+        const int ktg = kt0 + kt;
+        if (part_i < 4) {
+            const int cb = part_i >> 1, e = part_i & 1;
+            ws.w[cb][e] = buf_load16(
+                w_rsrc, wvoff, (unsigned)(((nt0 + 2 * cb) * KTall + ktg) * kTileBytes + e * 256));
         } else {
-            const unsigned jo = ppanel + 64u * (unsigned)(kt * (kTileK / GROUP));
-            if (part == 4) ws.sdw = buf_load4(s_rsrc, pvoff, jo);
+            const unsigned jo = ppanel + 64u * (unsigned)(ktg * (kTileK / GROUP));
+            if (part_i == 4) ws.sdw = buf_load4(s_rsrc, pvoff, jo);
             else ws.adw = buf_load4(a_rsrc, pvoff, jo);
         }
     };
@@ -487,9 +364,9 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
 #pragma unroll
     for (int p = 0; p < CPT; ++p) xo[p] = x_load(k1, p);
 #pragma unroll
-    for (int part = 0; part < 6; ++part) w_load(0, part, we);
+    for (int pi = 0; pi < 6; ++pi) w_load(0, pi, we);
 #pragma unroll
-    for (int part = 0; part < 6; ++part) w_load(k1, part, wo);
+    for (int pi = 0; pi < 6; ++pi) w_load(k1, pi, wo);
 #pragma unroll
     for (int p = 0; p < CPT; ++p) *reinterpret_cast<v4i*>(xs0 + xlds0 + p * 4096) = xe[p];
     wparams(we, tb, pp);
@@ -498,56 +375,55 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
     dq_group_all<2>(we, pp, B);
     dq_group_all<3>(we, pp, B);
     __syncthreads();
+    auto read_a = [&](const uint8_t* buf, int sI) {  // sI = RB*i + rb
+        return *reinterpret_cast<const v4i*>(buf + (sI % RB) * 4096 + aoff[sI / RB]);
+    };
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ring[q] = *reinterpret_cast<const v4i*>(xs0 + q * 4096 + aoff[0]);
+    for (int q = 0; q < 4; ++q) ring[q] = read_a(xs0, q);
 
-    // ---- one K-step, 64 matrix-core slots.  Slot s: instruction i = s/16,
-    // row block rb = (s/2)%8, channel block cb = s%2.  Entering step kt:
-    // LDS `cur` = X(kt); ring holds A for slots 0..7; B[*][0..2] = W(kt)
-    // operands and B[*][3] is produced in slots 0..15 from `wcur` (raw W(kt),
-    // parameters pp); `xnx` = X(kt+1) staged; `wnx` = raw W(kt+1).
-    //   slots 0..7    X(kt+2) -> xcur (the set that held X(kt))
-    //   slots 16..21  W(kt+2) -> wcur (done with it after slot 15)
-    //   slots 16..63  B[*][i-1] for step kt+1 from wnx, i = 1..3
-    //   slots 52..59  X(kt+1) -> LDS `nxt`
-    //   after slot 59: barrier, then step kt+1's first four A reads, then
-    //   slots 60..63 (their operands were read before the barrier).
+    // ---- one K-step, SLOTS matrix-core slots.  Slot s: instruction group
+    // i = s / GS, row block rb = (s/2) % RB, channel block cb = s % 2.
+    // Entering step kt: LDS `cur` = X(kt); ring holds A for the first
+    // slots; B[*][0..2] = W(kt) operands and B[*][3] is produced during
+    // group 0 from `wcur` (raw W(kt), parameters pp); `xnx` = X(kt+1)
+    // staged; `wnx` = raw W(kt+1).
+    //   group 0 slots      X(kt+2) -> xcur; B[*][3] of step kt
+    //   group 1 slots      W(kt+2) -> wcur; parameters of wnx, B[*][0] of kt+1
+    //   groups 2, 3        B[*][1], B[*][2] of step kt+1
+    //   last 4+CPT slots   X(kt+1) -> LDS `nxt` (before the last 4)
+    //   before the last 4  barrier, then step kt+1's first four A reads; the
+    //                      last four slots use operands read earlier.
     auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, v4i (&xcur)[CPT],
                     v4i (&xnx)[CPT], WStep32& wcur, WStep32& wnx) {
         const int k2 = min(kt + 2, KT - 1);
         DqTmp tmp;
-        auto read_a = [&](const uint8_t* buf, int sI) {  // sI = 8i + rb
-            return *reinterpret_cast<const v4i*>(buf + (sI & 7) * 4096 + aoff[sI >> 3]);
-        };
-        static_for<64>([&](auto sc) {
+        static_for<SLOTS>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
-            constexpr int sI = s / 2, i = sI / 8, rb = sI % 8, cb = s % 2;
-            if constexpr (s == 60) {
+            constexpr int sI = s / 2, i = sI / RB, rb = sI % RB, cb = s % 2;
+            constexpr int g = s / GS, sg = s % GS;
+            if constexpr (s == SLOTS - 4) {
                 __syncthreads();
 #pragma unroll
                 for (int q = 0; q < 4; ++q) ring[q] = read_a(nxt, q);
             }
             mfma32_i8_acc(acc[rb][cb], ring[sI % 8], B[cb][i]);
-            if constexpr (cb == 1 && sI + 4 < 32) ring[(sI + 4) % 8] = read_a(cur, sI + 4);
-            if constexpr (s < 8) xcur[s] = x_load(k2, s);
-            if constexpr (s >= 16 && s < 22) w_load(k2, s - 16, wcur);
-            if constexpr (s >= 52 && s < 60)
-                *reinterpret_cast<v4i*>(nxt + xlds0 + (s - 52) * 4096) = xnx[s - 52];
-            // dequantisation: 28 steps per 16 slots, 2 per slot (the
-            // parameter extraction for wnx takes slot 16's pair)
-            if constexpr (s < 16) {
-                constexpr int o0 = 2 * s;
-                if constexpr (o0 < 28) dq_group_step<3, o0>(tmp, wcur, pp, B);
-                if constexpr (o0 + 1 < 28) dq_group_step<3, o0 + 1>(tmp, wcur, pp, B);
-            } else if constexpr (s == 16) {
-                wparams(wnx, tb, pp);
-            } else {
-                constexpr int g = s / 16;            // producing B[*][g-1]
-                constexpr int o0 = 2 * (s % 16) - (g == 1 ? 2 : 0);
-                if constexpr (o0 >= 0 && o0 < 28) dq_group_step<g - 1, o0>(tmp, wnx, pp, B);
-                if constexpr (o0 + 1 >= 0 && o0 + 1 < 28)
-                    dq_group_step<g - 1, o0 + 1>(tmp, wnx, pp, B);
-            }
+            if constexpr (cb == 1 && sI + 4 < 4 * RB) ring[(sI + 4) % 8] = read_a(cur, sI + 4);
+            if constexpr (s < CPT) xcur[s] = x_load(k2, s);
+            if constexpr (s >= GS && s < GS + 6) w_load(k2, s - GS, wcur);
+            if constexpr (s >= SLOTS - 4 - CPT && s < SLOTS - 4)
+                *reinterpret_cast<v4i*>(nxt + xlds0 + (s - (SLOTS - 4 - CPT)) * 4096) =
+                    xnx[s - (SLOTS - 4 - CPT)];
+            static_for<DQ>([&](auto dc) {
+                constexpr int o = DQ * sg + decltype(dc)::value;
+                if constexpr (g == 0) {
+                    if constexpr (o < 28) dq_group_step<3, o>(tmp, wcur, pp, B);
+                } else if constexpr (g == 1) {
+                    if constexpr (o < 4) wparam_step<o>(wnx, tb, pp);
+                    else if constexpr (o - 4 < 28) dq_group_step<0, o - 4>(tmp, wnx, pp, B);
+                } else {
+                    if constexpr (o < 28) dq_group_step<g - 1, o>(tmp, wnx, pp, B);
+                }
+            });
         });
     };
 
@@ -562,16 +438,19 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
     __syncthreads();  // all waves done with the X buffers
 
     // ---- epilogue.  Accumulator (rb, cb) register v of lane (c, h): row
-    // 32rb + 8(v/4) + 4h + (v%4), channel n0 + 32cb + c.  Scaled values go
-    // to a per-wave LDS block [32 rows][64 channels]; each row is then
-    // written as whole 16-byte pieces.
-    if (OUT == 0) sxs[tid] = (m0 + tid < M) ? sx[m0 + tid] : 0.0f;
-    const float sw0 = (OUT == 0) ? sw[n0 + c] : 0.0f;
-    const float sw1 = (OUT == 0) ? sw[n0 + 32 + c] : 0.0f;
+    // 32rb + 8(v/4) + 4h + (v%4), channel n0 + 32cb + c.  Values go to a
+    // per-wave LDS block [32 rows][64 channels]; each row is then written as
+    // whole 16-byte pieces (final output, or this split's int32 partial).
+    constexpr bool SCALED = (OUT == 0) && !PARTIAL;
+    if (SCALED) sxs[tid % MT] = (m0 + tid % MT < M) ? sx[m0 + tid % MT] : 0.0f;
+    const float sw0 = SCALED ? sw[n0 + c] : 0.0f;
+    const float sw1 = SCALED ? sw[n0 + 32 + c] : 0.0f;
     __syncthreads();
-    constexpr int EB = (OUT == 1) ? 4 : 2;   // output element bytes
+    constexpr int EB = SCALED ? 2 : 4;       // output element bytes
     constexpr int ROWB = 64 * EB;             // bytes per staged row
     uint8_t* stage = xs0 + wave * (32 * ROWB);
+    uint8_t* out = PARTIAL ? reinterpret_cast<uint8_t*>(part + (size_t)ks * M * N)
+                           : reinterpret_cast<uint8_t*>(Y);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
@@ -580,7 +459,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
             for (int v = 0; v < 16; ++v) {
                 const int row = 8 * (v >> 2) + 4 * h + (v & 3);
                 const int col = 32 * cb + c;
-                if (OUT == 1) {
+                if (!SCALED) {
                     *reinterpret_cast<int*>(stage + row * ROWB + col * 4) = acc[rb][cb][v];
                 } else {
                     const float y = ((float)acc[rb][cb][v] * sxs[32 * rb + row]) * (cb ? sw1 : sw0);
@@ -600,48 +479,96 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma256_kernel(
             const int m = m0 + 32 * rb + row;
             const v4i val = *reinterpret_cast<const v4i*>(stage + row * ROWB + piece * 16);
             if (m < M)
-                *reinterpret_cast<v4i*>(reinterpret_cast<uint8_t*>(Y) +
-                                        ((size_t)m * N + n0) * EB + piece * 16) = val;
+                *reinterpret_cast<v4i*>(out + ((size_t)m * N + n0) * EB + piece * 16) = val;
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
     }
 }
 
-template <int MT>
-static hipError_t launch_mt(const int8_t* X, const float* sx, const uint8_t* wq,
-                            const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
-                            int out_type, int M, int N, int K, int group, hipStream_t st) {
+// Sum of the split-K partial tiles in split order (exact int32), then the
+// per-token x per-channel scale to fp16, or the raw int32 sums.  Each thread
+// handles four consecutive channels of one row.
+template <int OUT>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(
+    const int* __restrict__ part, int splits, int M, int N, const float* __restrict__ sx,
+    const float* __restrict__ sw, void* __restrict__ Y) {
+    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t MN = (size_t)M * N;
+    if (q * 4 >= MN) return;
+    const size_t e = q * 4;
+    v4i acc = *reinterpret_cast<const v4i*>(part + e);
+    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const v4i*>(part + s * MN + e);
+    if (OUT == 1) {
+        *reinterpret_cast<v4i*>(reinterpret_cast<int*>(Y) + e) = acc;
+    } else {
+        const int m = (int)(e / N), n = (int)(e % N);
+        const float sm = sx[m];
+        unsigned short hv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) hv[j] = f32_to_f16_bits(((float)acc[j] * sm) * sw[n + j]);
+        uint2 pk;
+        pk.x = hv[0] | ((unsigned)hv[1] << 16);
+        pk.y = hv[2] | ((unsigned)hv[3] << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<unsigned short*>(Y) + e) = pk;
+    }
+}
+
+// Workgroup tile height and K split for the matrix-core kernel.
+MfmaPlan plan_w4a8_mfma(int M, int N, int K) {
+    MfmaPlan p;
+    const int KT = K / kTileK;
+    const long long t256 = (long long)(N / kNT) * ((M + 255) / 256);
+    p.mt = (M > 128 && t256 >= 256) ? 256 : 128;
+    const long long tiles = (long long)(N / kNT) * ((M + p.mt - 1) / p.mt);
+    p.splits = 1;
+    while (p.splits < 16 && tiles * p.splits < 256 && KT / (2 * p.splits) >= 4) p.splits *= 2;
+    p.workspace = p.splits > 1 ? (size_t)p.splits * M * N * sizeof(int) : 0;
+    return p;
+}
+
+template <int MT, int OUT, bool PARTIAL>
+static void launch_tile(const int8_t* X, const float* sx, const uint8_t* wq, const uint8_t* s_u8,
+                        const uint8_t* a_u8, const float* sw, void* Y, int* part, int M, int N,
+                        int K, int group, int splits, hipStream_t st) {
     const int tiles_n = N / kNT;
     const int tiles_m = (M + MT - 1) / MT;
-    dim3 grid(tiles_n * tiles_m), block(256);
-    if (out_type == 1)
-        hipLaunchKernelGGL((w4a8_mfma_kernel<MT, 1>), grid, block, 0, st, X, sx, wq, s_u8, a_u8,
-                           sw, Y, M, N, K, group, tiles_n, tiles_m);
+    dim3 grid(tiles_n * tiles_m * splits), block(256);
+    if (group == 64)
+        hipLaunchKernelGGL((w4a8_mfma_kernel<MT, OUT, 64, PARTIAL>), grid, block, 0, st, X, sx, wq,
+                           s_u8, a_u8, sw, Y, part, M, N, K, tiles_n, tiles_m, splits);
     else
-        hipLaunchKernelGGL((w4a8_mfma_kernel<MT, 0>), grid, block, 0, st, X, sx, wq, s_u8, a_u8,
-                           sw, Y, M, N, K, group, tiles_n, tiles_m);
-    return hipGetLastError();
+        hipLaunchKernelGGL((w4a8_mfma_kernel<MT, OUT, 128, PARTIAL>), grid, block, 0, st, X, sx,
+                           wq, s_u8, a_u8, sw, Y, part, M, N, K, tiles_n, tiles_m, splits);
 }
 
 hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
                             const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
-                            int out_type, int M, int N, int K, int group, int mt,
-                            hipStream_t st) {
-    if (mt == 128)
-        return launch_mt<128>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, st);
-    const int tiles_n = N / kNT;
-    const int tiles_m = (M + 255) / 256;
-    dim3 grid(tiles_n * tiles_m), block(256);
-#define W4A8_L256(O, G)                                                                         \
-    hipLaunchKernelGGL((w4a8_mfma256_kernel<O, G>), grid, block, 0, st, X, sx, wq, s_u8, a_u8, \
-                       sw, Y, M, N, K, tiles_n, tiles_m)
-    if (out_type == 1) {
-        if (group == 64) W4A8_L256(1, 64); else W4A8_L256(1, 128);
-    } else {
-        if (group == 64) W4A8_L256(0, 64); else W4A8_L256(0, 128);
+                            int out_type, int M, int N, int K, int group, const MfmaPlan& plan,
+                            void* workspace, hipStream_t st) {
+    int* part = reinterpret_cast<int*>(workspace);
+    if (plan.splits == 1) {
+        if (plan.mt == 256) {
+            if (out_type == 1) launch_tile<256, 1, false>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st);
+            else launch_tile<256, 0, false>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st);
+        } else {
+            if (out_type == 1) launch_tile<128, 1, false>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st);
+            else launch_tile<128, 0, false>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st);
+        }
+        return hipGetLastError();
     }
-#undef W4A8_L256
+    if (plan.mt == 256)
+        launch_tile<256, 1, true>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, plan.splits, st);
+    else
+        launch_tile<128, 1, true>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, plan.splits, st);
+    const size_t quads = ((size_t)M * N) / 4;
+    const unsigned blocks = (unsigned)((quads + 255) / 256);
+    if (out_type == 1)
+        hipLaunchKernelGGL((splitk_reduce_kernel<1>), dim3(blocks), dim3(256), 0, st, part,
+                           plan.splits, M, N, sx, sw, Y);
+    else
+        hipLaunchKernelGGL((splitk_reduce_kernel<0>), dim3(blocks), dim3(256), 0, st, part,
+                           plan.splits, M, N, sx, sw, Y);
     return hipGetLastError();
 }
 

@@ -26,11 +26,20 @@ hipError_t launch_w4a8_stream(const int8_t* X, const float* sx, const uint8_t* w
                               void* Y, int out_type, int M, int N, int K, int group,
                               StreamCfg cfg, hipStream_t st);
 
-// Matrix-core tile kernel for large M: N % 256 == 0, mt = 128 or 256 rows.
+// Matrix-core tile kernel (N % 256 == 0): workgroup tiles of mt = 128 or
+// 256 rows x 256 channels; with splits > 1 each workgroup covers 1/splits of
+// K and writes int32 partial tiles to the workspace, then a reduction
+// kernel sums them in split order and applies the epilogue.
+struct MfmaPlan {
+    int mt;
+    int splits;
+    size_t workspace;  // bytes of int32 partials (0 when splits == 1)
+};
+MfmaPlan plan_w4a8_mfma(int M, int N, int K);
 hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
                             const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
-                            int out_type, int M, int N, int K, int group, int mt,
-                            hipStream_t st);
+                            int out_type, int M, int N, int K, int group, const MfmaPlan& plan,
+                            void* workspace, hipStream_t st);
 
 hipError_t launch_w4fp8_stream(const uint8_t* X, const float* sx, const uint8_t* wq,
                                const float* sw, void* Y, int out_type, int M, int N, int K,
