@@ -49,21 +49,32 @@ bool valid_group(int g) { return g == 64 || g == 128; }
 
 int k_tiles(int K) { return K / 128; }
 
-// Split of K across the waves of one workgroup, and weight tiles per wave.
-// Aim: enough waves in flight to cover HBM latency on 256 CUs without
-// shrinking each wave's K range below a few tiles.
+// Streamed kernel: NTW 16-channel tiles per workgroup, ks waves splitting K.
+// Aim for one workgroup per CU (256 CUs): NTW = tiles / 256 where that is a
+// supported width, else the widest supported NTW that divides the tile
+// count and still gives >= 256 workgroups; eight K-splitting waves (fewer
+// when K has fewer K-tiles).
 w4a8::StreamCfg choose_stream(int M, int N, int K, int splitk) {
+    (void)M;
     w4a8::StreamCfg c;
-    const int mt = (M + 15) / 16;
-    c.nt_per_wave = 2;  // N % 64 == 0
-    const long long wgs = (long long)(N / (16 * c.nt_per_wave)) * mt;
-    if (splitk > 0) {
+    const int tiles = N / 16;
+    const int widths[5] = {7, 4, 3, 2, 1};
+    c.nt_per_wave = 1;
+    for (int i = 0; i < 5; ++i) {
+        const int w = widths[i];
+        if (tiles % w == 0 && tiles / w >= 256) {
+            c.nt_per_wave = w;
+            break;
+        }
+    }
+    // Eight K-interleaved waves per workgroup (measured best for 1..7 tiles).
+    const int ks_max = 8;
+    if (splitk > 0) {  // an explicit split keeps the narrowest width (fits 16 waves)
+        c.nt_per_wave = 1;
         c.ks = splitk;
     } else {
-        const long long target_waves = 256LL * 24;
-        int ks = 1;
-        while (ks < 16 && wgs * ks < target_waves && k_tiles(K) / (ks * 2) >= 4) ks *= 2;
-        c.ks = ks;
+        c.ks = ks_max;
+        while (c.ks > 1 && k_tiles(K) < c.ks) c.ks /= 2;
     }
     return c;
 }

@@ -14,6 +14,9 @@ typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
 constexpr int kTileN = 16;     // rows of one packed tile
 constexpr int kTileK = 128;    // K columns of one packed tile
 constexpr int kTileBytes = 1024;
+// Cache-policy operand of buffer loads: non-temporal, for data read once
+// (the packed weight stream), so it does not displace L2-resident operands.
+constexpr int kNonTemporal = 2;
 
 // 16-byte global load through the vector memory path.
 __device__ __forceinline__ v4i load16(const void* p) {

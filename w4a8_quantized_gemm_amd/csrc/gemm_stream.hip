@@ -1,4 +1,4 @@
-// Streamed-tile W4A8 and W4FP8 GEMM kernels for gfx950 (any M; the
+// Streamed-tile W4A8 and W4FP8 GEMM kernels for gfx950 (small M; the
 // weight-bandwidth-bound decode path).
 //
 // Each wave streams packed weight tiles (16 rows x 128 K = 1 KiB, one
@@ -22,85 +22,218 @@
 
 namespace w4a8 {
 
-template <int NTW, int OUT>
-__global__ __launch_bounds__(1024) void w4a8_stream_kernel(
+// Panels (64 channels, four tiles) that NTW consecutive tiles can touch.
+template <int NTW>
+__host__ __device__ constexpr int stream_param_span() {
+    return (NTW + 3) / 4 + 1;
+}
+
+// Swizzled 16-byte piece position of row R's piece c in a 16 x 128-byte X
+// tile held in LDS (row stride 128 bytes): conflict-free for the row-wise
+// writes and for the MFMA-layout reads below.
+__device__ __forceinline__ int xpiece(int R, int c) {
+    return R * 128 + 16 * (c ^ ((R & 7) ^ ((R >> 3) & 1)));
+}
+
+// W4A8 decode-shaped GEMM (M < 64).  One workgroup per NTW packed tiles
+// (16 channels each) and one 16-row block of X, sized so the grid is about
+// one workgroup per CU; its `ks` waves take interleaved K-tiles (wave w:
+// w, w + ks, ...), so at any moment a CU reads adjacent tiles of its channel
+// rows.  Each wave keeps D K-tiles of weight loads in flight (a register
+// ring refilled as each stage is consumed); the weight stream is loaded
+// non-temporally.  The per-group parameters of the workgroup's tiles are
+// copied to LDS once (whole 64-byte panel rows) when they fit.  X tiles
+// (L2-resident) are loaded eight whole 128-byte rows per instruction and
+// re-laid out through a per-wave LDS slot into the MFMA operand layout.
+// The ks partial tiles are summed by all threads of the workgroup in wave
+// order (exact).
+template <int NTW, int D, int OUT, int GROUP, bool LDSP>
+__global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ s_u8, const uint8_t* __restrict__ a_u8,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, int group, int ks) {
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, int ks) {
     extern __shared__ int red[];
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    // X through LDS pays where X is a large share of the loads (narrow
+    // workgroups: 2 KB of X per K-tile against NTW KB of weights).
+    constexpr bool kXlds = true;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, G = lane >> 4;
     const int KT = K / kTileK;
-    const int groups = K / group;
-    const int nt0 = blockIdx.x * NTW;
+    const int groups = K / GROUP;
+    // Workgroups are dealt round-robin to the eight XCDs (b -> b % 8), each
+    // with its own L2: give workgroups b and b + 8 adjacent tile groups, so
+    // the parameter panels that neighbouring groups share are read once per
+    // XCD (when the group count is a multiple of 8).
+    const int nwg = gridDim.x, b = blockIdx.x;
+    const int g = (nwg & 7) ? b : (b & 7) * (nwg >> 3) + (b >> 3);
+    const int nt0 = g * NTW;
     const int m0 = blockIdx.y * 16;
-    const int kt_begin = (int)((long long)KT * wave / ks);
-    const int kt_end = (int)((long long)KT * (wave + 1) / ks);
-    const int m = m0 + r;
-    const bool mvalid = m < M;
-    const int8_t* xrow = X + (size_t)(mvalid ? m : 0) * K + 32 * G;
-    const uint8_t* wlane = wq + (size_t)lane * 16;
+    const int nk = (KT - wave + ks - 1) / ks;  // K-tiles of this wave (>= 1: ks <= KT)
+    // i-th K-tile of this wave (i < nk)
+    auto kt_of = [&](int i) { return wave + ks * i; };
+
+    const __amdgpu_buffer_rsrc_t x_rsrc =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(X), (short)0, M * K, 0x00020000);
+    const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(wq), (short)0, (int)((size_t)N * K / 2), 0x00020000);
+    const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(s_u8), (short)0, (int)((size_t)N * K / GROUP), 0x00020000);
+    const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(a_u8), (short)0, (int)((size_t)N * K / GROUP), 0x00020000);
+    // X loads (a row >= M lies past the buffer end and reads as 0).  With
+    // the LDS re-layout, lane l takes 16-byte piece (l & 7) of rows
+    // m0 + (l >> 3) and m0 + 8 + (l >> 3); otherwise lane (r, G) loads its
+    // MFMA operand directly: row m0 + r, columns 32G .. 32G+31.
+    const unsigned xvoff =
+        kXlds ? (unsigned)(m0 + (lane >> 3)) * (unsigned)K + 16u * (unsigned)(lane & 7)
+              : (unsigned)(m0 + r) * (unsigned)K + 32u * (unsigned)G;
+    const unsigned xvoff8 = kXlds ? xvoff + 8u * (unsigned)K : xvoff + 16u;
+    const unsigned wvoff = (unsigned)lane * 16u;
+    const int gsub = (GROUP == 64) ? (G >> 1) : 0;  // group within the K-tile
+
+    // ---- LDS: [parameters (LDSP)] [one 2 KB X slot per wave]; the
+    // reduction at the end reuses it from offset 0.
+    const int p0 = nt0 >> 2;
+    const int np = ((nt0 + NTW - 1) >> 2) - p0 + 1;
+    uint8_t* lds_s = reinterpret_cast<uint8_t*>(red);
+    uint8_t* lds_a = lds_s + (size_t)np * groups * 64;
+    const int pbytes = LDSP ? 2 * stream_param_span<NTW>() * groups * 64 : 0;
+    uint8_t* xslot = reinterpret_cast<uint8_t*>(red) + pbytes + wave * 2048;
+    // MFMA operand layout: lane (r, G) holds row r, columns 32G .. 32G+31.
+    const int xw0 = xpiece(lane >> 3, lane & 7), xw1 = xpiece(8 + (lane >> 3), lane & 7);
+    const int xr0 = xpiece(r, 2 * G), xr1 = xpiece(r, 2 * G + 1);
+
+    struct Stage {
+        v4i x0, x1;
+        v4i w[NTW];
+    };
+    auto issue = [&](int kt, Stage& st) {
+        const unsigned so = (unsigned)(kt * kTileK);
+        st.x0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xvoff, so, 0));
+        st.x1 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xvoff8, so, 0));
+#pragma unroll
+        for (int t = 0; t < NTW; ++t)
+            st.w[t] = __builtin_bit_cast(
+                v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                         w_rsrc, wvoff, (unsigned)(((size_t)(nt0 + t) * KT + kt) * kTileBytes),
+                         kNonTemporal));
+    };
+    auto params = [&](int kt, int t, unsigned& s, unsigned& a) {
+        const int j = kt * (kTileK / GROUP) + gsub;
+        const int nt = nt0 + t;
+        if (LDSP) {
+            const int o = (((nt >> 2) - p0) * groups + j) * 64 + 4 * r + (nt & 3);
+            s = lds_s[o];
+            a = lds_a[o];
+        } else {
+            const unsigned po = (unsigned)param_offset(nt * kTileN + r, j, groups);
+            s = __builtin_amdgcn_raw_buffer_load_b8(s_rsrc, po, 0, 0);
+            a = __builtin_amdgcn_raw_buffer_load_b8(a_rsrc, po, 0, 0);
+        }
+    };
 
     v4i acc[NTW];
 #pragma unroll
     for (int t = 0; t < NTW; ++t) acc[t] = v4i{0, 0, 0, 0};
 
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-        v4i xa0 = v4i{0, 0, 0, 0}, xa1 = v4i{0, 0, 0, 0};
-        if (mvalid) {
-            xa0 = load16(xrow + (size_t)kt * kTileK);
-            xa1 = load16(xrow + (size_t)kt * kTileK + 16);
+    // Multiply-accumulate of the K-tile held in stage S.
+    auto consume = [&](const Stage& S, int kt) {
+        v4i x0 = S.x0, x1 = S.x1;
+        if constexpr (kXlds) {
+            // X tile -> MFMA layout through this wave's LDS slot (LDS
+            // operations of one wave complete in order).
+            *reinterpret_cast<v4i*>(xslot + xw0) = S.x0;
+            *reinterpret_cast<v4i*>(xslot + xw1) = S.x1;
+            x0 = *reinterpret_cast<const v4i*>(xslot + xr0);
+            x1 = *reinterpret_cast<const v4i*>(xslot + xr1);
         }
-        const int j = (kt * kTileK + 32 * G) / group;
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
-            const int nt = nt0 + t;
-            const v4i w = load16(wlane + ((size_t)nt * KT + kt) * kTileBytes);
-            const size_t gi = param_offset(nt * kTileN + r, j, groups);
-            const unsigned s = s_u8[gi], a = a_u8[gi];
+            unsigned s, a;
+            params(kt, t, s, a);
             const u16x2 s2 = u16x2{(unsigned short)s, (unsigned short)s};
             const unsigned short aa = (unsigned short)(a * 0x101u);
             const u16x2 a4 = u16x2{aa, aa};
             unsigned b[8];
-            lqq_dequant8((unsigned)w.x, s2, a4, b[0], b[1]);
-            lqq_dequant8((unsigned)w.y, s2, a4, b[2], b[3]);
-            lqq_dequant8((unsigned)w.z, s2, a4, b[4], b[5]);
-            lqq_dequant8((unsigned)w.w, s2, a4, b[6], b[7]);
+            lqq_dequant8((unsigned)S.w[t].x, s2, a4, b[0], b[1]);
+            lqq_dequant8((unsigned)S.w[t].y, s2, a4, b[2], b[3]);
+            lqq_dequant8((unsigned)S.w[t].z, s2, a4, b[4], b[5]);
+            lqq_dequant8((unsigned)S.w[t].w, s2, a4, b[6], b[7]);
             const v4i B0 = v4i{(int)b[0], (int)b[1], (int)b[2], (int)b[3]};
             const v4i B1 = v4i{(int)b[4], (int)b[5], (int)b[6], (int)b[7]};
-            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa0, B0, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(xa1, B1, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x0, B0, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1, B1, acc[t], 0, 0, 0);
+        }
+    };
+
+    // Stage d holds this wave's K-tile i + d.  The steady-state loop has no
+    // conditional work, so the load counter waits it needs are exact (one
+    // stage at a time) and D stages stay in flight; the last 2D-1 K-tiles
+    // at most are drained after it.
+    Stage st[D];
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (d < nk) issue(kt_of(d), st[d]);
+
+    // Parameter copy, behind the first weight loads (panels p0 .. p0+np-1
+    // are contiguous in the panel-order arrays).
+    if (LDSP) {
+        const int n16 = np * groups * 4;  // 16-byte pieces per array
+        const size_t base = (size_t)p0 * groups * 64;
+        for (int q = tid; q < n16; q += blockDim.x) {
+            const v4i vs = *reinterpret_cast<const v4i*>(s_u8 + base + (size_t)q * 16);
+            const v4i va = *reinterpret_cast<const v4i*>(a_u8 + base + (size_t)q * 16);
+            *reinterpret_cast<v4i*>(lds_s + q * 16) = vs;
+            *reinterpret_cast<v4i*>(lds_a + q * 16) = va;
+        }
+        __syncthreads();
+    }
+
+    int i = 0;
+    for (; i + 2 * D <= nk; i += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+            consume(st[d], kt_of(i + d));
+            issue(kt_of(i + d + D), st[d]);
+            // keep each refill right behind its stage's use (the scheduler
+            // would otherwise sink every refill to the end of the iteration)
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
-
-    if (ks > 1) {
 #pragma unroll
-        for (int t = 0; t < NTW; ++t)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) red[((wave * NTW + t) * 4 + v) * 64 + lane] = acc[t][v];
-        __syncthreads();
-        if (wave != 0) return;
-        for (int w = 1; w < ks; ++w)
-#pragma unroll
-            for (int t = 0; t < NTW; ++t)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[t][v] += red[((w * NTW + t) * 4 + v) * 64 + lane];
+    for (int d = 0; d < D; ++d) {
+        if (i + d < nk) {
+            consume(st[d], kt_of(i + d));
+            if (i + d + D < nk) issue(kt_of(i + d + D), st[d]);
+        }
     }
+#pragma unroll
+    for (int d = 0; d < D; ++d)
+        if (i + D + d < nk) consume(st[d], kt_of(i + D + d));
 
-    // Output: lane holds rows m0 + 4G + v, column (nt*16 + r).
+    // Sum the ks partial tiles: element e = (t * 4 + v) * 64 + l of wave w
+    // lives at red[w * NTW * 256 + e] (reusing the parameter LDS).
+    __syncthreads();
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-        const int n = (nt0 + t) * kTileN + r;
+    for (int t = 0; t < NTW; ++t)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int mo = m0 + 4 * G + v;
-            if (mo >= M) continue;
+        for (int v = 0; v < 4; ++v) red[((wave * NTW + t) * 4 + v) * 64 + lane] = acc[t][v];
+    __syncthreads();
+    const int nel = NTW * 256;
+    for (int e = tid; e < nel; e += blockDim.x) {
+        int sum = 0;
+        for (int w = 0; w < ks; ++w) sum += red[w * nel + e];
+        const int t = e >> 8, v = (e >> 6) & 3, l = e & 63;
+        const int m = m0 + 4 * (l >> 4) + v;  // accumulator row (X row)
+        const int n = (nt0 + t) * kTileN + (l & 15);
+        if (m < M) {
             if (OUT == 1) {
-                reinterpret_cast<int*>(Y)[(size_t)mo * N + n] = acc[t][v];
+                reinterpret_cast<int*>(Y)[(size_t)m * N + n] = sum;
             } else {
-                const float y = ((float)acc[t][v] * sx[mo]) * sw[n];
-                reinterpret_cast<unsigned short*>(Y)[(size_t)mo * N + n] = f32_to_f16_bits(y);
+                const float y = ((float)sum * sx[m]) * sw[n];
+                reinterpret_cast<unsigned short*>(Y)[(size_t)m * N + n] = f32_to_f16_bits(y);
             }
         }
     }
@@ -181,20 +314,37 @@ __global__ __launch_bounds__(1024) void w4fp8_stream_kernel(
 }
 
 // ----------------------------------------------------------- launchers ----
-template <int NTW>
+template <int NTW, int D>
 static hipError_t w4a8_stream_ntw(const int8_t* X, const float* sx, const uint8_t* wq,
                                   const uint8_t* s_u8, const uint8_t* a_u8, const float* sw,
                                   void* Y, int out_type, int M, int N, int K, int group, int ks,
                                   hipStream_t st) {
     dim3 grid(N / (kTileN * NTW), (M + 15) / 16);
     dim3 block(64 * ks);
-    size_t lds = ks > 1 ? (size_t)ks * NTW * 4 * 64 * sizeof(int) : 0;
-    if (out_type == 1)
-        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, 1>), grid, block, lds, st, X, sx, wq, s_u8,
-                           a_u8, sw, Y, M, N, K, group, ks);
-    else
-        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, 0>), grid, block, lds, st, X, sx, wq, s_u8,
-                           a_u8, sw, Y, M, N, K, group, ks);
+    const int groups = K / group;
+    const size_t pbytes = (size_t)2 * stream_param_span<NTW>() * groups * 64;
+    const size_t xbytes = (size_t)ks * 2048;  // X slots
+    const size_t rbytes = (size_t)ks * NTW * 256 * sizeof(int);
+    const bool ldsp = pbytes + xbytes <= 128 * 1024;
+    const size_t used = (ldsp ? pbytes : 0) + xbytes;
+    const size_t lds = used > rbytes ? used : rbytes;
+#define W4A8_LS(O, G, P)                                                                       \
+    hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, O, G, P>), grid, block, lds, st, X, sx, wq, \
+                       s_u8, a_u8, sw, Y, M, N, K, ks)
+    if (ldsp) {
+        if (out_type == 1) {
+            if (group == 64) W4A8_LS(1, 64, true); else W4A8_LS(1, 128, true);
+        } else {
+            if (group == 64) W4A8_LS(0, 64, true); else W4A8_LS(0, 128, true);
+        }
+    } else {
+        if (out_type == 1) {
+            if (group == 64) W4A8_LS(1, 64, false); else W4A8_LS(1, 128, false);
+        } else {
+            if (group == 64) W4A8_LS(0, 64, false); else W4A8_LS(0, 128, false);
+        }
+    }
+#undef W4A8_LS
     return hipGetLastError();
 }
 
@@ -203,9 +353,11 @@ hipError_t launch_w4a8_stream(const int8_t* X, const float* sx, const uint8_t* w
                               void* Y, int out_type, int M, int N, int K, int group,
                               StreamCfg cfg, hipStream_t st) {
     switch (cfg.nt_per_wave) {
-        case 4: return w4a8_stream_ntw<4>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
-        case 2: return w4a8_stream_ntw<2>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
-        default: return w4a8_stream_ntw<1>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
+        case 7: return w4a8_stream_ntw<7, 2>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
+        case 4: return w4a8_stream_ntw<4, 3>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
+        case 3: return w4a8_stream_ntw<3, 3>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
+        case 2: return w4a8_stream_ntw<2, 4>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
+        default: return w4a8_stream_ntw<1, 3>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
     }
 }
 
