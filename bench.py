@@ -50,7 +50,61 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true")
     p.add_argument("--cpu-sample-cols", type=int, default=256)
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run plain 256 MiB device-to-device copies (the known-size "
+                        "kernel that scales the HBM byte counters)")
     return p.parse_args()
+
+
+def source_digest():
+    """sha256 of the kernel sources: counter readings taken from other
+    sources no longer describe the kernels that run."""
+    import hashlib
+    d = os.path.join(ROOT, "w4a8_quantized_gemm_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(d)):
+        if f.endswith((".hip", ".h")):
+            h.update(f.encode())
+            with open(os.path.join(d, f), "rb") as fh:
+                h.update(fh.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(slot_name):
+    """HBM bytes per launch of `slot_name`'s kernel from the committed
+    counter summary (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by
+    what the same counter reads for a copy of known size), or None when no
+    summary exists or the kernel sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{slot_name.replace(':', '_')}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as fh:
+        for line in fh:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    try:
+        if kv.get("source_sha256") != source_digest():
+            return None
+        fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"])
+        write = float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"])
+    except (KeyError, ValueError):
+        return None
+    return round((fetch + write) * 1024.0)
+
+
+def calibrate_copy():
+    """Plain device-to-device copies of 256 MiB (read 256 MiB, write
+    256 MiB per dispatch) for scaling FETCH_SIZE / WRITE_SIZE readings."""
+    import torch
+    n = 256 << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibrate_copy_bytes": n, "dispatches": 4}), flush=True)
 
 
 def cpu_baseline(slots_desc, ncols):
@@ -93,6 +147,9 @@ def main():
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); "
               "multi-GPU runs are not part of this library", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy()
+        return
 
     import numpy as np
     import torch
@@ -180,11 +237,12 @@ def main():
             a = 2.0 * e["M"] * e["N"] * e["K"] / (e["us_mean"] * 1e-6) / 1e12
             return {"bound": "mfma", "achieved": round(a, 2), "peak": INT8_PEAK_TOPS,
                     "unit": "TFLOP/s", "frac": round(a / INT8_PEAK_TOPS, 4),
-                    "traffic": None, "kernel_slot": slot_name,
+                    "traffic": profiled_traffic(slot_name), "kernel_slot": slot_name,
                     "us_per_launch": e["us_mean"]}
         a = algo_bytes(e["M"], e["N"], e["K"], g) / (e["us_mean"] * 1e-6) / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": None, "kernel_slot": slot_name,
+                "frac": round(a / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(slot_name),
+                "kernel_slot": slot_name,
                 "us_per_launch": e["us_mean"]}
 
     # dominant kernel: the slot with the largest share of the step
