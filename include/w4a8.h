@@ -123,14 +123,15 @@ w4a8_status_t w4fp8_quant_act(const float* X, int M, int K, uint8_t* Xq,
                               float* sx, hipStream_t stream);
 
 /*
- * Bytes of device workspace w4a8_gemm needs for this problem: when the
- * matrix-core kernel has too few output tiles to fill the GPU it splits K
- * across workgroups, writes int32 partial tiles (splits x M x N x 4 bytes)
- * and sums them in split order in a second kernel (exact and deterministic).
- * Returns 0 when no split is used, when splitk != 0 (streamed kernel, which
- * reduces on chip) and for w4fp8_gemm.  The workspace is scratch: its
- * contents on entry are ignored and undefined on return; calls that share a
- * workspace must be ordered on one stream.
+ * Bytes of device workspace w4a8_gemm and w4fp8_gemm need for this problem:
+ * when the matrix-core kernel has too few output tiles to fill the GPU it
+ * splits K across workgroups, writes partial tiles (splits x M x N x 4
+ * bytes: int32 for w4a8_gemm, float32 for w4fp8_gemm) and sums them in split
+ * order in a second kernel (deterministic; exact for int32).  Returns 0 when
+ * no split is used and when splitk != 0 (streamed kernel, which reduces on
+ * chip).  The workspace is scratch: its contents on entry are ignored and
+ * undefined on return; calls that share a workspace must be ordered on one
+ * stream.
  */
 size_t w4a8_workspace_size(int M, int N, int K, int splitk);
 
@@ -162,6 +163,11 @@ w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint8_t* wq,
  *   out_type W4FP8_OUT_BF16: Y = bf16_rne((acc * sx[m]) * sw[n])
  *   out_type W4FP8_OUT_F32:  Y = (acc * sx[m]) * sw[n] as float32
  * X: e4m3 bytes [M][K]; wq, sw from w4a8_pack in INT4_SYM mode.
+ * Kernel choice as for w4a8_gemm (matrix-core tiles for M >= 64 with
+ * N % 256 == 0, else streamed tiles; splitk != 0 forces the streamed kernel);
+ * workspace: at least w4a8_workspace_size(M, N, K, splitk) bytes, 16-byte
+ * aligned, NULL allowed when that is 0.  The float32 sum order depends on
+ * the kernel choice (results within the FP8 path's error bound either way).
  */
 w4a8_status_t w4fp8_gemm(const uint8_t* X_e4m3, const float* sx,
                          const uint8_t* wq, const float* sw, void* Y,

@@ -249,6 +249,114 @@ def test_w4fp8_gemm_parity(M):
     err_b = rel_fro(gv, wv)
     say(f"  bf16 vs bf16(fp64) rel fro {err_b:.3e}; vs fp64 {rel_fro(gv, ref):.3e}")
     assert err_b <= 1e-3
+    _check_fp8_outputs(host(Yf), got, ref, _fp8_bound(X8, sx, pk_ref["q"], pk_ref["sw"]))
+
+
+def _fp8_bound(X8, sx, q, sw):
+    """Elementwise bound for the FP8 paths against the exact value.
+
+    The products x_k q_k are exact, but the gfx950 FP8 matrix instruction
+    does not add them as IEEE float32: next to a large product of the same
+    instruction, smaller ones lose low-order bits (measured on crafted rows:
+    448 followed by 255 terms of 2^-9 gives 448.484375, not 448.498047; the
+    tile and streamed kernels agree bit for bit).  Bound: 2^-10 of the
+    largest |product| of every 64-column block (taken as max|x| * max|q| of
+    the block; the largest loss seen is about 2^-13 of it), plus float32
+    summation across blocks, (K + 2) u sum_k |x_k q_k| with u = 2^-24, both
+    scaled by sx sw.  A wrong operand index or a dropped K-chunk is an error
+    of whole average products, far above this; exact indexing is pinned
+    separately by the integer-valued test."""
+    xd = np.abs(oracle.e4m3_decode(X8))
+    qd = np.abs(q.astype(np.float64))
+    M, K = X8.shape
+    absum = xd @ qd.T
+    xm = xd.reshape(M, K // 64, 64).max(axis=2)
+    qm = qd.reshape(qd.shape[0], K // 64, 64).max(axis=2)
+    blk = xm @ qm.T
+    return ((K + 2) * 2.0 ** -24 * absum + 2.0 ** -10 * blk) \
+        * np.asarray(sx, np.float64)[:, None] * np.asarray(sw, np.float64)[None, :]
+
+
+def _check_fp8_outputs(yf, yb_bits, ref, bound):
+    """float32 output inside the bound elementwise; bfloat16 output inside it
+    plus one bfloat16 rounding (unit roundoff 2^-8); both within relative
+    Frobenius 1e-3 of the double reference (the bfloat16 one of the
+    bfloat16-rounded reference)."""
+    yf = np.asarray(yf, np.float64)
+    assert np.all(np.abs(yf - ref) <= bound + 1e-30)
+    assert rel_fro(yf, ref) <= 1e-3
+    gv = (yb_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    lim = bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(ref) + 1e-30
+    assert np.all(np.abs(gv - ref) <= lim)
+    wv = (oracle.round_bf16(ref).astype(np.uint32) << 16).view(np.float32)
+    assert rel_fro(gv, wv) <= 1e-3
+
+
+@pytest.mark.parametrize("M,N,K", [(16, 128, 1024), (100, 256, 1024), (300, 512, 2048),
+                                   (128, 256, 4096)])
+def test_w4fp8_integer_valued_exact(M, N, K):
+    """Integer activations in [-16, 16] (exact in e4m3) times |q| <= 7: every
+    product is an integer <= 112 and every partial sum an integer below
+    2^24, so any summation order and the instruction's internal alignment
+    are exact -- the float32 output (sx = sw = 1) must equal the integer sum
+    bit for bit.  Pins operand layout, K indexing and split-K partials."""
+    say(f"w4fp8 integer-valued exact M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N + K)
+    Xi = rng.integers(-16, 17, size=(M, K)).astype(np.float64)
+    q = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    X8 = oracle.e4m3_encode(Xi)
+    np.testing.assert_array_equal(oracle.e4m3_decode(X8), Xi)
+    wq = oracle.pack_nibbles(oracle.int4_sm_codes(q))
+    exact = Xi.astype(np.int64) @ q.astype(np.int64).T
+    pk = {"wq": to_dev(wq), "sw": to_dev(np.ones(N, np.float32)), "N": N, "K": K}
+    ones = to_dev(np.ones(M, np.float32))
+    for sk in (0, 1):
+        Y = poison((M, N), torch.float32)
+        w4.gemm_fp8(to_dev(X8), ones, pk, out_type=w4.OUT_F32, splitk=sk, out=Y)
+        np.testing.assert_array_equal(host(Y), exact.astype(np.float32))
+
+
+# Matrix-core tile path (M >= 64, N % 256 == 0): ragged M, several tiles in
+# both directions, one and two K-steps per split, and planned split-K with
+# float32 partials (M=128, K=4096: one tile, four splits).
+@pytest.mark.parametrize("M,N,K", [(64, 256, 1024), (100, 256, 1024), (256, 512, 2048),
+                                   (300, 512, 1024), (513, 256, 2048), (128, 256, 4096),
+                                   (100, 512, 2048), (1024, 1024, 256)])
+def test_w4fp8_tile_parity(M, N, K):
+    say(f"w4fp8 tile gemm M={M} N={N} K={K} workspace={w4.workspace_size(M, N, K)}")
+    W = wl.gen_weights(N, K, 500 + M + N)
+    X = wl.gen_activations(M, K, 501 + M, 502)
+    pk_ref = oracle.w4fp8_pack(W)
+    X8, sx = oracle.quant_rows_e4m3(X)
+    ref, _ = oracle.w4fp8_ref(X8, sx, pk_ref["q"], pk_ref["sw"])
+    bound = _fp8_bound(X8, sx, pk_ref["q"], pk_ref["sw"])
+    pk = {"wq": to_dev(pk_ref["wq"]), "sw": to_dev(pk_ref["sw"]), "N": N, "K": K}
+    Yf = poison((M, N), torch.float32)
+    w4.gemm_fp8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F32, out=Yf)
+    Yb = poison((M, N), torch.bfloat16)
+    w4.gemm_fp8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_BF16, out=Yb)
+    yf = host(Yf)
+    say(f"  f32 rel fro {rel_fro(yf, ref):.3e}; max |err|/bound "
+        f"{np.max(np.abs(yf - ref) / (bound + 1e-30)):.3f}")
+    _check_fp8_outputs(yf, bf16_bits_of(Yb), ref, bound)
+    # the streamed kernel (forced by splitk) meets the same bound
+    Ys = poison((M, N), torch.float32)
+    w4.gemm_fp8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F32, splitk=1, out=Ys)
+    assert np.all(np.abs(host(Ys) - ref) <= bound + 1e-30)
+
+
+def test_fp8_workspace_too_small_is_rejected():
+    M, N, K = 128, 256, 4096
+    need = w4.workspace_size(M, N, K)
+    assert need > 0
+    X8 = torch.zeros((M, K), dtype=torch.uint8, device=DEV)
+    sx = torch.ones(M, dtype=torch.float32, device=DEV)
+    pk = {"wq": torch.zeros(N * K // 2, dtype=torch.uint8, device=DEV),
+          "sw": torch.ones(N, dtype=torch.float32, device=DEV), "N": N, "K": K}
+    small = torch.empty(need - 16, dtype=torch.uint8, device=DEV)
+    with pytest.raises(w4.W4A8Error) as ei:
+        w4.gemm_fp8(X8, sx, pk, workspace=small)
+    assert ei.value.status == 4
 
 
 # ------------------------------------------- Llama-shaped workloads --------
@@ -322,6 +430,9 @@ def test_fp8_variant_full_size_sampled():
     X8, sx8 = oracle.quant_rows_e4m3(X[msel])
     np.testing.assert_array_equal(host(Xq)[msel], X8)
     ref, _ = oracle.w4fp8_ref(X8, sx8, ref_pk["q"], ref_pk["sw"])
+    bound = _fp8_bound(X8, sx8, ref_pk["q"], ref_pk["sw"])
+    _check_fp8_outputs(host(Yf)[np.ix_(msel, nsel)], bf16_bits_of(Yb)[np.ix_(msel, nsel)],
+                       ref, bound)
     err = rel_fro(host(Yf)[np.ix_(msel, nsel)], ref)
     gv = (bf16_bits_of(Yb)[np.ix_(msel, nsel)].astype(np.uint32) << 16).view(np.float32)
     wv = (oracle.round_bf16(ref).astype(np.uint32) << 16).view(np.float32)

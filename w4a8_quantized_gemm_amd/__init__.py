@@ -185,7 +185,9 @@ def gemm(Xq, sx, packed, out_type: int = OUT_F16, splitk: int = 0, out=None,
 
 def gemm_fp8(Xq, sx, packed, out_type: int = OUT_BF16, splitk: int = 0, out=None,
              workspace=None, stream=None):
-    """w4fp8_gemm: Y [M][N] bfloat16 (OUT_BF16) or float32 (OUT_F32)."""
+    """w4fp8_gemm: Y [M][N] bfloat16 (OUT_BF16) or float32 (OUT_F32).
+
+    `workspace` as for gemm() (same size: float32 split-K partials)."""
     torch = _torch()
     _need(Xq, torch.uint8, "Xq")
     _need(sx, torch.float32, "sx")
@@ -196,6 +198,10 @@ def gemm_fp8(Xq, sx, packed, out_type: int = OUT_BF16, splitk: int = 0, out=None
     ydt = torch.bfloat16 if out_type == OUT_BF16 else torch.float32
     Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
     _need(Y, ydt, "out")
+    if workspace is None:
+        need = workspace_size(M, N, K, splitk)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=Xq.device)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.w4fp8_gemm(_ptr(Xq), _ptr(sx), _ptr(packed["wq"]), _ptr(packed["sw"]),
                           _ptr(Y), out_type, M, N, K, splitk, _ptr(workspace), ws_bytes,

@@ -194,10 +194,16 @@ W4A8_EXPORT w4a8_status_t w4fp8_gemm(const uint8_t* X_e4m3, const float* sx, con
     if (!X_e4m3 || !sx || !wq || !sw || !Y) return W4A8_ERR_NULL_PTR;
     if (!aligned16(X_e4m3) || !aligned16(wq) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
     if (!aligned4(sx) || !aligned4(sw)) return W4A8_ERR_ALIGNMENT;
-    if (workspace_bytes < w4a8_workspace_size(M, N, K, splitk)) return W4A8_ERR_WORKSPACE;
-    (void)workspace;
+    const size_t need = w4a8_workspace_size(M, N, K, splitk);
+    if (workspace_bytes < need) return W4A8_ERR_WORKSPACE;
+    if (need > 0 && !workspace) return W4A8_ERR_NULL_PTR;
+    if (need > 0 && !aligned16(workspace)) return W4A8_ERR_ALIGNMENT;
     w4a8_status_t d = check_device();
     if (d != W4A8_OK) return d;
+    if (splitk == 0 && use_mfma_tiles(M, N, K))
+        return hip_status(w4a8::launch_w4fp8_mfma(X_e4m3, sx, wq, sw, Y, out_type, M, N, K,
+                                                  w4a8::plan_w4a8_mfma(M, N, K), workspace,
+                                                  stream));
     return hip_status(w4a8::launch_w4fp8_stream(X_e4m3, sx, wq, sw, Y, out_type, M, N, K,
                                                 choose_stream(M, N, K, splitk), stream));
 }

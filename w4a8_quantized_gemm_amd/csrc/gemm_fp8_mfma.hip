@@ -1,0 +1,355 @@
+// Large-M W4FP8 GEMM for gfx950: INT4 weights (sign-magnitude nibbles, per
+// output channel scale) converted to FP8 e4m3 in registers, multiplied with
+// e4m3 activations on the matrix cores with float32 accumulation (the
+// INT4-FP8 scheme of FireQ, arXiv 2505.20839, abstract); epilogue
+// Y = bf16((acc * sx[m]) * sw[n]) or float32.
+//
+// Same skeleton as the W4A8 tile kernel: workgroup tile MT (128 or 256)
+// rows x 256 channels, four waves of MT x 64, X staged global -> registers
+// -> LDS (double buffer, swizzled 16-byte slots), weights loaded two K-steps
+// ahead and converted in single instructions interleaved with the matrix-
+// core instructions.  Per 128-column K-step and 32 x 32 block there are two
+// v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3): instruction j of lane
+// (c = lane % 32, h = lane / 32) takes K columns 64h + 32j .. +31, which is
+// packed slot 2h + j of the lane's weight row (32 consecutive codes, low
+// nibble of byte i = code 8d+i, high nibble = code 8d+4+i for dword d) and
+// 16-byte X chunks 4h + 2j, 4h + 2j + 1 of the lane's row.
+//
+// |q| <= 7 is exact in e4m3; conversion of one packed dword (8 codes) is 8
+// VALU instructions: magnitude mask, byte permute through the 8-entry e4m3
+// table, sign moved to bit 7 -- for the low nibbles (sign at bit 3) and the
+// high nibbles (sign already at bit 7).
+#include "launch.h"
+#include "mfma_common.h"
+
+namespace w4a8 {
+
+namespace {
+
+__device__ __forceinline__ void mfma32_f8_acc(v16f& acc, const v8i& a, const v8i& b) {
+    asm volatile("v_mfma_f32_32x32x64_f8f6f4 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
+}
+
+// Raw weights of one K-step for one lane: w[cb][j] = slot 2h+j of the lane's
+// row in tile 2cb + c/16.
+struct F8Step {
+    v4i w[2][2];
+};
+
+// e4m3 magnitudes of 0..7 as two byte tables for v_perm_b32 (bytes 0..3 in
+// `lo`, 4..7 in `hi`); kept in registers (one VOP3 reads one scalar only).
+struct F8Lut {
+    unsigned lo, hi, sgn;
+};
+
+struct F8Tmp {
+    unsigned m, e, s;
+};
+
+// Producing operand B[cb][j] of a K-step is 32 single-instruction steps:
+// for cb in {0,1}, for the slot's four dwords d:
+//   m = w & 0x07070707; e = perm(table, m); s = w & 0x08080808;
+//   B[2d] = (s << 4) | e                               (low nibbles)
+//   t = w >> 4; m = t & 0x07070707; e = perm(table, m);
+//   B[2d+1] = (w & 0x80808080) | e                      (high nibbles)
+template <int J, int OP>
+__device__ __forceinline__ void f8_step(F8Tmp& t, const F8Step& w, const F8Lut& lut,
+                                        v8i (&B)[2][2]) {
+    constexpr int cb = OP / 32, q = OP % 32, d = q / 8, st = q % 8;
+    const unsigned wd = (unsigned)w.w[cb][J][d];
+    if constexpr (st == 0) {
+        asm volatile("v_and_b32 %0, 0x07070707, %1" : "=v"(t.m) : "v"(wd));
+    } else if constexpr (st == 1) {
+        asm volatile("v_perm_b32 %0, %1, %2, %3" : "=v"(t.e) : "v"(lut.hi), "v"(lut.lo), "v"(t.m));
+    } else if constexpr (st == 2) {
+        asm volatile("v_and_b32 %0, 0x08080808, %1" : "=v"(t.s) : "v"(wd));
+    } else if constexpr (st == 3) {
+        unsigned x;
+        asm volatile("v_lshl_or_b32 %0, %1, 4, %2" : "=v"(x) : "v"(t.s), "v"(t.e));
+        B[cb][J][2 * d] = (int)x;
+    } else if constexpr (st == 4) {
+        asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(t.m) : "v"(wd));
+    } else if constexpr (st == 5) {
+        asm volatile("v_and_b32 %0, 0x07070707, %1" : "=v"(t.m) : "v"(t.m));
+    } else if constexpr (st == 6) {
+        asm volatile("v_perm_b32 %0, %1, %2, %3" : "=v"(t.e) : "v"(lut.hi), "v"(lut.lo), "v"(t.m));
+    } else {
+        unsigned x;
+        asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(x) : "v"(wd), "v"(lut.sgn), "v"(t.e));
+        B[cb][J][2 * d + 1] = (int)x;
+    }
+}
+
+template <int J>
+__device__ __forceinline__ void f8_all(const F8Step& w, const F8Lut& lut, v8i (&B)[2][2]) {
+    F8Tmp t;
+    static_for<64>([&](auto oc) { f8_step<J, decltype(oc)::value>(t, w, lut, B); });
+}
+
+}  // namespace
+
+template <int MT, int OUT, bool PARTIAL>
+__global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
+    const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
+    const float* __restrict__ sw, void* __restrict__ Y, float* __restrict__ part, int M, int N,
+    int K, int tiles_n, int tiles_m, int splits) {
+    constexpr int RB = MT / 32;        // 32-row blocks per wave
+    constexpr int CPT = MT / 32;       // 16-byte X chunks per thread per K-step
+    constexpr int SLOTS = 4 * RB;      // matrix-core instructions per wave per K-step
+    constexpr int GS = SLOTS / 2;      // slots per instruction group j
+    constexpr int DQ = (64 + GS - 1) / GS;  // conversion steps per slot
+    __shared__ __attribute__((aligned(1024))) uint8_t xs0[MT * 128];
+    __shared__ __attribute__((aligned(1024))) uint8_t xs1[MT * 128];
+    __shared__ float sxs[MT];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+    const int c = lane & 31, h = lane >> 5;
+    const int tb = c >> 4, r = c & 15;
+
+    const TileCoord tcd = tile_coord(blockIdx.x, tiles_m, tiles_n, splits);
+    const int ks = tcd.ks;
+    const int m0 = tcd.tm * MT;
+    const int n0 = tcd.tn * kNT + wave * kColsPerWave;
+    const int KTall = K / kTileK;
+    const int kt0 = (int)((long long)KTall * ks / splits);
+    const int KT = (int)((long long)KTall * (ks + 1) / splits) - kt0;  // >= 1
+
+    // ---- X: chunk p of this thread is row (tid>>3) + 32p, 16-byte column
+    // tid & 7, in LDS slot col ^ xswz(row & 15).  Rows >= M lie past the end
+    // of the buffer and read as 0.
+    const __amdgpu_buffer_rsrc_t xr_rsrc = buf_rsrc(X, (unsigned)M * (unsigned)K);
+    const int xrow0 = tid >> 3, xcol = tid & 7;
+    const unsigned xvoff =
+        (unsigned)(m0 + xrow0) * (unsigned)K + (unsigned)(xcol * 16) + (unsigned)(kt0 * kTileK);
+    const unsigned xrowstep = 32u * (unsigned)K;
+    const int xlds0 = xrow0 * 128 + ((xcol ^ xswz(xrow0 & 15)) * 16);
+    // A operand of instruction group j: row 32rb + c, chunks 4h+2j, 4h+2j+1.
+    int aoff[2][2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int u = 0; u < 2; ++u) aoff[j][u] = c * 128 + (((4 * h + 2 * j + u) ^ xswz(r)) * 16);
+
+    // ---- weights of this wave: tiles n0/16 .. n0/16+3
+    const int nt0 = n0 / kTileN;
+    const __amdgpu_buffer_rsrc_t w_rsrc = buf_rsrc(wq, (unsigned)((size_t)N * K / 2));
+    const unsigned wvoff = (unsigned)(tb * KTall) * kTileBytes + (unsigned)(32 * h + r) * 16u;
+    auto w_load = [&](int kt, int part_i, F8Step& ws) {  // part_i 0..3
+        const int ktg = kt0 + kt;
+        const int cb = part_i >> 1, j = part_i & 1;
+        ws.w[cb][j] = buf_load16(
+            w_rsrc, wvoff, (unsigned)(((nt0 + 2 * cb) * KTall + ktg) * kTileBytes + j * 256));
+    };
+    auto x_load = [&](int kt, int p) {
+        return buf_load16(xr_rsrc, xvoff + (unsigned)p * xrowstep, (unsigned)(kt * kTileK));
+    };
+    F8Lut lut;
+    lut.lo = 0x44403800u;  // e4m3 of 3, 2, 1, 0
+    lut.hi = 0x4E4C4A48u;  // e4m3 of 7, 6, 5, 4
+    lut.sgn = 0x80808080u;
+
+    v16f acc[RB][2];
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        acc[rb][0] = v16f{};
+        acc[rb][1] = v16f{};
+    }
+
+    // ---- prologue: X(0) -> LDS xs0, X(1) staged; B[*][0] of step 0
+    // converted, W(0) kept raw for B[*][1], W(1) raw; A ring primed.
+    v4i xe[CPT], xo[CPT];  // X staging for even / odd steps
+    F8Step we, wo;         // raw weights for even / odd steps
+    v8i B[2][2];
+    v8i ring[4];
+    const int k1 = min(1, KT - 1);
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) xe[p] = x_load(0, p);
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) xo[p] = x_load(k1, p);
+#pragma unroll
+    for (int pi = 0; pi < 4; ++pi) w_load(0, pi, we);
+#pragma unroll
+    for (int pi = 0; pi < 4; ++pi) w_load(k1, pi, wo);
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) *reinterpret_cast<v4i*>(xs0 + xlds0 + p * 4096) = xe[p];
+    f8_all<0>(we, lut, B);
+    __syncthreads();
+    auto read_a = [&](const uint8_t* buf, int sI) {  // sI = RB*j + rb
+        const int j = sI / RB, rb = sI % RB;
+        const v4i lo = *reinterpret_cast<const v4i*>(buf + rb * 4096 + aoff[j][0]);
+        const v4i hi = *reinterpret_cast<const v4i*>(buf + rb * 4096 + aoff[j][1]);
+        return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+    };
+    ring[0] = read_a(xs0, 0);
+    ring[1] = read_a(xs0, 1);
+
+    // ---- one K-step, SLOTS matrix-core slots.  Slot s: group j = s / GS,
+    // row block rb = (s/2) % RB, channel block cb = s % 2.  Entering step
+    // kt: LDS `cur` = X(kt); ring holds A for the first two operand slots;
+    // B[*][0] = W(kt) operands; `wcur` = raw W(kt), `xnx` = X(kt+1) staged,
+    // `wnx` = raw W(kt+1).
+    //   group 0 slots      X(kt+2) -> xcur; B[*][1] of step kt from wcur
+    //   group 1 slots      W(kt+2) -> wcur; B[*][0] of step kt+1 from wnx
+    //   last 4+CPT slots   X(kt+1) -> LDS `nxt` (before the last 4)
+    //   before the last 4  barrier, then step kt+1's first two A reads.
+    auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, v4i (&xcur)[CPT],
+                    v4i (&xnx)[CPT], F8Step& wcur, F8Step& wnx) {
+        const int k2 = min(kt + 2, KT - 1);
+        F8Tmp tmp;
+        static_for<SLOTS>([&](auto sc) {
+            constexpr int s = decltype(sc)::value;
+            constexpr int sI = s / 2, j = sI / RB, rb = sI % RB, cb = s % 2;
+            constexpr int g = s / GS, sg = s % GS;
+            if constexpr (s == SLOTS - 4) {
+                __syncthreads();
+                ring[0] = read_a(nxt, 0);
+                ring[1] = read_a(nxt, 1);
+            }
+            mfma32_f8_acc(acc[rb][cb], ring[sI % 4], B[cb][j]);
+            if constexpr (cb == 1 && sI + 2 < 2 * RB) ring[(sI + 2) % 4] = read_a(cur, sI + 2);
+            if constexpr (s < CPT) xcur[s] = x_load(k2, s);
+            if constexpr (s >= GS && s < GS + 4) w_load(k2, s - GS, wcur);
+            if constexpr (s >= SLOTS - 4 - CPT && s < SLOTS - 4)
+                *reinterpret_cast<v4i*>(nxt + xlds0 + (s - (SLOTS - 4 - CPT)) * 4096) =
+                    xnx[s - (SLOTS - 4 - CPT)];
+            static_for<DQ>([&](auto dc) {
+                constexpr int o = DQ * sg + decltype(dc)::value;
+                if constexpr (o < 64) {
+                    if constexpr (g == 0) f8_step<1, o>(tmp, wcur, lut, B);
+                    else f8_step<0, o>(tmp, wnx, lut, B);
+                }
+            });
+        });
+    };
+
+    int kt = 0;
+    for (; kt + 1 < KT; kt += 2) {
+        step(kt, xs0, xs1, xe, xo, we, wo);
+        step(kt + 1, xs1, xs0, xo, xe, wo, we);
+    }
+    if (kt < KT) step(kt, xs0, xs1, xe, xo, we, wo);
+
+    mfma32_drain();
+    __syncthreads();  // all waves done with the X buffers
+
+    // ---- epilogue.  Accumulator (rb, cb) register v of lane (c, h): row
+    // 32rb + 8(v/4) + 4h + (v%4), channel n0 + 32cb + c.  Values go to a
+    // per-wave LDS block [32 rows][64 channels]; each row is then written as
+    // whole 16-byte pieces (final output, or this split's float32 partial).
+    constexpr bool SCALED = !PARTIAL;
+    constexpr bool BF16 = (OUT == 0) && !PARTIAL;
+    if (SCALED) sxs[tid % MT] = (m0 + tid % MT < M) ? sx[m0 + tid % MT] : 0.0f;
+    const float sw0 = SCALED ? sw[n0 + c] : 0.0f;
+    const float sw1 = SCALED ? sw[n0 + 32 + c] : 0.0f;
+    __syncthreads();
+    constexpr int EB = BF16 ? 2 : 4;          // output element bytes
+    constexpr int ROWB = 64 * EB;             // bytes per staged row
+    uint8_t* stage = xs0 + wave * (32 * ROWB);
+    uint8_t* out = PARTIAL ? reinterpret_cast<uint8_t*>(part + (size_t)ks * M * N)
+                           : reinterpret_cast<uint8_t*>(Y);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = 8 * (v >> 2) + 4 * h + (v & 3);
+                const int col = 32 * cb + c;
+                float y = acc[rb][cb][v];
+                if (SCALED) y = (y * sxs[32 * rb + row]) * (cb ? sw1 : sw0);
+                if (BF16)
+                    *reinterpret_cast<unsigned short*>(stage + row * ROWB + col * 2) =
+                        f32_to_bf16_bits(y);
+                else
+                    *reinterpret_cast<float*>(stage + row * ROWB + col * 4) = y;
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+        __builtin_amdgcn_wave_barrier();
+        constexpr int PIECES = 32 * ROWB / 16;  // 16-byte pieces per block
+        constexpr int PPR = ROWB / 16;          // pieces per row
+#pragma unroll
+        for (int u = 0; u < PIECES / 64; ++u) {
+            const int q = lane + 64 * u;
+            const int row = q / PPR, piece = q % PPR;
+            const int m = m0 + 32 * rb + row;
+            const v4i val = *reinterpret_cast<const v4i*>(stage + row * ROWB + piece * 16);
+            if (m < M)
+                *reinterpret_cast<v4i*>(out + ((size_t)m * N + n0) * EB + piece * 16) = val;
+        }
+        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_wave_barrier();
+    }
+}
+
+// Sum of the split-K float32 partial tiles in split order, then the
+// per-token x per-channel scale to bf16 or float32.  Each thread handles four
+// consecutive channels of one row.
+template <int OUT>
+__global__ __launch_bounds__(256) void splitk_reduce_f32_kernel(
+    const float* __restrict__ part, int splits, int M, int N, const float* __restrict__ sx,
+    const float* __restrict__ sw, void* __restrict__ Y) {
+    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const size_t MN = (size_t)M * N;
+    if (q * 4 >= MN) return;
+    const size_t e = q * 4;
+    v4f acc = *reinterpret_cast<const v4f*>(part + e);
+    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const v4f*>(part + s * MN + e);
+    const int m = (int)(e / N), n = (int)(e % N);
+    const float sm = sx[m];
+    float y[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) y[j] = (acc[j] * sm) * sw[n + j];
+    if (OUT == 1) {
+        *reinterpret_cast<v4f*>(reinterpret_cast<float*>(Y) + e) = v4f{y[0], y[1], y[2], y[3]};
+    } else {
+        uint2 pk;
+        pk.x = f32_to_bf16_bits(y[0]) | ((unsigned)f32_to_bf16_bits(y[1]) << 16);
+        pk.y = f32_to_bf16_bits(y[2]) | ((unsigned)f32_to_bf16_bits(y[3]) << 16);
+        *reinterpret_cast<uint2*>(reinterpret_cast<unsigned short*>(Y) + e) = pk;
+    }
+}
+
+template <int MT, int OUT, bool PARTIAL>
+static void launch_fp8_tile(const uint8_t* X, const float* sx, const uint8_t* wq, const float* sw,
+                            void* Y, float* part, int M, int N, int K, int splits,
+                            hipStream_t st) {
+    const int tiles_n = N / kNT;
+    const int tiles_m = (M + MT - 1) / MT;
+    dim3 grid(tiles_n * tiles_m * splits), block(256);
+    hipLaunchKernelGGL((w4fp8_mfma_kernel<MT, OUT, PARTIAL>), grid, block, 0, st, X, sx, wq, sw,
+                       Y, part, M, N, K, tiles_n, tiles_m, splits);
+}
+
+hipError_t launch_w4fp8_mfma(const uint8_t* X, const float* sx, const uint8_t* wq,
+                             const float* sw, void* Y, int out_type, int M, int N, int K,
+                             const MfmaPlan& plan, void* workspace, hipStream_t st) {
+    float* part = reinterpret_cast<float*>(workspace);
+    if (plan.splits == 1) {
+        if (plan.mt == 256) {
+            if (out_type == 1) launch_fp8_tile<256, 1, false>(X, sx, wq, sw, Y, part, M, N, K, 1, st);
+            else launch_fp8_tile<256, 0, false>(X, sx, wq, sw, Y, part, M, N, K, 1, st);
+        } else {
+            if (out_type == 1) launch_fp8_tile<128, 1, false>(X, sx, wq, sw, Y, part, M, N, K, 1, st);
+            else launch_fp8_tile<128, 0, false>(X, sx, wq, sw, Y, part, M, N, K, 1, st);
+        }
+        return hipGetLastError();
+    }
+    if (plan.mt == 256)
+        launch_fp8_tile<256, 1, true>(X, sx, wq, sw, Y, part, M, N, K, plan.splits, st);
+    else
+        launch_fp8_tile<128, 1, true>(X, sx, wq, sw, Y, part, M, N, K, plan.splits, st);
+    const size_t quads = ((size_t)M * N) / 4;
+    const unsigned blocks = (unsigned)((quads + 255) / 256);
+    if (out_type == 1)
+        hipLaunchKernelGGL((splitk_reduce_f32_kernel<1>), dim3(blocks), dim3(256), 0, st, part,
+                           plan.splits, M, N, sx, sw, Y);
+    else
+        hipLaunchKernelGGL((splitk_reduce_f32_kernel<0>), dim3(blocks), dim3(256), 0, st, part,
+                           plan.splits, M, N, sx, sw, Y);
+    return hipGetLastError();
+}
+
+}  // namespace w4a8

@@ -1,7 +1,7 @@
 // Large-M W4A8 GEMM for gfx950 (the matrix-core-bound regime).
 //
-// Workgroup tile: MT rows of X (M) x 4*64 output channels (N); four waves,
-// each owning all MT rows and its own 64 channels, so every weight is
+// Workgroup tile: MT (128 or 256) rows of X x 256 output channels; four
+// waves, each owning all MT rows and its own 64 channels, so every weight is
 // dequantised exactly once per workgroup tile and goes from registers
 // straight into the matrix cores.  The consumer dequantises what it
 // multiplies, as in the implicit pipeline of LiquidGEMM (Pith review of
@@ -11,146 +11,21 @@
 // weights after the nibble split (same review, paper Eq. 12; minor comment 1
 // / Sec. 5.3 for the instruction count).
 //
-// Per K-step of 128 columns:
-//   X[MT][128] int8 of the next step: global -> registers at the start of
-//     the step, registers -> LDS (double buffer) at its end; 16-byte slots
-//     XOR-swizzled per row so the 16 rows read by one ds_read_b128 fall in
-//     distinct banks;
-//   each wave: 4 packed tiles (16 ch x 128 K, 16 B per lane) of the next
-//     step loaded at the start, dequantised at the end of the step;
-//   MT/16 x 4 x 2 v_mfma_i32_16x16x64_i8 into MT/16 x 4 int32 accumulators
-//     held in accumulation registers, A operands streamed from LDS through a
-//     short register ring.
-// With 128-row tiles two workgroups share a CU, so one's barrier and
-// dequantisation phases overlap the other's matrix-core phase.
+// Per K-step of 128 columns: X[MT][128] int8 goes global -> registers ->
+// LDS (double buffer, 16-byte slots XOR-swizzled per row); each wave loads
+// its 4 packed tiles of a later step and dequantises them in single
+// instructions interleaved with the current step's matrix-core
+// instructions (v_mfma_i32_32x32x32_i8, accumulators in AGPRs).
 // Epilogue: Y = fp16((float(acc) * sx[m]) * sw[n]) or the raw int32.
-#include <utility>
-
-#include "device_common.h"
 #include "launch.h"
+#include "mfma_common.h"
 
 namespace w4a8 {
 
-namespace {
-
-constexpr int kWaves = 4;
-constexpr int kColsPerWave = 64;              // 4 packed tiles
-constexpr int kNT = kWaves * kColsPerWave;    // 256 channels per workgroup
-
-// Row-dependent XOR of the 16-byte slot index: distinct for rows r and r'
-// of a 16-row block whenever they share a bank window, for both 32- and
-// 64-bank LDS organisations.
-__device__ __forceinline__ int xswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
-// Raw weights of one K-step for one wave: 4 packed tiles (16 B per lane)
-// and the parameter bytes of the lane's row in those tiles (byte b = tile b).
-struct WStep {
-    v4i w[4];
-    unsigned sdw, adw;
-};
-
-__device__ __forceinline__ void dequant_half(const WStep& ws, int h, v4i (&B)[4][2]) {
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        const u16x2 s2 = scale_pair(ws.sdw, b);
-        const u16x2 a4 = offset_quad(ws.adw, b);
-        unsigned d0, d1, d2, d3;
-        const unsigned w0 = (unsigned)(h ? ws.w[b].z : ws.w[b].x);
-        const unsigned w1 = (unsigned)(h ? ws.w[b].w : ws.w[b].y);
-        lqq_dequant8(w0, s2, a4, d0, d1);
-        lqq_dequant8(w1, s2, a4, d2, d3);
-        B[b][h] = v4i{(int)d0, (int)d1, (int)d2, (int)d3};
-    }
-}
-
-// Accumulate into an int32 tile that stays in accumulation registers
-// (destination = source C).  Written as inline assembly so the register
-// allocator cannot split the accumulators between register files.
-__device__ __forceinline__ void mfma_i8_acc(v4i& acc, const v4i& a, const v4i& b) {
-    asm("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// Same instruction, volatile: keeps its place relative to the one-instruction
-// dequantisation steps interleaved with it below.
-__device__ __forceinline__ void mfma_i8_acc_v(v4i& acc, const v4i& a, const v4i& b) {
-    asm volatile("v_mfma_i32_16x16x64_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-// Dequantisation of the next K-step's four tiles as 120 single-instruction
-// steps, so that one can follow each matrix-core instruction of the current
-// step and run on the vector ALU while the matrix core is busy.
-//   steps 30b + 0, 1:   scale pair / offset quad of tile b (v_perm_b32)
-//   steps 30b + 2 + 7d + e, dword d of tile b, e = 0..6:
-//     lo = w & 0x0F0F0F0F; t = w >> 4; hi = t & 0x0F0F0F0F;
-//     lo = lo*s + a; hi = hi*s + a   (two 16-bit lanes, v_pk_mad_u16);
-//     lo ^= 0x80808080; hi ^= 0x80808080
-// Results land in B[b][d/2] components 2(d%2), 2(d%2)+1.
-struct DequantPipe {
-    unsigned s2[4], a4[4];
-    unsigned lo, t, hi;
-};
-
-template <int OP>
-__device__ __forceinline__ void dq_step(DequantPipe& p, const WStep& w, v4i (&B)[4][2]) {
-    constexpr int b = OP / 30, q = OP % 30;
-    if constexpr (q == 0) {
-        constexpr unsigned sel = (unsigned)b | 0x0C00u | ((unsigned)b << 16) | 0x0C000000u;
-        asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.s2[b]) : "v"(w.sdw), "s"(sel));
-    } else if constexpr (q == 1) {
-        constexpr unsigned sel = (unsigned)b * 0x01010101u;
-        asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.a4[b]) : "v"(w.adw), "s"(sel));
-    } else {
-        constexpr int d = (q - 2) / 7, e = (q - 2) % 7;
-        const unsigned wd = (unsigned)w.w[b][d];
-        if constexpr (e == 0) {
-            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(p.lo) : "v"(wd));
-        } else if constexpr (e == 1) {
-            asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(p.t) : "v"(wd));
-        } else if constexpr (e == 2) {
-            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(p.hi) : "v"(p.t));
-        } else if constexpr (e == 3) {
-            asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
-                         : "=v"(p.lo) : "v"(p.lo), "v"(p.s2[b]), "v"(p.a4[b]));
-        } else if constexpr (e == 4) {
-            asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
-                         : "=v"(p.hi) : "v"(p.hi), "v"(p.s2[b]), "v"(p.a4[b]));
-        } else if constexpr (e == 5) {
-            unsigned x;
-            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(p.lo));
-            B[b][d >> 1][2 * (d & 1)] = (int)x;
-        } else {
-            unsigned x;
-            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(p.hi));
-            B[b][d >> 1][2 * (d & 1) + 1] = (int)x;
-        }
-    }
-}
-
-// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
-template <typename F, int... Is>
-__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
-    (f(std::integral_constant<int, Is>{}), ...);
-}
-template <int N, typename F>
-__device__ __forceinline__ void static_for(F&& f) {
-    static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
-
-// Wait states between the last accumulation and the first read of the
-// accumulators (the compiler does not see the assembly instructions above).
-__device__ __forceinline__ void mfma_drain() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
-}  // namespace
-
-// 256-row variant (one workgroup per CU), built on v_mfma_i32_32x32x32_i8:
-// half as many matrix-core instructions per K-step as the 16x16 form, so
-// each one leaves a 32-cycle shadow for the dequantisation, LDS and memory
-// instructions of the same wave.
-//   wave tile 256 x 64 = 8 row blocks x 2 channel blocks of 32 x 32;
+// Built on v_mfma_i32_32x32x32_i8: each instruction leaves a 32-cycle
+// shadow for the dequantisation, LDS and memory instructions of the same
+// wave.
+//   wave tile MT x 64 = MT/32 row blocks x 2 channel blocks of 32 x 32;
 //   B operand of lane (c = lane % 32, h = lane / 32): packed tile row c % 16
 //     of tile 2*cb + c/16, slots 2h and 2h+1 (K columns 64h .. 64h+63 of
 //     the 128-column step); instruction i (0..3) consumes columns
@@ -166,17 +41,6 @@ namespace {
 
 __device__ __forceinline__ void mfma32_i8_acc(v16i& acc, const v4i& a, const v4i& b) {
     asm volatile("v_mfma_i32_32x32x32_i8 %0, %1, %2, %0" : "+a"(acc) : "v"(a), "v"(b));
-}
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, unsigned bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
-                                             0x00020000);
-}
-__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
-}
-__device__ __forceinline__ unsigned buf_load4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
-    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
 }
 
 // Raw weights of one K-step for one lane: w[cb][e] = slot 2h+e of the
@@ -258,12 +122,6 @@ __device__ __forceinline__ void dq_group_all(const WStep32& w, const WParams& p,
     static_for<28>([&](auto oc) { dq_group_step<I, decltype(oc)::value>(tmp, w, p, B); });
 }
 
-__device__ __forceinline__ void mfma32_drain() {
-    __builtin_amdgcn_sched_barrier(0);
-    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 }  // namespace
 
 template <int MT, int OUT, int GROUP, bool PARTIAL>
@@ -287,20 +145,10 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     const int c = lane & 31, h = lane >> 5;
     const int tb = c >> 4, r = c & 15;
 
-    // Workgroup -> (tile, K split).  Workgroups are dealt round-robin to the
-    // 8 XCDs; regroup so each XCD walks a contiguous run, with the M tiles of
-    // one channel panel adjacent (the weight panel stays in that L2).
-    const int ntiles = tiles_n * tiles_m;
-    const int nwg = ntiles * splits;
-    const int bid = blockIdx.x;
-    int lin = bid;
-    if ((nwg & 7) == 0) lin = (bid & 7) * (nwg >> 3) + (bid >> 3);
-    const int ks = lin / ntiles;
-    const int tile = lin % ntiles;
-    const int tm = tile % tiles_m;
-    const int tn = tile / tiles_m;
-    const int m0 = tm * MT;
-    const int n0 = tn * kNT + wave * kColsPerWave;
+    const TileCoord tc = tile_coord(blockIdx.x, tiles_m, tiles_n, splits);
+    const int ks = tc.ks;
+    const int m0 = tc.tm * MT;
+    const int n0 = tc.tn * kNT + wave * kColsPerWave;
     const int KTall = K / kTileK;
     const int kt0 = (int)((long long)KTall * ks / splits);
     const int KT = (int)((long long)KTall * (ks + 1) / splits) - kt0;  // >= 1

@@ -33,13 +33,19 @@ hipError_t launch_w4a8_stream(const int8_t* X, const float* sx, const uint8_t* w
 struct MfmaPlan {
     int mt;
     int splits;
-    size_t workspace;  // bytes of int32 partials (0 when splits == 1)
+    size_t workspace;  // bytes of 4-byte partials (0 when splits == 1)
 };
 MfmaPlan plan_w4a8_mfma(int M, int N, int K);
 hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
                             const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
                             int out_type, int M, int N, int K, int group, const MfmaPlan& plan,
                             void* workspace, hipStream_t st);
+
+// W4FP8 matrix-core tile kernel: same tiles and plan as the W4A8 one, with
+// float32 partials in the workspace when plan.splits > 1.
+hipError_t launch_w4fp8_mfma(const uint8_t* X, const float* sx, const uint8_t* wq,
+                             const float* sw, void* Y, int out_type, int M, int N, int K,
+                             const MfmaPlan& plan, void* workspace, hipStream_t st);
 
 hipError_t launch_w4fp8_stream(const uint8_t* X, const float* sx, const uint8_t* wq,
                                const float* sw, void* Y, int out_type, int M, int N, int K,

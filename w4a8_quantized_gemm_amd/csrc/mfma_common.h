@@ -1,0 +1,78 @@
+// Building blocks shared by the matrix-core tile kernels (W4A8 int8 and
+// W4FP8 e4m3): compile-time loops, buffer loads, the X tile swizzle, the
+// workgroup -> output tile order and the accumulator drain.
+#pragma once
+#include <utility>
+
+#include "device_common.h"
+
+namespace w4a8 {
+
+constexpr int kWaves = 4;
+constexpr int kColsPerWave = 64;              // 4 packed tiles
+constexpr int kNT = kWaves * kColsPerWave;    // 256 channels per workgroup
+
+// Row-dependent XOR of the 16-byte slot index of an X row held in LDS (row
+// stride 128 bytes): distinct for rows r and r' of a 16-row block whenever
+// they share a bank window, for both 32- and 64-bank LDS organisations.
+__device__ __forceinline__ int xswz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+// Compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1.
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, Is...>) {
+    (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buf_rsrc(const void* p, unsigned bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
+__device__ __forceinline__ unsigned buf_load4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
+    return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// Wait states between the last accumulation written in inline assembly and
+// the first read of the accumulators (the compiler does not see those).
+__device__ __forceinline__ void mfma32_drain() {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Workgroup -> (output tile, K split).  Workgroups are dealt round-robin to
+// the 8 XCDs (each with its own L2); regroup so each XCD walks a contiguous
+// run of tiles, and order the tiles in 4 (M) x 8 (channel panel) blocks so
+// that the 32 workgroups one XCD runs together share 4 X panels and 8
+// weight panels (X is re-fetched tiles_n / 8 times rather than once per
+// pair of channel panels).
+struct TileCoord {
+    int tm, tn, ks;
+};
+__device__ __forceinline__ TileCoord tile_coord(int bid, int tiles_m, int tiles_n, int splits) {
+    const int ntiles = tiles_n * tiles_m;
+    const int nwg = ntiles * splits;
+    int lin = bid;
+    if ((nwg & 7) == 0) lin = (bid & 7) * (nwg >> 3) + (bid >> 3);
+    TileCoord t;
+    t.ks = lin / ntiles;
+    const int tile = lin % ntiles;
+    if ((tiles_m & 3) == 0 && (tiles_n & 7) == 0) {
+        const int blk = tile >> 5, in = tile & 31;
+        const int bm = tiles_m >> 2;
+        t.tm = (blk % bm) * 4 + (in & 3);
+        t.tn = (blk / bm) * 8 + (in >> 2);
+    } else {
+        t.tm = tile % tiles_m;
+        t.tn = tile / tiles_m;
+    }
+    return t;
+}
+
+}  // namespace w4a8
