@@ -122,6 +122,22 @@ w4a8_status_t w4a8_quant_act(const float* X, int M, int K, int8_t* Xq,
 w4a8_status_t w4fp8_quant_act(const float* X, int M, int K, uint8_t* Xq,
                               float* sx, hipStream_t stream);
 
+/* Element types of the activations handed to the _ex quantisers. */
+enum { W4A8_IN_F32 = 0, W4A8_IN_F16 = 1, W4A8_IN_BF16 = 2 };
+
+/*
+ * The two quantisers above for activations held as float32, IEEE fp16 or
+ * bfloat16 (in_type), the forms a model's linear layers receive.  Each
+ * element is widened to float32 -- exact for all three types -- and then
+ * quantised exactly as w4a8_quant_act / w4fp8_quant_act do.  X: [M][K]
+ * elements of in_type, 16-byte aligned; Xq, sx as above; K % 16 == 0.
+ * Unknown in_type: W4A8_ERR_UNSUPPORTED.
+ */
+w4a8_status_t w4a8_quant_act_ex(const void* X, int in_type, int M, int K,
+                                int8_t* Xq, float* sx, hipStream_t stream);
+w4a8_status_t w4fp8_quant_act_ex(const void* X, int in_type, int M, int K,
+                                 uint8_t* Xq, float* sx, hipStream_t stream);
+
 /*
  * Bytes of device workspace w4a8_gemm and w4fp8_gemm need for this problem:
  * when the matrix-core kernel has too few output tiles to fill the GPU it

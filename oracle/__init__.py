@@ -199,6 +199,18 @@ def epilogue_f16(acc, sx, sw):
     return y, yd
 
 
+def widen_f16(bits):
+    """IEEE binary16 bit patterns -> float32 values (exact: every binary16
+    value, subnormals included, is a float32 value)."""
+    return np.asarray(bits, np.uint16).view(np.float16).astype(np.float32)
+
+
+def widen_bf16(bits):
+    """bfloat16 bit patterns -> float32 values: bfloat16 is the upper half of
+    a float32, so the value is the pattern shifted into the high 16 bits."""
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
 def e4m3_decode(b):
     b = _c(b, np.uint8)
     out = np.empty(b.shape, np.float64)

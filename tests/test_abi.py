@@ -115,6 +115,19 @@ def test_quant_act_validation():
         assert fn(A, 0, 64, A, A, None) == OK
 
 
+def test_quant_act_ex_validation():
+    for fn in (lib.w4a8_quant_act_ex, lib.w4fp8_quant_act_ex):
+        for it in (0, 1, 2):
+            assert fn(None, it, 4, 64, A, A, None) == NULL
+            assert fn(A, it, 4, 60, A, A, None) == SHAPE
+            assert fn(A, it, -1, 64, A, A, None) == SHAPE
+            assert fn(A + 8, it, 4, 64, A, A, None) == ALIGN
+            assert fn(A, it, 4, 64, A + 8, A, None) == ALIGN
+            assert fn(A, it, 0, 64, A, A, None) == OK
+        assert fn(A, 3, 4, 64, A, A, None) == UNSUP
+        assert fn(A, -1, 4, 64, A, A, None) == UNSUP
+
+
 def test_valid_call_without_gpu_reports_hip_error():
     """A call that passes validation reaches the HIP runtime; with no GPU
     the device query fails and the status is W4A8_ERR_HIP, not a crash."""

@@ -105,6 +105,41 @@ def test_quant_act_parity(M, K):
     np.testing.assert_array_equal(host(Xf), qf)
 
 
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+@pytest.mark.parametrize("M,K", [(1, 512), (16, 4096), (37, 1040)])
+def test_quant_act_typed_parity(dt, M, K):
+    """fp16 / bf16 activations: the device widens to float32 and quantises;
+    the oracle widens the same bit patterns (exact) and quantises.  Rows:
+    Gaussian with outlier channels, an all-zero row, a row of the format's
+    smallest subnormals and signed zeros, and a row at the largest finite
+    value."""
+    say(f"quant act {dt} M={M} K={K}")
+    X = wl.gen_activations(M, K, 310 + M, 311).astype(np.float64)
+    if dt == "f16":
+        bits = oracle.round_f16(X)
+        tiny, big = 0x0001, 0x7BFF
+        widen, tdt = oracle.widen_f16, torch.float16
+    else:
+        bits = oracle.round_bf16(X)
+        tiny, big = 0x0001, 0x7F7F
+        widen, tdt = oracle.widen_bf16, torch.bfloat16
+    if M > 3:
+        bits[1] = 0
+        bits[2] = np.where(np.arange(K) % 2 == 0, tiny, 0x8000 | tiny)
+        bits[2, ::3] = 0x8000
+        bits[3] = np.where(np.arange(K) % 5 == 0, 0x8000 | big, bits[3])
+    Xw = widen(bits)
+    Xd = to_dev(bits.view(np.int16)).view(tdt)
+    q8, s8 = oracle.quant_sym_rows(Xw, 127)
+    Xq, sx = w4.quant_act(Xd)
+    np.testing.assert_array_equal(host(sx), s8)
+    np.testing.assert_array_equal(host(Xq), q8)
+    qf, sf = oracle.quant_rows_e4m3(Xw)
+    Xf, sxf = w4.quant_act_fp8(Xd)
+    np.testing.assert_array_equal(host(sxf), sf)
+    np.testing.assert_array_equal(host(Xf), qf)
+
+
 # ------------------------------------------------------- W4A8 GEMM ---------
 def _small_problem(M, N, K, g, seed):
     W = wl.gen_weights(N, K, seed)

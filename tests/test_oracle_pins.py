@@ -445,6 +445,32 @@ def test_p6_fp8_reference_exact_special_case():
                                sw[None, :].astype(np.float64), rtol=1e-15)
 
 
+def test_widening_definition_points():
+    """Half and bfloat16 widening at points fixed by the formats'
+    definitions: one, the largest finite values, the smallest subnormals,
+    signed zero, and a mid-range value."""
+    f16 = oracle.widen_f16(np.array([0x3C00, 0x7BFF, 0x0001, 0x0400, 0x8000, 0xC500, 0x3555],
+                                    np.uint16))
+    want16 = [1.0, 65504.0, 2.0 ** -24, 2.0 ** -14, -0.0, -5.0, 1.0 / 3.0]
+    np.testing.assert_allclose(f16[:6], want16[:6], rtol=0, atol=0)
+    assert np.signbit(f16[4])
+    assert abs(float(f16[6]) - 1.0 / 3.0) < 2.0 ** -12     # 0x3555 = 0.333251953125
+    assert float(f16[6]) == 0.333251953125
+    bf = oracle.widen_bf16(np.array([0x3F80, 0x7F7F, 0x0001, 0x0080, 0x8000, 0xC0A0, 0x3EAB],
+                                    np.uint16))
+    wantb = [1.0, float(np.float32(3.3895313892515355e38)), 2.0 ** -133, 2.0 ** -126, -0.0, -5.0]
+    np.testing.assert_array_equal(bf[:6], np.array(wantb, np.float32))
+    assert np.signbit(bf[4])
+    assert float(bf[6]) == 0.333984375                      # 0x3EAB
+    # widening is exact: bfloat16 rounding of the widened value returns the bits
+    bits = np.arange(0, 65536, 7, dtype=np.uint32).astype(np.uint16)
+    finite = (bits & 0x7F80) != 0x7F80
+    np.testing.assert_array_equal(oracle.round_bf16(oracle.widen_bf16(bits[finite])),
+                                  bits[finite])
+    h = bits[(bits & 0x7C00) != 0x7C00]
+    np.testing.assert_array_equal(oracle.round_f16(oracle.widen_f16(h).astype(np.float64)), h)
+
+
 def test_generator_deterministic():
     a = wl.gen_weights(64, 128, 7)
     b = wl.gen_weights(64, 128, 7)

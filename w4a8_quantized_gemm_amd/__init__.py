@@ -36,16 +36,19 @@ STATUS_NAMES = {0: "W4A8_OK", 1: "W4A8_ERR_NULL_PTR", 2: "W4A8_ERR_SHAPE",
 PACK_LQQ, PACK_INT4_SYM = 0, 1
 OUT_F16, OUT_I32 = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
+IN_F32, IN_F16, IN_BF16 = 0, 1, 2
 LAYOUT_VERSION = 1
 
 EXPORTS = ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act",
-           "w4a8_workspace_size", "w4a8_gemm", "w4fp8_gemm",
+           "w4a8_quant_act_ex", "w4fp8_quant_act_ex", "w4a8_workspace_size", "w4a8_gemm", "w4fp8_gemm",
            "w4a8_status_str", "w4a8_last_hip_error", "w4a8_layout_version")
 
 _P, _I, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
 lib.w4a8_pack.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P]
 lib.w4a8_quant_act.argtypes = [_P, _I, _I, _P, _P, _P]
 lib.w4fp8_quant_act.argtypes = [_P, _I, _I, _P, _P, _P]
+lib.w4a8_quant_act_ex.argtypes = [_P, _I, _I, _I, _P, _P, _P]
+lib.w4fp8_quant_act_ex.argtypes = [_P, _I, _I, _I, _P, _P, _P]
 lib.w4a8_workspace_size.argtypes = [_I, _I, _I, _I]
 lib.w4a8_workspace_size.restype = _Z
 lib.w4a8_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]
@@ -54,7 +57,8 @@ lib.w4a8_status_str.argtypes = [_I]
 lib.w4a8_status_str.restype = ctypes.c_char_p
 lib.w4a8_last_hip_error.restype = _I
 lib.w4a8_layout_version.restype = _I
-for _n in ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act", "w4a8_gemm", "w4fp8_gemm"):
+for _n in ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act", "w4a8_quant_act_ex",
+           "w4fp8_quant_act_ex", "w4a8_gemm", "w4fp8_gemm"):
     getattr(lib, _n).restype = _I
 
 assert lib.w4a8_layout_version() == LAYOUT_VERSION
@@ -126,27 +130,38 @@ def pack(W, group: int = 64, qmax: int = 127, mode: int = PACK_LQQ, stream=None)
     return out
 
 
-def quant_act(X, stream=None):
-    """Per-token INT8: (Xq int8 [M][K], sx float32 [M])."""
+def _in_type(X):
     torch = _torch()
-    _need(X, torch.float32, "X")
+    types = {torch.float32: IN_F32, torch.float16: IN_F16, torch.bfloat16: IN_BF16}
+    if X.dtype not in types:
+        raise TypeError(f"X: expected float32, float16 or bfloat16, got {X.dtype}")
+    _need(X, X.dtype, "X")
+    if X.dim() != 2:
+        raise ValueError("X must be a 2-D tensor")
+    return types[X.dtype]
+
+
+def quant_act(X, stream=None):
+    """Per-token INT8 of float32 / fp16 / bf16 X: (Xq int8 [M][K], sx float32 [M])."""
+    torch = _torch()
+    it = _in_type(X)
     M, K = X.shape
     Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
     sx = torch.empty(M, dtype=torch.float32, device=X.device)
-    _check(lib.w4a8_quant_act(_ptr(X), M, K, _ptr(Xq), _ptr(sx), _stream(stream)),
-           "w4a8_quant_act")
+    _check(lib.w4a8_quant_act_ex(_ptr(X), it, M, K, _ptr(Xq), _ptr(sx), _stream(stream)),
+           "w4a8_quant_act_ex")
     return Xq, sx
 
 
 def quant_act_fp8(X, stream=None):
-    """Per-token e4m3: (Xq uint8 [M][K], sx float32 [M])."""
+    """Per-token e4m3 of float32 / fp16 / bf16 X: (Xq uint8 [M][K], sx float32 [M])."""
     torch = _torch()
-    _need(X, torch.float32, "X")
+    it = _in_type(X)
     M, K = X.shape
     Xq = torch.empty((M, K), dtype=torch.uint8, device=X.device)
     sx = torch.empty(M, dtype=torch.float32, device=X.device)
-    _check(lib.w4fp8_quant_act(_ptr(X), M, K, _ptr(Xq), _ptr(sx), _stream(stream)),
-           "w4fp8_quant_act")
+    _check(lib.w4fp8_quant_act_ex(_ptr(X), it, M, K, _ptr(Xq), _ptr(sx), _stream(stream)),
+           "w4fp8_quant_act_ex")
     return Xq, sx
 
 

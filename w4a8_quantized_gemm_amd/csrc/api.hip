@@ -135,26 +135,40 @@ W4A8_EXPORT w4a8_status_t w4a8_pack(const float* W, int N, int K, int group, int
     return hip_status(w4a8::launch_pack_int4(W, N, K, wq, sw, stream));
 }
 
-W4A8_EXPORT w4a8_status_t w4a8_quant_act(const float* X, int M, int K, int8_t* Xq, float* sx,
-                                         hipStream_t stream) {
+W4A8_EXPORT w4a8_status_t w4a8_quant_act_ex(const void* X, int in_type, int M, int K,
+                                            int8_t* Xq, float* sx, hipStream_t stream) {
+    if (in_type != W4A8_IN_F32 && in_type != W4A8_IN_F16 && in_type != W4A8_IN_BF16)
+        return W4A8_ERR_UNSUPPORTED;
     if (M < 0 || K <= 0 || K % 16 != 0) return W4A8_ERR_SHAPE;
     if (M == 0) return W4A8_OK;  // nothing to read or write
     if (!X || !Xq || !sx) return W4A8_ERR_NULL_PTR;
     if (!aligned16(X) || !aligned16(Xq) || !aligned4(sx)) return W4A8_ERR_ALIGNMENT;
     w4a8_status_t d = check_device();
     if (d != W4A8_OK) return d;
-    return hip_status(w4a8::launch_act_int8(X, M, K, Xq, sx, stream));
+    return hip_status(w4a8::launch_act_int8(X, in_type, M, K, Xq, sx, stream));
+}
+
+W4A8_EXPORT w4a8_status_t w4fp8_quant_act_ex(const void* X, int in_type, int M, int K,
+                                             uint8_t* Xq, float* sx, hipStream_t stream) {
+    if (in_type != W4A8_IN_F32 && in_type != W4A8_IN_F16 && in_type != W4A8_IN_BF16)
+        return W4A8_ERR_UNSUPPORTED;
+    if (M < 0 || K <= 0 || K % 16 != 0) return W4A8_ERR_SHAPE;
+    if (M == 0) return W4A8_OK;  // nothing to read or write
+    if (!X || !Xq || !sx) return W4A8_ERR_NULL_PTR;
+    if (!aligned16(X) || !aligned16(Xq) || !aligned4(sx)) return W4A8_ERR_ALIGNMENT;
+    w4a8_status_t d = check_device();
+    if (d != W4A8_OK) return d;
+    return hip_status(w4a8::launch_act_e4m3(X, in_type, M, K, Xq, sx, stream));
+}
+
+W4A8_EXPORT w4a8_status_t w4a8_quant_act(const float* X, int M, int K, int8_t* Xq, float* sx,
+                                         hipStream_t stream) {
+    return w4a8_quant_act_ex(X, W4A8_IN_F32, M, K, Xq, sx, stream);
 }
 
 W4A8_EXPORT w4a8_status_t w4fp8_quant_act(const float* X, int M, int K, uint8_t* Xq, float* sx,
                                           hipStream_t stream) {
-    if (M < 0 || K <= 0 || K % 16 != 0) return W4A8_ERR_SHAPE;
-    if (M == 0) return W4A8_OK;  // nothing to read or write
-    if (!X || !Xq || !sx) return W4A8_ERR_NULL_PTR;
-    if (!aligned16(X) || !aligned16(Xq) || !aligned4(sx)) return W4A8_ERR_ALIGNMENT;
-    w4a8_status_t d = check_device();
-    if (d != W4A8_OK) return d;
-    return hip_status(w4a8::launch_act_e4m3(X, M, K, Xq, sx, stream));
+    return w4fp8_quant_act_ex(X, W4A8_IN_F32, M, K, Xq, sx, stream);
 }
 
 W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint8_t* wq,

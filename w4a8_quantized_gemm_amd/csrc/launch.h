@@ -9,9 +9,10 @@ hipError_t launch_pack_lqq(const float* W, int N, int K, int group, int qmax, ui
                            uint8_t* s_u8, uint8_t* a_u8, float* sw, hipStream_t st);
 hipError_t launch_pack_int4(const float* W, int N, int K, uint8_t* wq, float* sw,
                             hipStream_t st);
-hipError_t launch_act_int8(const float* X, int M, int K, int8_t* Xq, float* sx,
+// Per-token activation quantisation; in_type 0 = float32, 1 = fp16, 2 = bf16.
+hipError_t launch_act_int8(const void* X, int in_type, int M, int K, int8_t* Xq, float* sx,
                            hipStream_t st);
-hipError_t launch_act_e4m3(const float* X, int M, int K, uint8_t* Xq, float* sx,
+hipError_t launch_act_e4m3(const void* X, int in_type, int M, int K, uint8_t* Xq, float* sx,
                            hipStream_t st);
 
 // Streamed-tile GEMMs: one workgroup per (16*nt_per_wave rows of N, 16 rows

@@ -132,23 +132,75 @@ __global__ __launch_bounds__(256) void int4_pack_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Per-token activation quantisation: one workgroup per row.
+// Per-token activation quantisation: one workgroup per row.  The input is
+// float32, fp16 or bf16 (IN = 0, 1, 2); each element is first widened to
+// float32, which is exact, so every input type quantises like float32.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void act_int8_kernel(const float* __restrict__ X, int K,
+template <int IN>
+struct Row8 {  // eight consecutive elements of a row, widened to float32
+    float v[8];
+};
+
+template <int IN>
+__device__ __forceinline__ Row8<IN> load_row8(const void* row, int i) {  // elements 8i..8i+7
+    Row8<IN> r;
+    if constexpr (IN == 0) {
+        const float4* p = reinterpret_cast<const float4*>(row) + 2 * i;
+        const float4 a = p[0], b = p[1];
+        r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
+        r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
+    } else {
+        const v4i w = reinterpret_cast<const v4i*>(row)[i];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const unsigned h = ((unsigned)w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+            if constexpr (IN == 1)
+                r.v[j] = (float)__builtin_bit_cast(_Float16, (unsigned short)h);
+            else
+                r.v[j] = __builtin_bit_cast(float, h << 16);
+        }
+    }
+    return r;
+}
+
+template <int IN>
+__device__ __forceinline__ float row_absmax(const void* row, int K) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < K / 8; i += 256) {
+        const Row8<IN> r = load_row8<IN>(row, i);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(r.v[j]));
+    }
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    __shared__ float part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    __syncthreads();
+    return m;
+}
+
+template <int IN>
+__device__ __forceinline__ const void* row_ptr(const void* X, int K) {
+    constexpr int EB = IN == 0 ? 4 : 2;
+    return reinterpret_cast<const uint8_t*>(X) + (size_t)blockIdx.x * K * EB;
+}
+
+template <int IN>
+__global__ __launch_bounds__(256) void act_int8_kernel(const void* __restrict__ X, int K,
                                                        int8_t* __restrict__ Xq,
                                                        float* __restrict__ sx) {
-    const float* row = X + (size_t)blockIdx.x * K;
-    const float s = scale_of(block_absmax_256(row, K), 127.0f);
+    const void* row = row_ptr<IN>(X, K);
+    const float s = scale_of(row_absmax<IN>(row, K), 127.0f);
     if (threadIdx.x == 0) sx[blockIdx.x] = s;
-    const float4* r4 = reinterpret_cast<const float4*>(row);
-    unsigned* out = reinterpret_cast<unsigned*>(Xq + (size_t)blockIdx.x * K);
-    for (int i = threadIdx.x; i < K / 4; i += 256) {
-        float4 v = r4[i];
-        unsigned b0 = (unsigned)(quant_sym(v.x, s, 127.0f) & 0xFF);
-        unsigned b1 = (unsigned)(quant_sym(v.y, s, 127.0f) & 0xFF);
-        unsigned b2 = (unsigned)(quant_sym(v.z, s, 127.0f) & 0xFF);
-        unsigned b3 = (unsigned)(quant_sym(v.w, s, 127.0f) & 0xFF);
-        out[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    uint2* out = reinterpret_cast<uint2*>(Xq + (size_t)blockIdx.x * K);
+    for (int i = threadIdx.x; i < K / 8; i += 256) {
+        const Row8<IN> r = load_row8<IN>(row, i);
+        unsigned b[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = (unsigned)(quant_sym(r.v[j], s, 127.0f) & 0xFF);
+        out[i] = uint2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                       b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
     }
 }
 
@@ -175,21 +227,21 @@ __device__ __forceinline__ unsigned f32_to_e4m3(float x) {
     return sign | code;
 }
 
-__global__ __launch_bounds__(256) void act_e4m3_kernel(const float* __restrict__ X, int K,
+template <int IN>
+__global__ __launch_bounds__(256) void act_e4m3_kernel(const void* __restrict__ X, int K,
                                                        uint8_t* __restrict__ Xq,
                                                        float* __restrict__ sx) {
-    const float* row = X + (size_t)blockIdx.x * K;
-    const float s = scale_of(block_absmax_256(row, K), 448.0f);
+    const void* row = row_ptr<IN>(X, K);
+    const float s = scale_of(row_absmax<IN>(row, K), 448.0f);
     if (threadIdx.x == 0) sx[blockIdx.x] = s;
-    const float4* r4 = reinterpret_cast<const float4*>(row);
-    unsigned* out = reinterpret_cast<unsigned*>(Xq + (size_t)blockIdx.x * K);
-    for (int i = threadIdx.x; i < K / 4; i += 256) {
-        float4 v = r4[i];
-        unsigned b0 = f32_to_e4m3(__fdiv_rn(v.x, s));
-        unsigned b1 = f32_to_e4m3(__fdiv_rn(v.y, s));
-        unsigned b2 = f32_to_e4m3(__fdiv_rn(v.z, s));
-        unsigned b3 = f32_to_e4m3(__fdiv_rn(v.w, s));
-        out[i] = b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+    uint2* out = reinterpret_cast<uint2*>(Xq + (size_t)blockIdx.x * K);
+    for (int i = threadIdx.x; i < K / 8; i += 256) {
+        const Row8<IN> r = load_row8<IN>(row, i);
+        unsigned b[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) b[j] = f32_to_e4m3(__fdiv_rn(r.v[j], s));
+        out[i] = uint2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                       b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
     }
 }
 
@@ -213,14 +265,25 @@ hipError_t launch_pack_int4(const float* W, int N, int K, uint8_t* wq, float* sw
     return hipGetLastError();
 }
 
-hipError_t launch_act_int8(const float* X, int M, int K, int8_t* Xq, float* sx, hipStream_t st) {
-    hipLaunchKernelGGL(act_int8_kernel, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
+hipError_t launch_act_int8(const void* X, int in_type, int M, int K, int8_t* Xq, float* sx,
+                           hipStream_t st) {
+    if (in_type == 1)
+        hipLaunchKernelGGL(act_int8_kernel<1>, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
+    else if (in_type == 2)
+        hipLaunchKernelGGL(act_int8_kernel<2>, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
+    else
+        hipLaunchKernelGGL(act_int8_kernel<0>, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
     return hipGetLastError();
 }
 
-hipError_t launch_act_e4m3(const float* X, int M, int K, uint8_t* Xq, float* sx,
+hipError_t launch_act_e4m3(const void* X, int in_type, int M, int K, uint8_t* Xq, float* sx,
                            hipStream_t st) {
-    hipLaunchKernelGGL(act_e4m3_kernel, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
+    if (in_type == 1)
+        hipLaunchKernelGGL(act_e4m3_kernel<1>, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
+    else if (in_type == 2)
+        hipLaunchKernelGGL(act_e4m3_kernel<2>, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
+    else
+        hipLaunchKernelGGL(act_e4m3_kernel<0>, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
     return hipGetLastError();
 }
 
