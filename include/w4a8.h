@@ -173,6 +173,31 @@ w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint8_t* wq,
                         size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Ablation variants of w4a8_gemm's matrix-core kernel, for measuring what
+ * the method's two ideas buy on this hardware ([LG] referee summary: the
+ * ablation separating LiquidQuant from the pipeline; "What carries the
+ * argument"):
+ *   W4A8_ABL_LQQ          the production kernel (same as w4a8_gemm);
+ *   W4A8_ABL_AFFINE16     same stored codes and parameters, decoded as the
+ *                         conventional signed value s*q + min (min =
+ *                         a_u8 - 128) one code per 16-bit lane, the
+ *                         overflow-safe form without the UINT8 shift;
+ *   W4A8_ABL_LQQ_COARSE   LiquidQuant decode, but each K-step's weights are
+ *                         decoded in one block after that step's matrix-core
+ *                         instructions instead of interleaved with them.
+ * All three return the same results bit for bit (the decode identity).
+ * Arguments as w4a8_gemm without splitk / workspace; only shapes that the
+ * unsplit matrix-core kernel serves (M >= 64, N % 256 == 0, no K split in
+ * w4a8_workspace_size) are accepted, others return W4A8_ERR_UNSUPPORTED.
+ */
+enum { W4A8_ABL_LQQ = 0, W4A8_ABL_AFFINE16 = 1, W4A8_ABL_LQQ_COARSE = 2 };
+w4a8_status_t w4a8_gemm_ablation(int variant, const int8_t* X, const float* sx,
+                                 const uint8_t* wq, const uint8_t* s_u8,
+                                 const uint8_t* a_u8, const float* sw, void* Y,
+                                 int out_type, int M, int N, int K, int group,
+                                 hipStream_t stream);
+
+/*
  * W4FP8 GEMM ([FQ] abstract: INT4 weights x FP8 activations):
  *   acc[m][n] = sum_k e4m3(X[m][k]) * q[n][k]  (float32 accumulation; q is
  *   converted exactly to e4m3, |q| <= 7)

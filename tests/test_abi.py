@@ -115,6 +115,23 @@ def test_quant_act_validation():
         assert fn(A, 0, 64, A, A, None) == OK
 
 
+def test_gemm_ablation_validation():
+    def abl(variant=1, M=256, N=256, K=512, g=128, out=0, X=A, wq=A, s=A, a=A, Y=A):
+        return lib.w4a8_gemm_ablation(variant, X, A, wq, s, a, A, Y, out, M, N, K, g, None)
+    assert abl(variant=3) == UNSUP
+    assert abl(variant=-1) == UNSUP
+    assert abl(out=2) == UNSUP
+    assert abl(K=100) == SHAPE
+    assert abl(g=32) == SHAPE
+    assert abl(M=0) == OK
+    for v in (0, 1, 2):
+        assert abl(variant=v, M=16) == UNSUP          # streamed-kernel shape
+        assert abl(variant=v, N=192) == UNSUP         # N % 256 != 0
+        assert abl(variant=v, M=128, K=8192) == UNSUP  # the plan splits K
+        assert abl(variant=v, wq=None) == NULL
+        assert abl(variant=v, X=A + 4) == ALIGN
+
+
 def test_quant_act_ex_validation():
     for fn in (lib.w4a8_quant_act_ex, lib.w4fp8_quant_act_ex):
         for it in (0, 1, 2):

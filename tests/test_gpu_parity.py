@@ -168,9 +168,13 @@ def test_w4a8_gemm_parity(M, N, K, g):
 
 
 # Shapes that the dispatcher sends to the matrix-core tile kernel (N a
-# multiple of 256, M >= 64), with 128- and 256-row tiles and ragged M.
+# multiple of 256, M >= 64), with 128- and 256-row tiles, ragged M, and odd
+# K-step counts (640 = 5 steps, 896 = 7): an odd count runs one extra step of
+# zero X, and the accumulators' last writes must be complete before the
+# epilogue reads them.
 @pytest.mark.parametrize("M", [64, 65, 100, 128, 129, 200, 256, 257, 300, 513, 777])
-@pytest.mark.parametrize("N,K,g", [(256, 512, 64), (512, 1024, 128)])
+@pytest.mark.parametrize("N,K,g", [(256, 512, 64), (512, 1024, 128), (1024, 640, 128),
+                                   (512, 896, 64)])
 def test_w4a8_gemm_mfma_parity(M, N, K, g):
     say(f"w4a8 mfma gemm M={M} N={N} K={K} g={g}")
     X8, sx, pk, acc, y = _small_problem(M, N, K, g, 2000 + M)
@@ -228,6 +232,30 @@ def test_mfma_split_k(M, N, K, g):
     w4.gemm(X8, sx, pk, out_type=w4.OUT_F16, out=Yh, workspace=ws)
     d = f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y)
     assert d.max() <= 1
+
+
+@pytest.mark.parametrize("M,N,K,g", [(256, 512, 512, 128), (300, 256, 768, 64),
+                                     (100, 512, 512, 64), (512, 1024, 896, 128),
+                                     (256, 1024, 640, 64), (2048, 8192, 512, 64)])
+def test_ablation_variants_bit_identical(M, N, K, g):
+    """The conventional affine decode and the coarse pipeline produce the
+    same int32 accumulators (bit-exact vs the oracle) and the same fp16 as
+    the production kernel.  Shapes the unsplit tile kernel serves: 128-row
+    tiles with one to seven K-steps, and 256-row tiles (last case)."""
+    say(f"ablation variants M={M} N={N} K={K} g={g}")
+    X8, sx, pk, acc, y = _small_problem(M, N, K, g, 11)
+    ref16 = None
+    for v in (w4.ABL_LQQ, w4.ABL_AFFINE16, w4.ABL_LQQ_COARSE):
+        Yi = poison((M, N), torch.int32)
+        w4.gemm_ablation(v, X8, sx, pk, out_type=w4.OUT_I32, out=Yi)
+        np.testing.assert_array_equal(host(Yi), acc)
+        Yh = poison((M, N), torch.float16)
+        w4.gemm_ablation(v, X8, sx, pk, out_type=w4.OUT_F16, out=Yh)
+        bits = host(Yh.view(torch.int16))
+        if ref16 is None:
+            ref16 = bits
+            assert f16_ulp_diff(bits.view(np.uint16), y).max() <= 1
+        np.testing.assert_array_equal(bits, ref16)
 
 
 def test_workspace_too_small_is_rejected():
@@ -328,7 +356,7 @@ def _check_fp8_outputs(yf, yb_bits, ref, bound):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 128, 1024), (100, 256, 1024), (300, 512, 2048),
-                                   (128, 256, 4096)])
+                                   (128, 256, 4096), (100, 256, 640), (300, 512, 1152)])
 def test_w4fp8_integer_valued_exact(M, N, K):
     """Integer activations in [-16, 16] (exact in e4m3) times |q| <= 7: every
     product is an integer <= 112 and every partial sum an integer below
@@ -354,7 +382,8 @@ def test_w4fp8_integer_valued_exact(M, N, K):
 # Matrix-core tile path (M >= 64, N % 256 == 0): ragged M, several tiles in
 # both directions, one and two K-steps per split, and planned split-K with
 # float32 partials (M=128, K=4096: one tile, four splits).
-@pytest.mark.parametrize("M,N,K", [(64, 256, 1024), (100, 256, 1024), (256, 512, 2048),
+@pytest.mark.parametrize("M,N,K", [(64, 256, 640), (512, 1024, 896), (300, 512, 1152),
+                                   (64, 256, 1024), (100, 256, 1024), (256, 512, 2048),
                                    (300, 512, 1024), (513, 256, 2048), (128, 256, 4096),
                                    (100, 512, 2048), (1024, 1024, 256)])
 def test_w4fp8_tile_parity(M, N, K):

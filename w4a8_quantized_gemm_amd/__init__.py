@@ -37,10 +37,12 @@ PACK_LQQ, PACK_INT4_SYM = 0, 1
 OUT_F16, OUT_I32 = 0, 1
 OUT_BF16, OUT_F32 = 0, 1
 IN_F32, IN_F16, IN_BF16 = 0, 1, 2
+ABL_LQQ, ABL_AFFINE16, ABL_LQQ_COARSE = 0, 1, 2
 LAYOUT_VERSION = 1
 
 EXPORTS = ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act",
-           "w4a8_quant_act_ex", "w4fp8_quant_act_ex", "w4a8_workspace_size", "w4a8_gemm", "w4fp8_gemm",
+           "w4a8_quant_act_ex", "w4fp8_quant_act_ex", "w4a8_workspace_size", "w4a8_gemm",
+           "w4a8_gemm_ablation", "w4fp8_gemm",
            "w4a8_status_str", "w4a8_last_hip_error", "w4a8_layout_version")
 
 _P, _I, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -53,12 +55,13 @@ lib.w4a8_workspace_size.argtypes = [_I, _I, _I, _I]
 lib.w4a8_workspace_size.restype = _Z
 lib.w4a8_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]
 lib.w4fp8_gemm.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]
+lib.w4a8_gemm_ablation.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
 lib.w4a8_status_str.argtypes = [_I]
 lib.w4a8_status_str.restype = ctypes.c_char_p
 lib.w4a8_last_hip_error.restype = _I
 lib.w4a8_layout_version.restype = _I
 for _n in ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act", "w4a8_quant_act_ex",
-           "w4fp8_quant_act_ex", "w4a8_gemm", "w4fp8_gemm"):
+           "w4fp8_quant_act_ex", "w4a8_gemm", "w4a8_gemm_ablation", "w4fp8_gemm"):
     getattr(lib, _n).restype = _I
 
 assert lib.w4a8_layout_version() == LAYOUT_VERSION
@@ -195,6 +198,29 @@ def gemm(Xq, sx, packed, out_type: int = OUT_F16, splitk: int = 0, out=None,
                          _ptr(packed["a_u8"]), _ptr(packed["sw"]), _ptr(Y), out_type, M, N,
                          K, packed["group"], splitk, _ptr(workspace), ws_bytes,
                          _stream(stream)), "w4a8_gemm")
+    return Y
+
+
+def gemm_ablation(variant: int, Xq, sx, packed, out_type: int = OUT_F16, out=None,
+                  stream=None):
+    """w4a8_gemm_ablation: the matrix-core kernel with decode variant
+    ABL_LQQ (production), ABL_AFFINE16 (conventional signed 16-bit-lane
+    decode) or ABL_LQQ_COARSE (decode not interleaved with the matrix core)."""
+    torch = _torch()
+    _need(Xq, torch.int8, "Xq")
+    M, K = Xq.shape
+    N = packed["N"]
+    if packed["K"] != K:
+        raise ValueError("K of X and of the packed weights differ")
+    if out_type == OUT_F16:
+        _need(sx, torch.float32, "sx")
+    ydt = torch.float16 if out_type == OUT_F16 else torch.int32
+    Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
+    _need(Y, ydt, "out")
+    _check(lib.w4a8_gemm_ablation(variant, _ptr(Xq), _ptr(sx), _ptr(packed["wq"]),
+                                  _ptr(packed["s_u8"]), _ptr(packed["a_u8"]), _ptr(packed["sw"]),
+                                  _ptr(Y), out_type, M, N, K, packed["group"], _stream(stream)),
+           "w4a8_gemm_ablation")
     return Y
 
 

@@ -198,6 +198,33 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint
                                                group, choose_stream(M, N, K, splitk), stream));
 }
 
+W4A8_EXPORT w4a8_status_t w4a8_gemm_ablation(int variant, const int8_t* X, const float* sx,
+                                             const uint8_t* wq, const uint8_t* s_u8,
+                                             const uint8_t* a_u8, const float* sw, void* Y,
+                                             int out_type, int M, int N, int K, int group,
+                                             hipStream_t stream) {
+    if (variant != W4A8_ABL_LQQ && variant != W4A8_ABL_AFFINE16 &&
+        variant != W4A8_ABL_LQQ_COARSE)
+        return W4A8_ERR_UNSUPPORTED;
+    if (out_type != W4A8_OUT_F16 && out_type != W4A8_OUT_I32) return W4A8_ERR_UNSUPPORTED;
+    if (M < 0 || !valid_nk(N, K) || !valid_group(group)) return W4A8_ERR_SHAPE;
+    if (M == 0 || N == 0) return W4A8_OK;  // nothing to read or write
+    if (!use_mfma_tiles(M, N, K) || w4a8::plan_w4a8_mfma(M, N, K).splits != 1)
+        return W4A8_ERR_UNSUPPORTED;  // the variants exist for the unsplit tile kernel only
+    if (!X || !wq || !s_u8 || !a_u8 || !Y) return W4A8_ERR_NULL_PTR;
+    if (out_type == W4A8_OUT_F16 && (!sx || !sw)) return W4A8_ERR_NULL_PTR;
+    if (!aligned16(X) || !aligned16(wq) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
+    if ((sx && !aligned4(sx)) || (sw && !aligned4(sw))) return W4A8_ERR_ALIGNMENT;
+    w4a8_status_t d = check_device();
+    if (d != W4A8_OK) return d;
+    const w4a8::MfmaPlan plan = w4a8::plan_w4a8_mfma(M, N, K);
+    if (variant == W4A8_ABL_LQQ)
+        return hip_status(w4a8::launch_w4a8_mfma(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
+                                                 group, plan, nullptr, stream));
+    return hip_status(w4a8::launch_w4a8_mfma_ablation(variant, X, sx, wq, s_u8, a_u8, sw, Y,
+                                                      out_type, M, N, K, group, plan, stream));
+}
+
 W4A8_EXPORT w4a8_status_t w4fp8_gemm(const uint8_t* X_e4m3, const float* sx, const uint8_t* wq,
                                      const float* sw, void* Y, int out_type, int M, int N, int K,
                                      int splitk, void* workspace, size_t workspace_bytes,

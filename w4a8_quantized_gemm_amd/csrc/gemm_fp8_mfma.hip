@@ -115,6 +115,9 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
     const int KTall = K / kTileK;
     const int kt0 = (int)((long long)KTall * ks / splits);
     const int KT = (int)((long long)KTall * (ks + 1) / splits) - kt0;  // >= 1
+    // The main loop runs K-steps in pairs with a single exit; an odd count
+    // gets one more step whose X tile reads as zero (contributing exactly 0).
+    const int KTe = KT + (KT & 1);
 
     // ---- X: chunk p of this thread is row (tid>>3) + 32p, 16-byte column
     // tid & 7, in LDS slot col ^ xswz(row & 15).  Rows >= M lie past the end
@@ -142,8 +145,11 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
         ws.w[cb][j] = buf_load16(
             w_rsrc, wvoff, (unsigned)(((nt0 + 2 * cb) * KTall + ktg) * kTileBytes + j * 256));
     };
-    auto x_load = [&](int kt, int p) {
-        return buf_load16(xr_rsrc, xvoff + (unsigned)p * xrowstep, (unsigned)(kt * kTileK));
+    auto x_load = [&](int kt, int p) {  // kt >= KT: offset past the buffer, reads 0
+        const bool live = kt < KT;  // wave-uniform: one load, selected offsets
+        const unsigned vo = live ? xvoff + (unsigned)p * xrowstep : 0xFFFFFFF0u;
+        const unsigned so = live ? (unsigned)(kt * kTileK) : 0u;
+        return buf_load16(xr_rsrc, vo, so);
     };
     F8Lut lut;
     lut.lo = 0x44403800u;  // e4m3 of 3, 2, 1, 0
@@ -163,7 +169,7 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
     F8Step we, wo;         // raw weights for even / odd steps
     v8i B[2][2];
     v8i ring[4];
-    const int k1 = min(1, KT - 1);
+    const int k1 = min(1, KTe - 1);
 #pragma unroll
     for (int p = 0; p < CPT; ++p) xe[p] = x_load(0, p);
 #pragma unroll
@@ -196,7 +202,7 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
     //   before the last 4  barrier, then step kt+1's first two A reads.
     auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, v4i (&xcur)[CPT],
                     v4i (&xnx)[CPT], F8Step& wcur, F8Step& wnx) {
-        const int k2 = min(kt + 2, KT - 1);
+        const int k2 = min(kt + 2, KTe - 1);
         F8Tmp tmp;
         static_for<SLOTS>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
@@ -224,14 +230,11 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
         });
     };
 
-    int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
+    for (int kt = 0; kt < KTe; kt += 2) {
         step(kt, xs0, xs1, xe, xo, we, wo);
         step(kt + 1, xs1, xs0, xo, xe, wo, we);
     }
-    if (kt < KT) step(kt, xs0, xs1, xe, xo, we, wo);
-
-    mfma32_drain();
+    mfma32_drain(acc);
     __syncthreads();  // all waves done with the X buffers
 
     // ---- epilogue.  Accumulator (rb, cb) register v of lane (c, h): row

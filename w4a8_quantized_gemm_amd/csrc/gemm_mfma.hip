@@ -50,81 +50,169 @@ struct WStep32 {
     unsigned sdw, adw;
 };
 
-// Scale pair / offset quad of the lane's tiles for one K-step.
-struct WParams {
-    unsigned s2[2], a4[2];
-};
-
-__device__ __forceinline__ void wparams(const WStep32& w, int tb, WParams& p) {
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-        const unsigned b = (unsigned)(2 * cb + tb);
-        const unsigned sel = b | 0x0C00u | (b << 16) | 0x0C000000u;
-        asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.s2[cb]) : "v"(w.sdw), "v"(sel));
-        asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.a4[cb]) : "v"(w.adw), "v"(b * 0x01010101u));
-    }
-}
-
-template <int K_>
-__device__ __forceinline__ void wparam_step(const WStep32& w, int tb, WParams& p) {
-    constexpr int cb = K_ / 2;
-    const unsigned b = (unsigned)(2 * cb + tb);
-    if constexpr (K_ % 2 == 0) {
-        const unsigned sel = b | 0x0C00u | (b << 16) | 0x0C000000u;
-        asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.s2[cb]) : "v"(w.sdw), "v"(sel));
-    } else {
-        asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.a4[cb]) : "v"(w.adw), "v"(b * 0x01010101u));
-    }
-}
-
-// Operands of instruction i (K columns 64h + 16i .. +15 of the lane) come
-// from dwords d = 2(i%2), 2(i%2)+1 of slot e = i/2.  Producing B[*][i] is 28
-// single-instruction steps: for cb in {0,1}, for the two dwords:
+// Decoders of one K-step's raw weights into the B operands, as policies
+// with single-instruction steps so the kernel can spread them over the
+// matrix-core slots:
+//   kParamOps  steps that turn the parameter dwords into per-lane operands;
+//   kOps       steps that produce B[*][i] of one instruction group i (both
+//              channel blocks, two packed dwords each);
+// plus the same work in one call (params(), group<i>()).
+//
+// LiquidQuant decode (the default): per packed dword (8 codes),
 //   lo = w & 0x0F0F0F0F; t = w >> 4; hi = t & 0x0F0F0F0F;
 //   lo = lo*s + a; hi = hi*s + a   (v_pk_mad_u16, two codes per 16-bit lane);
-//   B = lo ^ 0x80808080, hi ^ 0x80808080   (LiquidQuant decode)
-struct DqTmp {
-    unsigned lo, t, hi;
+//   B = lo ^ 0x80808080, hi ^ 0x80808080
+// 7 instructions per 8 weights (LiquidGEMM, Pith review of arXiv 2509.01229,
+// paper Eq. 12 and minor comment 1 / Sec. 5.3).
+struct DecLQQ {
+    struct Params {
+        unsigned s2[2], a4[2];  // scale pair, offset quad per channel block
+    };
+    struct Tmp {
+        unsigned lo, t, hi;
+    };
+    static constexpr int kParamOps = 4;
+    static constexpr int kOps = 28;
+
+    template <int K_>
+    __device__ __forceinline__ static void param_step(const WStep32& w, int tb, Params& p) {
+        constexpr int cb = K_ / 2;
+        const unsigned b = (unsigned)(2 * cb + tb);
+        if constexpr (K_ % 2 == 0) {
+            const unsigned sel = b | 0x0C00u | (b << 16) | 0x0C000000u;
+            asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.s2[cb]) : "v"(w.sdw), "v"(sel));
+        } else {
+            asm volatile("v_perm_b32 %0, 0, %1, %2"
+                         : "=v"(p.a4[cb]) : "v"(w.adw), "v"(b * 0x01010101u));
+        }
+    }
+
+    // Instruction group I takes dwords d = 2(I%2), 2(I%2)+1 of slot e = I/2.
+    template <int I, int OP>
+    __device__ __forceinline__ static void step(Tmp& tmp, const WStep32& w, const Params& p,
+                                                v4i (&B)[2][4]) {
+        constexpr int cb = OP / 14, q = OP % 14, dd = q / 7, st = q % 7;
+        constexpr int e = I / 2, d = 2 * (I % 2) + dd;
+        const unsigned wd = (unsigned)w.w[cb][e][d];
+        if constexpr (st == 0) {
+            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.lo) : "v"(wd));
+        } else if constexpr (st == 1) {
+            asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(tmp.t) : "v"(wd));
+        } else if constexpr (st == 2) {
+            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.hi) : "v"(tmp.t));
+        } else if constexpr (st == 3) {
+            asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
+                         : "=v"(tmp.lo) : "v"(tmp.lo), "v"(p.s2[cb]), "v"(p.a4[cb]));
+        } else if constexpr (st == 4) {
+            asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
+                         : "=v"(tmp.hi) : "v"(tmp.hi), "v"(p.s2[cb]), "v"(p.a4[cb]));
+        } else if constexpr (st == 5) {
+            unsigned x;
+            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(tmp.lo));
+            B[cb][I][2 * dd] = (int)x;
+        } else {
+            unsigned x;
+            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(tmp.hi));
+            B[cb][I][2 * dd + 1] = (int)x;
+        }
+    }
 };
 
-template <int I, int OP>
-__device__ __forceinline__ void dq_group_step(DqTmp& tmp, const WStep32& w, const WParams& p,
-                                              v4i (&B)[2][4]) {
-    constexpr int cb = OP / 14, q = OP % 14, dd = q / 7, st = q % 7;
-    constexpr int e = I / 2, d = 2 * (I % 2) + dd;
-    const unsigned wd = (unsigned)w.w[cb][e][d];
-    if constexpr (st == 0) {
-        asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.lo) : "v"(wd));
-    } else if constexpr (st == 1) {
-        asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(tmp.t) : "v"(wd));
-    } else if constexpr (st == 2) {
-        asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.hi) : "v"(tmp.t));
-    } else if constexpr (st == 3) {
-        asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
-                     : "=v"(tmp.lo) : "v"(tmp.lo), "v"(p.s2[cb]), "v"(p.a4[cb]));
-    } else if constexpr (st == 4) {
-        asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
-                     : "=v"(tmp.hi) : "v"(tmp.hi), "v"(p.s2[cb]), "v"(p.a4[cb]));
-    } else if constexpr (st == 5) {
-        unsigned x;
-        asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(tmp.lo));
-        B[cb][I][2 * dd] = (int)x;
-    } else {
-        unsigned x;
-        asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(tmp.hi));
-        B[cb][I][2 * dd + 1] = (int)x;
+// Conventional sign-safe decode, for the ablation: the same stored codes
+// and parameters decoded as the plain affine value s*q + min (min = a - 128)
+// in signed 16-bit lanes, one code per lane, because a negative result in
+// a byte lane would borrow from its neighbour -- the overflow handling the
+// LiquidQuant shift into UINT8 removes (same review, "What carries the
+// argument").  Per packed dword: the nibble split, then for each half two
+// byte spreads, two v_pk_mad_i16 and one byte gather: 13 instructions per 8
+// weights.  Equal to the LiquidQuant decode value for value (the identity
+// (q*s + a) XOR 0x80 = q*s + a - 128 on INT8 results).
+struct DecAffine16 {
+    struct Params {
+        unsigned s2[2], m2[2];  // scale, min in both 16-bit lanes
+    };
+    struct Tmp {
+        unsigned lo, t, hi, e0, e1;
+    };
+    static constexpr int kParamOps = 6;
+    static constexpr int kOps = 52;
+
+    template <int K_>
+    __device__ __forceinline__ static void param_step(const WStep32& w, int tb, Params& p) {
+        constexpr int cb = K_ / 3, st = K_ % 3;
+        const unsigned b = (unsigned)(2 * cb + tb);
+        const unsigned sel = b | 0x0C00u | (b << 16) | 0x0C000000u;
+        if constexpr (st == 0) {
+            asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.s2[cb]) : "v"(w.sdw), "v"(sel));
+        } else if constexpr (st == 1) {
+            asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(p.m2[cb]) : "v"(w.adw), "v"(sel));
+        } else {
+            asm volatile("v_pk_sub_u16 %0, %1, %2" : "=v"(p.m2[cb]) : "v"(p.m2[cb]), "s"(0x00800080u));
+        }
     }
+
+    template <int I, int OP>
+    __device__ __forceinline__ static void step(Tmp& tmp, const WStep32& w, const Params& p,
+                                                v4i (&B)[2][4]) {
+        constexpr int cb = OP / 26, q = OP % 26, dd = q / 13, st = q % 13;
+        constexpr int e = I / 2, d = 2 * (I % 2) + dd;
+        const unsigned wd = (unsigned)w.w[cb][e][d];
+        constexpr unsigned kEven = 0x0C020C00u, kOdd = 0x0C030C01u, kGather = 0x06020400u;
+        if constexpr (st == 0) {
+            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.lo) : "v"(wd));
+        } else if constexpr (st == 1) {
+            asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(tmp.t) : "v"(wd));
+        } else if constexpr (st == 2) {
+            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.hi) : "v"(tmp.t));
+        } else if constexpr (st == 3 || st == 8) {
+            const unsigned src = st == 3 ? tmp.lo : tmp.hi;
+            asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(tmp.e0) : "v"(src), "s"(kEven));
+        } else if constexpr (st == 4 || st == 9) {
+            const unsigned src = st == 4 ? tmp.lo : tmp.hi;
+            asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(tmp.e1) : "v"(src), "s"(kOdd));
+        } else if constexpr (st == 5 || st == 10) {
+            asm volatile("v_pk_mad_i16 %0, %1, %2, %3"
+                         : "=v"(tmp.e0) : "v"(tmp.e0), "v"(p.s2[cb]), "v"(p.m2[cb]));
+        } else if constexpr (st == 6 || st == 11) {
+            asm volatile("v_pk_mad_i16 %0, %1, %2, %3"
+                         : "=v"(tmp.e1) : "v"(tmp.e1), "v"(p.s2[cb]), "v"(p.m2[cb]));
+        } else {
+            unsigned x;
+            asm volatile("v_perm_b32 %0, %1, %2, %3" : "=v"(x) : "v"(tmp.e1), "v"(tmp.e0), "s"(kGather));
+            B[cb][I][2 * dd + (st == 12 ? 1 : 0)] = (int)x;
+        }
+    }
+};
+
+template <class DEC>
+__device__ __forceinline__ void dec_params(const WStep32& w, int tb, typename DEC::Params& p) {
+    static_for<DEC::kParamOps>([&](auto k) { DEC::template param_step<decltype(k)::value>(w, tb, p); });
 }
 
-template <int I>
-__device__ __forceinline__ void dq_group_all(const WStep32& w, const WParams& p, v4i (&B)[2][4]) {
-    DqTmp tmp;
-    static_for<28>([&](auto oc) { dq_group_step<I, decltype(oc)::value>(tmp, w, p, B); });
+template <class DEC, int I>
+__device__ __forceinline__ void dec_group(const WStep32& w, const typename DEC::Params& p,
+                                          v4i (&B)[2][4]) {
+    typename DEC::Tmp tmp;
+    static_for<DEC::kOps>([&](auto oc) { DEC::template step<I, decltype(oc)::value>(tmp, w, p, B); });
+}
+
+template <class DEC>
+__device__ __forceinline__ void dec_all(const WStep32& w, int tb, typename DEC::Params& p,
+                                        v4i (&B)[2][4]) {
+    dec_params<DEC>(w, tb, p);
+    dec_group<DEC, 0>(w, p, B);
+    dec_group<DEC, 1>(w, p, B);
+    dec_group<DEC, 2>(w, p, B);
+    dec_group<DEC, 3>(w, p, B);
 }
 
 }  // namespace
 
-template <int MT, int OUT, int GROUP, bool PARTIAL>
+// DEC: weight decoder policy (DecLQQ; DecAffine16 for the ablation).
+// COARSE: decode each K-step's weights in one block after that step's
+// matrix-core instructions instead of interleaving them (ablation of the
+// fine-grained overlap).
+template <int MT, int OUT, int GROUP, bool PARTIAL, class DEC, bool COARSE>
 __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ s_u8, const uint8_t* __restrict__ a_u8,
@@ -134,7 +222,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     constexpr int CPT = MT / 32;       // 16-byte X chunks per thread per K-step
     constexpr int SLOTS = 8 * RB;      // matrix-core instructions per wave per K-step
     constexpr int GS = SLOTS / 4;      // slots per instruction group i
-    constexpr int DQ = (32 + GS - 1) / GS;  // dequantisation steps per slot
+    constexpr int DQ = (DEC::kParamOps + DEC::kOps + GS - 1) / GS;  // decode steps per slot
     __shared__ __attribute__((aligned(1024))) uint8_t xs0[MT * 128];
     __shared__ __attribute__((aligned(1024))) uint8_t xs1[MT * 128];
     __shared__ float sxs[MT];
@@ -152,6 +240,9 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     const int KTall = K / kTileK;
     const int kt0 = (int)((long long)KTall * ks / splits);
     const int KT = (int)((long long)KTall * (ks + 1) / splits) - kt0;  // >= 1
+    // The main loop runs K-steps in pairs with a single exit; an odd count
+    // gets one more step whose X tile reads as zero (contributing exactly 0).
+    const int KTe = KT + (KT & 1);
     const int groups = K / GROUP;
 
     // ---- X: chunk p of this thread is row (tid>>3) + 32p, 16-byte column
@@ -188,8 +279,11 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
             else ws.adw = buf_load4(a_rsrc, pvoff, jo);
         }
     };
-    auto x_load = [&](int kt, int p) {
-        return buf_load16(xr_rsrc, xvoff + (unsigned)p * xrowstep, (unsigned)(kt * kTileK));
+    auto x_load = [&](int kt, int p) {  // kt >= KT: offset past the buffer, reads 0
+        const bool live = kt < KT;  // wave-uniform: one load, selected offsets
+        const unsigned vo = live ? xvoff + (unsigned)p * xrowstep : 0xFFFFFFF0u;
+        const unsigned so = live ? (unsigned)(kt * kTileK) : 0u;
+        return buf_load16(xr_rsrc, vo, so);
     };
 
     v16i acc[RB][2];
@@ -203,10 +297,10 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     // W(1) raw; A ring primed with step 0's first four operands.
     v4i xe[CPT], xo[CPT];   // X staging for even / odd steps (X(kt) in set kt%2)
     WStep32 we, wo;         // raw weights for even / odd steps
-    WParams pp;             // parameters of the raw set being dequantised
+    typename DEC::Params pp;  // parameters of the raw set being decoded
     v4i B[2][4];
     v4i ring[8];
-    const int k1 = min(1, KT - 1);
+    const int k1 = min(1, KTe - 1);
 #pragma unroll
     for (int p = 0; p < CPT; ++p) xe[p] = x_load(0, p);
 #pragma unroll
@@ -217,11 +311,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     for (int pi = 0; pi < 6; ++pi) w_load(k1, pi, wo);
 #pragma unroll
     for (int p = 0; p < CPT; ++p) *reinterpret_cast<v4i*>(xs0 + xlds0 + p * 4096) = xe[p];
-    wparams(we, tb, pp);
-    dq_group_all<0>(we, pp, B);
-    dq_group_all<1>(we, pp, B);
-    dq_group_all<2>(we, pp, B);
-    dq_group_all<3>(we, pp, B);
+    dec_all<DEC>(we, tb, pp, B);
     __syncthreads();
     auto read_a = [&](const uint8_t* buf, int sI) {  // sI = RB*i + rb
         return *reinterpret_cast<const v4i*>(buf + (sI % RB) * 4096 + aoff[sI / RB]);
@@ -243,8 +333,8 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     //                      last four slots use operands read earlier.
     auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, v4i (&xcur)[CPT],
                     v4i (&xnx)[CPT], WStep32& wcur, WStep32& wnx) {
-        const int k2 = min(kt + 2, KT - 1);
-        DqTmp tmp;
+        const int k2 = min(kt + 2, KTe - 1);
+        typename DEC::Tmp tmp;
         static_for<SLOTS>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
             constexpr int sI = s / 2, i = sI / RB, rb = sI % RB, cb = s % 2;
@@ -261,28 +351,31 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
             if constexpr (s >= SLOTS - 4 - CPT && s < SLOTS - 4)
                 *reinterpret_cast<v4i*>(nxt + xlds0 + (s - (SLOTS - 4 - CPT)) * 4096) =
                     xnx[s - (SLOTS - 4 - CPT)];
-            static_for<DQ>([&](auto dc) {
-                constexpr int o = DQ * sg + decltype(dc)::value;
-                if constexpr (g == 0) {
-                    if constexpr (o < 28) dq_group_step<3, o>(tmp, wcur, pp, B);
-                } else if constexpr (g == 1) {
-                    if constexpr (o < 4) wparam_step<o>(wnx, tb, pp);
-                    else if constexpr (o - 4 < 28) dq_group_step<0, o - 4>(tmp, wnx, pp, B);
-                } else {
-                    if constexpr (o < 28) dq_group_step<g - 1, o>(tmp, wnx, pp, B);
-                }
-            });
+            if constexpr (!COARSE) {
+                constexpr int PO = DEC::kParamOps, NO = DEC::kOps;
+                static_for<DQ>([&](auto dc) {
+                    constexpr int o = DQ * sg + decltype(dc)::value;
+                    if constexpr (g == 0) {
+                        if constexpr (o < NO) DEC::template step<3, o>(tmp, wcur, pp, B);
+                    } else if constexpr (g == 1) {
+                        if constexpr (o < PO) DEC::template param_step<o>(wnx, tb, pp);
+                        else if constexpr (o - PO < NO)
+                            DEC::template step<0, o - PO>(tmp, wnx, pp, B);
+                    } else {
+                        if constexpr (o < NO) DEC::template step<g - 1, o>(tmp, wnx, pp, B);
+                    }
+                });
+            }
         });
+        // Coarse variant: the whole next step decoded here, the matrix cores idle.
+        if constexpr (COARSE) dec_all<DEC>(wnx, tb, pp, B);
     };
 
-    int kt = 0;
-    for (; kt + 1 < KT; kt += 2) {
+    for (int kt = 0; kt < KTe; kt += 2) {
         step(kt, xs0, xs1, xe, xo, we, wo);
         step(kt + 1, xs1, xs0, xo, xe, wo, we);
     }
-    if (kt < KT) step(kt, xs0, xs1, xe, xo, we, wo);
-
-    mfma32_drain();
+    mfma32_drain(acc);
     __syncthreads();  // all waves done with the X buffers
 
     // ---- epilogue.  Accumulator (rb, cb) register v of lane (c, h): row
@@ -375,7 +468,7 @@ MfmaPlan plan_w4a8_mfma(int M, int N, int K) {
     return p;
 }
 
-template <int MT, int OUT, bool PARTIAL>
+template <int MT, int OUT, bool PARTIAL, class DEC = DecLQQ, bool COARSE = false>
 static void launch_tile(const int8_t* X, const float* sx, const uint8_t* wq, const uint8_t* s_u8,
                         const uint8_t* a_u8, const float* sw, void* Y, int* part, int M, int N,
                         int K, int group, int splits, hipStream_t st) {
@@ -383,11 +476,13 @@ static void launch_tile(const int8_t* X, const float* sx, const uint8_t* wq, con
     const int tiles_m = (M + MT - 1) / MT;
     dim3 grid(tiles_n * tiles_m * splits), block(256);
     if (group == 64)
-        hipLaunchKernelGGL((w4a8_mfma_kernel<MT, OUT, 64, PARTIAL>), grid, block, 0, st, X, sx, wq,
-                           s_u8, a_u8, sw, Y, part, M, N, K, tiles_n, tiles_m, splits);
+        hipLaunchKernelGGL((w4a8_mfma_kernel<MT, OUT, 64, PARTIAL, DEC, COARSE>), grid, block, 0,
+                           st, X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, tiles_n, tiles_m,
+                           splits);
     else
-        hipLaunchKernelGGL((w4a8_mfma_kernel<MT, OUT, 128, PARTIAL>), grid, block, 0, st, X, sx,
-                           wq, s_u8, a_u8, sw, Y, part, M, N, K, tiles_n, tiles_m, splits);
+        hipLaunchKernelGGL((w4a8_mfma_kernel<MT, OUT, 128, PARTIAL, DEC, COARSE>), grid, block, 0,
+                           st, X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, tiles_n, tiles_m,
+                           splits);
 }
 
 hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
@@ -417,6 +512,32 @@ hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
     else
         hipLaunchKernelGGL((splitk_reduce_kernel<0>), dim3(blocks), dim3(256), 0, st, part,
                            plan.splits, M, N, sx, sw, Y);
+    return hipGetLastError();
+}
+
+template <class DEC, bool COARSE>
+static void launch_ablation(const int8_t* X, const float* sx, const uint8_t* wq,
+                            const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
+                            int out_type, int M, int N, int K, int group, int mt, hipStream_t st) {
+    if (mt == 256) {
+        if (out_type == 1) launch_tile<256, 1, false, DEC, COARSE>(X, sx, wq, s_u8, a_u8, sw, Y, nullptr, M, N, K, group, 1, st);
+        else launch_tile<256, 0, false, DEC, COARSE>(X, sx, wq, s_u8, a_u8, sw, Y, nullptr, M, N, K, group, 1, st);
+    } else {
+        if (out_type == 1) launch_tile<128, 1, false, DEC, COARSE>(X, sx, wq, s_u8, a_u8, sw, Y, nullptr, M, N, K, group, 1, st);
+        else launch_tile<128, 0, false, DEC, COARSE>(X, sx, wq, s_u8, a_u8, sw, Y, nullptr, M, N, K, group, 1, st);
+    }
+}
+
+hipError_t launch_w4a8_mfma_ablation(int variant, const int8_t* X, const float* sx,
+                                     const uint8_t* wq, const uint8_t* s_u8, const uint8_t* a_u8,
+                                     const float* sw, void* Y, int out_type, int M, int N, int K,
+                                     int group, const MfmaPlan& plan, hipStream_t st) {
+    if (variant == 1)
+        launch_ablation<DecAffine16, false>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
+                                            group, plan.mt, st);
+    else
+        launch_ablation<DecLQQ, true>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group,
+                                      plan.mt, st);
     return hipGetLastError();
 }
 

@@ -42,6 +42,14 @@ hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
                             int out_type, int M, int N, int K, int group, const MfmaPlan& plan,
                             void* workspace, hipStream_t st);
 
+// Ablation variants of the W4A8 tile kernel (plan.splits must be 1):
+// variant 1 = conventional signed affine decode in 16-bit lanes, variant 2 =
+// LiquidQuant decode done per K-step in one block (no fine-grained overlap).
+hipError_t launch_w4a8_mfma_ablation(int variant, const int8_t* X, const float* sx,
+                                     const uint8_t* wq, const uint8_t* s_u8, const uint8_t* a_u8,
+                                     const float* sw, void* Y, int out_type, int M, int N, int K,
+                                     int group, const MfmaPlan& plan, hipStream_t st);
+
 // W4FP8 matrix-core tile kernel: same tiles and plan as the W4A8 one, with
 // float32 partials in the workspace when plan.splits > 1.
 hipError_t launch_w4fp8_mfma(const uint8_t* X, const float* sx, const uint8_t* wq,

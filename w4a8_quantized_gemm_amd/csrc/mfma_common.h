@@ -39,10 +39,22 @@ __device__ __forceinline__ unsigned buf_load4(__amdgpu_buffer_rsrc_t r, unsigned
 }
 
 // Wait states between the last accumulation written in inline assembly and
-// the first read of the accumulators (the compiler does not see those).
-__device__ __forceinline__ void mfma32_drain() {
+// any read of the accumulators.  The compiler sees neither the matrix-core
+// instructions nor their latency, so after the wait every accumulator is
+// passed through an empty assembly statement that it must treat as the
+// accumulator's new definition: copies the register allocator makes (into
+// VGPRs for the epilogue, or between the allocations of two control-flow
+// paths) can then only come after the wait.  Call at the end of every path
+// that leaves the main loop.
+template <typename ACC, int RB>
+__device__ __forceinline__ void mfma32_drain(ACC (&acc)[RB][2]) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
+        asm volatile("" : "+a"(acc[rb][0]));
+        asm volatile("" : "+a"(acc[rb][1]));
+    }
     __builtin_amdgcn_sched_barrier(0);
 }
 
