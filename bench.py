@@ -49,6 +49,7 @@ def parse():
     p.add_argument("--only", default="", help="run one slot, e.g. upgate:M4096")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true")
+    p.add_argument("--no-ablation", action="store_true")
     p.add_argument("--cpu-sample-cols", type=int, default=256)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 256 MiB device-to-device copies (the known-size "
@@ -263,6 +264,32 @@ def main():
         "kernel_ms_per_step": round(kern_ms_sum, 4),
         "sweep": sweep,
     }
+
+    # ---- decode ablation on the matrix-core slots (outside the timed step):
+    # the production LiquidQuant decode interleaved with the matrix cores, the
+    # conventional signed affine decode, and the LiquidQuant decode done per
+    # K-step in one block.  Same codes, same results bit for bit.
+    if not args.no_ablation:
+        abl = []
+        names = {w4.ABL_LQQ: "lqq", w4.ABL_AFFINE16: "affine16", w4.ABL_LQQ_COARSE: "lqq_coarse"}
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for sl in slots:
+            if sl["M"] < 1024:
+                continue
+            row = {"slot": sl["name"]}
+            for v, nm in names.items():
+                w4.gemm_ablation(v, sl["X"], sl["sx"], sl["pk"], out=sl["Y"])
+                reps = 5
+                e0.record(stream)
+                for _ in range(reps):
+                    w4.gemm_ablation(v, sl["X"], sl["sx"], sl["pk"], out=sl["Y"])
+                e1.record(stream)
+                torch.cuda.synchronize()
+                row[nm + "_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+            row["affine16_vs_lqq"] = round(row["affine16_us"] / row["lqq_us"], 3)
+            row["coarse_vs_lqq"] = round(row["lqq_coarse_us"] / row["lqq_us"], 3)
+            abl.append(row)
+        out["ablation"] = abl
 
     # ---- FP8 variant (INT4 weights x e4m3 activations), reported alongside
     if not args.no_fp8 and not args.only:
