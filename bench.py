@@ -50,6 +50,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true")
     p.add_argument("--no-ablation", action="store_true")
+    p.add_argument("--no-moe", action="store_true")
     p.add_argument("--cpu-sample-cols", type=int, default=256)
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 256 MiB device-to-device copies (the known-size "
@@ -290,6 +291,50 @@ def main():
             row["coarse_vs_lqq"] = round(row["lqq_coarse_us"] / row["lqq_us"], 3)
             abl.append(row)
         out["ablation"] = abl
+
+    # ---- grouped (mixture-of-experts) GEMM: Mixtral-8x7B expert layers, 8
+    # experts with top-2 routing drawn from a seeded generator (each token to
+    # two distinct experts), synthetic weights and activations of those shapes
+    if not args.no_moe and not args.only:
+        rng = np.random.default_rng(8)
+        E, g_moe = 8, 128
+        moe = []
+        for (Nm, Km, tag) in ((14336, 4096, "up"), (4096, 14336, "down")):
+            Ws = torch.from_numpy(np.stack([wl.gen_weights(Nm, Km, 800 + e) for e in range(E)]))
+            pkm = w4.pack_experts(Ws.to(dev), group=g_moe)
+            del Ws
+            for T in (16, 2048):
+                picks = np.stack([rng.choice(E, 2, replace=False) for _ in range(T)])
+                counts = np.bincount(picks.ravel(), minlength=E)
+                offs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
+                Mm = int(counts.sum())
+                Xm = torch.from_numpy(wl.gen_activations(Mm, Km, 900 + T, 901)).to(dev)
+                Xq_m, sx_m = w4.quant_act(Xm)
+                Ym = torch.empty((Mm, Nm), dtype=torch.float16, device=dev)
+                mr = int(counts.max())
+                for _ in range(3):
+                    w4.gemm_grouped(Xq_m, sx_m, offs, pkm, mr, out=Ym)
+                reps = 10
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                for _ in range(reps):
+                    w4.gemm_grouped(Xq_m, sx_m, offs, pkm, mr, out=Ym)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                active = int((counts > 0).sum())
+                wbytes = active * weight_bytes(Nm, Km, g_moe)
+                moe.append({"layer": tag, "N": Nm, "K": Km, "tokens": T, "rows": Mm,
+                            "max_rows_per_expert": mr, "active_experts": active,
+                            "us": round(us, 2),
+                            "tops": round(2.0 * Mm * Nm * Km / (us * 1e-6) / 1e12, 2),
+                            "weight_stream_gbs": round(wbytes / (us * 1e-6) / 1e9, 1)})
+            del pkm
+        out["variant_moe"] = {"workload": "Mixtral-8x7B expert layers, 8 experts top-2, "
+                                          "W4A8 group 128, fp16 out; events over 10 back-to-back "
+                                          "launches (inputs L2/MALL-warm)",
+                              "results": moe}
 
     # ---- FP8 variant (INT4 weights x e4m3 activations), reported alongside
     if not args.no_fp8 and not args.only:

@@ -173,6 +173,32 @@ w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint8_t* wq,
                         size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Grouped W4A8 GEMM for mixture-of-experts layers (the pages evaluate
+ * Mixtral-8x7B; [LG] review, "What would settle it"): E experts, each a
+ * w4a8_gemm of its own rows against its own packed weights, in one launch.
+ *   X, Y: [M][K] int8 / [M][N] fp16 or int32, rows grouped by expert:
+ *     rows offsets[e] .. offsets[e+1]-1 belong to expert e.
+ *   offsets: device int32 [E+1], non-decreasing, offsets[0] = 0,
+ *     offsets[E] <= M (read on the device; values are clamped to [0, M], so
+ *     inconsistent offsets leave rows unwritten but never access outside X,
+ *     Y or sx).
+ *   wq, s_u8, a_u8, sw: the E experts' w4a8_pack outputs (same N, K, group)
+ *     laid end to end: expert e at wq + e*N*K/2, s_u8/a_u8 + e*N*K/group,
+ *     sw + e*N.
+ *   max_rows: host-side bound on any expert's row count (sizes the grid;
+ *     rows beyond it are not computed).
+ * Results per expert are exactly those of w4a8_gemm on that expert's rows.
+ * Kernel: streamed tiles when max_rows < 64, else matrix-core tiles (N % 256
+ * == 0); no K split, no workspace.  M * K < 2^31.
+ */
+w4a8_status_t w4a8_gemm_grouped(const int8_t* X, const float* sx,
+                                const int32_t* offsets, int E,
+                                const uint8_t* wq, const uint8_t* s_u8,
+                                const uint8_t* a_u8, const float* sw, void* Y,
+                                int out_type, int M, int N, int K, int group,
+                                int max_rows, hipStream_t stream);
+
+/*
  * Ablation variants of w4a8_gemm's matrix-core kernel, for measuring what
  * the method's two ideas buy on this hardware ([LG] referee summary: the
  * ablation separating LiquidQuant from the pipeline; "What carries the

@@ -132,6 +132,24 @@ def test_gemm_ablation_validation():
         assert abl(variant=v, X=A + 4) == ALIGN
 
 
+def test_gemm_grouped_validation():
+    def grp(M=64, E=4, N=256, K=512, g=64, out=0, rows=16, X=A, off=A, wq=A, Y=A):
+        return lib.w4a8_gemm_grouped(X, A, off, E, wq, A, A, A, Y, out, M, N, K, g, rows, None)
+    assert grp(out=2) == UNSUP
+    assert grp(E=0) == SHAPE
+    assert grp(K=100) == SHAPE
+    assert grp(N=48) == SHAPE
+    assert grp(g=32) == SHAPE
+    assert grp(rows=-1) == SHAPE
+    assert grp(M=1 << 20, K=4096) == SHAPE      # M*K >= 2^31
+    assert grp(M=0) == OK
+    assert grp(rows=0) == OK
+    assert grp(off=None) == NULL
+    assert grp(wq=None) == NULL
+    assert grp(off=A + 2) == ALIGN
+    assert grp(X=A + 4) == ALIGN
+
+
 def test_quant_act_ex_validation():
     for fn in (lib.w4a8_quant_act_ex, lib.w4fp8_quant_act_ex):
         for it in (0, 1, 2):

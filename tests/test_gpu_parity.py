@@ -258,6 +258,45 @@ def test_ablation_variants_bit_identical(M, N, K, g):
         np.testing.assert_array_equal(bits, ref16)
 
 
+@pytest.mark.parametrize("counts,N,K,g", [
+    ([5, 0, 16, 19], 256, 512, 64),          # streamed kernel; an empty expert
+    ([1, 1, 1, 1, 1, 1, 1, 1], 512, 640, 128),  # one row each (decode, top-1)
+    ([33, 7, 0, 40], 128, 1024, 64),          # ragged, several 16-row blocks
+    ([70, 0, 130, 300], 512, 640, 128),       # matrix-core tiles, odd K-steps
+    ([257, 64, 1], 256, 512, 64),             # tiles; an expert with one row
+])
+def test_grouped_gemm_parity(counts, N, K, g):
+    """Each expert's rows equal w4a8_gemm of those rows against that
+    expert's weights: int32 bit-exact, fp16 within 1 ulp; rows past every
+    expert's range are not written."""
+    E = len(counts)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    M = int(offs[-1]) + 3                  # three trailing rows no expert owns
+    say(f"grouped gemm E={E} counts={counts} N={N} K={K} g={g}")
+    X = wl.gen_activations(M, K, 600 + M, 601)
+    X8, sx = oracle.quant_sym_rows(X, 127)
+    refs = [oracle.w4a8_pack(wl.gen_weights(N, K, 610 + e), g) for e in range(E)]
+    pk = {"wq": to_dev(np.concatenate([r["wq"].ravel() for r in refs])),
+          "s_u8": to_dev(np.concatenate([r["s_panels"] for r in refs])),
+          "a_u8": to_dev(np.concatenate([r["a_panels"] for r in refs])),
+          "sw": to_dev(np.concatenate([r["sw"] for r in refs])),
+          "N": N, "K": K, "group": g, "E": E}
+    off_d = to_dev(offs)
+    Yi = poison((M, N), torch.int32)
+    w4.gemm_grouped(to_dev(X8), to_dev(sx), off_d, pk, max(counts), out_type=w4.OUT_I32, out=Yi)
+    Yh = poison((M, N), torch.float16)
+    w4.gemm_grouped(to_dev(X8), to_dev(sx), off_d, pk, max(counts), out_type=w4.OUT_F16, out=Yh)
+    yi, yh = host(Yi), host(Yh.view(torch.int16)).view(np.uint16)
+    for e in range(E):
+        r0, r1 = offs[e], offs[e + 1]
+        if r1 == r0:
+            continue
+        acc, y, _ = oracle.w4a8_gemm(X8[r0:r1], sx[r0:r1], refs[e], g)
+        np.testing.assert_array_equal(yi[r0:r1], acc)
+        assert f16_ulp_diff(yh[r0:r1], y).max() <= 1
+    assert np.all(yi[offs[-1]:].view(np.uint32) == 0xABABABAB)   # untouched
+
+
 def test_workspace_too_small_is_rejected():
     M, N, K = 128, 512, 4096
     X8, sx, pk, acc, y = _small_problem(M, N, K, 128, 3)

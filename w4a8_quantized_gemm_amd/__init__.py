@@ -42,7 +42,7 @@ LAYOUT_VERSION = 1
 
 EXPORTS = ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act",
            "w4a8_quant_act_ex", "w4fp8_quant_act_ex", "w4a8_workspace_size", "w4a8_gemm",
-           "w4a8_gemm_ablation", "w4fp8_gemm",
+           "w4a8_gemm_ablation", "w4a8_gemm_grouped", "w4fp8_gemm",
            "w4a8_status_str", "w4a8_last_hip_error", "w4a8_layout_version")
 
 _P, _I, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -56,12 +56,14 @@ lib.w4a8_workspace_size.restype = _Z
 lib.w4a8_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]
 lib.w4fp8_gemm.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]
 lib.w4a8_gemm_ablation.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
+lib.w4a8_gemm_grouped.argtypes = [_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
 lib.w4a8_status_str.argtypes = [_I]
 lib.w4a8_status_str.restype = ctypes.c_char_p
 lib.w4a8_last_hip_error.restype = _I
 lib.w4a8_layout_version.restype = _I
 for _n in ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act", "w4a8_quant_act_ex",
-           "w4fp8_quant_act_ex", "w4a8_gemm", "w4a8_gemm_ablation", "w4fp8_gemm"):
+           "w4fp8_quant_act_ex", "w4a8_gemm", "w4a8_gemm_ablation", "w4a8_gemm_grouped",
+           "w4fp8_gemm"):
     getattr(lib, _n).restype = _I
 
 assert lib.w4a8_layout_version() == LAYOUT_VERSION
@@ -198,6 +200,41 @@ def gemm(Xq, sx, packed, out_type: int = OUT_F16, splitk: int = 0, out=None,
                          _ptr(packed["a_u8"]), _ptr(packed["sw"]), _ptr(Y), out_type, M, N,
                          K, packed["group"], splitk, _ptr(workspace), ws_bytes,
                          _stream(stream)), "w4a8_gemm")
+    return Y
+
+
+def pack_experts(Ws, group: int = 128, stream=None):
+    """w4a8_pack of each expert's float32 [N][K] weights, laid end to end as
+    w4a8_gemm_grouped expects (Ws: float32 [E][N][K] tensor or list)."""
+    torch = _torch()
+    parts = [pack(W, group=group, stream=stream) for W in Ws]
+    out = {k: torch.cat([p[k] for p in parts]) for k in ("wq", "s_u8", "a_u8", "sw")}
+    out.update(N=parts[0]["N"], K=parts[0]["K"], group=group, E=len(parts))
+    return out
+
+
+def gemm_grouped(Xq, sx, offsets, packed, max_rows: int, out_type: int = OUT_F16, out=None,
+                 stream=None):
+    """w4a8_gemm_grouped: rows offsets[e]..offsets[e+1]-1 of Xq use expert e
+    of `packed` (from pack_experts); offsets is a device int32 [E+1] tensor."""
+    torch = _torch()
+    _need(Xq, torch.int8, "Xq")
+    _need(offsets, torch.int32, "offsets")
+    M, K = Xq.shape
+    N, E = packed["N"], packed["E"]
+    if packed["K"] != K:
+        raise ValueError("K of X and of the packed weights differ")
+    if offsets.numel() != E + 1:
+        raise ValueError("offsets must hold E + 1 entries")
+    if out_type == OUT_F16:
+        _need(sx, torch.float32, "sx")
+    ydt = torch.float16 if out_type == OUT_F16 else torch.int32
+    Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
+    _need(Y, ydt, "out")
+    _check(lib.w4a8_gemm_grouped(_ptr(Xq), _ptr(sx), _ptr(offsets), E, _ptr(packed["wq"]),
+                                 _ptr(packed["s_u8"]), _ptr(packed["a_u8"]), _ptr(packed["sw"]),
+                                 _ptr(Y), out_type, M, N, K, packed["group"], max_rows,
+                                 _stream(stream)), "w4a8_gemm_grouped")
     return Y
 
 

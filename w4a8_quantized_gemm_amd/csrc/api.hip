@@ -198,6 +198,42 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint
                                                group, choose_stream(M, N, K, splitk), stream));
 }
 
+W4A8_EXPORT w4a8_status_t w4a8_gemm_grouped(const int8_t* X, const float* sx,
+                                            const int32_t* offsets, int E, const uint8_t* wq,
+                                            const uint8_t* s_u8, const uint8_t* a_u8,
+                                            const float* sw, void* Y, int out_type, int M, int N,
+                                            int K, int group, int max_rows, hipStream_t stream) {
+    if (out_type != W4A8_OUT_F16 && out_type != W4A8_OUT_I32) return W4A8_ERR_UNSUPPORTED;
+    if (M < 0 || E < 1 || E > 65535 || max_rows < 0 || !valid_nk(N, K) || !valid_group(group))
+        return W4A8_ERR_SHAPE;
+    if ((long long)M * K >= (1LL << 31)) return W4A8_ERR_SHAPE;
+    if (M == 0 || N == 0 || max_rows == 0) return W4A8_OK;  // nothing to read or write
+    if (!X || !offsets || !wq || !s_u8 || !a_u8 || !Y) return W4A8_ERR_NULL_PTR;
+    if (out_type == W4A8_OUT_F16 && (!sx || !sw)) return W4A8_ERR_NULL_PTR;
+    if (!aligned16(X) || !aligned16(wq) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
+    if (!aligned4(offsets) || (sx && !aligned4(sx)) || (sw && !aligned4(sw)))
+        return W4A8_ERR_ALIGNMENT;
+    w4a8_status_t d = check_device();
+    if (d != W4A8_OK) return d;
+    const int rows = max_rows < M ? max_rows : M;
+    if (rows >= 64 && N % 256 == 0) {
+        // matrix-core tiles; 256 rows when that still gives a full grid
+        const long long t256 = (long long)E * (N / 256) * ((rows + 255) / 256);
+        const int mt = (rows > 128 && t256 >= 256) ? 256 : 128;
+        return hip_status(w4a8::launch_w4a8_mfma_grouped(X, sx, wq, s_u8, a_u8, sw, Y, out_type,
+                                                         M, N, K, group, offsets, E, rows, mt,
+                                                         stream));
+    }
+    // streamed tiles: the width rule of the dense problem applied to all
+    // experts' tiles together
+    w4a8::StreamCfg c = choose_stream(rows, N * E, K, 0);
+    while (c.nt_per_wave > 1 && (N / 16) % c.nt_per_wave != 0) {
+        c.nt_per_wave = c.nt_per_wave == 7 ? 4 : c.nt_per_wave == 4 ? 2 : 1;
+    }
+    return hip_status(w4a8::launch_w4a8_stream(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
+                                               group, c, stream, offsets, E, rows));
+}
+
 W4A8_EXPORT w4a8_status_t w4a8_gemm_ablation(int variant, const int8_t* X, const float* sx,
                                              const uint8_t* wq, const uint8_t* s_u8,
                                              const uint8_t* a_u8, const float* sw, void* Y,

@@ -217,7 +217,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ s_u8, const uint8_t* __restrict__ a_u8,
     const float* __restrict__ sw, void* __restrict__ Y, int* __restrict__ part, int M, int N,
-    int K, int tiles_n, int tiles_m, int splits) {
+    int K, int tiles_n, int tiles_m, int splits, const int* __restrict__ offsets) {
     constexpr int RB = MT / 32;        // 32-row blocks per wave
     constexpr int CPT = MT / 32;       // 16-byte X chunks per thread per K-step
     constexpr int SLOTS = 8 * RB;      // matrix-core instructions per wave per K-step
@@ -235,7 +235,21 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
 
     const TileCoord tc = tile_coord(blockIdx.x, tiles_m, tiles_n, splits);
     const int ks = tc.ks;
-    const int m0 = tc.tm * MT;
+    // Grouped problems (offsets != nullptr): expert blockIdx.y owns rows
+    // offsets[e] .. offsets[e+1]-1 (clamped to [0, M]) and the e-th weight
+    // slab; its M tiles start at offsets[e].
+    int row_lo = 0, row_hi = M;
+    if (offsets) {
+        const int e = blockIdx.y;
+        row_lo = min(max(offsets[e], 0), M);
+        row_hi = min(max(offsets[e + 1], row_lo), M);
+        wq += (size_t)e * N * (K / 2);
+        s_u8 += (size_t)e * N * (K / GROUP);
+        a_u8 += (size_t)e * N * (K / GROUP);
+        sw += (size_t)e * N;
+    }
+    const int m0 = row_lo + tc.tm * MT;
+    if (m0 >= row_hi) return;  // whole workgroup: no rows of this expert here
     const int n0 = tc.tn * kNT + wave * kColsPerWave;
     const int KTall = K / kTileK;
     const int kt0 = (int)((long long)KTall * ks / splits);
@@ -383,7 +397,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     // per-wave LDS block [32 rows][64 channels]; each row is then written as
     // whole 16-byte pieces (final output, or this split's int32 partial).
     constexpr bool SCALED = (OUT == 0) && !PARTIAL;
-    if (SCALED) sxs[tid % MT] = (m0 + tid % MT < M) ? sx[m0 + tid % MT] : 0.0f;
+    if (SCALED) sxs[tid % MT] = (m0 + tid % MT < row_hi) ? sx[m0 + tid % MT] : 0.0f;
     const float sw0 = SCALED ? sw[n0 + c] : 0.0f;
     const float sw1 = SCALED ? sw[n0 + 32 + c] : 0.0f;
     __syncthreads();
@@ -419,7 +433,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
             const int row = q / PPR, piece = q % PPR;
             const int m = m0 + 32 * rb + row;
             const v4i val = *reinterpret_cast<const v4i*>(stage + row * ROWB + piece * 16);
-            if (m < M)
+            if (m < row_hi)
                 *reinterpret_cast<v4i*>(out + ((size_t)m * N + n0) * EB + piece * 16) = val;
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -471,18 +485,34 @@ MfmaPlan plan_w4a8_mfma(int M, int N, int K) {
 template <int MT, int OUT, bool PARTIAL, class DEC = DecLQQ, bool COARSE = false>
 static void launch_tile(const int8_t* X, const float* sx, const uint8_t* wq, const uint8_t* s_u8,
                         const uint8_t* a_u8, const float* sw, void* Y, int* part, int M, int N,
-                        int K, int group, int splits, hipStream_t st) {
+                        int K, int group, int splits, hipStream_t st,
+                        const int* offsets = nullptr, int E = 1, int max_rows = 0) {
     const int tiles_n = N / kNT;
-    const int tiles_m = (M + MT - 1) / MT;
-    dim3 grid(tiles_n * tiles_m * splits), block(256);
+    const int tiles_m = ((offsets ? max_rows : M) + MT - 1) / MT;
+    dim3 grid(tiles_n * tiles_m * splits, offsets ? E : 1), block(256);
     if (group == 64)
         hipLaunchKernelGGL((w4a8_mfma_kernel<MT, OUT, 64, PARTIAL, DEC, COARSE>), grid, block, 0,
                            st, X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, tiles_n, tiles_m,
-                           splits);
+                           splits, offsets);
     else
         hipLaunchKernelGGL((w4a8_mfma_kernel<MT, OUT, 128, PARTIAL, DEC, COARSE>), grid, block, 0,
                            st, X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, tiles_n, tiles_m,
-                           splits);
+                           splits, offsets);
+}
+
+hipError_t launch_w4a8_mfma_grouped(const int8_t* X, const float* sx, const uint8_t* wq,
+                                    const uint8_t* s_u8, const uint8_t* a_u8, const float* sw,
+                                    void* Y, int out_type, int M, int N, int K, int group,
+                                    const int* offsets, int E, int max_rows, int mt,
+                                    hipStream_t st) {
+    if (mt == 256) {
+        if (out_type == 1) launch_tile<256, 1, false>(X, sx, wq, s_u8, a_u8, sw, Y, nullptr, M, N, K, group, 1, st, offsets, E, max_rows);
+        else launch_tile<256, 0, false>(X, sx, wq, s_u8, a_u8, sw, Y, nullptr, M, N, K, group, 1, st, offsets, E, max_rows);
+    } else {
+        if (out_type == 1) launch_tile<128, 1, false>(X, sx, wq, s_u8, a_u8, sw, Y, nullptr, M, N, K, group, 1, st, offsets, E, max_rows);
+        else launch_tile<128, 0, false>(X, sx, wq, s_u8, a_u8, sw, Y, nullptr, M, N, K, group, 1, st, offsets, E, max_rows);
+    }
+    return hipGetLastError();
 }
 
 hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,

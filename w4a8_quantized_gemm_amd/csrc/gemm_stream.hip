@@ -51,8 +51,25 @@ template <int NTW, int D, int OUT, int GROUP, bool LDSP>
 __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ s_u8, const uint8_t* __restrict__ a_u8,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, int ks) {
+    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, int ks,
+    const int* __restrict__ offsets) {
     extern __shared__ int red[];
+    // Grouped problems (offsets != nullptr): expert blockIdx.z owns rows
+    // offsets[e] .. offsets[e+1]-1 of X and Y and the e-th slab of the
+    // packed weights.  Rows are clamped to [0, M], so bad offsets can only
+    // leave rows unwritten, never move an access out of the buffers.
+    int row_lo = 0, row_hi = M;
+    if (offsets) {
+        const int e = blockIdx.z;
+        row_lo = min(max(offsets[e], 0), M);
+        row_hi = min(max(offsets[e + 1], row_lo), M);
+        wq += (size_t)e * N * (K / 2);
+        s_u8 += (size_t)e * N * (K / GROUP);
+        a_u8 += (size_t)e * N * (K / GROUP);
+        sw += (size_t)e * N;
+    }
+    const int m0 = row_lo + blockIdx.y * 16;
+    if (m0 >= row_hi) return;  // whole workgroup: no rows of this expert here
     // X through LDS pays where X is a large share of the loads (narrow
     // workgroups: 2 KB of X per K-tile against NTW KB of weights).
     constexpr bool kXlds = true;
@@ -69,7 +86,6 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
     const int nwg = gridDim.x, b = blockIdx.x;
     const int g = (nwg & 7) ? b : (b & 7) * (nwg >> 3) + (b >> 3);
     const int nt0 = g * NTW;
-    const int m0 = blockIdx.y * 16;
     const int nk = (KT - wave + ks - 1) / ks;  // K-tiles of this wave (>= 1: ks <= KT)
     // i-th K-tile of this wave (i < nk)
     auto kt_of = [&](int i) { return wave + ks * i; };
@@ -228,7 +244,7 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
         const int t = e >> 8, v = (e >> 6) & 3, l = e & 63;
         const int m = m0 + 4 * (l >> 4) + v;  // accumulator row (X row)
         const int n = (nt0 + t) * kTileN + (l & 15);
-        if (m < M) {
+        if (m < row_hi) {
             if (OUT == 1) {
                 reinterpret_cast<int*>(Y)[(size_t)m * N + n] = sum;
             } else {
@@ -318,8 +334,8 @@ template <int NTW, int D>
 static hipError_t w4a8_stream_ntw(const int8_t* X, const float* sx, const uint8_t* wq,
                                   const uint8_t* s_u8, const uint8_t* a_u8, const float* sw,
                                   void* Y, int out_type, int M, int N, int K, int group, int ks,
-                                  hipStream_t st) {
-    dim3 grid(N / (kTileN * NTW), (M + 15) / 16);
+                                  const int* offsets, int E, int max_rows, hipStream_t st) {
+    dim3 grid(N / (kTileN * NTW), (max_rows + 15) / 16, E);
     dim3 block(64 * ks);
     const int groups = K / group;
     const size_t pbytes = (size_t)2 * stream_param_span<NTW>() * groups * 64;
@@ -330,7 +346,7 @@ static hipError_t w4a8_stream_ntw(const int8_t* X, const float* sx, const uint8_
     const size_t lds = used > rbytes ? used : rbytes;
 #define W4A8_LS(O, G, P)                                                                       \
     hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, O, G, P>), grid, block, lds, st, X, sx, wq, \
-                       s_u8, a_u8, sw, Y, M, N, K, ks)
+                       s_u8, a_u8, sw, Y, M, N, K, ks, offsets)
     if (ldsp) {
         if (out_type == 1) {
             if (group == 64) W4A8_LS(1, 64, true); else W4A8_LS(1, 128, true);
@@ -351,14 +367,23 @@ static hipError_t w4a8_stream_ntw(const int8_t* X, const float* sx, const uint8_
 hipError_t launch_w4a8_stream(const int8_t* X, const float* sx, const uint8_t* wq,
                               const uint8_t* s_u8, const uint8_t* a_u8, const float* sw,
                               void* Y, int out_type, int M, int N, int K, int group,
-                              StreamCfg cfg, hipStream_t st) {
-    switch (cfg.nt_per_wave) {
-        case 7: return w4a8_stream_ntw<7, 2>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
-        case 4: return w4a8_stream_ntw<4, 3>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
-        case 3: return w4a8_stream_ntw<3, 3>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
-        case 2: return w4a8_stream_ntw<2, 4>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
-        default: return w4a8_stream_ntw<1, 3>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, cfg.ks, st);
+                              StreamCfg cfg, hipStream_t st, const int* offsets, int E,
+                              int max_rows) {
+    if (!offsets) {
+        E = 1;
+        max_rows = M;
     }
+#define W4A8_NTW(W, D)                                                                      \
+    return w4a8_stream_ntw<W, D>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group,   \
+                                 cfg.ks, offsets, E, max_rows, st)
+    switch (cfg.nt_per_wave) {
+        case 7: W4A8_NTW(7, 2);
+        case 4: W4A8_NTW(4, 3);
+        case 3: W4A8_NTW(3, 3);
+        case 2: W4A8_NTW(2, 4);
+        default: W4A8_NTW(1, 3);
+    }
+#undef W4A8_NTW
 }
 
 template <int NTW>

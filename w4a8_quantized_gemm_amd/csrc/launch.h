@@ -22,10 +22,21 @@ struct StreamCfg {
     int ks;           // waves per workgroup splitting K (1..16)
 };
 
+// offsets != nullptr: grouped problem of E experts (rows offsets[e] ..
+// offsets[e+1]-1, e-th weight slab), at most max_rows rows per expert.
 hipError_t launch_w4a8_stream(const int8_t* X, const float* sx, const uint8_t* wq,
                               const uint8_t* s_u8, const uint8_t* a_u8, const float* sw,
                               void* Y, int out_type, int M, int N, int K, int group,
-                              StreamCfg cfg, hipStream_t st);
+                              StreamCfg cfg, hipStream_t st, const int* offsets = nullptr,
+                              int E = 1, int max_rows = 0);
+
+// Grouped problem on the matrix-core tile kernel (no K split): expert
+// blockIdx.y, M tiles up to ceil(max_rows / mt).
+hipError_t launch_w4a8_mfma_grouped(const int8_t* X, const float* sx, const uint8_t* wq,
+                                    const uint8_t* s_u8, const uint8_t* a_u8, const float* sw,
+                                    void* Y, int out_type, int M, int N, int K, int group,
+                                    const int* offsets, int E, int max_rows, int mt,
+                                    hipStream_t st);
 
 // Matrix-core tile kernel (N % 256 == 0): workgroup tiles of mt = 128 or
 // 256 rows x 256 channels; with splits > 1 each workgroup covers 1/splits of
