@@ -70,6 +70,9 @@ def _declare(L):
         "orc_int4_sm_codes": ([_P, _I, _P], None),
         "orc_int4_sm_values": ([_P, _I, _P], None),
         "orc_w4fp8_ref": ([_P, _P, _P, _P, _I, _I, _I, _P, _P], None),
+        "orc_w4fp8g_pack": ([_P, _I, _I, _I, _P, _P, _P, _P], None),
+        "orc_w4fp8g_weights": ([_P, _P, _I, _I, _I, _P], None),
+        "orc_w4fp8g_ref": ([_P, _P, _P, _F, _I, _I, _I, _P, _P], None),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -282,6 +285,38 @@ def w4fp8_pack(W):
     q, sw = quant_sym_rows(W, 7)
     codes = int4_sm_codes(q)
     return {"q": q, "sw": sw, "codes": codes, "wq": pack_nibbles(codes)}
+
+
+def w4fp8g_pack(W, group: int):
+    """FP8 variant with per-group scales folded into the FP8 weights
+    (oracle section 11): q, s_g [N][K/g], f [N][K/g], t, the folded e4m3
+    weights w8 [N][K], sign-magnitude codes and the packed nibbles."""
+    W = _c(W, np.float32)
+    N, K = W.shape
+    G = K // group
+    q = np.empty((N, K), np.int8)
+    sg = np.empty((N, G), np.float32)
+    f = np.empty((N, G), np.float32)
+    t = np.empty(1, np.float32)
+    lib().orc_w4fp8g_pack(_p(W), N, K, group, _p(q), _p(sg), _p(f), _p(t))
+    w8 = np.empty((N, K), np.uint8)
+    lib().orc_w4fp8g_weights(_p(q), _p(f), N, K, group, _p(w8))
+    codes = int4_sm_codes(q)
+    return {"q": q, "sg": sg, "f": f, "t": float(t[0]), "w8": w8, "codes": codes,
+            "wq": pack_nibbles(codes)}
+
+
+def w4fp8g_ref(X8, sx, w8, t: float):
+    """(scaled float64 reference [M][N], exact unscaled sums [M][N])."""
+    X8 = _c(X8, np.uint8)
+    sx = _c(sx, np.float32)
+    w8 = _c(w8, np.uint8)
+    M, K = X8.shape
+    N = w8.shape[0]
+    ref = np.empty((M, N), np.float64)
+    pre = np.empty((M, N), np.float64)
+    lib().orc_w4fp8g_ref(_p(X8), _p(sx), _p(w8), float(t), M, N, K, _p(ref), _p(pre))
+    return ref, pre
 
 
 def w4a8_gemm(X8, sx, pk, group: int):

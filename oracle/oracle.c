@@ -413,3 +413,89 @@ ORC_API void orc_w4fp8_ref(const uint8_t* X8, const float* sx, const int8_t* q,
     }
     free(xd);
 }
+
+/* ------------------------------------------------------------------------ *
+ * 11. FP8 variant with per-group scales folded into the FP8 weights and a
+ *     per-tensor rescale against underflow (FireQ, arXiv 2505.20839,
+ *     abstract: INT4 weights, FP8 activations, "per-tensor scaling to
+ *     prevent underflow" of the FP8 weights, finer scaling for the coarse
+ *     INT4 grid).  READING (the abstract fixes no formula), all in float32
+ *     with correctly rounded division and round-half-even:
+ *       per group j of g K-columns of channel n:
+ *         s_g[n][j] = max_k |W[n][k]| / 7   (a zero group gets 1)
+ *         q[n][k]   = clamp(rne(W[n][k] / s_g[n][j]), -7, 7)
+ *       per tensor: t = max |W| / 448       (all-zero W gets 1)
+ *       folded factor f[n][j] = s_g[n][j] / t
+ *       FP8 weight w8[n][k] = sign(q) * e4m3(float(|q| * f[n][j]))
+ *     so W ~= w8 * t, and the largest folded value 7 f is at most 448
+ *     (up to one rounding of f): FP8's range holds every group's grid.
+ * ------------------------------------------------------------------------ */
+ORC_API void orc_w4fp8g_pack(const float* W, int64_t N, int64_t K, int64_t g, int8_t* q,
+                             float* sg, float* f, float* t_out) {
+    const int64_t G = K / g;
+    float wmax = 0.0f;
+    for (int64_t i = 0; i < N * K; ++i) {
+        float a = fabsf(W[i]);
+        if (a > wmax) wmax = a;
+    }
+    float t = wmax / 448.0f;
+    if (!(t > 0.0f)) t = 1.0f;
+    *t_out = t;
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t j = 0; j < G; ++j) {
+            const float* w = W + n * K + j * g;
+            float amax = 0.0f;
+            for (int64_t k = 0; k < g; ++k) {
+                float a = fabsf(w[k]);
+                if (a > amax) amax = a;
+            }
+            float s = amax / 7.0f;
+            if (!(s > 0.0f)) s = 1.0f;
+            sg[n * G + j] = s;
+            f[n * G + j] = s / t;
+            for (int64_t k = 0; k < g; ++k) {
+                float v = rintf(w[k] / s);
+                if (v > 7.0f) v = 7.0f;
+                if (v < -7.0f) v = -7.0f;
+                q[n * K + j * g + k] = (int8_t)v;
+            }
+        }
+    }
+}
+
+/* The folded FP8 weights (e4m3 bytes) of section 11. */
+ORC_API void orc_w4fp8g_weights(const int8_t* q, const float* f, int64_t N, int64_t K,
+                                int64_t g, uint8_t* w8) {
+    const int64_t G = K / g;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t k = 0; k < K; ++k) {
+            const int v = q[n * K + k];
+            const float mag = (float)(v < 0 ? -v : v) * f[n * G + k / g];
+            const uint8_t e = e4m3_encode(mag);
+            w8[n * K + k] = (uint8_t)(v < 0 ? (e | 0x80u) : e);
+        }
+    }
+}
+
+/* Reference of section 11 in double: ref = (sum_k x * w8) * sx[m] * t.  Both
+ * factors are e4m3 values (at most 4 significant bits each), so every
+ * product and the whole sum are exact in double; pre = the unscaled sum. */
+ORC_API void orc_w4fp8g_ref(const uint8_t* X8, const float* sx, const uint8_t* w8, float t,
+                            int64_t M, int64_t N, int64_t K, double* ref, double* pre) {
+    double* xd = (double*)malloc(sizeof(double) * (size_t)(M * K));
+    double* wd = (double*)malloc(sizeof(double) * (size_t)(N * K));
+    for (int64_t i = 0; i < M * K; ++i) xd[i] = e4m3_value(X8[i]);
+    for (int64_t i = 0; i < N * K; ++i) wd[i] = e4m3_value(w8[i]);
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t m = 0; m < M; ++m) {
+        for (int64_t n = 0; n < N; ++n) {
+            double s = 0.0;
+            for (int64_t k = 0; k < K; ++k) s += xd[m * K + k] * wd[n * K + k];
+            if (pre) pre[m * N + n] = s;
+            ref[m * N + n] = s * (double)sx[m] * (double)t;
+        }
+    }
+    free(xd);
+    free(wd);
+}

@@ -471,6 +471,77 @@ def test_widening_definition_points():
     np.testing.assert_array_equal(oracle.round_f16(oracle.widen_f16(h).astype(np.float64)), h)
 
 
+def test_fp8_group_fold_golden(golden_dir):
+    """Hand-worked folded per-group FP8 weights (tests/golden/fp8_group_fold.txt)."""
+    N, K, g = 16, 128, 64
+    W = np.zeros((N, K), np.float32)
+    exp_t, exp_s, exp_q = None, [], []
+    for line in open(os.path.join(golden_dir, "fp8_group_fold.txt")):
+        f = line.split()
+        if not f or f[0].startswith("#"):
+            continue
+        if f[0] == "W":
+            W[int(f[1]), int(f[2])] = float(f[3])
+        elif f[0] == "T":
+            exp_t = float(f[1])
+        elif f[0] == "S":
+            exp_s.append((int(f[1]), int(f[2]), float(f[3]), float(f[4])))
+        elif f[0] == "Q":
+            exp_q.append((int(f[1]), int(f[2]), int(f[3]), int(f[4], 16)))
+    pk = oracle.w4fp8g_pack(W, g)
+    assert pk["t"] == exp_t
+    for r, j, sg, fo in exp_s:
+        assert pk["sg"][r, j] == np.float32(sg) and pk["f"][r, j] == np.float32(fo), (r, j)
+    for r, k, q, w8 in exp_q:
+        assert pk["q"][r, k] == q and pk["w8"][r, k] == w8, (r, k, pk["q"][r, k], hex(pk["w8"][r, k]))
+
+
+def test_fp8_group_fold_exact_case():
+    """Power-of-two group scales with small |q| * f: the folded FP8 weights
+    are exactly q * s_g / t, so the reference equals an exact float64 matmul
+    of the original weights (scaled by sx), independent of e4m3 rounding."""
+    rng = np.random.default_rng(21)
+    N, K, g = 32, 256, 128
+    q = rng.integers(-7, 8, size=(N, K)).astype(np.float64)
+    q[:, ::g] = 7                                           # every group reaches 7
+    e = rng.integers(-9, -3, size=(N, K // g))
+    e[0, 0] = -3                                            # the largest group: 7*2^-3
+    W = (q * np.repeat(2.0 ** e, g, axis=1)).astype(np.float32)
+    pk = oracle.w4fp8g_pack(W, g)
+    np.testing.assert_array_equal(pk["q"], q.astype(np.int8))
+    t = pk["t"]
+    assert t == 7 * 2.0 ** -3 / 448                          # 2^-9, exact
+    w8v = oracle.e4m3_decode(pk["w8"])
+    np.testing.assert_array_equal(w8v * t, W.astype(np.float64))
+    M = 5
+    X8 = rng.integers(0, 256, size=(M, K)).astype(np.uint8)
+    X8[(X8 & 0x7F) == 0x7F] = 0                              # no NaN codes
+    sx = rng.random(M).astype(np.float32)
+    ref, pre = oracle.w4fp8g_ref(X8, sx, pk["w8"], t)
+    exact = oracle.e4m3_decode(X8) @ W.astype(np.float64).T
+    np.testing.assert_array_equal(pre * t, exact)
+
+
+def test_fp8_group_fold_error_bound():
+    """At any size: |w8 t - W| <= s_g / 2 (INT4 rounding) + the e4m3 error of
+    |q| f (relative 2^-4 for normals, absolute 2^-10 for subnormals) times t,
+    and no folded value exceeds 448."""
+    rng = np.random.default_rng(22)
+    N, K, g = 64, 512, 64
+    W = rng.normal(0, 0.02, (N, K)).astype(np.float32)
+    W[3, 64:128] = 0.0
+    pk = oracle.w4fp8g_pack(W, g)
+    t = pk["t"]
+    sg = np.repeat(pk["sg"].astype(np.float64), g, axis=1)
+    f = np.repeat(pk["f"].astype(np.float64), g, axis=1)
+    qf = np.abs(pk["q"].astype(np.float64)) * f
+    assert qf.max() <= 448.0 * (1 + 2.0 ** -22)
+    e4_err = np.maximum(qf * 2.0 ** -4, 2.0 ** -10)
+    err = np.abs(oracle.e4m3_decode(pk["w8"]) * t - W.astype(np.float64))
+    assert np.all(err <= sg / 2 * (1 + 2.0 ** -20) + e4_err * t)
+    assert np.all(pk["w8"][3, 64:128] == 0)
+
+
 def test_generator_deterministic():
     a = wl.gen_weights(64, 128, 7)
     b = wl.gen_weights(64, 128, 7)
