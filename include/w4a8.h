@@ -242,6 +242,40 @@ w4a8_status_t w4fp8_gemm(const uint8_t* X_e4m3, const float* sx,
                          void* workspace, size_t workspace_bytes,
                          hipStream_t stream);
 
+/*
+ * Packing for the folded per-group FP8 format ([FQ] abstract: a per-tensor
+ * scale keeps the FP8 weights from underflowing once the INT4 scaling
+ * factors are folded into them; the formulas are this library's reading):
+ *   t         = max|W| / 448                      (1 for an all-zero W)
+ *   s_g[n][j] = max_{k in group j} |W[n][k]| / 7  (1 for an all-zero group)
+ *   f[n][j]   = s_g[n][j] / t                     (float32 divisions, RNE)
+ *   q[n][k]   = clamp(rne(W[n][k] / s_g[n][k/group]), -7, 7)
+ * W: float32 [N][K]; wq: N*K/2 bytes, sign-magnitude codes in the packed
+ * layout above (as INT4_SYM mode); fsc: float32 [K/group][N], fsc[j][n] =
+ * f[n][j] (group-major, so one K-step's factors of adjacent channels are
+ * adjacent); tscale: one float32, t.  Four kernels on `stream`; fsc is
+ * scratch between them.  N * (K/group) < 2^29.
+ */
+w4a8_status_t w4fp8g_pack(const float* W, int N, int K, int group, uint8_t* wq,
+                          float* fsc, float* tscale, hipStream_t stream);
+
+/*
+ * GEMM on the folded per-group FP8 weights of w4fp8g_pack:
+ *   w8[n][k]  = sign(q) * e4m3_rne(float32(|q[n][k]| * f[n][k/group]))
+ *   acc[m][n] = sum_k e4m3(X[m][k]) * w8[n][k]   (float32 accumulation)
+ *   out_type W4FP8_OUT_BF16: Y = bf16_rne((acc * sx[m]) * t)
+ *   out_type W4FP8_OUT_F32:  Y = (acc * sx[m]) * t as float32
+ * w8 is formed in registers per (channel, group) from a table of the eight
+ * magnitudes; it is never stored.  X, sx: w4fp8_quant_act outputs; fsc,
+ * tscale, wq from w4fp8g_pack with the same N, K, group.  Kernel choice,
+ * splitk and workspace as for w4fp8_gemm.
+ */
+w4a8_status_t w4fp8g_gemm(const uint8_t* X_e4m3, const float* sx,
+                          const uint8_t* wq, const float* fsc,
+                          const float* tscale, void* Y, int out_type, int M,
+                          int N, int K, int group, int splitk, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char* w4a8_status_str(w4a8_status_t status);
 

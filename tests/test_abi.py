@@ -163,6 +163,34 @@ def test_quant_act_ex_validation():
         assert fn(A, -1, 4, 64, A, A, None) == UNSUP
 
 
+def test_fp8_group_fold_validation():
+    def gp(W=A, N=64, K=256, g=128, wq=A, f=A, t=A):
+        return lib.w4fp8g_pack(W, N, K, g, wq, f, t, None)
+    assert gp(g=32) == SHAPE
+    assert gp(K=100) == SHAPE
+    assert gp(N=8) == SHAPE
+    assert gp(N=0) == OK
+    assert gp(f=None) == NULL
+    assert gp(t=None) == NULL
+    assert gp(W=A + 4) == ALIGN
+    assert gp(t=A + 2) == ALIGN
+
+    def gg(M=16, N=256, K=512, g=64, out=0, splitk=0, X=A, f=A, t=A, Y=A, ws=0, wsb=0):
+        return lib.w4fp8g_gemm(X, A, A, f, t, Y, out, M, N, K, g, splitk, ws, wsb, None)
+    assert gg(out=2) == UNSUP
+    assert gg(g=96) == SHAPE
+    assert gg(K=100) == SHAPE
+    assert gg(splitk=3) == SHAPE
+    assert gg(M=0) == OK
+    assert gg(f=None) == NULL
+    assert gg(t=None) == NULL
+    assert gg(Y=A + 4) == ALIGN
+    need = lib.w4a8_workspace_size(128, 256, 8192, 0)
+    assert need > 0
+    assert gg(M=128, K=8192, wsb=need - 1, ws=A) == WS
+    assert gg(M=128, K=8192, wsb=need, ws=0) == NULL
+
+
 def test_valid_call_without_gpu_reports_hip_error():
     """A call that passes validation reaches the HIP runtime; with no GPU
     the device query fails and the status is W4A8_ERR_HIP, not a crash."""

@@ -368,15 +368,21 @@ def _fp8_bound(X8, sx, q, sw):
     scaled by sx sw.  A wrong operand index or a dropped K-chunk is an error
     of whole average products, far above this; exact indexing is pinned
     separately by the integer-valued test."""
+    return _fp8_bound_w(X8, sx, np.abs(q.astype(np.float64)), sw)
+
+
+def _fp8_bound_w(X8, sx, qd, sw):
+    """_fp8_bound for weight magnitudes qd [N][K] (any exact e4m3 values)
+    and a column scale sw [N] (a vector, or the tensor scale broadcast)."""
     xd = np.abs(oracle.e4m3_decode(X8))
-    qd = np.abs(q.astype(np.float64))
     M, K = X8.shape
     absum = xd @ qd.T
     xm = xd.reshape(M, K // 64, 64).max(axis=2)
     qm = qd.reshape(qd.shape[0], K // 64, 64).max(axis=2)
     blk = xm @ qm.T
+    sw = np.broadcast_to(np.asarray(sw, np.float64), (qd.shape[0],))
     return ((K + 2) * 2.0 ** -24 * absum + 2.0 ** -10 * blk) \
-        * np.asarray(sx, np.float64)[:, None] * np.asarray(sw, np.float64)[None, :]
+        * np.asarray(sx, np.float64)[:, None] * sw[None, :]
 
 
 def _check_fp8_outputs(yf, yb_bits, ref, bound):
@@ -460,6 +466,104 @@ def test_fp8_workspace_too_small_is_rejected():
     with pytest.raises(w4.W4A8Error) as ei:
         w4.gemm_fp8(X8, sx, pk, workspace=small)
     assert ei.value.status == 4
+
+
+# ----------------------------- folded per-group FP8 (FireQ-style) ----------
+def _fp8g_weights(N, K, g, seed):
+    """Normal(0, 0.02) weights with one all-zero row and one all-zero group
+    (scale 1, codes 0) and a tiny-valued group (folded weights in the e4m3
+    subnormal range)."""
+    W = wl.gen_weights(N, K, seed)
+    W[3, :] = 0.0
+    W[5, g:2 * g] = 0.0
+    W[7, :g] *= np.float32(1e-4)
+    return W
+
+
+def _fp8g_device(pk_ref, N, K, g):
+    return {"wq": to_dev(pk_ref["wq"]), "fsc": to_dev(np.ascontiguousarray(pk_ref["f"].T)),
+            "tscale": to_dev(np.array([pk_ref["t"]], np.float32)), "N": N, "K": K, "group": g}
+
+
+@pytest.mark.parametrize("N,K,g", [(64, 256, 64), (320, 1024, 128), (256, 1152, 64)])
+def test_fp8g_pack_parity(N, K, g):
+    """Device packing bit-exact: codes, group-major folded factors, t."""
+    say(f"w4fp8g pack N={N} K={K} g={g}")
+    W = _fp8g_weights(N, K, g, 600 + N + K)
+    ref = oracle.w4fp8g_pack(W, g)
+    pk = w4.pack_fp8g(to_dev(W), group=g)
+    np.testing.assert_array_equal(host(pk["wq"]), ref["wq"])
+    np.testing.assert_array_equal(host(pk["fsc"]).view(np.uint32),
+                                  np.ascontiguousarray(ref["f"].T).view(np.uint32))
+    assert host(pk["tscale"]).view(np.uint32)[0] == np.float32(ref["t"]).view(np.uint32)
+
+
+@pytest.mark.parametrize("K,N,g,sk", [(256, 256, 64, 0), (512, 512, 128, 0), (384, 256, 64, 0),
+                                      (256, 192, 128, 0), (512, 256, 64, 1),
+                                      (384, 128, 128, 2)])
+def test_fp8g_folded_weights_exact(K, N, g, sk):
+    """X = identity (M = K rows, e4m3 1.0, sx = 1): output row k, column n is
+    the single product w8[n][k] * 1, so the float32 output must equal
+    float32(w8 * t) bit for bit -- every folded e4m3 weight the kernel forms
+    in registers is checked against the oracle's encoding (tile kernel for
+    N % 256 == 0, streamed kernel otherwise or when splitk forces it)."""
+    say(f"w4fp8g folded weights K={K} N={N} g={g} splitk={sk}")
+    W = _fp8g_weights(N, K, g, 700 + K + N)
+    ref = oracle.w4fp8g_pack(W, g)
+    X8 = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(X8, 0x38)
+    sx = np.ones(K, np.float32)
+    want = (oracle.e4m3_decode(ref["w8"]).T.astype(np.float32) * np.float32(ref["t"]))
+    Y = poison((K, N), torch.float32)
+    w4.gemm_fp8g(to_dev(X8), to_dev(sx), _fp8g_device(ref, N, K, g), out_type=w4.OUT_F32,
+                 splitk=sk, out=Y)
+    np.testing.assert_array_equal(host(Y).view(np.uint32), want.astype(np.float32).view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K,g", [(1, 256, 1024, 128), (16, 512, 2048, 64),
+                                     (37, 128, 640, 128), (64, 256, 640, 64),
+                                     (300, 512, 1152, 128), (513, 256, 2048, 64),
+                                     (128, 256, 4096, 128), (100, 512, 2048, 64),
+                                     (1024, 1024, 256, 128)])
+def test_fp8g_gemm_parity(M, N, K, g):
+    """Realistic weights and activations against the oracle's double result:
+    elementwise inside the FP8 bound (with |w8| in place of |q| and t as the
+    column scale), relative Frobenius <= 1e-3; both output types; the
+    streamed kernel forced by splitk meets the same bound.  Covers streamed
+    and tile kernels, ragged M, odd K-step counts and planned split-K."""
+    say(f"w4fp8g gemm M={M} N={N} K={K} g={g} workspace={w4.workspace_size(M, N, K)}")
+    W = _fp8g_weights(N, K, g, 800 + M + N)
+    X = wl.gen_activations(M, K, 801 + M, 802)
+    ref_pk = oracle.w4fp8g_pack(W, g)
+    X8, sx = oracle.quant_rows_e4m3(X)
+    ref, _ = oracle.w4fp8g_ref(X8, sx, ref_pk["w8"], ref_pk["t"])
+    bound = _fp8_bound_w(X8, sx, np.abs(oracle.e4m3_decode(ref_pk["w8"])), ref_pk["t"])
+    pk = _fp8g_device(ref_pk, N, K, g)
+    Yf = poison((M, N), torch.float32)
+    w4.gemm_fp8g(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F32, out=Yf)
+    Yb = poison((M, N), torch.bfloat16)
+    w4.gemm_fp8g(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_BF16, out=Yb)
+    yf = host(Yf)
+    say(f"  f32 rel fro {rel_fro(yf, ref):.3e}; max |err|/bound "
+        f"{np.max(np.abs(yf - ref) / (bound + 1e-30)):.3f}")
+    _check_fp8_outputs(yf, bf16_bits_of(Yb), ref, bound)
+    Ys = poison((M, N), torch.float32)
+    w4.gemm_fp8g(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F32, splitk=1, out=Ys)
+    assert np.all(np.abs(host(Ys) - ref) <= bound + 1e-30)
+
+
+def test_fp8g_end_to_end_device_pack():
+    """Device pack then device GEMM equals oracle pack then device GEMM bit
+    for bit (the packed inputs are identical, so the outputs must be)."""
+    M, N, K, g = 200, 512, 1024, 128
+    W = _fp8g_weights(N, K, g, 901)
+    X = wl.gen_activations(M, K, 902, 903)
+    X8, sx = oracle.quant_rows_e4m3(X)
+    ref_pk = oracle.w4fp8g_pack(W, g)
+    a = w4.gemm_fp8g(to_dev(X8), to_dev(sx), w4.pack_fp8g(to_dev(W), group=g),
+                     out_type=w4.OUT_F32)
+    b = w4.gemm_fp8g(to_dev(X8), to_dev(sx), _fp8g_device(ref_pk, N, K, g), out_type=w4.OUT_F32)
+    np.testing.assert_array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
 
 
 # ------------------------------------------- Llama-shaped workloads --------

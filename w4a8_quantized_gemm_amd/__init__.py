@@ -42,7 +42,8 @@ LAYOUT_VERSION = 1
 
 EXPORTS = ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act",
            "w4a8_quant_act_ex", "w4fp8_quant_act_ex", "w4a8_workspace_size", "w4a8_gemm",
-           "w4a8_gemm_ablation", "w4a8_gemm_grouped", "w4fp8_gemm",
+           "w4a8_gemm_ablation", "w4a8_gemm_grouped", "w4fp8_gemm", "w4fp8g_pack",
+           "w4fp8g_gemm",
            "w4a8_status_str", "w4a8_last_hip_error", "w4a8_layout_version")
 
 _P, _I, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -57,13 +58,15 @@ lib.w4a8_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P
 lib.w4fp8_gemm.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]
 lib.w4a8_gemm_ablation.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
 lib.w4a8_gemm_grouped.argtypes = [_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
+lib.w4fp8g_pack.argtypes = [_P, _I, _I, _I, _P, _P, _P, _P]
+lib.w4fp8g_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]
 lib.w4a8_status_str.argtypes = [_I]
 lib.w4a8_status_str.restype = ctypes.c_char_p
 lib.w4a8_last_hip_error.restype = _I
 lib.w4a8_layout_version.restype = _I
 for _n in ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act", "w4a8_quant_act_ex",
            "w4fp8_quant_act_ex", "w4a8_gemm", "w4a8_gemm_ablation", "w4a8_gemm_grouped",
-           "w4fp8_gemm"):
+           "w4fp8_gemm", "w4fp8g_pack", "w4fp8g_gemm"):
     getattr(lib, _n).restype = _I
 
 assert lib.w4a8_layout_version() == LAYOUT_VERSION
@@ -284,4 +287,46 @@ def gemm_fp8(Xq, sx, packed, out_type: int = OUT_BF16, splitk: int = 0, out=None
     _check(lib.w4fp8_gemm(_ptr(Xq), _ptr(sx), _ptr(packed["wq"]), _ptr(packed["sw"]),
                           _ptr(Y), out_type, M, N, K, splitk, _ptr(workspace), ws_bytes,
                           _stream(stream)), "w4fp8_gemm")
+    return Y
+
+
+def pack_fp8g(W, group: int = 128, stream=None):
+    """w4fp8g_pack: INT4 codes with per-group scales folded into FP8.
+
+    Returns a dict with wq (uint8 [N*K/2]), fsc (float32 [K/group][N],
+    group-major folded factors) and tscale (float32 [1])."""
+    torch = _torch()
+    _need(W, torch.float32, "W")
+    N, K = W.shape
+    dev = W.device
+    wq = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+    fsc = torch.empty((K // group, N), dtype=torch.float32, device=dev)
+    tscale = torch.empty(1, dtype=torch.float32, device=dev)
+    _check(lib.w4fp8g_pack(_ptr(W), N, K, group, _ptr(wq), _ptr(fsc), _ptr(tscale),
+                           _stream(stream)), "w4fp8g_pack")
+    return {"wq": wq, "fsc": fsc, "tscale": tscale, "N": N, "K": K, "group": group}
+
+
+def gemm_fp8g(Xq, sx, packed, out_type: int = OUT_BF16, splitk: int = 0, out=None,
+              workspace=None, stream=None):
+    """w4fp8g_gemm on pack_fp8g output: Y [M][N] bfloat16 or float32."""
+    torch = _torch()
+    _need(Xq, torch.uint8, "Xq")
+    _need(sx, torch.float32, "sx")
+    M, K = Xq.shape
+    N = packed["N"]
+    if packed["K"] != K:
+        raise ValueError("K of X and of the packed weights differ")
+    ydt = torch.bfloat16 if out_type == OUT_BF16 else torch.float32
+    Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
+    _need(Y, ydt, "out")
+    if workspace is None:
+        need = workspace_size(M, N, K, splitk)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=Xq.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.w4fp8g_gemm(_ptr(Xq), _ptr(sx), _ptr(packed["wq"]), _ptr(packed["fsc"]),
+                           _ptr(packed["tscale"]), _ptr(Y), out_type, M, N, K,
+                           packed["group"], splitk, _ptr(workspace), ws_bytes,
+                           _stream(stream)), "w4fp8g_gemm")
     return Y

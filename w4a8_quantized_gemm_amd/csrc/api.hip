@@ -284,3 +284,44 @@ W4A8_EXPORT w4a8_status_t w4fp8_gemm(const uint8_t* X_e4m3, const float* sx, con
     return hip_status(w4a8::launch_w4fp8_stream(X_e4m3, sx, wq, sw, Y, out_type, M, N, K,
                                                 choose_stream(M, N, K, splitk), stream));
 }
+
+W4A8_EXPORT w4a8_status_t w4fp8g_pack(const float* W, int N, int K, int group, uint8_t* wq,
+                                      float* fsc, float* tscale, hipStream_t stream) {
+    if (!valid_nk(N, K) || !valid_group(group)) return W4A8_ERR_SHAPE;
+    if ((long long)N * (K / group) >= (1LL << 29)) return W4A8_ERR_SHAPE;
+    if (N == 0) return W4A8_OK;  // nothing to read or write
+    if (!W || !wq || !fsc || !tscale) return W4A8_ERR_NULL_PTR;
+    if (!aligned16(W) || !aligned16(wq) || !aligned4(fsc) || !aligned4(tscale))
+        return W4A8_ERR_ALIGNMENT;
+    w4a8_status_t d = check_device();
+    if (d != W4A8_OK) return d;
+    return hip_status(w4a8::launch_pack_fp8g(W, N, K, group, wq, fsc, tscale, stream));
+}
+
+W4A8_EXPORT w4a8_status_t w4fp8g_gemm(const uint8_t* X_e4m3, const float* sx, const uint8_t* wq,
+                                      const float* fsc, const float* tscale, void* Y,
+                                      int out_type, int M, int N, int K, int group, int splitk,
+                                      void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream) {
+    if (out_type != W4FP8_OUT_BF16 && out_type != W4FP8_OUT_F32) return W4A8_ERR_UNSUPPORTED;
+    if (M < 0 || !valid_nk(N, K) || !valid_group(group) || !valid_splitk(splitk, K))
+        return W4A8_ERR_SHAPE;
+    if ((long long)N * (K / group) >= (1LL << 29)) return W4A8_ERR_SHAPE;
+    if (M == 0 || N == 0) return W4A8_OK;  // nothing to read or write
+    if (!X_e4m3 || !sx || !wq || !fsc || !tscale || !Y) return W4A8_ERR_NULL_PTR;
+    if (!aligned16(X_e4m3) || !aligned16(wq) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
+    if (!aligned4(sx) || !aligned4(fsc) || !aligned4(tscale)) return W4A8_ERR_ALIGNMENT;
+    const size_t need = w4a8_workspace_size(M, N, K, splitk);
+    if (workspace_bytes < need) return W4A8_ERR_WORKSPACE;
+    if (need > 0 && !workspace) return W4A8_ERR_NULL_PTR;
+    if (need > 0 && !aligned16(workspace)) return W4A8_ERR_ALIGNMENT;
+    w4a8_status_t d = check_device();
+    if (d != W4A8_OK) return d;
+    if (splitk == 0 && use_mfma_tiles(M, N, K))
+        return hip_status(w4a8::launch_w4fp8g_mfma(X_e4m3, sx, wq, fsc, tscale, Y, out_type, M, N,
+                                                   K, group, w4a8::plan_w4a8_mfma(M, N, K),
+                                                   workspace, stream));
+    return hip_status(w4a8::launch_w4fp8g_stream(X_e4m3, sx, wq, fsc, tscale, Y, out_type, M, N,
+                                                 K, group, choose_stream(M, N, K, splitk),
+                                                 stream));
+}

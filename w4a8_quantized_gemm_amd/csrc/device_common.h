@@ -71,18 +71,32 @@ __device__ __forceinline__ void lqq_dequant8(unsigned w, u16x2 s2, u16x2 a4,
 constexpr unsigned kE4m3LutLo = 0x44403800u;  // bytes for 3,2,1,0
 constexpr unsigned kE4m3LutHi = 0x4E4C4A48u;  // bytes for 7,6,5,4
 
-__device__ __forceinline__ unsigned int4_to_e4m3_lo(unsigned w) {
+__device__ __forceinline__ unsigned int4_to_e4m3_lo(unsigned w, unsigned lut_lo = kE4m3LutLo,
+                                                    unsigned lut_hi = kE4m3LutHi) {
     // low nibbles: magnitude bits 0..2, sign bit 3 -> e4m3 sign bit 7
     unsigned mag = w & 0x07070707u;
-    unsigned e = __builtin_amdgcn_perm(kE4m3LutHi, kE4m3LutLo, mag);
+    unsigned e = __builtin_amdgcn_perm(lut_hi, lut_lo, mag);
     return e | ((w << 4) & 0x80808080u);
 }
 
-__device__ __forceinline__ unsigned int4_to_e4m3_hi(unsigned w) {
+__device__ __forceinline__ unsigned int4_to_e4m3_hi(unsigned w, unsigned lut_lo = kE4m3LutLo,
+                                                    unsigned lut_hi = kE4m3LutHi) {
     // high nibbles: magnitude bits 4..6, sign bit 7 is already in place
     unsigned mag = (w >> 4) & 0x07070707u;
-    unsigned e = __builtin_amdgcn_perm(kE4m3LutHi, kE4m3LutLo, mag);
+    unsigned e = __builtin_amdgcn_perm(lut_hi, lut_lo, mag);
     return e | (w & 0x80808080u);
+}
+
+// Table words of e4m3(|q| f) for |q| = 0..7 (entry 0 is +0) in the layout
+// above, by the hardware conversion (nearest even; for the products used,
+// which stay below 464, it agrees with OCP e4m3).
+__device__ __forceinline__ void e4m3_fold_table(float f, unsigned& lo, unsigned& hi) {
+    const float f2 = 2.0f * f, f3 = 3.0f * f, f4 = 4.0f * f;
+    const float f5 = 5.0f * f, f6 = 6.0f * f, f7 = 7.0f * f;
+    const int l = __builtin_amdgcn_cvt_pk_fp8_f32(0.0f, f, 0, false);
+    lo = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(f2, f3, l, true);
+    const int u = __builtin_amdgcn_cvt_pk_fp8_f32(f4, f5, 0, false);
+    hi = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(f6, f7, u, true);
 }
 
 // float -> IEEE binary16 bits, nearest-even (hardware conversion).

@@ -19,6 +19,14 @@
 // VALU instructions: magnitude mask, byte permute through the 8-entry e4m3
 // table, sign moved to bit 7 -- for the low nibbles (sign at bit 3) and the
 // high nibbles (sign already at bit 7).
+//
+// GROUP = 64 or 128 selects the folded per-group format (per-group scale
+// folded into the FP8 weights, per-tensor rescale; FireQ abstract): the
+// table then holds e4m3(|q| f) for the lane's channel and group, rebuilt
+// every K-step from the folded factor f (six multiplies and four packed
+// conversions per 32-channel block), and the epilogue scales by the tensor
+// scale t instead of sw[n].  One K-step of a lane lies in one group for
+// both group sizes (lane half h selects the 64-column group).
 #include "launch.h"
 #include "mfma_common.h"
 
@@ -37,9 +45,10 @@ struct F8Step {
 };
 
 // e4m3 magnitudes of 0..7 as two byte tables for v_perm_b32 (bytes 0..3 in
-// `lo`, 4..7 in `hi`); kept in registers (one VOP3 reads one scalar only).
+// `lo`, 4..7 in `hi`), one table per 32-channel block cb; kept in registers
+// (one VOP3 reads one scalar only).
 struct F8Lut {
-    unsigned lo, hi, sgn;
+    unsigned lo[2], hi[2];
 };
 
 struct F8Tmp {
@@ -54,13 +63,15 @@ struct F8Tmp {
 //   B[2d+1] = (w & 0x80808080) | e                      (high nibbles)
 template <int J, int OP>
 __device__ __forceinline__ void f8_step(F8Tmp& t, const F8Step& w, const F8Lut& lut,
-                                        v8i (&B)[2][2]) {
+                                        unsigned sgn, v8i (&B)[2][2]) {
     constexpr int cb = OP / 32, q = OP % 32, d = q / 8, st = q % 8;
     const unsigned wd = (unsigned)w.w[cb][J][d];
     if constexpr (st == 0) {
         asm volatile("v_and_b32 %0, 0x07070707, %1" : "=v"(t.m) : "v"(wd));
     } else if constexpr (st == 1) {
-        asm volatile("v_perm_b32 %0, %1, %2, %3" : "=v"(t.e) : "v"(lut.hi), "v"(lut.lo), "v"(t.m));
+        asm volatile("v_perm_b32 %0, %1, %2, %3"
+                     : "=v"(t.e)
+                     : "v"(lut.hi[cb]), "v"(lut.lo[cb]), "v"(t.m));
     } else if constexpr (st == 2) {
         asm volatile("v_and_b32 %0, 0x08080808, %1" : "=v"(t.s) : "v"(wd));
     } else if constexpr (st == 3) {
@@ -72,27 +83,32 @@ __device__ __forceinline__ void f8_step(F8Tmp& t, const F8Step& w, const F8Lut& 
     } else if constexpr (st == 5) {
         asm volatile("v_and_b32 %0, 0x07070707, %1" : "=v"(t.m) : "v"(t.m));
     } else if constexpr (st == 6) {
-        asm volatile("v_perm_b32 %0, %1, %2, %3" : "=v"(t.e) : "v"(lut.hi), "v"(lut.lo), "v"(t.m));
+        asm volatile("v_perm_b32 %0, %1, %2, %3"
+                     : "=v"(t.e)
+                     : "v"(lut.hi[cb]), "v"(lut.lo[cb]), "v"(t.m));
     } else {
         unsigned x;
-        asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(x) : "v"(wd), "v"(lut.sgn), "v"(t.e));
+        asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(x) : "v"(wd), "v"(sgn), "v"(t.e));
         B[cb][J][2 * d + 1] = (int)x;
     }
 }
 
 template <int J>
-__device__ __forceinline__ void f8_all(const F8Step& w, const F8Lut& lut, v8i (&B)[2][2]) {
+__device__ __forceinline__ void f8_all(const F8Step& w, const F8Lut& lut, unsigned sgn,
+                                       v8i (&B)[2][2]) {
     F8Tmp t;
-    static_for<64>([&](auto oc) { f8_step<J, decltype(oc)::value>(t, w, lut, B); });
+    static_for<64>([&](auto oc) { f8_step<J, decltype(oc)::value>(t, w, lut, sgn, B); });
 }
 
 }  // namespace
 
-template <int MT, int OUT, bool PARTIAL>
+template <int MT, int OUT, bool PARTIAL, int GROUP>
 __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
-    const float* __restrict__ sw, void* __restrict__ Y, float* __restrict__ part, int M, int N,
-    int K, int tiles_n, int tiles_m, int splits) {
+    const float* __restrict__ sw, const float* __restrict__ fsc, const float* __restrict__ tsc,
+    void* __restrict__ Y, float* __restrict__ part, int M, int N, int K, int tiles_n,
+    int tiles_m, int splits) {
+    constexpr bool FOLD = GROUP != 0;
     constexpr int RB = MT / 32;        // 32-row blocks per wave
     constexpr int CPT = MT / 32;       // 16-byte X chunks per thread per K-step
     constexpr int SLOTS = 4 * RB;      // matrix-core instructions per wave per K-step
@@ -151,10 +167,27 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
         const unsigned so = live ? (unsigned)(kt * kTileK) : 0u;
         return buf_load16(xr_rsrc, vo, so);
     };
-    F8Lut lut;
-    lut.lo = 0x44403800u;  // e4m3 of 3, 2, 1, 0
-    lut.hi = 0x4E4C4A48u;  // e4m3 of 7, 6, 5, 4
-    lut.sgn = 0x80808080u;
+    // Folded factors, group-major fsc[g][N]: K-step ktg of channel n lies in
+    // group ktg * (128 / GROUP) + (GROUP == 64 ? h : 0).
+    constexpr int GPS = FOLD ? 128 / GROUP : 1;  // groups per K-step
+    const __amdgpu_buffer_rsrc_t f_rsrc =
+        buf_rsrc(fsc, FOLD ? (unsigned)((size_t)KTall * GPS * N * 4) : 0u);
+    const unsigned fvoff = (unsigned)(n0 + c) * 4u + (GROUP == 64 ? (unsigned)h * N * 4u : 0u);
+    auto f_load = [&](int kt, float (&fv)[2]) {
+        const unsigned so = (unsigned)((kt0 + kt) * GPS) * (unsigned)N * 4u;
+        fv[0] = __builtin_bit_cast(float, buf_load4(f_rsrc, fvoff, so));
+        fv[1] = __builtin_bit_cast(float, buf_load4(f_rsrc, fvoff + 128u, so));
+    };
+    const unsigned sgn = 0x80808080u;
+    F8Lut le, lo;  // tables of even / odd K-steps
+    float fe[2] = {0.f, 0.f}, fo[2] = {0.f, 0.f};
+    if constexpr (!FOLD) {
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            le.lo[cb] = lo.lo[cb] = 0x44403800u;  // e4m3 of 3, 2, 1, 0
+            le.hi[cb] = lo.hi[cb] = 0x4E4C4A48u;  // e4m3 of 7, 6, 5, 4
+        }
+    }
 
     v16f acc[RB][2];
 #pragma unroll
@@ -169,7 +202,13 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
     F8Step we, wo;         // raw weights for even / odd steps
     v8i B[2][2];
     v8i ring[4];
-    const int k1 = min(1, KTe - 1);
+    // X of the padding step reads as zero; its weights (and factors) are
+    // those of the last real step, so no load leaves this split's K range.
+    const int k1 = min(1, KTe - 1), kw1 = min(1, KT - 1);
+    if constexpr (FOLD) {
+        f_load(0, fe);
+        f_load(kw1, fo);
+    }
 #pragma unroll
     for (int p = 0; p < CPT; ++p) xe[p] = x_load(0, p);
 #pragma unroll
@@ -177,10 +216,14 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
 #pragma unroll
     for (int pi = 0; pi < 4; ++pi) w_load(0, pi, we);
 #pragma unroll
-    for (int pi = 0; pi < 4; ++pi) w_load(k1, pi, wo);
+    for (int pi = 0; pi < 4; ++pi) w_load(kw1, pi, wo);
 #pragma unroll
     for (int p = 0; p < CPT; ++p) *reinterpret_cast<v4i*>(xs0 + xlds0 + p * 4096) = xe[p];
-    f8_all<0>(we, lut, B);
+    if constexpr (FOLD) {
+        e4m3_fold_table(fe[0], le.lo[0], le.hi[0]);
+        e4m3_fold_table(fe[1], le.lo[1], le.hi[1]);
+    }
+    f8_all<0>(we, le, sgn, B);
     __syncthreads();
     auto read_a = [&](const uint8_t* buf, int sI) {  // sI = RB*j + rb
         const int j = sI / RB, rb = sI % RB;
@@ -200,9 +243,13 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
     //   group 1 slots      W(kt+2) -> wcur; B[*][0] of step kt+1 from wnx
     //   last 4+CPT slots   X(kt+1) -> LDS `nxt` (before the last 4)
     //   before the last 4  barrier, then step kt+1's first two A reads.
+    // Folded format: `lcur` = table of step kt (group 0), `lnx` = table of
+    // step kt+1 (group 1), built from `fnx` in the last two group-0 slots;
+    // f(kt+2) -> `fcur` at slot 0.
     auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, v4i (&xcur)[CPT],
-                    v4i (&xnx)[CPT], F8Step& wcur, F8Step& wnx) {
-        const int k2 = min(kt + 2, KTe - 1);
+                    v4i (&xnx)[CPT], F8Step& wcur, F8Step& wnx, F8Lut& lcur, F8Lut& lnx,
+                    float (&fcur)[2], float (&fnx)[2]) {
+        const int k2 = min(kt + 2, KTe - 1), kw2 = min(kt + 2, KT - 1);
         F8Tmp tmp;
         static_for<SLOTS>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
@@ -214,25 +261,28 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
                 ring[1] = read_a(nxt, 1);
             }
             mfma32_f8_acc(acc[rb][cb], ring[sI % 4], B[cb][j]);
+            if constexpr (FOLD && s == 0) f_load(kw2, fcur);
+            if constexpr (FOLD && (s == GS - 2 || s == GS - 1))
+                e4m3_fold_table(fnx[s - (GS - 2)], lnx.lo[s - (GS - 2)], lnx.hi[s - (GS - 2)]);
             if constexpr (cb == 1 && sI + 2 < 2 * RB) ring[(sI + 2) % 4] = read_a(cur, sI + 2);
             if constexpr (s < CPT) xcur[s] = x_load(k2, s);
-            if constexpr (s >= GS && s < GS + 4) w_load(k2, s - GS, wcur);
+            if constexpr (s >= GS && s < GS + 4) w_load(kw2, s - GS, wcur);
             if constexpr (s >= SLOTS - 4 - CPT && s < SLOTS - 4)
                 *reinterpret_cast<v4i*>(nxt + xlds0 + (s - (SLOTS - 4 - CPT)) * 4096) =
                     xnx[s - (SLOTS - 4 - CPT)];
             static_for<DQ>([&](auto dc) {
                 constexpr int o = DQ * sg + decltype(dc)::value;
                 if constexpr (o < 64) {
-                    if constexpr (g == 0) f8_step<1, o>(tmp, wcur, lut, B);
-                    else f8_step<0, o>(tmp, wnx, lut, B);
+                    if constexpr (g == 0) f8_step<1, o>(tmp, wcur, lcur, sgn, B);
+                    else f8_step<0, o>(tmp, wnx, lnx, sgn, B);
                 }
             });
         });
     };
 
     for (int kt = 0; kt < KTe; kt += 2) {
-        step(kt, xs0, xs1, xe, xo, we, wo);
-        step(kt + 1, xs1, xs0, xo, xe, wo, we);
+        step(kt, xs0, xs1, xe, xo, we, wo, le, lo, fe, fo);
+        step(kt + 1, xs1, xs0, xo, xe, wo, we, lo, le, fo, fe);
     }
     mfma32_drain(acc);
     __syncthreads();  // all waves done with the X buffers
@@ -244,8 +294,9 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
     constexpr bool SCALED = !PARTIAL;
     constexpr bool BF16 = (OUT == 0) && !PARTIAL;
     if (SCALED) sxs[tid % MT] = (m0 + tid % MT < M) ? sx[m0 + tid % MT] : 0.0f;
-    const float sw0 = SCALED ? sw[n0 + c] : 0.0f;
-    const float sw1 = SCALED ? sw[n0 + 32 + c] : 0.0f;
+    const float tval = (SCALED && FOLD) ? tsc[0] : 0.0f;
+    const float sw0 = SCALED ? (FOLD ? tval : sw[n0 + c]) : 0.0f;
+    const float sw1 = SCALED ? (FOLD ? tval : sw[n0 + 32 + c]) : 0.0f;
     __syncthreads();
     constexpr int EB = BF16 ? 2 : 4;          // output element bytes
     constexpr int ROWB = 64 * EB;             // bytes per staged row
@@ -288,12 +339,12 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
 }
 
 // Sum of the split-K float32 partial tiles in split order, then the
-// per-token x per-channel scale to bf16 or float32.  Each thread handles four
-// consecutive channels of one row.
+// per-token x per-channel scale (or, with `tsc`, the per-tensor scale) to
+// bf16 or float32.  Each thread handles four consecutive channels of one row.
 template <int OUT>
 __global__ __launch_bounds__(256) void splitk_reduce_f32_kernel(
     const float* __restrict__ part, int splits, int M, int N, const float* __restrict__ sx,
-    const float* __restrict__ sw, void* __restrict__ Y) {
+    const float* __restrict__ sw, const float* __restrict__ tsc, void* __restrict__ Y) {
     const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
     const size_t MN = (size_t)M * N;
     if (q * 4 >= MN) return;
@@ -304,7 +355,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_f32_kernel(
     const float sm = sx[m];
     float y[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) y[j] = (acc[j] * sm) * sw[n + j];
+    for (int j = 0; j < 4; ++j) y[j] = (acc[j] * sm) * (tsc ? tsc[0] : sw[n + j]);
     if (OUT == 1) {
         *reinterpret_cast<v4f*>(reinterpret_cast<float*>(Y) + e) = v4f{y[0], y[1], y[2], y[3]};
     } else {
@@ -315,44 +366,65 @@ __global__ __launch_bounds__(256) void splitk_reduce_f32_kernel(
     }
 }
 
-template <int MT, int OUT, bool PARTIAL>
+template <int MT, int OUT, bool PARTIAL, int GROUP>
 static void launch_fp8_tile(const uint8_t* X, const float* sx, const uint8_t* wq, const float* sw,
-                            void* Y, float* part, int M, int N, int K, int splits,
-                            hipStream_t st) {
+                            const float* fsc, const float* tsc, void* Y, float* part, int M,
+                            int N, int K, int splits, hipStream_t st) {
     const int tiles_n = N / kNT;
     const int tiles_m = (M + MT - 1) / MT;
     dim3 grid(tiles_n * tiles_m * splits), block(256);
-    hipLaunchKernelGGL((w4fp8_mfma_kernel<MT, OUT, PARTIAL>), grid, block, 0, st, X, sx, wq, sw,
-                       Y, part, M, N, K, tiles_n, tiles_m, splits);
+    hipLaunchKernelGGL((w4fp8_mfma_kernel<MT, OUT, PARTIAL, GROUP>), grid, block, 0, st, X, sx,
+                       wq, sw, fsc, tsc, Y, part, M, N, K, tiles_n, tiles_m, splits);
+}
+
+template <int GROUP>
+static hipError_t w4fp8_mfma_group(const uint8_t* X, const float* sx, const uint8_t* wq,
+                                   const float* sw, const float* fsc, const float* tsc, void* Y,
+                                   int out_type, int M, int N, int K, const MfmaPlan& plan,
+                                   void* workspace, hipStream_t st) {
+    float* part = reinterpret_cast<float*>(workspace);
+#define FP8_TILE(MT_, O_, P_, S_) \
+    launch_fp8_tile<MT_, O_, P_, GROUP>(X, sx, wq, sw, fsc, tsc, Y, part, M, N, K, S_, st)
+    if (plan.splits == 1) {
+        if (plan.mt == 256) {
+            if (out_type == 1) FP8_TILE(256, 1, false, 1);
+            else FP8_TILE(256, 0, false, 1);
+        } else {
+            if (out_type == 1) FP8_TILE(128, 1, false, 1);
+            else FP8_TILE(128, 0, false, 1);
+        }
+        return hipGetLastError();
+    }
+    if (plan.mt == 256) FP8_TILE(256, 1, true, plan.splits);
+    else FP8_TILE(128, 1, true, plan.splits);
+#undef FP8_TILE
+    const size_t quads = ((size_t)M * N) / 4;
+    const unsigned blocks = (unsigned)((quads + 255) / 256);
+    if (out_type == 1)
+        hipLaunchKernelGGL((splitk_reduce_f32_kernel<1>), dim3(blocks), dim3(256), 0, st, part,
+                           plan.splits, M, N, sx, sw, tsc, Y);
+    else
+        hipLaunchKernelGGL((splitk_reduce_f32_kernel<0>), dim3(blocks), dim3(256), 0, st, part,
+                           plan.splits, M, N, sx, sw, tsc, Y);
+    return hipGetLastError();
 }
 
 hipError_t launch_w4fp8_mfma(const uint8_t* X, const float* sx, const uint8_t* wq,
                              const float* sw, void* Y, int out_type, int M, int N, int K,
                              const MfmaPlan& plan, void* workspace, hipStream_t st) {
-    float* part = reinterpret_cast<float*>(workspace);
-    if (plan.splits == 1) {
-        if (plan.mt == 256) {
-            if (out_type == 1) launch_fp8_tile<256, 1, false>(X, sx, wq, sw, Y, part, M, N, K, 1, st);
-            else launch_fp8_tile<256, 0, false>(X, sx, wq, sw, Y, part, M, N, K, 1, st);
-        } else {
-            if (out_type == 1) launch_fp8_tile<128, 1, false>(X, sx, wq, sw, Y, part, M, N, K, 1, st);
-            else launch_fp8_tile<128, 0, false>(X, sx, wq, sw, Y, part, M, N, K, 1, st);
-        }
-        return hipGetLastError();
-    }
-    if (plan.mt == 256)
-        launch_fp8_tile<256, 1, true>(X, sx, wq, sw, Y, part, M, N, K, plan.splits, st);
-    else
-        launch_fp8_tile<128, 1, true>(X, sx, wq, sw, Y, part, M, N, K, plan.splits, st);
-    const size_t quads = ((size_t)M * N) / 4;
-    const unsigned blocks = (unsigned)((quads + 255) / 256);
-    if (out_type == 1)
-        hipLaunchKernelGGL((splitk_reduce_f32_kernel<1>), dim3(blocks), dim3(256), 0, st, part,
-                           plan.splits, M, N, sx, sw, Y);
-    else
-        hipLaunchKernelGGL((splitk_reduce_f32_kernel<0>), dim3(blocks), dim3(256), 0, st, part,
-                           plan.splits, M, N, sx, sw, Y);
-    return hipGetLastError();
+    return w4fp8_mfma_group<0>(X, sx, wq, sw, nullptr, nullptr, Y, out_type, M, N, K, plan,
+                               workspace, st);
+}
+
+hipError_t launch_w4fp8g_mfma(const uint8_t* X, const float* sx, const uint8_t* wq,
+                              const float* fsc, const float* tsc, void* Y, int out_type, int M,
+                              int N, int K, int group, const MfmaPlan& plan, void* workspace,
+                              hipStream_t st) {
+    if (group == 64)
+        return w4fp8_mfma_group<64>(X, sx, wq, nullptr, fsc, tsc, Y, out_type, M, N, K, plan,
+                                    workspace, st);
+    return w4fp8_mfma_group<128>(X, sx, wq, nullptr, fsc, tsc, Y, out_type, M, N, K, plan,
+                                 workspace, st);
 }
 
 }  // namespace w4a8

@@ -314,7 +314,9 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     typename DEC::Params pp;  // parameters of the raw set being decoded
     v4i B[2][4];
     v4i ring[8];
-    const int k1 = min(1, KTe - 1);
+    // X of the padding step reads as zero; its weights (and factors) are
+    // those of the last real step, so no load leaves this split's K range.
+    const int k1 = min(1, KTe - 1), kw1 = min(1, KT - 1);
 #pragma unroll
     for (int p = 0; p < CPT; ++p) xe[p] = x_load(0, p);
 #pragma unroll
@@ -322,7 +324,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
 #pragma unroll
     for (int pi = 0; pi < 6; ++pi) w_load(0, pi, we);
 #pragma unroll
-    for (int pi = 0; pi < 6; ++pi) w_load(k1, pi, wo);
+    for (int pi = 0; pi < 6; ++pi) w_load(kw1, pi, wo);
 #pragma unroll
     for (int p = 0; p < CPT; ++p) *reinterpret_cast<v4i*>(xs0 + xlds0 + p * 4096) = xe[p];
     dec_all<DEC>(we, tb, pp, B);
@@ -347,7 +349,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     //                      last four slots use operands read earlier.
     auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, v4i (&xcur)[CPT],
                     v4i (&xnx)[CPT], WStep32& wcur, WStep32& wnx) {
-        const int k2 = min(kt + 2, KTe - 1);
+        const int k2 = min(kt + 2, KTe - 1), kw2 = min(kt + 2, KT - 1);
         typename DEC::Tmp tmp;
         static_for<SLOTS>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
@@ -361,7 +363,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
             mfma32_i8_acc(acc[rb][cb], ring[sI % 8], B[cb][i]);
             if constexpr (cb == 1 && sI + 4 < 4 * RB) ring[(sI + 4) % 8] = read_a(cur, sI + 4);
             if constexpr (s < CPT) xcur[s] = x_load(k2, s);
-            if constexpr (s >= GS && s < GS + 6) w_load(k2, s - GS, wcur);
+            if constexpr (s >= GS && s < GS + 6) w_load(kw2, s - GS, wcur);
             if constexpr (s >= SLOTS - 4 - CPT && s < SLOTS - 4)
                 *reinterpret_cast<v4i*>(nxt + xlds0 + (s - (SLOTS - 4 - CPT)) * 4096) =
                     xnx[s - (SLOTS - 4 - CPT)];

@@ -255,10 +255,16 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
     }
 }
 
-template <int NTW, int OUT>
+// GROUP = 0: per-channel scale sw[n].  GROUP = 64 or 128: the folded
+// per-group format -- each (tile, K-step) converts its codes through the
+// table e4m3(|q| f) of the lane's channel and group (fsc group-major
+// [K/GROUP][N]; lane quarter G covers K columns 32G..32G+31, so with 64-wide
+// groups it lies in group 2kt + G/2), and the epilogue scales by tsc[0].
+template <int NTW, int OUT, int GROUP>
 __global__ __launch_bounds__(1024) void w4fp8_stream_kernel(
     const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
-    const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, int ks) {
+    const float* __restrict__ sw, const float* __restrict__ fsc, const float* __restrict__ tsc,
+    void* __restrict__ Y, int M, int N, int K, int ks) {
     extern __shared__ int red[];
     float* redf = reinterpret_cast<float*>(red);
     const int lane = threadIdx.x & 63;
@@ -289,10 +295,15 @@ __global__ __launch_bounds__(1024) void w4fp8_stream_kernel(
         for (int t = 0; t < NTW; ++t) {
             const int nt = nt0 + t;
             const v4i w = load16(wlane + ((size_t)nt * KT + kt) * kTileBytes);
-            const v8i B = v8i{(int)int4_to_e4m3_lo(w.x), (int)int4_to_e4m3_hi(w.x),
-                              (int)int4_to_e4m3_lo(w.y), (int)int4_to_e4m3_hi(w.y),
-                              (int)int4_to_e4m3_lo(w.z), (int)int4_to_e4m3_hi(w.z),
-                              (int)int4_to_e4m3_lo(w.w), (int)int4_to_e4m3_hi(w.w)};
+            unsigned tlo = kE4m3LutLo, thi = kE4m3LutHi;
+            if constexpr (GROUP != 0) {
+                const int gi = GROUP == 64 ? 2 * kt + (G >> 1) : kt;
+                e4m3_fold_table(fsc[(size_t)gi * N + nt * kTileN + r], tlo, thi);
+            }
+            const v8i B = v8i{(int)int4_to_e4m3_lo(w.x, tlo, thi), (int)int4_to_e4m3_hi(w.x, tlo, thi),
+                              (int)int4_to_e4m3_lo(w.y, tlo, thi), (int)int4_to_e4m3_hi(w.y, tlo, thi),
+                              (int)int4_to_e4m3_lo(w.z, tlo, thi), (int)int4_to_e4m3_hi(w.z, tlo, thi),
+                              (int)int4_to_e4m3_lo(w.w, tlo, thi), (int)int4_to_e4m3_hi(w.w, tlo, thi)};
             // formats 0/0 = e4m3 x e4m3; E8M0 scale 127 = 2^0 on both sides
             acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[t], 0, 0, 0, 127,
                                                                       0, 127);
@@ -313,6 +324,7 @@ __global__ __launch_bounds__(1024) void w4fp8_stream_kernel(
                 for (int v = 0; v < 4; ++v) acc[t][v] += redf[((w * NTW + t) * 4 + v) * 64 + lane];
     }
 
+    const float tval = GROUP != 0 ? tsc[0] : 0.0f;
 #pragma unroll
     for (int t = 0; t < NTW; ++t) {
         const int n = (nt0 + t) * kTileN + r;
@@ -320,7 +332,7 @@ __global__ __launch_bounds__(1024) void w4fp8_stream_kernel(
         for (int v = 0; v < 4; ++v) {
             const int mo = m0 + 4 * G + v;
             if (mo >= M) continue;
-            const float y = (acc[t][v] * sx[mo]) * sw[n];
+            const float y = (acc[t][v] * sx[mo]) * (GROUP != 0 ? tval : sw[n]);
             if (OUT == 1)
                 reinterpret_cast<float*>(Y)[(size_t)mo * N + n] = y;
             else
@@ -386,30 +398,53 @@ hipError_t launch_w4a8_stream(const int8_t* X, const float* sx, const uint8_t* w
 #undef W4A8_NTW
 }
 
-template <int NTW>
+template <int NTW, int GROUP>
 static hipError_t w4fp8_stream_ntw(const uint8_t* X, const float* sx, const uint8_t* wq,
-                                   const float* sw, void* Y, int out_type, int M, int N, int K,
-                                   int ks, hipStream_t st) {
+                                   const float* sw, const float* fsc, const float* tsc, void* Y,
+                                   int out_type, int M, int N, int K, int ks, hipStream_t st) {
     dim3 grid(N / (kTileN * NTW), (M + 15) / 16);
     dim3 block(64 * ks);
     size_t lds = ks > 1 ? (size_t)ks * NTW * 4 * 64 * sizeof(float) : 0;
     if (out_type == 1)
-        hipLaunchKernelGGL((w4fp8_stream_kernel<NTW, 1>), grid, block, lds, st, X, sx, wq, sw, Y,
-                           M, N, K, ks);
+        hipLaunchKernelGGL((w4fp8_stream_kernel<NTW, 1, GROUP>), grid, block, lds, st, X, sx, wq,
+                           sw, fsc, tsc, Y, M, N, K, ks);
     else
-        hipLaunchKernelGGL((w4fp8_stream_kernel<NTW, 0>), grid, block, lds, st, X, sx, wq, sw, Y,
-                           M, N, K, ks);
+        hipLaunchKernelGGL((w4fp8_stream_kernel<NTW, 0, GROUP>), grid, block, lds, st, X, sx, wq,
+                           sw, fsc, tsc, Y, M, N, K, ks);
     return hipGetLastError();
+}
+
+template <int GROUP>
+static hipError_t w4fp8_stream_group(const uint8_t* X, const float* sx, const uint8_t* wq,
+                                     const float* sw, const float* fsc, const float* tsc, void* Y,
+                                     int out_type, int M, int N, int K, StreamCfg cfg,
+                                     hipStream_t st) {
+    switch (cfg.nt_per_wave) {
+        case 4:
+            return w4fp8_stream_ntw<4, GROUP>(X, sx, wq, sw, fsc, tsc, Y, out_type, M, N, K,
+                                              cfg.ks, st);
+        case 2:
+            return w4fp8_stream_ntw<2, GROUP>(X, sx, wq, sw, fsc, tsc, Y, out_type, M, N, K,
+                                              cfg.ks, st);
+        default:
+            return w4fp8_stream_ntw<1, GROUP>(X, sx, wq, sw, fsc, tsc, Y, out_type, M, N, K,
+                                              cfg.ks, st);
+    }
 }
 
 hipError_t launch_w4fp8_stream(const uint8_t* X, const float* sx, const uint8_t* wq,
                                const float* sw, void* Y, int out_type, int M, int N, int K,
                                StreamCfg cfg, hipStream_t st) {
-    switch (cfg.nt_per_wave) {
-        case 4: return w4fp8_stream_ntw<4>(X, sx, wq, sw, Y, out_type, M, N, K, cfg.ks, st);
-        case 2: return w4fp8_stream_ntw<2>(X, sx, wq, sw, Y, out_type, M, N, K, cfg.ks, st);
-        default: return w4fp8_stream_ntw<1>(X, sx, wq, sw, Y, out_type, M, N, K, cfg.ks, st);
-    }
+    return w4fp8_stream_group<0>(X, sx, wq, sw, nullptr, nullptr, Y, out_type, M, N, K, cfg, st);
+}
+
+hipError_t launch_w4fp8g_stream(const uint8_t* X, const float* sx, const uint8_t* wq,
+                                const float* fsc, const float* tsc, void* Y, int out_type, int M,
+                                int N, int K, int group, StreamCfg cfg, hipStream_t st) {
+    if (group == 64)
+        return w4fp8_stream_group<64>(X, sx, wq, nullptr, fsc, tsc, Y, out_type, M, N, K, cfg,
+                                      st);
+    return w4fp8_stream_group<128>(X, sx, wq, nullptr, fsc, tsc, Y, out_type, M, N, K, cfg, st);
 }
 
 }  // namespace w4a8

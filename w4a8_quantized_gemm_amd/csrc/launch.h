@@ -9,6 +9,10 @@ hipError_t launch_pack_lqq(const float* W, int N, int K, int group, int qmax, ui
                            uint8_t* s_u8, uint8_t* a_u8, float* sw, hipStream_t st);
 hipError_t launch_pack_int4(const float* W, int N, int K, uint8_t* wq, float* sw,
                             hipStream_t st);
+// INT4 codes with per-group scales folded into FP8 (fsc [K/group][N] float32
+// folded factors, tscale[0] the per-tensor scale).
+hipError_t launch_pack_fp8g(const float* W, int N, int K, int group, uint8_t* wq, float* fsc,
+                            float* tscale, hipStream_t st);
 // Per-token activation quantisation; in_type 0 = float32, 1 = fp16, 2 = bf16.
 hipError_t launch_act_int8(const void* X, int in_type, int M, int K, int8_t* Xq, float* sx,
                            hipStream_t st);
@@ -70,5 +74,15 @@ hipError_t launch_w4fp8_mfma(const uint8_t* X, const float* sx, const uint8_t* w
 hipError_t launch_w4fp8_stream(const uint8_t* X, const float* sx, const uint8_t* wq,
                                const float* sw, void* Y, int out_type, int M, int N, int K,
                                StreamCfg cfg, hipStream_t st);
+
+// Folded per-group FP8 weights (fsc [K/group][N] factors, tsc[0] tensor scale).
+hipError_t launch_w4fp8g_mfma(const uint8_t* X, const float* sx, const uint8_t* wq,
+                              const float* fsc, const float* tsc, void* Y, int out_type, int M,
+                              int N, int K, int group, const MfmaPlan& plan, void* workspace,
+                              hipStream_t st);
+
+hipError_t launch_w4fp8g_stream(const uint8_t* X, const float* sx, const uint8_t* wq,
+                                const float* fsc, const float* tsc, void* Y, int out_type, int M,
+                                int N, int K, int group, StreamCfg cfg, hipStream_t st);
 
 }  // namespace w4a8

@@ -132,6 +132,65 @@ __global__ __launch_bounds__(256) void int4_pack_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// INT4 with per-group scales folded into FP8 weights and a per-tensor
+// rescale (FireQ, arXiv 2505.20839, abstract; the formulas are this
+// library's reading): s_g = max|group| / 7, t = max|W| / 448, f = s_g / t,
+// q = clamp(rne(W / s_g), -7, 7) in sign-magnitude nibbles.  The GEMM
+// turns q into e4m3(|q| f) with q's sign and rescales by t.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void row_absmax_kernel(const float* __restrict__ W, int K,
+                                                         float* __restrict__ rmax) {
+    const float m = block_absmax_256(W + (size_t)blockIdx.x * K, K);
+    if (threadIdx.x == 0) rmax[blockIdx.x] = m;
+}
+
+// t = max_n rmax[n] / 448 (an all-zero tensor gets 1); one workgroup.
+__global__ __launch_bounds__(256) void tensor_scale_kernel(const float* __restrict__ rmax, int N,
+                                                           float* __restrict__ t) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < N; i += 256) m = fmaxf(m, rmax[i]);
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    __shared__ float part[4];
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+        t[0] = scale_of(m, 448.0f);
+    }
+}
+
+// One thread per (group, row): its scale, folded factor (group-major
+// fsc[j][n], so a K-step's factors of consecutive channels are adjacent)
+// and packed codes.
+__global__ __launch_bounds__(256) void fp8g_group_kernel(const float* __restrict__ W,
+                                                         const float* __restrict__ t, int N, int K,
+                                                         int group, uint8_t* __restrict__ wq,
+                                                         float* __restrict__ fsc) {
+    const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
+    const int groups = K / group;
+    if (tid >= (long long)N * groups) return;
+    const int j = (int)(tid / N), n = (int)(tid % N);
+    const float* w = W + (size_t)n * K + (size_t)j * group;
+    float amax = 0.0f;
+    for (int k = 0; k < group; ++k) amax = fmaxf(amax, fabsf(w[k]));
+    const float sg = scale_of(amax, 7.0f);
+    fsc[tid] = __fdiv_rn(sg, t[0]);
+    const int KT = K / kTileK, nt = n / kTileN, r = n % kTileN;
+    for (int k8 = 0; k8 < group; k8 += 8) {
+        unsigned word = 0;
+        for (int e = 0; e < 8; ++e) {
+            const int q = quant_sym(w[k8 + e], sg, 7.0f);
+            const unsigned c = q < 0 ? (0x8u | (unsigned)(-q)) : (unsigned)q;
+            word |= c << (8 * (e & 3) + 4 * (e >> 2));
+        }
+        const int k = j * group + k8;
+        const int kt = k / kTileK, kk = k % kTileK;
+        const size_t off = packed_dword_offset(nt, kt, KT, kk / 32, r, (kk % 32) / 8);
+        *reinterpret_cast<unsigned*>(wq + off) = word;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Per-token activation quantisation: one workgroup per row.  The input is
 // float32, fp16 or bf16 (IN = 0, 1, 2); each element is first widened to
 // float32, which is exact, so every input type quantises like float32.
@@ -262,6 +321,19 @@ hipError_t launch_pack_int4(const float* W, int N, int K, uint8_t* wq, float* sw
     long long threads = (long long)N * (K / 8);
     unsigned blocks = (unsigned)((threads + 255) / 256);
     hipLaunchKernelGGL(int4_pack_kernel, dim3(blocks), dim3(256), 0, st, W, sw, N, K, wq);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_fp8g(const float* W, int N, int K, int group, uint8_t* wq, float* fsc,
+                            float* tscale, hipStream_t st) {
+    // fsc's first N floats hold the row maxima until the group kernel
+    // overwrites them (it reads only tscale).
+    hipLaunchKernelGGL(row_absmax_kernel, dim3(N), dim3(256), 0, st, W, K, fsc);
+    hipLaunchKernelGGL(tensor_scale_kernel, dim3(1), dim3(256), 0, st, fsc, N, tscale);
+    long long threads = (long long)N * (K / group);
+    unsigned blocks = (unsigned)((threads + 255) / 256);
+    hipLaunchKernelGGL(fp8g_group_kernel, dim3(blocks), dim3(256), 0, st, W, tscale, N, K, group,
+                       wq, fsc);
     return hipGetLastError();
 }
 
