@@ -336,30 +336,50 @@ def main():
                                           "launches (inputs L2/MALL-warm)",
                               "results": moe}
 
-    # ---- FP8 variant (INT4 weights x e4m3 activations), reported alongside
+    # ---- FP8 variants (INT4 weights x e4m3 activations), reported alongside:
+    # per-channel scales, and per-group scales folded into the FP8 weights
+    # with a per-tensor rescale; prefill shape and a 16-token decode shape
     if not args.no_fp8 and not args.only:
         sh = wl.CONFIGS[4].shapes[0]
         Wf = torch.from_numpy(wl.gen_weights(sh.N, sh.K, wl.seed_w(4))).to(dev)
         pk8 = w4.pack(Wf, mode=w4.PACK_INT4_SYM)
+        pk8g = w4.pack_fp8g(Wf, group=128)
         del Wf
         Xf = torch.from_numpy(wl.gen_activations(sh.M, sh.K, wl.seed_x(4),
                                                  wl.seed_outliers(4))).to(dev)
         X8, sx8 = w4.quant_act_fp8(Xf)
-        Yb = torch.empty((sh.M, sh.N), dtype=torch.bfloat16, device=dev)
-        for _ in range(3):
-            w4.gemm_fp8(X8, sx8, pk8, out=Yb)
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 20
-        e0.record(stream)
-        for _ in range(reps):
-            w4.gemm_fp8(X8, sx8, pk8, out=Yb)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / reps
-        tf = 2.0 * sh.M * sh.N * sh.K / (us * 1e-6) / 1e12
-        out["variant_fp8"] = {"workload": "int4-fp8 2048x8192x8192, bf16 out",
-                              "us": round(us, 2), "tflops": round(tf, 2),
-                              "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4)}
+        del Xf
+
+        def timed(fn, reps):
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(reps):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            return e0.elapsed_time(e1) * 1e3 / reps
+
+        res = {}
+        for M in (sh.M, 16):
+            Yb = torch.empty((M, sh.N), dtype=torch.bfloat16, device=dev)
+            Xm, sxm = X8[:M], sx8[:M]
+            for tag, fn in (("per_channel", lambda: w4.gemm_fp8(Xm, sxm, pk8, out=Yb)),
+                            ("group128_folded", lambda: w4.gemm_fp8g(Xm, sxm, pk8g, out=Yb))):
+                us = timed(fn, 20)
+                tf = 2.0 * M * sh.N * sh.K / (us * 1e-6) / 1e12
+                wb = sh.N * sh.K / 2 + (sh.N * 4 if tag == "per_channel"
+                                        else sh.N * sh.K // 128 * 4 + 4)
+                ab = wb + M * sh.K + M * 4 + M * sh.N * 2
+                res[f"{tag}_M{M}"] = {"us": round(us, 2), "tflops": round(tf, 2),
+                                      "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                                      "hbm_frac_algo": round(ab / (us * 1e-6) / 1e9
+                                                             / HBM_PEAK_GBS, 4)}
+        out["variant_fp8"] = {"workload": f"int4-fp8 N={sh.N} K={sh.K}, M={sh.M} and 16, "
+                                          "bf16 out; events over 20 back-to-back launches",
+                              "results": res}
+        del pk8, pk8g, X8
 
     if not args.no_cpu_baseline and not args.only:
         desc = [(s["name"], s["M"], s["N"], s["K"], g, s["pair"]) for s in slots]
