@@ -73,6 +73,8 @@ def _declare(L):
         "orc_w4fp8g_pack": ([_P, _I, _I, _I, _P, _P, _P, _P], None),
         "orc_w4fp8g_weights": ([_P, _P, _I, _I, _I, _P], None),
         "orc_w4fp8g_ref": ([_P, _P, _P, _F, _I, _I, _I, _P, _P], None),
+        "orc_pack_w8": ([_P, _I, _I, _P], None),
+        "orc_unpack_w8": ([_P, _I, _I, _P], None),
     }
     for name, (args, res) in sig.items():
         fn = getattr(L, name)
@@ -323,5 +325,39 @@ def w4a8_gemm(X8, sx, pk, group: int):
     """Decoded-weight GEMM: (int32 acc, fp16 bits, unrounded float64)."""
     Qhat = lqq_decode(pk["codes"], pk["s_u8"], pk["a_u8"], group)
     acc = gemm_i32(X8, Qhat)
+    y, yd = epilogue_f16(acc, sx, pk["sw"])
+    return acc, y, yd
+
+
+# ----------------------------------------------- W8A8 comparison (section 12)
+
+def pack_w8(Q):
+    """INT8 codes [N][K] in the 8-bit tile layout (flat int8 [N*K])."""
+    Q = _c(Q, np.int8)
+    N, K = Q.shape
+    assert N % 16 == 0 and K % 128 == 0
+    out = np.empty(N * K, np.int8)
+    lib().orc_pack_w8(_p(Q), N, K, _p(out))
+    return out
+
+
+def unpack_w8(packed, N: int, K: int):
+    packed = _c(packed, np.int8).reshape(-1)
+    assert packed.size == N * K
+    Q = np.empty((N, K), np.int8)
+    lib().orc_unpack_w8(_p(packed), N, K, _p(Q))
+    return Q
+
+
+def w8a8_pack(W, qmax: int = 127):
+    """The first LiquidQuant level alone: per-channel INT8 codes and scales,
+    plus their 8-bit tile layout."""
+    Q, sw = quant_sym_rows(W, qmax)
+    return {"Q": Q, "sw": sw, "wq8": pack_w8(Q)}
+
+
+def w8a8_gemm(X8, sx, pk):
+    """INT8 x INT8 GEMM with the fp16 epilogue: (int32 acc, fp16 bits, float64)."""
+    acc = gemm_i32(X8, pk["Q"])
     y, yd = epilogue_f16(acc, sx, pk["sw"])
     return acc, y, yd

@@ -499,3 +499,40 @@ ORC_API void orc_w4fp8g_ref(const uint8_t* X8, const float* sx, const uint8_t* w
     free(xd);
     free(wd);
 }
+
+/* ------------------------------------------------------------------------ *
+ * 12. The W8A8 comparison path.  [LG] ("If this is right") sets W4A8 against
+ *     W8A8: lower memory traffic should win in small-batch, memory-bound
+ *     runs, and in large-batch, compute-bound runs W4A8 should match or beat
+ *     it.  The W8A8 weights are the first LiquidQuant level alone: the
+ *     per-channel INT8 codes and scales of section 1 (qmax 127), multiplied
+ *     by the INT8 GEMM above with the same epilogue.  This library's 8-bit
+ *     tile layout (READING: the pages give none) holds the codes as:
+ *       tile (nt, kt) of 16 rows x 128 K at byte 2048 * (nt * (K/128) + kt);
+ *       inside it, byte 1024*u + 16*(16*G + r) + j is row 16*nt + r,
+ *       column 128*kt + 32*G + 16*u + j   (G 0..3, u 0..1, j 0..15).
+ * ------------------------------------------------------------------------ */
+ORC_API void orc_pack_w8(const int8_t* Q, int64_t N, int64_t K, int8_t* out) {
+    const int64_t KT = K / 128;
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t nt = n / 16, r = n % 16;
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t kt = k / 128, kk = k % 128;
+            const int64_t G = kk / 32, u = (kk % 32) / 16, j = kk % 16;
+            const int64_t off = 2048 * (nt * KT + kt) + 1024 * u + 16 * (16 * G + r) + j;
+            out[off] = Q[n * K + k];
+        }
+    }
+}
+
+ORC_API void orc_unpack_w8(const int8_t* packed, int64_t N, int64_t K, int8_t* Q) {
+    const int64_t KT = K / 128;
+    for (int64_t n = 0; n < N; ++n) {
+        const int64_t nt = n / 16, r = n % 16;
+        for (int64_t k = 0; k < K; ++k) {
+            const int64_t kt = k / 128, kk = k % 128;
+            const int64_t G = kk / 32, u = (kk % 32) / 16, j = kk % 16;
+            Q[n * K + k] = packed[2048 * (nt * KT + kt) + 1024 * u + 16 * (16 * G + r) + j];
+        }
+    }
+}

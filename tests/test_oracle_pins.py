@@ -550,3 +550,84 @@ def test_generator_deterministic():
     ch = wl.outlier_channels(1000, 2)
     assert ch.size == 10 and np.unique(ch).size == 10
     assert abs(float(a.std()) - 0.02) < 0.002
+
+
+# ------------------------------------------------- W8A8 comparison path ----
+def test_w8_layout_golden(golden_dir):
+    n = 0
+    for line in open(os.path.join(golden_dir, "w8_layout.txt")):
+        if not line.strip() or line.startswith("#"):
+            continue
+        N, K, r, k, byte = map(int, line.split())
+        Q = np.zeros((N, K), np.int8)
+        Q[r, k] = -77
+        out = oracle.pack_w8(Q)
+        assert list(np.nonzero(out)[0]) == [byte], line
+        assert out[byte] == -77
+        n += 1
+    assert n == 13
+
+
+def test_w8_layout_is_a_permutation():
+    """Every code lands in exactly one byte and unpacking restores it."""
+    rng = np.random.default_rng(12)
+    N, K = 48, 384
+    Q = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    np.testing.assert_array_equal(oracle.unpack_w8(oracle.pack_w8(Q), N, K), Q)
+    idx = np.arange(N * K, dtype=np.int64)
+    # pack the index itself byte-wise: low byte and high bytes separately
+    lo = oracle.pack_w8((idx & 0x7F).astype(np.int8).reshape(N, K)).astype(np.int64)
+    mid = oracle.pack_w8(((idx >> 7) & 0x7F).astype(np.int8).reshape(N, K)).astype(np.int64)
+    hi = oracle.pack_w8(((idx >> 14) & 0x7F).astype(np.int8).reshape(N, K)).astype(np.int64)
+    where = lo | (mid << 7) | (hi << 14)
+    assert sorted(where.tolist()) == list(range(N * K))
+
+
+def test_w8a8_brute_force_tiny():
+    """W8A8 on tiny shapes against pure-Python loops: per-channel INT8 codes
+    from the definition (scale max/127, round half even, clamp), integer
+    sums, and the fp16 epilogue value before rounding."""
+    rng = np.random.default_rng(13)
+    M, N, K = 3, 16, 128
+    W = rng.standard_normal((N, K)).astype(np.float32)
+    X = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    sx = (rng.random(M).astype(np.float32) + np.float32(0.5)) / np.float32(100)
+    pk = oracle.w8a8_pack(W)
+    for n in range(N):
+        s = np.float32(np.max(np.abs(W[n]))) / np.float32(127)
+        assert pk["sw"][n] == s
+        for k in range(0, K, 7):
+            v = np.float32(W[n, k]) / s
+            q = int(np.clip(np.rint(v), -127, 127))
+            assert pk["Q"][n, k] == q
+    acc, y, yd = oracle.w8a8_gemm(X, sx, pk)
+    for m in range(M):
+        for n in range(N):
+            tot = sum(int(X[m, k]) * int(pk["Q"][n, k]) for k in range(K))
+            assert acc[m, n] == tot
+            assert yd[m, n] == float(tot) * float(sx[m]) * float(pk["sw"][n])
+
+
+def test_w8a8_equals_w4a8_when_groups_lossless():
+    """When every LiquidQuant group spans at most 15 INT8 steps, its second
+    level is lossless (s = 1), so the W4A8 and W8A8 integer results agree."""
+    rng = np.random.default_rng(14)
+    M, N, K, g = 5, 32, 256, 64
+    base = rng.integers(-100, 90, size=(N, K // g, 1))
+    base[:, 0] = 112  # group 0 spans 112..127
+    Q = (base + rng.integers(0, 16, size=(N, K // g, g))).reshape(N, K)
+    Q[:, 0] = 127  # fixes every channel's scale: W = Q exactly with sw = 1
+    Wf = Q.astype(np.float32)
+    X = rng.integers(-127, 128, size=(M, K)).astype(np.int8)
+    sx = np.ones(M, np.float32)
+    p8 = oracle.w8a8_pack(Wf)
+    np.testing.assert_array_equal(p8["Q"], Q.astype(np.int8))
+    Qg = p8["Q"].reshape(N, K // g, g)
+    lossless = (Qg.max(axis=2).astype(int) - Qg.min(axis=2).astype(int) <= 15)
+    p4 = oracle.w4a8_pack(Wf, g)
+    acc4, _, _ = oracle.w4a8_gemm(X, sx, p4, g)
+    acc8, _, _ = oracle.w8a8_gemm(X, sx, p8)
+    assert lossless.all()
+    assert np.all(p4["s_u8"] == 1)
+    np.testing.assert_array_equal(acc4, acc8)
+    np.testing.assert_array_equal(acc8, X.astype(np.int64) @ Q.astype(np.int64).T)
