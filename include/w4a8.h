@@ -276,6 +276,29 @@ w4a8_status_t w4fp8g_gemm(const uint8_t* X_e4m3, const float* sx,
                           int N, int K, int group, int splitk, void* workspace,
                           size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * W8A8 comparison path ([LG] "If this is right": W4A8's lower memory
+ * traffic should beat W8A8 in small-batch, memory-bound runs and match or
+ * beat it in large-batch, compute-bound ones).  The weights are the first
+ * LiquidQuant level alone: per output channel, sw[n] = max|W[n]|/127 and
+ * Q[n][k] = clamp(rne(W[n][k]/sw[n]), -127, 127) (float32, as w4a8_pack's
+ * first level), stored as int8 in the 8-bit tile layout:
+ *   tile (nt, kt) of 16 rows x 128 K occupies bytes [2048*(nt*(K/128)+kt),
+ *   +2048); inside it, byte 1024*u + 16*(16*G + r) + j holds row 16nt + r,
+ *   column 128kt + 32G + 16u + j (G 0..3, u 0..1, j 0..15).
+ * w8a8_pack: W float32 [N][K] -> wq8 (N*K bytes), sw (N floats).
+ * w8a8_gemm: acc[m][n] = sum_k X[m][k] * Q[n][k] (exact int32), then the
+ *   w4a8_gemm epilogue (out_type W4A8_OUT_F16 or W4A8_OUT_I32).  The same
+ *   kernels as w4a8_gemm with the decode step removed; kernel choice,
+ *   splitk and workspace as for w4a8_gemm.  N * K < 2^31.
+ */
+w4a8_status_t w8a8_pack(const float* W, int N, int K, int8_t* wq8, float* sw,
+                        hipStream_t stream);
+w4a8_status_t w8a8_gemm(const int8_t* X, const float* sx, const int8_t* wq8,
+                        const float* sw, void* Y, int out_type, int M, int N,
+                        int K, int splitk, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
+
 /* Static English text for a status code (never NULL). */
 const char* w4a8_status_str(w4a8_status_t status);
 

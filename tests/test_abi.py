@@ -191,6 +191,29 @@ def test_fp8_group_fold_validation():
     assert gg(M=128, K=8192, wsb=need, ws=0) == NULL
 
 
+def test_w8a8_validation():
+    def pk(W=A, N=64, K=256, wq=A, sw=A):
+        return lib.w8a8_pack(W, N, K, wq, sw, None)
+    assert pk(K=100) == SHAPE
+    assert pk(N=8) == SHAPE
+    assert pk(N=1 << 16, K=1 << 15) == SHAPE   # N*K >= 2^31
+    assert pk(N=0) == OK
+    assert pk(wq=None) == NULL
+    assert pk(W=A + 4) == ALIGN
+
+    def gm(M=16, N=256, K=512, out=0, splitk=0, X=A, wq=A, sx=A, sw=A, Y=A, ws=0, wsb=0):
+        return lib.w8a8_gemm(X, sx, wq, sw, Y, out, M, N, K, splitk, ws, wsb, None)
+    assert gm(out=2) == UNSUP
+    assert gm(K=100) == SHAPE
+    assert gm(splitk=3) == SHAPE
+    assert gm(M=0) == OK
+    assert gm(wq=None) == NULL
+    assert gm(sw=None) == NULL
+    assert gm(Y=A + 4) == ALIGN
+    need = lib.w4a8_workspace_size(128, 256, 8192, 0)
+    assert gm(M=128, K=8192, ws=A, wsb=need - 1) == WS
+
+
 def test_valid_call_without_gpu_reports_hip_error():
     """A call that passes validation reaches the HIP runtime; with no GPU
     the device query fails and the status is W4A8_ERR_HIP, not a crash."""

@@ -468,6 +468,46 @@ def test_fp8_workspace_too_small_is_rejected():
     assert ei.value.status == 4
 
 
+# ------------------------------------------------ W8A8 comparison ---------
+@pytest.mark.parametrize("N,K", [(64, 256), (320, 1152), (256, 640)])
+def test_w8a8_pack_parity(N, K):
+    say(f"w8a8 pack N={N} K={K}")
+    W = wl.gen_weights(N, K, 1100 + N)
+    W[2, :] = 0.0
+    ref = oracle.w8a8_pack(W)
+    pk = w4.pack_w8(to_dev(W))
+    np.testing.assert_array_equal(host(pk["wq8"]), ref["wq8"])
+    np.testing.assert_array_equal(host(pk["sw"]).view(np.uint32), ref["sw"].view(np.uint32))
+
+
+@pytest.mark.parametrize("M,N,K,sk", [(1, 128, 640, 0), (5, 64, 512, 0), (16, 448, 1024, 0),
+                                      (33, 256, 512, 0), (64, 256, 640, 0), (100, 512, 1024, 0),
+                                      (300, 512, 1152, 0), (513, 256, 512, 0),
+                                      (128, 256, 4096, 0), (100, 256, 896, 2), (257, 1024, 256, 0)])
+def test_w8a8_gemm_parity(M, N, K, sk):
+    """int32 bit-exact and fp16 within 1 ulp against the oracle: streamed
+    kernel (M < 64, N % 256 != 0, or forced by splitk), tile kernel with
+    128- and 256-row tiles, ragged M, odd K-step counts and planned split-K."""
+    say(f"w8a8 gemm M={M} N={N} K={K} splitk={sk} workspace={w4.workspace_size(M, N, K, sk)}")
+    W = wl.gen_weights(N, K, 1200 + M + N)
+    X = wl.gen_activations(M, K, 1201 + M, 1202)
+    ref = oracle.w8a8_pack(W)
+    X8, sx = oracle.quant_sym_rows(X, 127)
+    acc, y, _ = oracle.w8a8_gemm(X8, sx, ref)
+    pk = {"wq8": to_dev(ref["wq8"]), "sw": to_dev(ref["sw"]), "N": N, "K": K}
+    Yi = poison((M, N), torch.int32)
+    w4.gemm_w8a8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_I32, splitk=sk, out=Yi)
+    np.testing.assert_array_equal(host(Yi), acc)
+    Yh = poison((M, N), torch.float16)
+    w4.gemm_w8a8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F16, splitk=sk, out=Yh)
+    d = f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y)
+    assert d.max() <= 1
+    if sk == 0 and M >= 64:  # the streamed kernel agrees
+        Ys = poison((M, N), torch.int32)
+        w4.gemm_w8a8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_I32, splitk=1, out=Ys)
+        np.testing.assert_array_equal(host(Ys), acc)
+
+
 # ----------------------------- folded per-group FP8 (FireQ-style) ----------
 def _fp8g_weights(N, K, g, seed):
     """Normal(0, 0.02) weights with one all-zero row and one all-zero group

@@ -43,7 +43,7 @@ LAYOUT_VERSION = 1
 EXPORTS = ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act",
            "w4a8_quant_act_ex", "w4fp8_quant_act_ex", "w4a8_workspace_size", "w4a8_gemm",
            "w4a8_gemm_ablation", "w4a8_gemm_grouped", "w4fp8_gemm", "w4fp8g_pack",
-           "w4fp8g_gemm",
+           "w4fp8g_gemm", "w8a8_pack", "w8a8_gemm",
            "w4a8_status_str", "w4a8_last_hip_error", "w4a8_layout_version")
 
 _P, _I, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
@@ -60,13 +60,15 @@ lib.w4a8_gemm_ablation.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _
 lib.w4a8_gemm_grouped.argtypes = [_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
 lib.w4fp8g_pack.argtypes = [_P, _I, _I, _I, _P, _P, _P, _P]
 lib.w4fp8g_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]
+lib.w8a8_pack.argtypes = [_P, _I, _I, _P, _P, _P]
+lib.w8a8_gemm.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]
 lib.w4a8_status_str.argtypes = [_I]
 lib.w4a8_status_str.restype = ctypes.c_char_p
 lib.w4a8_last_hip_error.restype = _I
 lib.w4a8_layout_version.restype = _I
 for _n in ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act", "w4a8_quant_act_ex",
            "w4fp8_quant_act_ex", "w4a8_gemm", "w4a8_gemm_ablation", "w4a8_gemm_grouped",
-           "w4fp8_gemm", "w4fp8g_pack", "w4fp8g_gemm"):
+           "w4fp8_gemm", "w4fp8g_pack", "w4fp8g_gemm", "w8a8_pack", "w8a8_gemm"):
     getattr(lib, _n).restype = _I
 
 assert lib.w4a8_layout_version() == LAYOUT_VERSION
@@ -329,4 +331,40 @@ def gemm_fp8g(Xq, sx, packed, out_type: int = OUT_BF16, splitk: int = 0, out=Non
                            _ptr(packed["tscale"]), _ptr(Y), out_type, M, N, K,
                            packed["group"], splitk, _ptr(workspace), ws_bytes,
                            _stream(stream)), "w4fp8g_gemm")
+    return Y
+
+
+def pack_w8(W, stream=None):
+    """w8a8_pack: per-channel INT8 weights in the 8-bit tile layout.
+
+    Returns a dict with wq8 (int8 [N*K]) and sw (float32 [N])."""
+    torch = _torch()
+    _need(W, torch.float32, "W")
+    N, K = W.shape
+    wq8 = torch.empty(N * K, dtype=torch.int8, device=W.device)
+    sw = torch.empty(N, dtype=torch.float32, device=W.device)
+    _check(lib.w8a8_pack(_ptr(W), N, K, _ptr(wq8), _ptr(sw), _stream(stream)), "w8a8_pack")
+    return {"wq8": wq8, "sw": sw, "N": N, "K": K}
+
+
+def gemm_w8a8(Xq, sx, packed, out_type: int = OUT_F16, splitk: int = 0, out=None,
+              workspace=None, stream=None):
+    """w8a8_gemm on pack_w8 output: Y [M][N] fp16 (OUT_F16) or int32 (OUT_I32)."""
+    torch = _torch()
+    _need(Xq, torch.int8, "Xq")
+    M, K = Xq.shape
+    N = packed["N"]
+    if packed["K"] != K:
+        raise ValueError("K of X and of the packed weights differ")
+    ydt = torch.float16 if out_type == OUT_F16 else torch.int32
+    Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
+    _need(Y, ydt, "out")
+    if workspace is None:
+        need = workspace_size(M, N, K, splitk)
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=Xq.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.w8a8_gemm(_ptr(Xq), _ptr(sx), _ptr(packed["wq8"]), _ptr(packed["sw"]), _ptr(Y),
+                         out_type, M, N, K, splitk, _ptr(workspace), ws_bytes, _stream(stream)),
+           "w8a8_gemm")
     return Y

@@ -325,3 +325,41 @@ W4A8_EXPORT w4a8_status_t w4fp8g_gemm(const uint8_t* X_e4m3, const float* sx, co
                                                  K, group, choose_stream(M, N, K, splitk),
                                                  stream));
 }
+
+W4A8_EXPORT w4a8_status_t w8a8_pack(const float* W, int N, int K, int8_t* wq8, float* sw,
+                                    hipStream_t stream) {
+    if (!valid_nk(N, K)) return W4A8_ERR_SHAPE;
+    if ((long long)N * K >= (1LL << 31)) return W4A8_ERR_SHAPE;
+    if (N == 0) return W4A8_OK;  // nothing to read or write
+    if (!W || !wq8 || !sw) return W4A8_ERR_NULL_PTR;
+    if (!aligned16(W) || !aligned16(wq8) || !aligned4(sw)) return W4A8_ERR_ALIGNMENT;
+    w4a8_status_t d = check_device();
+    if (d != W4A8_OK) return d;
+    return hip_status(w4a8::launch_pack_w8(W, N, K, wq8, sw, stream));
+}
+
+W4A8_EXPORT w4a8_status_t w8a8_gemm(const int8_t* X, const float* sx, const int8_t* wq8,
+                                    const float* sw, void* Y, int out_type, int M, int N, int K,
+                                    int splitk, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    if (out_type != W4A8_OUT_F16 && out_type != W4A8_OUT_I32) return W4A8_ERR_UNSUPPORTED;
+    if (M < 0 || !valid_nk(N, K) || !valid_splitk(splitk, K)) return W4A8_ERR_SHAPE;
+    if ((long long)N * K >= (1LL << 31)) return W4A8_ERR_SHAPE;
+    if (M == 0 || N == 0) return W4A8_OK;  // nothing to read or write
+    if (!X || !wq8 || !Y) return W4A8_ERR_NULL_PTR;
+    if (out_type == W4A8_OUT_F16 && (!sx || !sw)) return W4A8_ERR_NULL_PTR;
+    if (!aligned16(X) || !aligned16(wq8) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
+    if ((sx && !aligned4(sx)) || (sw && !aligned4(sw))) return W4A8_ERR_ALIGNMENT;
+    const size_t need = w4a8_workspace_size(M, N, K, splitk);
+    if (workspace_bytes < need) return W4A8_ERR_WORKSPACE;
+    if (need > 0 && !workspace) return W4A8_ERR_NULL_PTR;
+    if (need > 0 && !aligned16(workspace)) return W4A8_ERR_ALIGNMENT;
+    w4a8_status_t d = check_device();
+    if (d != W4A8_OK) return d;
+    if (splitk == 0 && use_mfma_tiles(M, N, K))
+        return hip_status(w4a8::launch_w8a8_mfma(X, sx, wq8, sw, Y, out_type, M, N, K,
+                                                 w4a8::plan_w4a8_mfma(M, N, K), workspace,
+                                                 stream));
+    return hip_status(w4a8::launch_w8a8_stream(X, sx, wq8, sw, Y, out_type, M, N, K,
+                                               choose_stream(M, N, K, splitk), stream));
+}

@@ -65,6 +65,9 @@ struct WStep32 {
 // 7 instructions per 8 weights (LiquidGEMM, Pith review of arXiv 2509.01229,
 // paper Eq. 12 and minor comment 1 / Sec. 5.3).
 struct DecLQQ {
+    using Raw = WStep32;
+    static constexpr bool kW8 = false;
+    static constexpr int kLoads = 6;  // raw loads per K-step: 4 weight slots, s, a
     struct Params {
         unsigned s2[2], a4[2];  // scale pair, offset quad per channel block
     };
@@ -128,6 +131,9 @@ struct DecLQQ {
 // weights.  Equal to the LiquidQuant decode value for value (the identity
 // (q*s + a) XOR 0x80 = q*s + a - 128 on INT8 results).
 struct DecAffine16 {
+    using Raw = WStep32;
+    static constexpr bool kW8 = false;
+    static constexpr int kLoads = 6;
     struct Params {
         unsigned s2[2], m2[2];  // scale, min in both 16-bit lanes
     };
@@ -184,20 +190,48 @@ struct DecAffine16 {
     }
 };
 
+// No decode, for the W8A8 comparison: the INT8 weights of the first
+// quantisation level alone, in the 8-bit tile layout.  A lane's raw K-step
+// (w[cb][i] = its 16 bytes for instruction i, read straight from the 8-bit
+// tile layout) is already the B operand set; "decoding" copies it into B,
+// which register allocation may turn into nothing.
+struct WStep8 {
+    v4i w[2][4];
+};
+struct DecW8 {
+    using Raw = WStep8;
+    static constexpr bool kW8 = true;
+    static constexpr int kLoads = 8;
+    struct Params {};
+    struct Tmp {};
+    static constexpr int kParamOps = 0;
+    static constexpr int kOps = 2;
+
+    template <int K_>
+    __device__ __forceinline__ static void param_step(const Raw&, int, Params&) {}
+
+    template <int I, int OP>
+    __device__ __forceinline__ static void step(Tmp&, const Raw& w, const Params&,
+                                                v4i (&B)[2][4]) {
+        B[OP][I] = w.w[OP][I];
+    }
+};
+
 template <class DEC>
-__device__ __forceinline__ void dec_params(const WStep32& w, int tb, typename DEC::Params& p) {
+__device__ __forceinline__ void dec_params(const typename DEC::Raw& w, int tb,
+                                           typename DEC::Params& p) {
     static_for<DEC::kParamOps>([&](auto k) { DEC::template param_step<decltype(k)::value>(w, tb, p); });
 }
 
 template <class DEC, int I>
-__device__ __forceinline__ void dec_group(const WStep32& w, const typename DEC::Params& p,
+__device__ __forceinline__ void dec_group(const typename DEC::Raw& w, const typename DEC::Params& p,
                                           v4i (&B)[2][4]) {
     typename DEC::Tmp tmp;
     static_for<DEC::kOps>([&](auto oc) { DEC::template step<I, decltype(oc)::value>(tmp, w, p, B); });
 }
 
 template <class DEC>
-__device__ __forceinline__ void dec_all(const WStep32& w, int tb, typename DEC::Params& p,
+__device__ __forceinline__ void dec_all(const typename DEC::Raw& w, int tb, typename DEC::Params& p,
                                         v4i (&B)[2][4]) {
     dec_params<DEC>(w, tb, p);
     dec_group<DEC, 0>(w, p, B);
@@ -208,7 +242,8 @@ __device__ __forceinline__ void dec_all(const WStep32& w, int tb, typename DEC::
 
 }  // namespace
 
-// DEC: weight decoder policy (DecLQQ; DecAffine16 for the ablation).
+// DEC: weight decoder policy (DecLQQ; DecAffine16 for the ablation; DecW8
+// for the W8A8 comparison, whose `wq` is the 8-bit tile layout).
 // COARSE: decode each K-step's weights in one block after that step's
 // matrix-core instructions instead of interleaving them (ablation of the
 // fine-grained overlap).
@@ -243,7 +278,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
         const int e = blockIdx.y;
         row_lo = min(max(offsets[e], 0), M);
         row_hi = min(max(offsets[e + 1], row_lo), M);
-        wq += (size_t)e * N * (K / 2);
+        wq += (size_t)e * N * (DEC::kW8 ? K : K / 2);
         s_u8 += (size_t)e * N * (K / GROUP);
         a_u8 += (size_t)e * N * (K / GROUP);
         sw += (size_t)e * N;
@@ -275,15 +310,25 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
 
     // ---- weights of this wave: tiles nt0 .. nt0+3 (one parameter panel)
     const int nt0 = n0 / kTileN;
-    const __amdgpu_buffer_rsrc_t w_rsrc = buf_rsrc(wq, (unsigned)((size_t)N * K / 2));
+    const __amdgpu_buffer_rsrc_t w_rsrc =
+        buf_rsrc(wq, (unsigned)((size_t)N * K / (DEC::kW8 ? 1 : 2)));
     const __amdgpu_buffer_rsrc_t s_rsrc = buf_rsrc(s_u8, (unsigned)((size_t)N * K / GROUP));
     const __amdgpu_buffer_rsrc_t a_rsrc = buf_rsrc(a_u8, (unsigned)((size_t)N * K / GROUP));
     const unsigned wvoff = (unsigned)(tb * KTall) * kTileBytes + (unsigned)(32 * h + r) * 16u;
     const unsigned pvoff = 4u * (unsigned)r + (GROUP == 64 ? 64u * (unsigned)h : 0u);
     const unsigned ppanel = 64u * (unsigned)(n0 >> 6) * (unsigned)groups;
-    auto w_load = [&](int kt, int part_i, WStep32& ws) {  // part_i 0..5
+    // 8-bit layout: tile (nt, kt) of 2 KiB; the bytes for instruction i of
+    // lane (c, h) (K columns 64h + 16i .. +15 of row r) sit at
+    // 1024 (i & 1) + 256 (2h + i / 2) + 16 r inside it.
+    const unsigned w8voff = (unsigned)(tb * KTall) * 2048u + 512u * (unsigned)h + 16u * (unsigned)r;
+    auto w_load = [&](int kt, int part_i, typename DEC::Raw& ws) {  // part_i < DEC::kLoads
         const int ktg = kt0 + kt;
-        if (part_i < 4) {
+        if constexpr (DEC::kW8) {
+            const int cb = part_i >> 2, i = part_i & 3;
+            ws.w[cb][i] = buf_load16(w_rsrc, w8voff,
+                                     (unsigned)(((nt0 + 2 * cb) * KTall + ktg) * 2048 +
+                                                1024 * (i & 1) + 256 * (i >> 1)));
+        } else if (part_i < 4) {
             const int cb = part_i >> 1, e = part_i & 1;
             ws.w[cb][e] = buf_load16(
                 w_rsrc, wvoff, (unsigned)(((nt0 + 2 * cb) * KTall + ktg) * kTileBytes + e * 256));
@@ -310,7 +355,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     // ---- prologue: X(0) -> LDS xs0, X(1) staged; W(0) dequantised fully,
     // W(1) raw; A ring primed with step 0's first four operands.
     v4i xe[CPT], xo[CPT];   // X staging for even / odd steps (X(kt) in set kt%2)
-    WStep32 we, wo;         // raw weights for even / odd steps
+    typename DEC::Raw we, wo;  // raw weights for even / odd steps
     typename DEC::Params pp;  // parameters of the raw set being decoded
     v4i B[2][4];
     v4i ring[8];
@@ -322,9 +367,9 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
 #pragma unroll
     for (int p = 0; p < CPT; ++p) xo[p] = x_load(k1, p);
 #pragma unroll
-    for (int pi = 0; pi < 6; ++pi) w_load(0, pi, we);
+    for (int pi = 0; pi < DEC::kLoads; ++pi) w_load(0, pi, we);
 #pragma unroll
-    for (int pi = 0; pi < 6; ++pi) w_load(kw1, pi, wo);
+    for (int pi = 0; pi < DEC::kLoads; ++pi) w_load(kw1, pi, wo);
 #pragma unroll
     for (int p = 0; p < CPT; ++p) *reinterpret_cast<v4i*>(xs0 + xlds0 + p * 4096) = xe[p];
     dec_all<DEC>(we, tb, pp, B);
@@ -348,7 +393,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     //   before the last 4  barrier, then step kt+1's first four A reads; the
     //                      last four slots use operands read earlier.
     auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, v4i (&xcur)[CPT],
-                    v4i (&xnx)[CPT], WStep32& wcur, WStep32& wnx) {
+                    v4i (&xnx)[CPT], typename DEC::Raw& wcur, typename DEC::Raw& wnx) {
         const int k2 = min(kt + 2, KTe - 1), kw2 = min(kt + 2, KT - 1);
         typename DEC::Tmp tmp;
         static_for<SLOTS>([&](auto sc) {
@@ -363,7 +408,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
             mfma32_i8_acc(acc[rb][cb], ring[sI % 8], B[cb][i]);
             if constexpr (cb == 1 && sI + 4 < 4 * RB) ring[(sI + 4) % 8] = read_a(cur, sI + 4);
             if constexpr (s < CPT) xcur[s] = x_load(k2, s);
-            if constexpr (s >= GS && s < GS + 6) w_load(kw2, s - GS, wcur);
+            if constexpr (s >= GS && s < GS + DEC::kLoads) w_load(kw2, s - GS, wcur);
             if constexpr (s >= SLOTS - 4 - CPT && s < SLOTS - 4)
                 *reinterpret_cast<v4i*>(nxt + xlds0 + (s - (SLOTS - 4 - CPT)) * 4096) =
                     xnx[s - (SLOTS - 4 - CPT)];
@@ -517,25 +562,26 @@ hipError_t launch_w4a8_mfma_grouped(const int8_t* X, const float* sx, const uint
     return hipGetLastError();
 }
 
-hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
-                            const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
-                            int out_type, int M, int N, int K, int group, const MfmaPlan& plan,
-                            void* workspace, hipStream_t st) {
+template <class DEC>
+static hipError_t run_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
+                           const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
+                           int out_type, int M, int N, int K, int group, const MfmaPlan& plan,
+                           void* workspace, hipStream_t st) {
     int* part = reinterpret_cast<int*>(workspace);
     if (plan.splits == 1) {
         if (plan.mt == 256) {
-            if (out_type == 1) launch_tile<256, 1, false>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st);
-            else launch_tile<256, 0, false>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st);
+            if (out_type == 1) launch_tile<256, 1, false, DEC>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st);
+            else launch_tile<256, 0, false, DEC>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st);
         } else {
-            if (out_type == 1) launch_tile<128, 1, false>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st);
-            else launch_tile<128, 0, false>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st);
+            if (out_type == 1) launch_tile<128, 1, false, DEC>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st);
+            else launch_tile<128, 0, false, DEC>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st);
         }
         return hipGetLastError();
     }
     if (plan.mt == 256)
-        launch_tile<256, 1, true>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, plan.splits, st);
+        launch_tile<256, 1, true, DEC>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, plan.splits, st);
     else
-        launch_tile<128, 1, true>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, plan.splits, st);
+        launch_tile<128, 1, true, DEC>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, plan.splits, st);
     const size_t quads = ((size_t)M * N) / 4;
     const unsigned blocks = (unsigned)((quads + 255) / 256);
     if (out_type == 1)
@@ -545,6 +591,21 @@ hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
         hipLaunchKernelGGL((splitk_reduce_kernel<0>), dim3(blocks), dim3(256), 0, st, part,
                            plan.splits, M, N, sx, sw, Y);
     return hipGetLastError();
+}
+
+hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
+                            const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
+                            int out_type, int M, int N, int K, int group, const MfmaPlan& plan,
+                            void* workspace, hipStream_t st) {
+    return run_mfma<DecLQQ>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, plan,
+                            workspace, st);
+}
+
+hipError_t launch_w8a8_mfma(const int8_t* X, const float* sx, const int8_t* wq8, const float* sw,
+                            void* Y, int out_type, int M, int N, int K, const MfmaPlan& plan,
+                            void* workspace, hipStream_t st) {
+    return run_mfma<DecW8>(X, sx, reinterpret_cast<const uint8_t*>(wq8), nullptr, nullptr, sw, Y,
+                           out_type, M, N, K, 128, plan, workspace, st);
 }
 
 template <class DEC, bool COARSE>

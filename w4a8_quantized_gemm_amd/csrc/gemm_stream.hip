@@ -47,7 +47,10 @@ __device__ __forceinline__ int xpiece(int R, int c) {
 // re-laid out through a per-wave LDS slot into the MFMA operand layout.
 // The ks partial tiles are summed by all threads of the workgroup in wave
 // order (exact).
-template <int NTW, int D, int OUT, int GROUP, bool LDSP>
+// W8: the W8A8 comparison -- `wq` holds INT8 weights in the 8-bit tile
+// layout (2 KiB per tile, a lane's 32 bytes as two 16-byte halves 1 KiB
+// apart), used as B operands without decode; no group parameters.
+template <int NTW, int D, int OUT, int GROUP, bool LDSP, bool W8 = false>
 __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ s_u8, const uint8_t* __restrict__ a_u8,
@@ -63,7 +66,7 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
         const int e = blockIdx.z;
         row_lo = min(max(offsets[e], 0), M);
         row_hi = min(max(offsets[e + 1], row_lo), M);
-        wq += (size_t)e * N * (K / 2);
+        wq += (size_t)e * N * (W8 ? K : K / 2);
         s_u8 += (size_t)e * N * (K / GROUP);
         a_u8 += (size_t)e * N * (K / GROUP);
         sw += (size_t)e * N;
@@ -93,7 +96,7 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
     const __amdgpu_buffer_rsrc_t x_rsrc =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(X), (short)0, M * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint8_t*>(wq), (short)0, (int)((size_t)N * K / 2), 0x00020000);
+        const_cast<uint8_t*>(wq), (short)0, (int)((size_t)N * K / (W8 ? 1 : 2)), 0x00020000);
     const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(s_u8), (short)0, (int)((size_t)N * K / GROUP), 0x00020000);
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -121,20 +124,32 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
     const int xw0 = xpiece(lane >> 3, lane & 7), xw1 = xpiece(8 + (lane >> 3), lane & 7);
     const int xr0 = xpiece(r, 2 * G), xr1 = xpiece(r, 2 * G + 1);
 
+    constexpr int WPT = W8 ? 2 : 1;  // 16-byte weight loads per lane and tile
     struct Stage {
         v4i x0, x1;
-        v4i w[NTW];
+        v4i w[NTW * WPT];
     };
     auto issue = [&](int kt, Stage& st) {
         const unsigned so = (unsigned)(kt * kTileK);
         st.x0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xvoff, so, 0));
         st.x1 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xvoff8, so, 0));
 #pragma unroll
-        for (int t = 0; t < NTW; ++t)
-            st.w[t] = __builtin_bit_cast(
-                v4i, __builtin_amdgcn_raw_buffer_load_b128(
-                         w_rsrc, wvoff, (unsigned)(((size_t)(nt0 + t) * KT + kt) * kTileBytes),
-                         kNonTemporal));
+        for (int t = 0; t < NTW; ++t) {
+            if constexpr (W8) {
+#pragma unroll
+                for (int u = 0; u < 2; ++u)
+                    st.w[2 * t + u] = __builtin_bit_cast(
+                        v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                                 w_rsrc, wvoff,
+                                 (unsigned)(((size_t)(nt0 + t) * KT + kt) * 2048 + 1024 * u),
+                                 kNonTemporal));
+            } else {
+                st.w[t] = __builtin_bit_cast(
+                    v4i, __builtin_amdgcn_raw_buffer_load_b128(
+                             w_rsrc, wvoff, (unsigned)(((size_t)(nt0 + t) * KT + kt) * kTileBytes),
+                             kNonTemporal));
+            }
+        }
     };
     auto params = [&](int kt, int t, unsigned& s, unsigned& a) {
         const int j = kt * (kTileK / GROUP) + gsub;
@@ -167,6 +182,11 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
         }
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
+            if constexpr (W8) {
+                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x0, S.w[2 * t], acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1, S.w[2 * t + 1], acc[t], 0, 0, 0);
+                continue;
+            }
             unsigned s, a;
             params(kt, t, s, a);
             const u16x2 s2 = u16x2{(unsigned short)s, (unsigned short)s};
@@ -195,7 +215,7 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
 
     // Parameter copy, behind the first weight loads (panels p0 .. p0+np-1
     // are contiguous in the panel-order arrays).
-    if (LDSP) {
+    if (LDSP && !W8) {
         const int n16 = np * groups * 4;  // 16-byte pieces per array
         const size_t base = (size_t)p0 * groups * 64;
         for (int q = tid; q < n16; q += blockDim.x) {
@@ -396,6 +416,37 @@ hipError_t launch_w4a8_stream(const int8_t* X, const float* sx, const uint8_t* w
         default: W4A8_NTW(1, 3);
     }
 #undef W4A8_NTW
+}
+
+template <int NTW, int D>
+static hipError_t w8a8_stream_ntw(const int8_t* X, const float* sx, const int8_t* wq8,
+                                  const float* sw, void* Y, int out_type, int M, int N, int K,
+                                  int ks, hipStream_t st) {
+    dim3 grid(N / (kTileN * NTW), (M + 15) / 16, 1);
+    dim3 block(64 * ks);
+    const size_t xbytes = (size_t)ks * 2048;
+    const size_t rbytes = (size_t)ks * NTW * 256 * sizeof(int);
+    const size_t lds = xbytes > rbytes ? xbytes : rbytes;
+    const uint8_t* w = reinterpret_cast<const uint8_t*>(wq8);
+    if (out_type == 1)
+        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, 1, 128, false, true>), grid, block, lds, st,
+                           X, sx, w, nullptr, nullptr, sw, Y, M, N, K, ks, nullptr);
+    else
+        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, 0, 128, false, true>), grid, block, lds, st,
+                           X, sx, w, nullptr, nullptr, sw, Y, M, N, K, ks, nullptr);
+    return hipGetLastError();
+}
+
+hipError_t launch_w8a8_stream(const int8_t* X, const float* sx, const int8_t* wq8,
+                              const float* sw, void* Y, int out_type, int M, int N, int K,
+                              StreamCfg cfg, hipStream_t st) {
+    switch (cfg.nt_per_wave) {
+        case 7: return w8a8_stream_ntw<7, 2>(X, sx, wq8, sw, Y, out_type, M, N, K, cfg.ks, st);
+        case 4: return w8a8_stream_ntw<4, 3>(X, sx, wq8, sw, Y, out_type, M, N, K, cfg.ks, st);
+        case 3: return w8a8_stream_ntw<3, 3>(X, sx, wq8, sw, Y, out_type, M, N, K, cfg.ks, st);
+        case 2: return w8a8_stream_ntw<2, 4>(X, sx, wq8, sw, Y, out_type, M, N, K, cfg.ks, st);
+        default: return w8a8_stream_ntw<1, 3>(X, sx, wq8, sw, Y, out_type, M, N, K, cfg.ks, st);
+    }
 }
 
 template <int NTW, int GROUP>

@@ -75,6 +75,17 @@ hipError_t launch_w4fp8_stream(const uint8_t* X, const float* sx, const uint8_t*
                                const float* sw, void* Y, int out_type, int M, int N, int K,
                                StreamCfg cfg, hipStream_t st);
 
+// W8A8 comparison: per-channel INT8 weights in the 8-bit tile layout.
+hipError_t launch_pack_w8(const float* W, int N, int K, int8_t* wq8, float* sw, hipStream_t st);
+
+hipError_t launch_w8a8_mfma(const int8_t* X, const float* sx, const int8_t* wq8, const float* sw,
+                            void* Y, int out_type, int M, int N, int K, const MfmaPlan& plan,
+                            void* workspace, hipStream_t st);
+
+hipError_t launch_w8a8_stream(const int8_t* X, const float* sx, const int8_t* wq8,
+                              const float* sw, void* Y, int out_type, int M, int N, int K,
+                              StreamCfg cfg, hipStream_t st);
+
 // Folded per-group FP8 weights (fsc [K/group][N] factors, tsc[0] tensor scale).
 hipError_t launch_w4fp8g_mfma(const uint8_t* X, const float* sx, const uint8_t* wq,
                               const float* fsc, const float* tsc, void* Y, int out_type, int M,

@@ -132,6 +132,32 @@ __global__ __launch_bounds__(256) void int4_pack_kernel(const float* __restrict_
 }
 
 // ---------------------------------------------------------------------------
+// W8A8 comparison: the per-channel INT8 codes of the first quantisation
+// level in the 8-bit tile layout.  One thread per 16-byte piece: piece
+// (nt, kt, u, G, r) = row 16nt + r, columns 128kt + 32G + 16u .. +15, stored
+// at byte 2048 (nt KT + kt) + 1024 u + 16 (16 G + r).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void w8_pack_kernel(const float* __restrict__ W,
+                                                      const float* __restrict__ sw, int N, int K,
+                                                      int8_t* __restrict__ wq8) {
+    const long long p = (long long)blockIdx.x * 256 + threadIdx.x;
+    if (p >= (long long)N * K / 16) return;
+    const int KT = K / kTileK;
+    const int lane = (int)(p & 63), u = (int)((p >> 6) & 1);
+    const long long tile = p >> 7;  // nt * KT + kt
+    const int nt = (int)(tile / KT), kt = (int)(tile % KT);
+    const int r = lane & 15, G = lane >> 4;
+    const int n = nt * kTileN + r;
+    const float* w = W + (size_t)n * K + (size_t)kt * kTileK + 32 * G + 16 * u;
+    const float s = sw[n];
+    unsigned b[4] = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < 16; ++j)
+        b[j >> 2] |= ((unsigned)quant_sym(w[j], s, 127.0f) & 0xFFu) << (8 * (j & 3));
+    *reinterpret_cast<v4i*>(wq8 + (size_t)tile * 2048 + 1024 * u + 16 * lane) =
+        v4i{(int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+// ---------------------------------------------------------------------------
 // INT4 with per-group scales folded into FP8 weights and a per-tensor
 // rescale (FireQ, arXiv 2505.20839, abstract; the formulas are this
 // library's reading): s_g = max|group| / 7, t = max|W| / 448, f = s_g / t,
@@ -321,6 +347,14 @@ hipError_t launch_pack_int4(const float* W, int N, int K, uint8_t* wq, float* sw
     long long threads = (long long)N * (K / 8);
     unsigned blocks = (unsigned)((threads + 255) / 256);
     hipLaunchKernelGGL(int4_pack_kernel, dim3(blocks), dim3(256), 0, st, W, sw, N, K, wq);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_w8(const float* W, int N, int K, int8_t* wq8, float* sw, hipStream_t st) {
+    hipLaunchKernelGGL(row_scale_kernel, dim3(N), dim3(256), 0, st, W, K, 127.0f, sw);
+    const long long pieces = (long long)N * K / 16;
+    const unsigned blocks = (unsigned)((pieces + 255) / 256);
+    hipLaunchKernelGGL(w8_pack_kernel, dim3(blocks), dim3(256), 0, st, W, sw, N, K, wq8);
     return hipGetLastError();
 }
 
