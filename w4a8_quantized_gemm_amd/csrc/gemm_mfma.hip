@@ -258,8 +258,8 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     constexpr int SLOTS = 8 * RB;      // matrix-core instructions per wave per K-step
     constexpr int GS = SLOTS / 4;      // slots per instruction group i
     constexpr int DQ = (DEC::kParamOps + DEC::kOps + GS - 1) / GS;  // decode steps per slot
-    __shared__ __attribute__((aligned(1024))) uint8_t xs0[MT * 128];
-    __shared__ __attribute__((aligned(1024))) uint8_t xs1[MT * 128];
+    constexpr unsigned XB = MT * 128;  // bytes of one X tile (MT rows x 128 K)
+    __shared__ __attribute__((aligned(1024))) uint8_t xs[3 * XB];  // X(kt), X(kt+1), X(kt+2)
     __shared__ float sxs[MT];
 
     const int tid = threadIdx.x;
@@ -294,15 +294,20 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     const int KTe = KT + (KT & 1);
     const int groups = K / GROUP;
 
-    // ---- X: chunk p of this thread is row (tid>>3) + 32p, 16-byte column
-    // tid & 7, stored in LDS slot col ^ xswz(row & 15) (row & 15 is the same
-    // for all p).  Rows >= M lie past the end of the buffer and read as 0.
+    // ---- X goes from global memory straight into one of three LDS tiles
+    // (no register round trip).  Tile row R keeps its 16-byte column chunk
+    // k in slot k ^ xswz(R & 15).  Wave w's load p (p < CPT) fills rows
+    // 32p + 8w .. +7 (1 KiB): lane l writes slot l % 8 of row
+    // 32p + 8w + l / 8, so it fetches that row's chunk (l % 8) ^ xswz(row & 15)
+    // (row & 15 does not depend on p).  Rows >= M lie past the end of the
+    // buffer and read as 0.
     const __amdgpu_buffer_rsrc_t xr_rsrc = buf_rsrc(X, (unsigned)M * (unsigned)K);
-    const int xrow0 = tid >> 3, xcol = tid & 7;
+    const int xr = 8 * wave + (lane >> 3);
+    const int xc = (lane & 7) ^ xswz(xr & 15);
     const unsigned xvoff =
-        (unsigned)(m0 + xrow0) * (unsigned)K + (unsigned)(xcol * 16) + (unsigned)(kt0 * kTileK);
+        (unsigned)(m0 + xr) * (unsigned)K + (unsigned)(xc * 16) + (unsigned)(kt0 * kTileK);
     const unsigned xrowstep = 32u * (unsigned)K;
-    const int xlds0 = xrow0 * 128 + ((xcol ^ xswz(xrow0 & 15)) * 16);
+    const unsigned xsbase = lds_addr(xs);
     // A operand (row block rb, instruction i): row 32rb + c, column 4h + i.
     int aoff[4];
 #pragma unroll
@@ -338,11 +343,11 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
             else ws.adw = buf_load4(a_rsrc, pvoff, jo);
         }
     };
-    auto x_load = [&](int kt, int p) {  // kt >= KT: offset past the buffer, reads 0
-        const bool live = kt < KT;  // wave-uniform: one load, selected offsets
+    auto x_load = [&](int kt, int p, unsigned buf) {  // into LDS tile at byte `buf`
+        const bool live = kt < KT;  // kt >= KT: offset past the buffer, reads 0
         const unsigned vo = live ? xvoff + (unsigned)p * xrowstep : 0xFFFFFFF0u;
         const unsigned so = live ? (unsigned)(kt * kTileK) : 0u;
-        return buf_load16(xr_rsrc, vo, so);
+        buf_load16_lds(xr_rsrc, vo, so, xsbase + buf + (unsigned)(4 * p + wave) * 1024u);
     };
 
     v16i acc[RB][2];
@@ -352,9 +357,8 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
         acc[rb][1] = v16i{};
     }
 
-    // ---- prologue: X(0) -> LDS xs0, X(1) staged; W(0) dequantised fully,
+    // ---- prologue: X(0), X(1) -> LDS tiles 0, 1; W(0) dequantised fully,
     // W(1) raw; A ring primed with step 0's first four operands.
-    v4i xe[CPT], xo[CPT];   // X staging for even / odd steps (X(kt) in set kt%2)
     typename DEC::Raw we, wo;  // raw weights for even / odd steps
     typename DEC::Params pp;  // parameters of the raw set being decoded
     v4i B[2][4];
@@ -362,56 +366,66 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     // X of the padding step reads as zero; its weights (and factors) are
     // those of the last real step, so no load leaves this split's K range.
     const int k1 = min(1, KTe - 1), kw1 = min(1, KT - 1);
+    unsigned bc = 0, bn = XB, bd = 2 * XB;  // LDS tiles of X(kt), X(kt+1), X(kt+2)
 #pragma unroll
-    for (int p = 0; p < CPT; ++p) xe[p] = x_load(0, p);
+    for (int p = 0; p < CPT; ++p) x_load(0, p, bc);
 #pragma unroll
-    for (int p = 0; p < CPT; ++p) xo[p] = x_load(k1, p);
+    for (int p = 0; p < CPT; ++p) x_load(k1, p, bn);
 #pragma unroll
     for (int pi = 0; pi < DEC::kLoads; ++pi) w_load(0, pi, we);
 #pragma unroll
     for (int pi = 0; pi < DEC::kLoads; ++pi) w_load(kw1, pi, wo);
-#pragma unroll
-    for (int p = 0; p < CPT; ++p) *reinterpret_cast<v4i*>(xs0 + xlds0 + p * 4096) = xe[p];
     dec_all<DEC>(we, tb, pp, B);
+    // X(0) and X(1) were issued before W(0) and W(1): once at most the W(1)
+    // loads are outstanding, every wave's part of the two X tiles is in LDS.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(DEC::kLoads, 0));
     __syncthreads();
-    auto read_a = [&](const uint8_t* buf, int sI) {  // sI = RB*i + rb
-        return *reinterpret_cast<const v4i*>(buf + (sI % RB) * 4096 + aoff[sI / RB]);
+    auto read_a = [&](unsigned buf, int sI) {  // sI = RB*i + rb
+        return *reinterpret_cast<const v4i*>(xs + buf + (sI % RB) * 4096 + aoff[sI / RB]);
     };
 #pragma unroll
-    for (int q = 0; q < 4; ++q) ring[q] = read_a(xs0, q);
+    for (int q = 0; q < 4; ++q) ring[q] = read_a(bc, q);
 
     // ---- one K-step, SLOTS matrix-core slots.  Slot s: instruction group
     // i = s / GS, row block rb = (s/2) % RB, channel block cb = s % 2.
-    // Entering step kt: LDS `cur` = X(kt); ring holds A for the first
-    // slots; B[*][0..2] = W(kt) operands and B[*][3] is produced during
-    // group 0 from `wcur` (raw W(kt), parameters pp); `xnx` = X(kt+1)
-    // staged; `wnx` = raw W(kt+1).
-    //   group 0 slots      X(kt+2) -> xcur; B[*][3] of step kt
+    // Entering step kt: LDS tile `cur` = X(kt), `nxt` = X(kt+1) (loads in
+    // flight), `dst` free (its X(kt-1) was last read before the previous
+    // barrier); ring holds A for the first slots; B[*][0..2] = W(kt)
+    // operands and B[*][3] is produced during group 0 from `wcur` (raw W(kt),
+    // parameters pp); `wnx` = raw W(kt+1).
+    //   group 0 slots      B[*][3] of step kt
     //   group 1 slots      W(kt+2) -> wcur; parameters of wnx, B[*][0] of kt+1
     //   groups 2, 3        B[*][1], B[*][2] of step kt+1
-    //   last 4+CPT slots   X(kt+1) -> LDS `nxt` (before the last 4)
-    //   before the last 4  barrier, then step kt+1's first four A reads; the
-    //                      last four slots use operands read earlier.
-    auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, v4i (&xcur)[CPT],
-                    v4i (&xnx)[CPT], typename DEC::Raw& wcur, typename DEC::Raw& wnx) {
+    //   CPT slots from XS  X(kt+2) -> LDS `dst`, after this step's first use
+    //                      of wnx: the compiler does not see these loads, so
+    //                      its wait before that use covers only loads a
+    //                      step old
+    //   before the last 4  wait for this wave's X(kt+1) loads (CPT + kLoads
+    //                      loads were issued after them), barrier, then step
+    //                      kt+1's first four A reads; the last four slots
+    //                      use operands read earlier.
+    auto step = [&](int kt, unsigned cur, unsigned nxt, unsigned dst, typename DEC::Raw& wcur,
+                    typename DEC::Raw& wnx) {
         const int k2 = min(kt + 2, KTe - 1), kw2 = min(kt + 2, KT - 1);
+        constexpr int XS = GS + DEC::kLoads;  // first X load slot
+        static_assert(XS + CPT <= SLOTS - 4, "X loads must precede the barrier");
         typename DEC::Tmp tmp;
         static_for<SLOTS>([&](auto sc) {
             constexpr int s = decltype(sc)::value;
             constexpr int sI = s / 2, i = sI / RB, rb = sI % RB, cb = s % 2;
             constexpr int g = s / GS, sg = s % GS;
             if constexpr (s == SLOTS - 4) {
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(CPT + DEC::kLoads, 0));
                 __syncthreads();
 #pragma unroll
                 for (int q = 0; q < 4; ++q) ring[q] = read_a(nxt, q);
             }
             mfma32_i8_acc(acc[rb][cb], ring[sI % 8], B[cb][i]);
             if constexpr (cb == 1 && sI + 4 < 4 * RB) ring[(sI + 4) % 8] = read_a(cur, sI + 4);
-            if constexpr (s < CPT) xcur[s] = x_load(k2, s);
             if constexpr (s >= GS && s < GS + DEC::kLoads) w_load(kw2, s - GS, wcur);
-            if constexpr (s >= SLOTS - 4 - CPT && s < SLOTS - 4)
-                *reinterpret_cast<v4i*>(nxt + xlds0 + (s - (SLOTS - 4 - CPT)) * 4096) =
-                    xnx[s - (SLOTS - 4 - CPT)];
+            if constexpr (s >= XS && s < XS + CPT) x_load(k2, s - XS, dst);
             if constexpr (!COARSE) {
                 constexpr int PO = DEC::kParamOps, NO = DEC::kOps;
                 static_for<DQ>([&](auto dc) {
@@ -433,11 +447,16 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     };
 
     for (int kt = 0; kt < KTe; kt += 2) {
-        step(kt, xs0, xs1, xe, xo, we, wo);
-        step(kt + 1, xs1, xs0, xo, xe, wo, we);
+        step(kt, bc, bn, bd, we, wo);
+        step(kt + 1, bn, bd, bc, wo, we);
+        const unsigned t0 = bc;  // next pair: X(kt+2) in bd, X(kt+3) in bc
+        bc = bd;
+        bd = bn;
+        bn = t0;
     }
     mfma32_drain(acc);
-    __syncthreads();  // all waves done with the X buffers
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));  // the last steps' X loads
+    __syncthreads();  // all waves done with the X tiles
 
     // ---- epilogue.  Accumulator (rb, cb) register v of lane (c, h): row
     // 32rb + 8(v/4) + 4h + (v%4), channel n0 + 32cb + c.  Values go to a
@@ -450,7 +469,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     __syncthreads();
     constexpr int EB = SCALED ? 2 : 4;       // output element bytes
     constexpr int ROWB = 64 * EB;             // bytes per staged row
-    uint8_t* stage = xs0 + wave * (32 * ROWB);
+    uint8_t* stage = xs + wave * (32 * ROWB);
     uint8_t* out = PARTIAL ? reinterpret_cast<uint8_t*>(part + (size_t)ks * M * N)
                            : reinterpret_cast<uint8_t*>(Y);
 #pragma unroll

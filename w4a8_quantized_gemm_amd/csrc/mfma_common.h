@@ -2,6 +2,8 @@
 // W4FP8 e4m3): compile-time loops, buffer loads, the X tile swizzle, the
 // workgroup -> output tile order and the accumulator drain.
 #pragma once
+#include <stdint.h>
+
 #include <utility>
 
 #include "device_common.h"
@@ -36,6 +38,35 @@ __device__ __forceinline__ v4i buf_load16(__amdgpu_buffer_rsrc_t r, unsigned vof
 }
 __device__ __forceinline__ unsigned buf_load4(__amdgpu_buffer_rsrc_t r, unsigned voff, unsigned soff) {
     return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+
+// 32-bit LDS address of a pointer into a __shared__ object.
+__device__ __forceinline__ unsigned lds_addr(const void* p) {
+    return (unsigned)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Global -> LDS load of 16 bytes per lane, no register round trip: lane l's
+// bytes land at LDS address `lds` + 16 l (`lds` wave-uniform); a lane whose
+// offset lies outside the buffer writes zeros.  Written as assembly so the
+// compiler does not track it: its own load-counter waits stay exact for the
+// register loads, and the kernel waits for these loads itself (a
+// s_waitcnt on the load counter before the barrier that publishes the
+// tile).  M0 carries the LDS address; the compiler keeps nothing in M0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void buf_load16_lds(__amdgpu_buffer_rsrc_t r, unsigned voff,
+                                               unsigned soff, unsigned lds) {
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt immediate: load counter <= vm and LDS/scalar counter <= lgkm
+// (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4 left at 7).
+constexpr int waitcnt_imm(int vm, int lgkm) {
+    return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14);
 }
 
 // Wait states between the last accumulation written in inline assembly and
