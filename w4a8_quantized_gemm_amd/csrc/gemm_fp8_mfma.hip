@@ -114,8 +114,8 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
     constexpr int SLOTS = 4 * RB;      // matrix-core instructions per wave per K-step
     constexpr int GS = SLOTS / 2;      // slots per instruction group j
     constexpr int DQ = (64 + GS - 1) / GS;  // conversion steps per slot
-    __shared__ __attribute__((aligned(1024))) uint8_t xs0[MT * 128];
-    __shared__ __attribute__((aligned(1024))) uint8_t xs1[MT * 128];
+    constexpr unsigned XB = MT * 128;  // bytes of one X tile (MT rows x 128 K)
+    __shared__ __attribute__((aligned(1024))) uint8_t xs[3 * XB];  // X(kt), X(kt+1), X(kt+2)
     __shared__ float sxs[MT];
 
     const int tid = threadIdx.x;
@@ -135,15 +135,19 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
     // gets one more step whose X tile reads as zero (contributing exactly 0).
     const int KTe = KT + (KT & 1);
 
-    // ---- X: chunk p of this thread is row (tid>>3) + 32p, 16-byte column
-    // tid & 7, in LDS slot col ^ xswz(row & 15).  Rows >= M lie past the end
-    // of the buffer and read as 0.
+    // ---- X goes from global memory straight into one of three LDS tiles.
+    // Tile row R keeps its 16-byte column chunk k in slot k ^ xswz(R & 15).
+    // Wave w's load p (p < CPT) fills rows 32p + 8w .. +7: lane l writes
+    // slot l % 8 of row 32p + 8w + l / 8, so it fetches that row's chunk
+    // (l % 8) ^ xswz(row & 15).  Rows >= M lie past the end of the buffer
+    // and read as 0.
     const __amdgpu_buffer_rsrc_t xr_rsrc = buf_rsrc(X, (unsigned)M * (unsigned)K);
-    const int xrow0 = tid >> 3, xcol = tid & 7;
+    const int xr = 8 * wave + (lane >> 3);
+    const int xc = (lane & 7) ^ xswz(xr & 15);
     const unsigned xvoff =
-        (unsigned)(m0 + xrow0) * (unsigned)K + (unsigned)(xcol * 16) + (unsigned)(kt0 * kTileK);
+        (unsigned)(m0 + xr) * (unsigned)K + (unsigned)(xc * 16) + (unsigned)(kt0 * kTileK);
     const unsigned xrowstep = 32u * (unsigned)K;
-    const int xlds0 = xrow0 * 128 + ((xcol ^ xswz(xrow0 & 15)) * 16);
+    const unsigned xsbase = lds_addr(xs);
     // A operand of instruction group j: row 32rb + c, chunks 4h+2j, 4h+2j+1.
     int aoff[2][2];
 #pragma unroll
@@ -161,11 +165,11 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
         ws.w[cb][j] = buf_load16(
             w_rsrc, wvoff, (unsigned)(((nt0 + 2 * cb) * KTall + ktg) * kTileBytes + j * 256));
     };
-    auto x_load = [&](int kt, int p) {  // kt >= KT: offset past the buffer, reads 0
-        const bool live = kt < KT;  // wave-uniform: one load, selected offsets
+    auto x_load = [&](int kt, int p, unsigned buf) {  // into LDS tile at byte `buf`
+        const bool live = kt < KT;  // kt >= KT: offset past the buffer, reads 0
         const unsigned vo = live ? xvoff + (unsigned)p * xrowstep : 0xFFFFFFF0u;
         const unsigned so = live ? (unsigned)(kt * kTileK) : 0u;
-        return buf_load16(xr_rsrc, vo, so);
+        buf_load16_lds(xr_rsrc, vo, so, xsbase + buf + (unsigned)(4 * p + wave) * 1024u);
     };
     // Folded factors, group-major fsc[g][N]: K-step ktg of channel n lies in
     // group ktg * (128 / GROUP) + (GROUP == 64 ? h : 0).
@@ -196,59 +200,71 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
         acc[rb][1] = v16f{};
     }
 
-    // ---- prologue: X(0) -> LDS xs0, X(1) staged; B[*][0] of step 0
+    // ---- prologue: X(0), X(1) -> LDS tiles 0, 1; B[*][0] of step 0
     // converted, W(0) kept raw for B[*][1], W(1) raw; A ring primed.
-    v4i xe[CPT], xo[CPT];  // X staging for even / odd steps
     F8Step we, wo;         // raw weights for even / odd steps
     v8i B[2][2];
     v8i ring[4];
     // X of the padding step reads as zero; its weights (and factors) are
     // those of the last real step, so no load leaves this split's K range.
     const int k1 = min(1, KTe - 1), kw1 = min(1, KT - 1);
+    unsigned bc = 0, bn = XB, bd = 2 * XB;  // LDS tiles of X(kt), X(kt+1), X(kt+2)
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) x_load(0, p, bc);
+#pragma unroll
+    for (int p = 0; p < CPT; ++p) x_load(k1, p, bn);
     if constexpr (FOLD) {
         f_load(0, fe);
         f_load(kw1, fo);
     }
 #pragma unroll
-    for (int p = 0; p < CPT; ++p) xe[p] = x_load(0, p);
-#pragma unroll
-    for (int p = 0; p < CPT; ++p) xo[p] = x_load(k1, p);
-#pragma unroll
     for (int pi = 0; pi < 4; ++pi) w_load(0, pi, we);
 #pragma unroll
     for (int pi = 0; pi < 4; ++pi) w_load(kw1, pi, wo);
-#pragma unroll
-    for (int p = 0; p < CPT; ++p) *reinterpret_cast<v4i*>(xs0 + xlds0 + p * 4096) = xe[p];
     if constexpr (FOLD) {
         e4m3_fold_table(fe[0], le.lo[0], le.hi[0]);
         e4m3_fold_table(fe[1], le.lo[1], le.hi[1]);
     }
     f8_all<0>(we, le, sgn, B);
+    // X(0) and X(1) were issued first: once at most the W(1) loads are
+    // outstanding, every wave's part of the two X tiles is in LDS.
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(4, 0));
     __syncthreads();
-    auto read_a = [&](const uint8_t* buf, int sI) {  // sI = RB*j + rb
+    auto read_a = [&](unsigned buf, int sI) {  // sI = RB*j + rb
         const int j = sI / RB, rb = sI % RB;
-        const v4i lo = *reinterpret_cast<const v4i*>(buf + rb * 4096 + aoff[j][0]);
-        const v4i hi = *reinterpret_cast<const v4i*>(buf + rb * 4096 + aoff[j][1]);
+        const v4i lo = *reinterpret_cast<const v4i*>(xs + buf + rb * 4096 + aoff[j][0]);
+        const v4i hi = *reinterpret_cast<const v4i*>(xs + buf + rb * 4096 + aoff[j][1]);
         return v8i{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
     };
-    ring[0] = read_a(xs0, 0);
-    ring[1] = read_a(xs0, 1);
+    ring[0] = read_a(bc, 0);
+    ring[1] = read_a(bc, 1);
 
     // ---- one K-step, SLOTS matrix-core slots.  Slot s: group j = s / GS,
     // row block rb = (s/2) % RB, channel block cb = s % 2.  Entering step
-    // kt: LDS `cur` = X(kt); ring holds A for the first two operand slots;
-    // B[*][0] = W(kt) operands; `wcur` = raw W(kt), `xnx` = X(kt+1) staged,
-    // `wnx` = raw W(kt+1).
-    //   group 0 slots      X(kt+2) -> xcur; B[*][1] of step kt from wcur
+    // kt: LDS tile `cur` = X(kt), `nxt` = X(kt+1) (loads possibly in
+    // flight), `dst` free (X(kt-1), last read before the previous barrier);
+    // ring holds A for the first two operand slots; B[*][0] = W(kt)
+    // operands; `wcur` = raw W(kt), `wnx` = raw W(kt+1).
+    //   group 0 slots      B[*][1] of step kt from wcur
     //   group 1 slots      W(kt+2) -> wcur; B[*][0] of step kt+1 from wnx
-    //   last 4+CPT slots   X(kt+1) -> LDS `nxt` (before the last 4)
-    //   before the last 4  barrier, then step kt+1's first two A reads.
+    //   CPT slots from XS  X(kt+2) -> LDS `dst`, after this step's first use
+    //                      of wnx (the compiler does not see these loads, so
+    //                      its wait before that use covers only older ones);
+    //                      with 128-row tiles some follow the barrier
+    //   before the last 4  wait for this wave's X(kt+1) loads, barrier, then
+    //                      step kt+1's first two A reads.
     // Folded format: `lcur` = table of step kt (group 0), `lnx` = table of
     // step kt+1 (group 1), built from `fnx` in the last two group-0 slots;
     // f(kt+2) -> `fcur` at slot 0.
-    auto step = [&](int kt, const uint8_t* cur, uint8_t* nxt, v4i (&xcur)[CPT],
-                    v4i (&xnx)[CPT], F8Step& wcur, F8Step& wnx, F8Lut& lcur, F8Lut& lnx,
-                    float (&fcur)[2], float (&fnx)[2]) {
+    constexpr int XS = GS + 4;  // first X load slot
+    static_assert(XS + CPT <= SLOTS, "X loads fit in the step");
+    // Loads issued after a step's last X load, up to the next step's
+    // barrier: that step's factor, weight and pre-barrier X loads.
+    constexpr int XPRE = (SLOTS - 4 - XS) < 0 ? 0 : ((SLOTS - 4 - XS) > CPT ? CPT : (SLOTS - 4 - XS));
+    constexpr int XWAIT = (FOLD ? 2 : 0) + 4 + XPRE;
+    auto step = [&](int kt, unsigned cur, unsigned nxt, unsigned dst, F8Step& wcur, F8Step& wnx,
+                    F8Lut& lcur, F8Lut& lnx, float (&fcur)[2], float (&fnx)[2]) {
         const int k2 = min(kt + 2, KTe - 1), kw2 = min(kt + 2, KT - 1);
         F8Tmp tmp;
         static_for<SLOTS>([&](auto sc) {
@@ -256,6 +272,8 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
             constexpr int sI = s / 2, j = sI / RB, rb = sI % RB, cb = s % 2;
             constexpr int g = s / GS, sg = s % GS;
             if constexpr (s == SLOTS - 4) {
+                __builtin_amdgcn_sched_barrier(0);
+                __builtin_amdgcn_s_waitcnt(waitcnt_imm(XWAIT, 0));
                 __syncthreads();
                 ring[0] = read_a(nxt, 0);
                 ring[1] = read_a(nxt, 1);
@@ -265,11 +283,17 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
             if constexpr (FOLD && (s == GS - 2 || s == GS - 1))
                 e4m3_fold_table(fnx[s - (GS - 2)], lnx.lo[s - (GS - 2)], lnx.hi[s - (GS - 2)]);
             if constexpr (cb == 1 && sI + 2 < 2 * RB) ring[(sI + 2) % 4] = read_a(cur, sI + 2);
-            if constexpr (s < CPT) xcur[s] = x_load(k2, s);
             if constexpr (s >= GS && s < GS + 4) w_load(kw2, s - GS, wcur);
-            if constexpr (s >= SLOTS - 4 - CPT && s < SLOTS - 4)
-                *reinterpret_cast<v4i*>(nxt + xlds0 + (s - (SLOTS - 4 - CPT)) * 4096) =
-                    xnx[s - (SLOTS - 4 - CPT)];
+            // All of wnx must be complete here, before the X loads: the
+            // compiler's wait for a part first used later (here or in the
+            // next step's group 0) would also wait for X loads issued since.
+            if constexpr (s == GS) {
+                asm volatile("" ::"v"(wnx.w[0][0]), "v"(wnx.w[1][0]), "v"(wnx.w[0][1]),
+                             "v"(wnx.w[1][1]));
+                // likewise this step's factors, which the next step's tables use
+                if constexpr (FOLD) asm volatile("" ::"v"(fcur[0]), "v"(fcur[1]));
+            }
+            if constexpr (s >= XS && s < XS + CPT) x_load(k2, s - XS, dst);
             static_for<DQ>([&](auto dc) {
                 constexpr int o = DQ * sg + decltype(dc)::value;
                 if constexpr (o < 64) {
@@ -281,11 +305,16 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
     };
 
     for (int kt = 0; kt < KTe; kt += 2) {
-        step(kt, xs0, xs1, xe, xo, we, wo, le, lo, fe, fo);
-        step(kt + 1, xs1, xs0, xo, xe, wo, we, lo, le, fo, fe);
+        step(kt, bc, bn, bd, we, wo, le, lo, fe, fo);
+        step(kt + 1, bn, bd, bc, wo, we, lo, le, fo, fe);
+        const unsigned t0 = bc;  // next pair: X(kt+2) in bd, X(kt+3) in bc
+        bc = bd;
+        bd = bn;
+        bn = t0;
     }
     mfma32_drain(acc);
-    __syncthreads();  // all waves done with the X buffers
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));  // the last steps' X loads
+    __syncthreads();  // all waves done with the X tiles
 
     // ---- epilogue.  Accumulator (rb, cb) register v of lane (c, h): row
     // 32rb + 8(v/4) + 4h + (v%4), channel n0 + 32cb + c.  Values go to a
@@ -300,7 +329,7 @@ __global__ __launch_bounds__(256, 1) void w4fp8_mfma_kernel(
     __syncthreads();
     constexpr int EB = BF16 ? 2 : 4;          // output element bytes
     constexpr int ROWB = 64 * EB;             // bytes per staged row
-    uint8_t* stage = xs0 + wave * (32 * ROWB);
+    uint8_t* stage = xs + wave * (32 * ROWB);
     uint8_t* out = PARTIAL ? reinterpret_cast<uint8_t*>(part + (size_t)ks * M * N)
                            : reinterpret_cast<uint8_t*>(Y);
 #pragma unroll
