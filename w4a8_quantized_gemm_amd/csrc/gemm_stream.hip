@@ -17,6 +17,8 @@
 // L2.  `ks` waves of a workgroup split the K range of the same output tile;
 // their partial sums are reduced in LDS in wave order (exact for int32), and
 // the per-token x per-channel scale epilogue is fused into the store.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -47,15 +49,32 @@ __device__ __forceinline__ int xpiece(int R, int c) {
 // re-laid out through a per-wave LDS slot into the MFMA operand layout.
 // The ks partial tiles are summed by all threads of the workgroup in wave
 // order (exact).
-// W8: the W8A8 comparison -- `wq` holds INT8 weights in the 8-bit tile
-// layout (2 KiB per tile, a lane's 32 bytes as two 16-byte halves 1 KiB
-// apart), used as B operands without decode; no group parameters.
-template <int NTW, int D, int OUT, int GROUP, bool LDSP, bool W8 = false>
+// WK selects the weight kind (the rest of the kernel is shared):
+//   kWkLQQ  LiquidQuant codes + group parameters, INT8 matrix cores;
+//   kWkW8   the W8A8 comparison: INT8 weights in the 8-bit tile layout
+//           (2 KiB per tile, a lane's 32 bytes as two 16-byte halves 1 KiB
+//           apart), used as B operands without decode;
+//   kWkF8   sign-magnitude INT4 codes -> e4m3 by byte table, X is e4m3,
+//           one v_mfma_scale_f32_16x16x128_f8f6f4 per tile (unit scales),
+//           float32 accumulation; epilogue scale sw[n];
+//   kWkF8G  the same with per-group scales folded into the FP8 weights:
+//           each tile's table is e4m3(|q| f) for the lane's channel and
+//           group (fsc group-major [K/GROUP][N]; with 64-wide groups lane
+//           quarter G lies in group 2 kt + G/2), loaded with the weights,
+//           and the epilogue scales by tsc[0].
+// OUT: 0 = fp16 (INT8 kinds) or bf16 (FP8 kinds), 1 = int32 or float32.
+constexpr int kWkLQQ = 0, kWkW8 = 1, kWkF8 = 2, kWkF8G = 3;
+
+template <int NTW, int D, int OUT, int GROUP, bool LDSP, int WK = kWkLQQ>
 __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ s_u8, const uint8_t* __restrict__ a_u8,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, int ks,
-    const int* __restrict__ offsets) {
+    const int* __restrict__ offsets, const float* __restrict__ fsc = nullptr,
+    const float* __restrict__ tsc = nullptr) {
+    constexpr bool W8 = WK == kWkW8;
+    constexpr bool F8 = WK == kWkF8 || WK == kWkF8G;
+    using Acc = std::conditional_t<F8, v4f, v4i>;
     extern __shared__ int red[];
     // Grouped problems (offsets != nullptr): expert blockIdx.z owns rows
     // offsets[e] .. offsets[e+1]-1 of X and Y and the e-th slab of the
@@ -97,6 +116,9 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
         __builtin_amdgcn_make_buffer_rsrc(const_cast<int8_t*>(X), (short)0, M * K, 0x00020000);
     const __amdgpu_buffer_rsrc_t w_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(wq), (short)0, (int)((size_t)N * K / (W8 ? 1 : 2)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t f_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(fsc), (short)0,
+        WK == kWkF8G ? (int)((size_t)(K / GROUP) * N * sizeof(float)) : 0, 0x00020000);
     const __amdgpu_buffer_rsrc_t s_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t*>(s_u8), (short)0, (int)((size_t)N * K / GROUP), 0x00020000);
     const __amdgpu_buffer_rsrc_t a_rsrc = __builtin_amdgcn_make_buffer_rsrc(
@@ -125,9 +147,11 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
     const int xr0 = xpiece(r, 2 * G), xr1 = xpiece(r, 2 * G + 1);
 
     constexpr int WPT = W8 ? 2 : 1;  // 16-byte weight loads per lane and tile
+    constexpr int NF = WK == kWkF8G ? NTW : 1;  // folded factors per stage
     struct Stage {
         v4i x0, x1;
         v4i w[NTW * WPT];
+        float f[NF];
     };
     auto issue = [&](int kt, Stage& st) {
         const unsigned so = (unsigned)(kt * kTileK);
@@ -149,6 +173,15 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
                              w_rsrc, wvoff, (unsigned)(((size_t)(nt0 + t) * KT + kt) * kTileBytes),
                              kNonTemporal));
             }
+            if constexpr (WK == kWkF8G) {
+                // factor of this lane's channel and group, loaded with the
+                // stage so using it waits for nothing younger
+                const int gi = GROUP == 64 ? 2 * kt + (G >> 1) : kt;
+                st.f[t] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(
+                               f_rsrc, (unsigned)((size_t)gi * N + (nt0 + t) * kTileN + r) * 4u,
+                               0u, 0));
+            }
         }
     };
     auto params = [&](int kt, int t, unsigned& s, unsigned& a) {
@@ -165,9 +198,9 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
         }
     };
 
-    v4i acc[NTW];
+    Acc acc[NTW];
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) acc[t] = v4i{0, 0, 0, 0};
+    for (int t = 0; t < NTW; ++t) acc[t] = Acc{};
 
     // Multiply-accumulate of the K-tile held in stage S.
     auto consume = [&](const Stage& S, int kt) {
@@ -185,6 +218,19 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
             if constexpr (W8) {
                 acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x0, S.w[2 * t], acc[t], 0, 0, 0);
                 acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1, S.w[2 * t + 1], acc[t], 0, 0, 0);
+                continue;
+            } else if constexpr (F8) {
+                unsigned lo = kE4m3LutLo, hi = kE4m3LutHi;
+                if constexpr (WK == kWkF8G) e4m3_fold_table(S.f[t], lo, hi);
+                const v4i w = S.w[t];
+                const v8i Bf = v8i{(int)int4_to_e4m3_lo(w.x, lo, hi), (int)int4_to_e4m3_hi(w.x, lo, hi),
+                                   (int)int4_to_e4m3_lo(w.y, lo, hi), (int)int4_to_e4m3_hi(w.y, lo, hi),
+                                   (int)int4_to_e4m3_lo(w.z, lo, hi), (int)int4_to_e4m3_hi(w.z, lo, hi),
+                                   (int)int4_to_e4m3_lo(w.w, lo, hi), (int)int4_to_e4m3_hi(w.w, lo, hi)};
+                const v8i A = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+                // formats 0/0 = e4m3 x e4m3; E8M0 scale 127 = 2^0 on both sides
+                acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bf, acc[t], 0, 0, 0, 127,
+                                                                          0, 127);
                 continue;
             }
             unsigned s, a;
@@ -215,7 +261,7 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
 
     // Parameter copy, behind the first weight loads (panels p0 .. p0+np-1
     // are contiguous in the panel-order arrays).
-    if (LDSP && !W8) {
+    if (LDSP && WK == kWkLQQ) {
         const int n16 = np * groups * 4;  // 16-byte pieces per array
         const size_t base = (size_t)p0 * groups * 64;
         for (int q = tid; q < n16; q += blockDim.x) {
@@ -251,112 +297,36 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
 
     // Sum the ks partial tiles: element e = (t * 4 + v) * 64 + l of wave w
     // lives at red[w * NTW * 256 + e] (reusing the parameter LDS).
+    // (float32 sums, for the FP8 kinds, are added in the same wave order.)
+    using Sum = std::conditional_t<F8, float, int>;
+    Sum* reds = reinterpret_cast<Sum*>(red);
     __syncthreads();
 #pragma unroll
     for (int t = 0; t < NTW; ++t)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) red[((wave * NTW + t) * 4 + v) * 64 + lane] = acc[t][v];
+        for (int v = 0; v < 4; ++v) reds[((wave * NTW + t) * 4 + v) * 64 + lane] = acc[t][v];
     __syncthreads();
     const int nel = NTW * 256;
+    const float tval = WK == kWkF8G ? tsc[0] : 0.0f;
     for (int e = tid; e < nel; e += blockDim.x) {
-        int sum = 0;
-        for (int w = 0; w < ks; ++w) sum += red[w * nel + e];
+        Sum sum = reds[e];
+        for (int w = 1; w < ks; ++w) sum += reds[w * nel + e];
         const int t = e >> 8, v = (e >> 6) & 3, l = e & 63;
         const int m = m0 + 4 * (l >> 4) + v;  // accumulator row (X row)
         const int n = (nt0 + t) * kTileN + (l & 15);
         if (m < row_hi) {
-            if (OUT == 1) {
+            if constexpr (F8) {
+                const float y = (sum * sx[m]) * (WK == kWkF8G ? tval : sw[n]);
+                if (OUT == 1)
+                    reinterpret_cast<float*>(Y)[(size_t)m * N + n] = y;
+                else
+                    reinterpret_cast<unsigned short*>(Y)[(size_t)m * N + n] = f32_to_bf16_bits(y);
+            } else if (OUT == 1) {
                 reinterpret_cast<int*>(Y)[(size_t)m * N + n] = sum;
             } else {
                 const float y = ((float)sum * sx[m]) * sw[n];
                 reinterpret_cast<unsigned short*>(Y)[(size_t)m * N + n] = f32_to_f16_bits(y);
             }
-        }
-    }
-}
-
-// GROUP = 0: per-channel scale sw[n].  GROUP = 64 or 128: the folded
-// per-group format -- each (tile, K-step) converts its codes through the
-// table e4m3(|q| f) of the lane's channel and group (fsc group-major
-// [K/GROUP][N]; lane quarter G covers K columns 32G..32G+31, so with 64-wide
-// groups it lies in group 2kt + G/2), and the epilogue scales by tsc[0].
-template <int NTW, int OUT, int GROUP>
-__global__ __launch_bounds__(1024) void w4fp8_stream_kernel(
-    const uint8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
-    const float* __restrict__ sw, const float* __restrict__ fsc, const float* __restrict__ tsc,
-    void* __restrict__ Y, int M, int N, int K, int ks) {
-    extern __shared__ int red[];
-    float* redf = reinterpret_cast<float*>(red);
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int r = lane & 15, G = lane >> 4;
-    const int KT = K / kTileK;
-    const int nt0 = blockIdx.x * NTW;
-    const int m0 = blockIdx.y * 16;
-    const int kt_begin = (int)((long long)KT * wave / ks);
-    const int kt_end = (int)((long long)KT * (wave + 1) / ks);
-    const int m = m0 + r;
-    const bool mvalid = m < M;
-    const uint8_t* xrow = X + (size_t)(mvalid ? m : 0) * K + 32 * G;
-    const uint8_t* wlane = wq + (size_t)lane * 16;
-
-    v4f acc[NTW];
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) acc[t] = v4f{0.f, 0.f, 0.f, 0.f};
-
-    for (int kt = kt_begin; kt < kt_end; ++kt) {
-        v4i xa0 = v4i{0, 0, 0, 0}, xa1 = v4i{0, 0, 0, 0};
-        if (mvalid) {
-            xa0 = load16(xrow + (size_t)kt * kTileK);
-            xa1 = load16(xrow + (size_t)kt * kTileK + 16);
-        }
-        const v8i A = v8i{xa0.x, xa0.y, xa0.z, xa0.w, xa1.x, xa1.y, xa1.z, xa1.w};
-#pragma unroll
-        for (int t = 0; t < NTW; ++t) {
-            const int nt = nt0 + t;
-            const v4i w = load16(wlane + ((size_t)nt * KT + kt) * kTileBytes);
-            unsigned tlo = kE4m3LutLo, thi = kE4m3LutHi;
-            if constexpr (GROUP != 0) {
-                const int gi = GROUP == 64 ? 2 * kt + (G >> 1) : kt;
-                e4m3_fold_table(fsc[(size_t)gi * N + nt * kTileN + r], tlo, thi);
-            }
-            const v8i B = v8i{(int)int4_to_e4m3_lo(w.x, tlo, thi), (int)int4_to_e4m3_hi(w.x, tlo, thi),
-                              (int)int4_to_e4m3_lo(w.y, tlo, thi), (int)int4_to_e4m3_hi(w.y, tlo, thi),
-                              (int)int4_to_e4m3_lo(w.z, tlo, thi), (int)int4_to_e4m3_hi(w.z, tlo, thi),
-                              (int)int4_to_e4m3_lo(w.w, tlo, thi), (int)int4_to_e4m3_hi(w.w, tlo, thi)};
-            // formats 0/0 = e4m3 x e4m3; E8M0 scale 127 = 2^0 on both sides
-            acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, acc[t], 0, 0, 0, 127,
-                                                                      0, 127);
-        }
-    }
-
-    if (ks > 1) {
-#pragma unroll
-        for (int t = 0; t < NTW; ++t)
-#pragma unroll
-            for (int v = 0; v < 4; ++v) redf[((wave * NTW + t) * 4 + v) * 64 + lane] = acc[t][v];
-        __syncthreads();
-        if (wave != 0) return;
-        for (int w = 1; w < ks; ++w)
-#pragma unroll
-            for (int t = 0; t < NTW; ++t)
-#pragma unroll
-                for (int v = 0; v < 4; ++v) acc[t][v] += redf[((w * NTW + t) * 4 + v) * 64 + lane];
-    }
-
-    const float tval = GROUP != 0 ? tsc[0] : 0.0f;
-#pragma unroll
-    for (int t = 0; t < NTW; ++t) {
-        const int n = (nt0 + t) * kTileN + r;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            const int mo = m0 + 4 * G + v;
-            if (mo >= M) continue;
-            const float y = (acc[t][v] * sx[mo]) * (GROUP != 0 ? tval : sw[n]);
-            if (OUT == 1)
-                reinterpret_cast<float*>(Y)[(size_t)mo * N + n] = y;
-            else
-                reinterpret_cast<unsigned short*>(Y)[(size_t)mo * N + n] = f32_to_bf16_bits(y);
         }
     }
 }
@@ -429,10 +399,10 @@ static hipError_t w8a8_stream_ntw(const int8_t* X, const float* sx, const int8_t
     const size_t lds = xbytes > rbytes ? xbytes : rbytes;
     const uint8_t* w = reinterpret_cast<const uint8_t*>(wq8);
     if (out_type == 1)
-        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, 1, 128, false, true>), grid, block, lds, st,
+        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, 1, 128, false, kWkW8>), grid, block, lds, st,
                            X, sx, w, nullptr, nullptr, sw, Y, M, N, K, ks, nullptr);
     else
-        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, 0, 128, false, true>), grid, block, lds, st,
+        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, 0, 128, false, kWkW8>), grid, block, lds, st,
                            X, sx, w, nullptr, nullptr, sw, Y, M, N, K, ks, nullptr);
     return hipGetLastError();
 }
@@ -449,53 +419,58 @@ hipError_t launch_w8a8_stream(const int8_t* X, const float* sx, const int8_t* wq
     }
 }
 
-template <int NTW, int GROUP>
+template <int NTW, int D, int WK, int GROUP>
 static hipError_t w4fp8_stream_ntw(const uint8_t* X, const float* sx, const uint8_t* wq,
                                    const float* sw, const float* fsc, const float* tsc, void* Y,
                                    int out_type, int M, int N, int K, int ks, hipStream_t st) {
-    dim3 grid(N / (kTileN * NTW), (M + 15) / 16);
+    dim3 grid(N / (kTileN * NTW), (M + 15) / 16, 1);
     dim3 block(64 * ks);
-    size_t lds = ks > 1 ? (size_t)ks * NTW * 4 * 64 * sizeof(float) : 0;
+    const size_t xbytes = (size_t)ks * 2048;
+    const size_t rbytes = (size_t)ks * NTW * 256 * sizeof(float);
+    const size_t lds = xbytes > rbytes ? xbytes : rbytes;
+    const int8_t* Xb = reinterpret_cast<const int8_t*>(X);
     if (out_type == 1)
-        hipLaunchKernelGGL((w4fp8_stream_kernel<NTW, 1, GROUP>), grid, block, lds, st, X, sx, wq,
-                           sw, fsc, tsc, Y, M, N, K, ks);
+        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, 1, GROUP, false, WK>), grid, block, lds, st,
+                           Xb, sx, wq, nullptr, nullptr, sw, Y, M, N, K, ks, nullptr, fsc, tsc);
     else
-        hipLaunchKernelGGL((w4fp8_stream_kernel<NTW, 0, GROUP>), grid, block, lds, st, X, sx, wq,
-                           sw, fsc, tsc, Y, M, N, K, ks);
+        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, 0, GROUP, false, WK>), grid, block, lds, st,
+                           Xb, sx, wq, nullptr, nullptr, sw, Y, M, N, K, ks, nullptr, fsc, tsc);
     return hipGetLastError();
 }
 
-template <int GROUP>
-static hipError_t w4fp8_stream_group(const uint8_t* X, const float* sx, const uint8_t* wq,
-                                     const float* sw, const float* fsc, const float* tsc, void* Y,
-                                     int out_type, int M, int N, int K, StreamCfg cfg,
-                                     hipStream_t st) {
+template <int WK, int GROUP>
+static hipError_t w4fp8_stream_run(const uint8_t* X, const float* sx, const uint8_t* wq,
+                                   const float* sw, const float* fsc, const float* tsc, void* Y,
+                                   int out_type, int M, int N, int K, StreamCfg cfg,
+                                   hipStream_t st) {
+#define F8_NTW(W, D)                                                                          \
+    return w4fp8_stream_ntw<W, D, WK, GROUP>(X, sx, wq, sw, fsc, tsc, Y, out_type, M, N, K, \
+                                             cfg.ks, st)
     switch (cfg.nt_per_wave) {
-        case 4:
-            return w4fp8_stream_ntw<4, GROUP>(X, sx, wq, sw, fsc, tsc, Y, out_type, M, N, K,
-                                              cfg.ks, st);
-        case 2:
-            return w4fp8_stream_ntw<2, GROUP>(X, sx, wq, sw, fsc, tsc, Y, out_type, M, N, K,
-                                              cfg.ks, st);
-        default:
-            return w4fp8_stream_ntw<1, GROUP>(X, sx, wq, sw, fsc, tsc, Y, out_type, M, N, K,
-                                              cfg.ks, st);
+        case 7: F8_NTW(7, 2);
+        case 4: F8_NTW(4, 3);
+        case 3: F8_NTW(3, 3);
+        case 2: F8_NTW(2, 4);
+        default: F8_NTW(1, 3);
     }
+#undef F8_NTW
 }
 
 hipError_t launch_w4fp8_stream(const uint8_t* X, const float* sx, const uint8_t* wq,
                                const float* sw, void* Y, int out_type, int M, int N, int K,
                                StreamCfg cfg, hipStream_t st) {
-    return w4fp8_stream_group<0>(X, sx, wq, sw, nullptr, nullptr, Y, out_type, M, N, K, cfg, st);
+    return w4fp8_stream_run<kWkF8, 128>(X, sx, wq, sw, nullptr, nullptr, Y, out_type, M, N, K,
+                                        cfg, st);
 }
 
 hipError_t launch_w4fp8g_stream(const uint8_t* X, const float* sx, const uint8_t* wq,
                                 const float* fsc, const float* tsc, void* Y, int out_type, int M,
                                 int N, int K, int group, StreamCfg cfg, hipStream_t st) {
     if (group == 64)
-        return w4fp8_stream_group<64>(X, sx, wq, nullptr, fsc, tsc, Y, out_type, M, N, K, cfg,
-                                      st);
-    return w4fp8_stream_group<128>(X, sx, wq, nullptr, fsc, tsc, Y, out_type, M, N, K, cfg, st);
+        return w4fp8_stream_run<kWkF8G, 64>(X, sx, wq, nullptr, fsc, tsc, Y, out_type, M, N, K,
+                                            cfg, st);
+    return w4fp8_stream_run<kWkF8G, 128>(X, sx, wq, nullptr, fsc, tsc, Y, out_type, M, N, K, cfg,
+                                         st);
 }
 
 }  // namespace w4a8
