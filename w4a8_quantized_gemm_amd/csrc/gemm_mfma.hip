@@ -64,6 +64,13 @@ struct WStep32 {
 //   B = lo ^ 0x80808080, hi ^ 0x80808080
 // 7 instructions per 8 weights (LiquidGEMM, Pith review of arXiv 2509.01229,
 // paper Eq. 12 and minor comment 1 / Sec. 5.3).
+// Empty assembly reading every register of a raw set: the compiler must
+// have all of its loads complete at this point.
+__device__ __forceinline__ void touch_raw(const WStep32& w) {
+    asm volatile("" ::"v"(w.w[0][0]), "v"(w.w[0][1]), "v"(w.w[1][0]), "v"(w.w[1][1]), "v"(w.sdw),
+                 "v"(w.adw));
+}
+
 struct DecLQQ {
     using Raw = WStep32;
     static constexpr bool kW8 = false;
@@ -193,11 +200,15 @@ struct DecAffine16 {
 // No decode, for the W8A8 comparison: the INT8 weights of the first
 // quantisation level alone, in the 8-bit tile layout.  A lane's raw K-step
 // (w[cb][i] = its 16 bytes for instruction i, read straight from the 8-bit
-// tile layout) is already the B operand set; "decoding" copies it into B,
-// which register allocation may turn into nothing.
+// tile layout) is already the B operand set; "decoding" copies it into B.
 struct WStep8 {
     v4i w[2][4];
 };
+__device__ __forceinline__ void touch_raw(const WStep8& w) {
+    asm volatile("" ::"v"(w.w[0][0]), "v"(w.w[0][1]), "v"(w.w[0][2]), "v"(w.w[0][3]),
+                 "v"(w.w[1][0]), "v"(w.w[1][1]), "v"(w.w[1][2]), "v"(w.w[1][3]));
+}
+
 struct DecW8 {
     using Raw = WStep8;
     static constexpr bool kW8 = true;
@@ -205,15 +216,21 @@ struct DecW8 {
     struct Params {};
     struct Tmp {};
     static constexpr int kParamOps = 0;
-    static constexpr int kOps = 2;
+    static constexpr int kOps = 8;
 
     template <int K_>
     __device__ __forceinline__ static void param_step(const Raw&, int, Params&) {}
 
+    // one dword per step (explicit moves: a copy the register allocator
+    // could fold would leave loop-carried copies of registers still being
+    // loaded)
     template <int I, int OP>
     __device__ __forceinline__ static void step(Tmp&, const Raw& w, const Params&,
                                                 v4i (&B)[2][4]) {
-        B[OP][I] = w.w[OP][I];
+        constexpr int cb = OP / 4, d = OP % 4;
+        int x;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(x) : "v"(w.w[cb][I][d]));
+        B[cb][I][d] = x;
     }
 };
 
@@ -425,6 +442,10 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
             mfma32_i8_acc(acc[rb][cb], ring[sI % 8], B[cb][i]);
             if constexpr (cb == 1 && sI + 4 < 4 * RB) ring[(sI + 4) % 8] = read_a(cur, sI + 4);
             if constexpr (s >= GS && s < GS + DEC::kLoads) w_load(kw2, s - GS, wcur);
+            // All of wnx complete here, before the X loads: the compiler's
+            // wait for a part first used later would also cover X loads
+            // issued in between, which it does not see.
+            if constexpr (s == GS) touch_raw(wnx);
             if constexpr (s >= XS && s < XS + CPT) x_load(k2, s - XS, dst);
             if constexpr (!COARSE) {
                 constexpr int PO = DEC::kParamOps, NO = DEC::kOps;
