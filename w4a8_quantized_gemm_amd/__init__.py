@@ -151,25 +151,41 @@ def _in_type(X):
     return types[X.dtype]
 
 
-def quant_act(X, stream=None):
-    """Per-token INT8 of float32 / fp16 / bf16 X: (Xq int8 [M][K], sx float32 [M])."""
+def _act_outs(X, out, qdtype):
+    torch = _torch()
+    M, K = X.shape
+    if out is None:
+        return (torch.empty((M, K), dtype=qdtype, device=X.device),
+                torch.empty(M, dtype=torch.float32, device=X.device))
+    Xq, sx = out
+    _need(Xq, qdtype, "out[0]")
+    _need(sx, torch.float32, "out[1]")
+    if tuple(Xq.shape) != (M, K) or tuple(sx.shape) != (M,):
+        raise ValueError("out tensors must be [M][K] and [M]")
+    return Xq, sx
+
+
+def quant_act(X, stream=None, out=None):
+    """Per-token INT8 of float32 / fp16 / bf16 X: (Xq int8 [M][K], sx float32 [M]).
+
+    `out` = (Xq, sx) writes into existing tensors (nothing is allocated, as a
+    captured graph needs)."""
     torch = _torch()
     it = _in_type(X)
     M, K = X.shape
-    Xq = torch.empty((M, K), dtype=torch.int8, device=X.device)
-    sx = torch.empty(M, dtype=torch.float32, device=X.device)
+    Xq, sx = _act_outs(X, out, torch.int8)
     _check(lib.w4a8_quant_act_ex(_ptr(X), it, M, K, _ptr(Xq), _ptr(sx), _stream(stream)),
            "w4a8_quant_act_ex")
     return Xq, sx
 
 
-def quant_act_fp8(X, stream=None):
-    """Per-token e4m3 of float32 / fp16 / bf16 X: (Xq uint8 [M][K], sx float32 [M])."""
+def quant_act_fp8(X, stream=None, out=None):
+    """Per-token e4m3 of float32 / fp16 / bf16 X: (Xq uint8 [M][K], sx float32 [M]);
+    `out` as for quant_act."""
     torch = _torch()
     it = _in_type(X)
     M, K = X.shape
-    Xq = torch.empty((M, K), dtype=torch.uint8, device=X.device)
-    sx = torch.empty(M, dtype=torch.float32, device=X.device)
+    Xq, sx = _act_outs(X, out, torch.uint8)
     _check(lib.w4fp8_quant_act_ex(_ptr(X), it, M, K, _ptr(Xq), _ptr(sx), _stream(stream)),
            "w4fp8_quant_act_ex")
     return Xq, sx
