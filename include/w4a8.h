@@ -30,7 +30,10 @@
  *     valid the call returns W4A8_OK without checking pointers (nothing is
  *     read or written) and launches nothing.
  *   - Shape constraints: K a positive multiple of 128, N a multiple of 64,
- *     group in {64, 128}; every device pointer 16-byte aligned.
+ *     group in {64, 128}; every device pointer 16-byte aligned.  For every
+ *     GEMM: M*K < 2^31 and N*K < 2^32 (the kernels address operands with
+ *     32-bit buffer ranges); larger problems return W4A8_ERR_SHAPE (split M
+ *     across calls).
  *
  * Packed 4-bit weight layout (W4A8_LAYOUT_VERSION 1), wq = N*K/2 bytes:
  *   the [N][K] matrix of 4-bit codes is cut into tiles of 16 rows x 128 K.

@@ -214,6 +214,26 @@ def test_w8a8_validation():
     assert gm(M=128, K=8192, ws=A, wsb=need - 1) == WS
 
 
+def test_gemm_extent_limits():
+    """M*K >= 2^31 or N*K >= 2^32 is rejected before any HIP call, by every
+    GEMM entry point (sizes only; the fake pointers are never used)."""
+    big_m, k = 1 << 20, 4096            # M*K = 2^32
+    n_big = 1 << 20                     # N*K = 2^32 at K = 4096
+    assert lib.w4a8_gemm(A, A, A, A, A, A, A, 0, big_m, 256, k, 128, 0, None, 0, None) == SHAPE
+    assert lib.w4a8_gemm(A, A, A, A, A, A, A, 0, 16, n_big, k, 128, 0, None, 0, None) == SHAPE
+    assert lib.w4fp8_gemm(A, A, A, A, A, 0, big_m, 256, k, 0, None, 0, None) == SHAPE
+    assert lib.w4fp8_gemm(A, A, A, A, A, 0, 16, n_big, k, 0, None, 0, None) == SHAPE
+    assert lib.w8a8_gemm(A, A, A, A, A, 0, big_m, 256, k, 0, None, 0, None) == SHAPE
+    assert lib.w4a8_gemm_ablation(1, A, A, A, A, A, A, A, 0, big_m, 256, k, 128, None) == SHAPE
+    assert lib.w4a8_gemm_grouped(A, A, A, 2, A, A, A, A, A, 0, 16, n_big, k, 128, 8,
+                                 None) == SHAPE
+    assert lib.w4fp8g_gemm(A, A, A, A, A, A, 0, big_m, 256, k, 128, 0, None, 0, None) == SHAPE
+    # just inside the limits the sizes are accepted (validation then stops at
+    # the NULL output pointer, before any HIP call)
+    assert lib.w4a8_gemm(A, A, A, A, A, A, None, 0, (1 << 19) - 1, 256, k, 128, 0, None, 0,
+                         None) == NULL
+
+
 def test_valid_call_without_gpu_reports_hip_error():
     """A call that passes validation reaches the HIP runtime; with no GPU
     the device query fails and the status is W4A8_ERR_HIP, not a crash."""

@@ -47,6 +47,12 @@ w4a8_status_t check_device() {
 bool valid_nk(int N, int K) { return N >= 0 && K > 0 && K % 128 == 0 && N % 64 == 0; }
 bool valid_group(int g) { return g == 64 || g == 128; }
 
+// GEMM operand sizes the kernels address with 32-bit buffer ranges: the
+// activations M*K bytes < 2^31, the weights N*K < 2^32 codes.
+bool valid_extent(int M, int N, int K) {
+    return (long long)M * K < (1LL << 31) && (long long)N * K < (1LL << 32);
+}
+
 int k_tiles(int K) { return K / 128; }
 
 // Streamed kernel: NTW 16-channel tiles per workgroup, ks waves splitting K.
@@ -179,6 +185,7 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint
     if (out_type != W4A8_OUT_F16 && out_type != W4A8_OUT_I32) return W4A8_ERR_UNSUPPORTED;
     if (M < 0 || !valid_nk(N, K) || !valid_group(group) || !valid_splitk(splitk, K))
         return W4A8_ERR_SHAPE;
+    if (!valid_extent(M, N, K)) return W4A8_ERR_SHAPE;
     if (M == 0 || N == 0) return W4A8_OK;  // nothing to read or write
     if (!X || !wq || !s_u8 || !a_u8 || !Y) return W4A8_ERR_NULL_PTR;
     if (out_type == W4A8_OUT_F16 && (!sx || !sw)) return W4A8_ERR_NULL_PTR;
@@ -206,7 +213,7 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm_grouped(const int8_t* X, const float* sx,
     if (out_type != W4A8_OUT_F16 && out_type != W4A8_OUT_I32) return W4A8_ERR_UNSUPPORTED;
     if (M < 0 || E < 1 || E > 65535 || max_rows < 0 || !valid_nk(N, K) || !valid_group(group))
         return W4A8_ERR_SHAPE;
-    if ((long long)M * K >= (1LL << 31)) return W4A8_ERR_SHAPE;
+    if (!valid_extent(M, N, K)) return W4A8_ERR_SHAPE;
     if (M == 0 || N == 0 || max_rows == 0) return W4A8_OK;  // nothing to read or write
     if (!X || !offsets || !wq || !s_u8 || !a_u8 || !Y) return W4A8_ERR_NULL_PTR;
     if (out_type == W4A8_OUT_F16 && (!sx || !sw)) return W4A8_ERR_NULL_PTR;
@@ -245,6 +252,7 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm_ablation(int variant, const int8_t* X, const
         return W4A8_ERR_UNSUPPORTED;
     if (out_type != W4A8_OUT_F16 && out_type != W4A8_OUT_I32) return W4A8_ERR_UNSUPPORTED;
     if (M < 0 || !valid_nk(N, K) || !valid_group(group)) return W4A8_ERR_SHAPE;
+    if (!valid_extent(M, N, K)) return W4A8_ERR_SHAPE;
     if (M == 0 || N == 0) return W4A8_OK;  // nothing to read or write
     if (!use_mfma_tiles(M, N, K) || w4a8::plan_w4a8_mfma(M, N, K).splits != 1)
         return W4A8_ERR_UNSUPPORTED;  // the variants exist for the unsplit tile kernel only
@@ -268,6 +276,7 @@ W4A8_EXPORT w4a8_status_t w4fp8_gemm(const uint8_t* X_e4m3, const float* sx, con
                                      hipStream_t stream) {
     if (out_type != W4FP8_OUT_BF16 && out_type != W4FP8_OUT_F32) return W4A8_ERR_UNSUPPORTED;
     if (M < 0 || !valid_nk(N, K) || !valid_splitk(splitk, K)) return W4A8_ERR_SHAPE;
+    if (!valid_extent(M, N, K)) return W4A8_ERR_SHAPE;
     if (M == 0 || N == 0) return W4A8_OK;  // nothing to read or write
     if (!X_e4m3 || !sx || !wq || !sw || !Y) return W4A8_ERR_NULL_PTR;
     if (!aligned16(X_e4m3) || !aligned16(wq) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
@@ -308,6 +317,7 @@ W4A8_EXPORT w4a8_status_t w4fp8g_gemm(const uint8_t* X_e4m3, const float* sx, co
     if (M < 0 || !valid_nk(N, K) || !valid_group(group) || !valid_splitk(splitk, K))
         return W4A8_ERR_SHAPE;
     if ((long long)N * (K / group) >= (1LL << 29)) return W4A8_ERR_SHAPE;
+    if (!valid_extent(M, N, K)) return W4A8_ERR_SHAPE;
     if (M == 0 || N == 0) return W4A8_OK;  // nothing to read or write
     if (!X_e4m3 || !sx || !wq || !fsc || !tscale || !Y) return W4A8_ERR_NULL_PTR;
     if (!aligned16(X_e4m3) || !aligned16(wq) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
@@ -346,6 +356,7 @@ W4A8_EXPORT w4a8_status_t w8a8_gemm(const int8_t* X, const float* sx, const int8
     if (out_type != W4A8_OUT_F16 && out_type != W4A8_OUT_I32) return W4A8_ERR_UNSUPPORTED;
     if (M < 0 || !valid_nk(N, K) || !valid_splitk(splitk, K)) return W4A8_ERR_SHAPE;
     if ((long long)N * K >= (1LL << 31)) return W4A8_ERR_SHAPE;
+    if (!valid_extent(M, N, K)) return W4A8_ERR_SHAPE;
     if (M == 0 || N == 0) return W4A8_OK;  // nothing to read or write
     if (!X || !wq8 || !Y) return W4A8_ERR_NULL_PTR;
     if (out_type == W4A8_OUT_F16 && (!sx || !sw)) return W4A8_ERR_NULL_PTR;
