@@ -568,8 +568,18 @@ MfmaPlan plan_w4a8_mfma(int M, int N, int K) {
     const long long pad128 = (long long)((M + 127) / 128) * 128;
     p.mt = (M > 128 && t256 >= 256 && pad256 * 100 <= pad128 * 103) ? 256 : 128;
     const long long tiles = (long long)(N / kNT) * ((M + p.mt - 1) / p.mt);
+    // Few tiles: split K so the grid fills one wave of the 256 CUs (the
+    // largest split count with tiles * splits <= 256; each split keeps at
+    // least 8 K-steps).  Overshooting to a second, partial wave costs more
+    // than the idle CUs of an exact fit, and every split adds M*N int32
+    // partials to write and read back.
     p.splits = 1;
-    while (p.splits < 16 && tiles * p.splits < 256 && KT / (2 * p.splits) >= 4) p.splits *= 2;
+    if (tiles < 256) {
+        int s = (int)(256 / tiles);
+        if (s > 16) s = 16;
+        while (s > 1 && KT < 8 * s) --s;
+        p.splits = s;
+    }
     p.workspace = p.splits > 1 ? (size_t)p.splits * M * N * sizeof(int) : 0;
     return p;
 }
