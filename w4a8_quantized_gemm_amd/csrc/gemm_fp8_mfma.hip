@@ -5,8 +5,8 @@
 // Y = bf16((acc * sx[m]) * sw[n]) or float32.
 //
 // Same skeleton as the W4A8 tile kernel: workgroup tile MT (128 or 256)
-// rows x 256 channels, four waves of MT x 64, X staged global -> registers
-// -> LDS (double buffer, swizzled 16-byte slots), weights loaded two K-steps
+// rows x 256 channels, four waves of MT x 64, X global -> LDS directly
+// (three rotating tiles, swizzled 16-byte slots), weights loaded two K-steps
 // ahead and converted in single instructions interleaved with the matrix-
 // core instructions.  Per 128-column K-step and 32 x 32 block there are two
 // v_mfma_f32_32x32x64_f8f6f4 (e4m3 x e4m3): instruction j of lane

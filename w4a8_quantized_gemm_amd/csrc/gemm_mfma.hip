@@ -11,8 +11,8 @@
 // weights after the nibble split (same review, paper Eq. 12; minor comment 1
 // / Sec. 5.3 for the instruction count).
 //
-// Per K-step of 128 columns: X[MT][128] int8 goes global -> registers ->
-// LDS (double buffer, 16-byte slots XOR-swizzled per row); each wave loads
+// Per K-step of 128 columns: X[MT][128] int8 goes global -> LDS directly
+// (three rotating tiles, 16-byte slots XOR-swizzled per row); each wave loads
 // its 4 packed tiles of a later step and dequantises them in single
 // instructions interleaved with the current step's matrix-core
 // instructions (v_mfma_i32_32x32x32_i8, accumulators in AGPRs).
@@ -31,7 +31,8 @@ namespace w4a8 {
 //     the 128-column step); instruction i (0..3) consumes columns
 //     64h + 16i .. +15, and the A operand (X row, same columns) matches;
 //   every global load is a buffer load (SGPR step offset, no per-load
-//     address arithmetic) issued two K-steps ahead; X rows past M fall
+//     address arithmetic); weights are loaded two K-steps ahead into
+//     registers, X tiles two K-steps ahead into LDS; X rows past M fall
 //     outside the buffer and read as zero;
 //   the next step's weights are dequantised in single-instruction steps
 //     interleaved with this step's matrix-core instructions;
