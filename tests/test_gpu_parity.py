@@ -297,6 +297,34 @@ def test_grouped_gemm_parity(counts, N, K, g):
     assert np.all(yi[offs[-1]:].view(np.uint32) == 0xABABABAB)   # untouched
 
 
+@pytest.mark.parametrize("M,N,K,splits", [(600, 4352, 3072, 3), (300, 4352, 5120, 5),
+                                           (500, 2304, 7168, 7), (100, 256, 16384, 16)])
+def test_split_counts_any_integer(M, N, K, splits):
+    """The split-K plan fills one wave of CUs with any integer split count:
+    int32 results bit-exact against the oracle on sampled rows (the oracle
+    quantises per row, so a row sample is exact) and against the streamed
+    kernel on every element."""
+    assert w4.workspace_size(M, N, K) == splits * M * N * 4
+    g = 128
+    say(f"w4a8 split-K {splits} M={M} N={N} K={K}")
+    W = wl.gen_weights(N, K, 3000 + splits)
+    X = wl.gen_activations(M, K, 3001 + splits, 3002)
+    pk_ref = oracle.w4a8_pack(W, g)
+    X8, sx = oracle.quant_sym_rows(X, 127)
+    pk = {"wq": to_dev(pk_ref["wq"]), "s_u8": to_dev(pk_ref["s_panels"]),
+          "a_u8": to_dev(pk_ref["a_panels"]), "sw": to_dev(pk_ref["sw"]),
+          "N": N, "K": K, "group": g}
+    Yi = poison((M, N), torch.int32)
+    w4.gemm(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_I32, out=Yi)
+    got = host(Yi)
+    rows = np.unique(np.concatenate([[0, M - 1], np.random.default_rng(splits).choice(M, 6)]))
+    acc, _, _ = oracle.w4a8_gemm(X8[rows], sx[rows], pk_ref, g)
+    np.testing.assert_array_equal(got[rows], acc)
+    Ys = poison((M, N), torch.int32)
+    w4.gemm(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_I32, splitk=1, out=Ys)
+    np.testing.assert_array_equal(got, host(Ys))
+
+
 def test_workspace_too_small_is_rejected():
     M, N, K = 128, 512, 4096
     X8, sx, pk, acc, y = _small_problem(M, N, K, 128, 3)
