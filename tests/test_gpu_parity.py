@@ -536,6 +536,33 @@ def test_w8a8_gemm_parity(M, N, K, sk):
         np.testing.assert_array_equal(host(Ys), acc)
 
 
+def test_w8a8_256_row_tiles():
+    """W8A8 on 256-row tiles (the 16 x 16 x 64 tile kernel): int32 bit-exact
+    against the oracle on sampled rows and against the streamed kernel on
+    every element; fp16 within 1 ulp on the sampled rows."""
+    M, N, K = 4096, 4096, 384
+    assert w4.workspace_size(M, N, K) == 0
+    say(f"w8a8 256-row tiles M={M} N={N} K={K}")
+    W = wl.gen_weights(N, K, 1301)
+    X = wl.gen_activations(M, K, 1302, 1303)
+    ref = oracle.w8a8_pack(W)
+    X8, sx = oracle.quant_sym_rows(X, 127)
+    pk = {"wq8": to_dev(ref["wq8"]), "sw": to_dev(ref["sw"]), "N": N, "K": K}
+    Yi = poison((M, N), torch.int32)
+    w4.gemm_w8a8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_I32, out=Yi)
+    Yh = poison((M, N), torch.float16)
+    w4.gemm_w8a8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F16, out=Yh)
+    got = host(Yi)
+    rows = np.unique(np.concatenate([[0, 255, 256, M - 1], np.random.default_rng(9).choice(M, 8)]))
+    acc, y, _ = oracle.w8a8_gemm(X8[rows], sx[rows], ref)
+    np.testing.assert_array_equal(got[rows], acc)
+    d = f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16)[rows], y)
+    assert d.max() <= 1
+    Ys = poison((M, N), torch.int32)
+    w4.gemm_w8a8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_I32, splitk=1, out=Ys)
+    np.testing.assert_array_equal(got, host(Ys))
+
+
 # ----------------------------- folded per-group FP8 (FireQ-style) ----------
 def _fp8g_weights(N, K, g, seed):
     """Normal(0, 0.02) weights with one all-zero row and one all-zero group

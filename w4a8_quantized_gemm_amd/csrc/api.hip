@@ -270,9 +270,6 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm_ablation(int variant, const int8_t* X, const
     w4a8_status_t d = check_device();
     if (d != W4A8_OK) return d;
     const w4a8::MfmaPlan plan = w4a8::plan_w4a8_mfma(M, N, K);
-    if (variant == W4A8_ABL_LQQ)
-        return hip_status(w4a8::launch_w4a8_mfma(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
-                                                 group, plan, nullptr, stream));
     return hip_status(w4a8::launch_w4a8_mfma_ablation(variant, X, sx, wq, s_u8, a_u8, sw, Y,
                                                       out_type, M, N, K, group, plan, stream));
 }

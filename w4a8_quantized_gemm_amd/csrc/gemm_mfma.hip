@@ -557,6 +557,19 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
     }
 }
 
+hipError_t launch_splitk_reduce(const int* part, int splits, int M, int N, const float* sx,
+                                const float* sw, void* Y, int out_type, hipStream_t st) {
+    const size_t quads = ((size_t)M * N) / 4;
+    const unsigned blocks = (unsigned)((quads + 255) / 256);
+    if (out_type == 1)
+        hipLaunchKernelGGL((splitk_reduce_kernel<1>), dim3(blocks), dim3(256), 0, st, part,
+                           splits, M, N, sx, sw, Y);
+    else
+        hipLaunchKernelGGL((splitk_reduce_kernel<0>), dim3(blocks), dim3(256), 0, st, part,
+                           splits, M, N, sx, sw, Y);
+    return hipGetLastError();
+}
+
 // Workgroup tile height and K split for the matrix-core kernel.
 MfmaPlan plan_w4a8_mfma(int M, int N, int K) {
     MfmaPlan p;
@@ -638,21 +651,19 @@ static hipError_t run_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
         launch_tile<256, 1, true, DEC>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, plan.splits, st);
     else
         launch_tile<128, 1, true, DEC>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, plan.splits, st);
-    const size_t quads = ((size_t)M * N) / 4;
-    const unsigned blocks = (unsigned)((quads + 255) / 256);
-    if (out_type == 1)
-        hipLaunchKernelGGL((splitk_reduce_kernel<1>), dim3(blocks), dim3(256), 0, st, part,
-                           plan.splits, M, N, sx, sw, Y);
-    else
-        hipLaunchKernelGGL((splitk_reduce_kernel<0>), dim3(blocks), dim3(256), 0, st, part,
-                           plan.splits, M, N, sx, sw, Y);
-    return hipGetLastError();
+    return launch_splitk_reduce(part, plan.splits, M, N, sx, sw, Y, out_type, st);
 }
 
+// 256-row plans run the 16 x 16 x 64 kernel (3-6 % faster there, same
+// results bit for bit); 128-row plans this kernel, which is faster at that
+// height (the 16 x 16 slots leave less room for the decode per weight).
 hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
                             const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
                             int out_type, int M, int N, int K, int group, const MfmaPlan& plan,
                             void* workspace, hipStream_t st) {
+    if (plan.mt == 256)
+        return launch_w4a8_mfma16(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, plan,
+                                  workspace, st);
     return run_mfma<DecLQQ>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, plan,
                             workspace, st);
 }
@@ -660,6 +671,8 @@ hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
 hipError_t launch_w8a8_mfma(const int8_t* X, const float* sx, const int8_t* wq8, const float* sw,
                             void* Y, int out_type, int M, int N, int K, const MfmaPlan& plan,
                             void* workspace, hipStream_t st) {
+    if (plan.mt == 256)  // same kernel choice as the W4A8 GEMM
+        return launch_w8a8_mfma16(X, sx, wq8, sw, Y, out_type, M, N, K, plan, workspace, st);
     return run_mfma<DecW8>(X, sx, reinterpret_cast<const uint8_t*>(wq8), nullptr, nullptr, sw, Y,
                            out_type, M, N, K, 128, plan, workspace, st);
 }
@@ -681,7 +694,11 @@ hipError_t launch_w4a8_mfma_ablation(int variant, const int8_t* X, const float* 
                                      const uint8_t* wq, const uint8_t* s_u8, const uint8_t* a_u8,
                                      const float* sw, void* Y, int out_type, int M, int N, int K,
                                      int group, const MfmaPlan& plan, hipStream_t st) {
-    if (variant == 1)
+    // all three decoders on this (32 x 32 x 32) skeleton
+    if (variant == 0)
+        launch_ablation<DecLQQ, false>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group,
+                                       plan.mt, st);
+    else if (variant == 1)
         launch_ablation<DecAffine16, false>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
                                             group, plan.mt, st);
     else

@@ -75,6 +75,24 @@ hipError_t launch_w4fp8_stream(const uint8_t* X, const float* sx, const uint8_t*
                                const float* sw, void* Y, int out_type, int M, int N, int K,
                                StreamCfg cfg, hipStream_t st);
 
+// Sum of `splits` int32 partial tiles in split order, then the fp16
+// epilogue (out_type 0) or the raw int32 sums (out_type 1).
+hipError_t launch_splitk_reduce(const int* part, int splits, int M, int N, const float* sx,
+                                const float* sw, void* Y, int out_type, hipStream_t st);
+
+// The W4A8 tile kernel on v_mfma_i32_16x16x64_i8 (offsets != nullptr: the
+// grouped problem with E experts and max_rows rows at most per expert).
+hipError_t launch_w4a8_mfma16(const int8_t* X, const float* sx, const uint8_t* wq,
+                              const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
+                              int out_type, int M, int N, int K, int group, const MfmaPlan& plan,
+                              void* workspace, hipStream_t st, const int* offsets = nullptr,
+                              int E = 1, int max_rows = 0);
+
+// The W8A8 comparison on the 16 x 16 x 64 tile kernel.
+hipError_t launch_w8a8_mfma16(const int8_t* X, const float* sx, const int8_t* wq8,
+                              const float* sw, void* Y, int out_type, int M, int N, int K,
+                              const MfmaPlan& plan, void* workspace, hipStream_t st);
+
 // W8A8 comparison: per-channel INT8 weights in the 8-bit tile layout.
 hipError_t launch_pack_w8(const float* W, int N, int K, int8_t* wq8, float* sw, hipStream_t st);
 
