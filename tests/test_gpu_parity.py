@@ -217,6 +217,23 @@ def test_mfma256_tiles(M, N, K, g):
     assert d.max() <= 1
 
 
+# More than one wave of 256-row tiles (512, 544 and 768 tiles for 256
+# compute units): ragged M, K-step counts 2 and 4, a partial last wave.
+@pytest.mark.parametrize("M,N,K,g", [(4000, 8192, 512, 128), (4352, 8192, 256, 64),
+                                     (4096, 12288, 512, 64)])
+def test_mfma256_several_waves(M, N, K, g):
+    say(f"w4a8 mfma256 gemm, several waves of tiles: M={M} N={N} K={K} g={g}")
+    assert w4.workspace_size(M, N, K) == 0
+    X8, sx, pk, acc, y = _small_problem(M, N, K, g, 61 + K)
+    Yi = poison((M, N), torch.int32)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, out=Yi)
+    np.testing.assert_array_equal(host(Yi), acc)
+    Yh = poison((M, N), torch.float16)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_F16, out=Yh)
+    d = f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y)
+    assert d.max() <= 1
+
+
 # Few output tiles -> the matrix-core kernel splits K across workgroups and
 # reduces int32 partials in a second kernel (8 splits here).
 @pytest.mark.parametrize("M,N,K,g", [(128, 512, 4096, 128), (100, 256, 2048, 64)])
@@ -482,6 +499,42 @@ def test_w4fp8_tile_parity(M, N, K):
     assert np.all(np.abs(host(Ys) - ref) <= bound + 1e-30)
 
 
+# 256-row FP8 tiles (at least 256 of them: M x N = 4096 x 4096 and more) run
+# on the 16 x 16 x 128 kernel.  K = 384: odd K-step count (the tail step);
+# M = 4000: ragged last row tile.
+@pytest.mark.parametrize("M,N,K", [(4000, 4096, 384), (4096, 4096, 512)])
+def test_w4fp8_256_row_tiles(M, N, K):
+    say(f"w4fp8 256-row tiles M={M} N={N} K={K} workspace={w4.workspace_size(M, N, K)}")
+    assert w4.workspace_size(M, N, K) == 0
+    # integer-valued operands: exact in any summation order, bit for bit
+    rng = np.random.default_rng(M + K)
+    Xi = rng.integers(-16, 17, size=(M, K)).astype(np.float64)
+    q = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    X8 = oracle.e4m3_encode(Xi)
+    exact = Xi.astype(np.int64) @ q.astype(np.int64).T
+    pk = {"wq": to_dev(oracle.pack_nibbles(oracle.int4_sm_codes(q))),
+          "sw": to_dev(np.ones(N, np.float32)), "N": N, "K": K}
+    Y = poison((M, N), torch.float32)
+    w4.gemm_fp8(to_dev(X8), to_dev(np.ones(M, np.float32)), pk, out_type=w4.OUT_F32, out=Y)
+    np.testing.assert_array_equal(host(Y), exact.astype(np.float32))
+    # realistic data against the double reference, both output types
+    W = wl.gen_weights(N, K, 510 + K)
+    X = wl.gen_activations(M, K, 511 + K, 512)
+    pk_ref = oracle.w4fp8_pack(W)
+    X8, sx = oracle.quant_rows_e4m3(X)
+    ref, _ = oracle.w4fp8_ref(X8, sx, pk_ref["q"], pk_ref["sw"])
+    bound = _fp8_bound(X8, sx, pk_ref["q"], pk_ref["sw"])
+    pk = {"wq": to_dev(pk_ref["wq"]), "sw": to_dev(pk_ref["sw"]), "N": N, "K": K}
+    Yf = poison((M, N), torch.float32)
+    w4.gemm_fp8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F32, out=Yf)
+    Yb = poison((M, N), torch.bfloat16)
+    w4.gemm_fp8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_BF16, out=Yb)
+    yf = host(Yf)
+    say(f"  f32 rel fro {rel_fro(yf, ref):.3e}; max |err|/bound "
+        f"{np.max(np.abs(yf - ref) / (bound + 1e-30)):.3f}")
+    _check_fp8_outputs(yf, bf16_bits_of(Yb), ref, bound)
+
+
 def test_fp8_workspace_too_small_is_rejected():
     M, N, K = 128, 256, 4096
     need = w4.workspace_size(M, N, K)
@@ -645,6 +698,40 @@ def test_fp8g_gemm_parity(M, N, K, g):
     Ys = poison((M, N), torch.float32)
     w4.gemm_fp8g(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F32, splitk=1, out=Ys)
     assert np.all(np.abs(host(Ys) - ref) <= bound + 1e-30)
+
+
+# Folded format on 256-row tiles (16 x 16 x 128 kernel): identity X with
+# M = K = 4096 checks every folded e4m3 weight bit for bit; realistic data
+# with ragged M and an odd K-step count against the double reference.
+@pytest.mark.parametrize("g", [64, 128])
+def test_fp8g_256_row_tiles(g):
+    N = K = 4096
+    say(f"w4fp8g 256-row tiles identity K={K} N={N} g={g}")
+    assert w4.workspace_size(K, N, K) == 0
+    W = _fp8g_weights(N, K, g, 710 + g)
+    ref = oracle.w4fp8g_pack(W, g)
+    X8 = np.zeros((K, K), np.uint8)
+    np.fill_diagonal(X8, 0x38)
+    want = (oracle.e4m3_decode(ref["w8"]).T.astype(np.float32) * np.float32(ref["t"]))
+    Y = poison((K, N), torch.float32)
+    w4.gemm_fp8g(to_dev(X8), to_dev(np.ones(K, np.float32)), _fp8g_device(ref, N, K, g),
+                 out_type=w4.OUT_F32, out=Y)
+    np.testing.assert_array_equal(host(Y).view(np.uint32), want.astype(np.float32).view(np.uint32))
+    del Y
+    M, K = 4000, 384
+    say(f"w4fp8g 256-row tiles M={M} N={N} K={K} g={g}")
+    W = _fp8g_weights(N, K, g, 720 + g)
+    X = wl.gen_activations(M, K, 721, 722)
+    ref_pk = oracle.w4fp8g_pack(W, g)
+    X8, sx = oracle.quant_rows_e4m3(X)
+    ref, _ = oracle.w4fp8g_ref(X8, sx, ref_pk["w8"], ref_pk["t"])
+    bound = _fp8_bound_w(X8, sx, np.abs(oracle.e4m3_decode(ref_pk["w8"])), ref_pk["t"])
+    pk = _fp8g_device(ref_pk, N, K, g)
+    Yf = poison((M, N), torch.float32)
+    w4.gemm_fp8g(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F32, out=Yf)
+    Yb = poison((M, N), torch.bfloat16)
+    w4.gemm_fp8g(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_BF16, out=Yb)
+    _check_fp8_outputs(host(Yf), bf16_bits_of(Yb), ref, bound)
 
 
 def test_fp8g_end_to_end_device_pack():
