@@ -23,12 +23,14 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+import workloads as wl  # noqa: E402  (seeded inputs and shapes only)
+
 METRIC = ("W4A8 GEMM TOPS + weight-stream GB/s at Llama-7B/70B linear shapes, "
           "M=1..4096")
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
-CFG = 3
+CFG = wl.LLAMA70B_SWEEP
 MS = (1, 16, 128, 1024, 4096)
 
 
@@ -416,8 +418,8 @@ def main():
     # per-channel scales, and per-group scales folded into the FP8 weights
     # with a per-tensor rescale; prefill shape and a 16-token decode shape
     if not args.no_fp8 and not args.only:
-        sh = wl.CONFIGS[4].shapes[0]
-        Wf = torch.from_numpy(wl.gen_weights(sh.N, sh.K, wl.seed_w(4))).to(dev)
+        sh = wl.CONFIGS[wl.FP8_VARIANT].shapes[0]
+        Wf = torch.from_numpy(wl.gen_weights(sh.N, sh.K, wl.seed_w(wl.FP8_VARIANT))).to(dev)
         pk8 = w4.pack(Wf, mode=w4.PACK_INT4_SYM)
         pk8g = w4.pack_fp8g(Wf, group=128)
         del Wf
@@ -428,8 +430,8 @@ def main():
                         for _ in range(ncp - 1)]
         cps8g = [pk8g] + [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in pk8g.items()}
                           for _ in range(ncp - 1)]
-        Xf = torch.from_numpy(wl.gen_activations(sh.M, sh.K, wl.seed_x(4),
-                                                 wl.seed_outliers(4))).to(dev)
+        Xf = torch.from_numpy(wl.gen_activations(sh.M, sh.K, wl.seed_x(wl.FP8_VARIANT),
+                                                 wl.seed_outliers(wl.FP8_VARIANT))).to(dev)
         X8, sx8 = w4.quant_act_fp8(Xf)
         del Xf
 

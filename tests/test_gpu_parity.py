@@ -749,9 +749,8 @@ def test_fp8g_end_to_end_device_pack():
 
 
 # ------------------------------------------- Llama-shaped workloads --------
-_FULL = [(1, sh) for sh in wl.CONFIGS[1].shapes] + \
-        [(2, sh) for sh in wl.CONFIGS[2].shapes] + \
-        [(3, sh) for sh in wl.CONFIGS[3].shapes]
+_FULL = [(c, sh) for c in (wl.LLAMA7B_DECODE, wl.LLAMA7B_PREFILL, wl.LLAMA70B_SWEEP)
+         for sh in wl.CONFIGS[c].shapes]
 
 _packed_cache = {}
 
@@ -802,10 +801,10 @@ def test_llama_shapes_sampled(cfg, sh):
 
 
 def test_fp8_variant_full_size_sampled():
-    sh = wl.CONFIGS[4].shapes[0]
+    sh = wl.CONFIGS[wl.FP8_VARIANT].shapes[0]
     say(f"full-size {sh.name}: M={sh.M} N={sh.N} K={sh.K}")
-    W = wl.gen_weights(sh.N, sh.K, wl.seed_w(4))
-    X = wl.gen_activations(sh.M, sh.K, wl.seed_x(4), wl.seed_outliers(4))
+    W = wl.gen_weights(sh.N, sh.K, wl.seed_w(wl.FP8_VARIANT))
+    X = wl.gen_activations(sh.M, sh.K, wl.seed_x(wl.FP8_VARIANT), wl.seed_outliers(wl.FP8_VARIANT))
     pk = w4.pack(to_dev(W), mode=w4.PACK_INT4_SYM)
     Xq, sx = w4.quant_act_fp8(to_dev(X))
     Yf = w4.gemm_fp8(Xq, sx, pk, out_type=w4.OUT_F32)

@@ -54,20 +54,28 @@ def _sweep(cfg, name, Ms, NK, group):
     return tuple(out)
 
 
+# Workload ids (they also select the seeds below).
+TINY = 0               # one small GEMM the oracle finishes at once
+LLAMA7B_DECODE = 1     # Llama-2-7B attention projections, 1-16 tokens
+LLAMA7B_PREFILL = 2    # Llama-2-7B MLP, 2048 tokens
+LLAMA70B_SWEEP = 3     # Llama-2-70B MLP, 1 .. 4096 tokens
+FP8_VARIANT = 4        # INT4 x FP8, 2048 x 8192 x 8192
+
 # Workloads: the Llama-2 linear-layer shapes (7B: hidden 4096, MLP 11008;
 # 70B: hidden 8192, MLP 28672) at decode and prefill token counts.
 CONFIGS = {
-    0: Config(0, "tiny", (Shape(16, 256, 512, 64, "tiny:M16"),)),
-    1: Config(1, "llama2-7b attn-proj decode",
-              _sweep(1, "7b-attn", (1, 4, 16), ((4096, 4096, "qkvo"),), 64)),
-    2: Config(2, "llama2-7b mlp prefill",
-              _sweep(2, "7b-mlp", (2048,), ((11008, 4096, "upgate"),
-                                          (4096, 11008, "down")), 64)),
-    3: Config(3, "llama2-70b linear sweep",
-              _sweep(3, "70b", (1, 16, 128, 1024, 4096),
-                     ((28672, 8192, "upgate"), (8192, 28672, "down")), 128)),
-    4: Config(4, "int4-fp8 variant", (Shape(2048, 8192, 8192, 0, "fp8:M2048"),),
-              fp8=True),
+    TINY: Config(TINY, "tiny", (Shape(16, 256, 512, 64, "tiny:M16"),)),
+    LLAMA7B_DECODE: Config(LLAMA7B_DECODE, "llama2-7b attn-proj decode",
+                           _sweep(LLAMA7B_DECODE, "7b-attn", (1, 4, 16),
+                                  ((4096, 4096, "qkvo"),), 64)),
+    LLAMA7B_PREFILL: Config(LLAMA7B_PREFILL, "llama2-7b mlp prefill",
+                            _sweep(LLAMA7B_PREFILL, "7b-mlp", (2048,),
+                                   ((11008, 4096, "upgate"), (4096, 11008, "down")), 64)),
+    LLAMA70B_SWEEP: Config(LLAMA70B_SWEEP, "llama2-70b linear sweep",
+                           _sweep(LLAMA70B_SWEEP, "70b", (1, 16, 128, 1024, 4096),
+                                  ((28672, 8192, "upgate"), (8192, 28672, "down")), 128)),
+    FP8_VARIANT: Config(FP8_VARIANT, "int4-fp8 variant",
+                        (Shape(2048, 8192, 8192, 0, "fp8:M2048"),), fp8=True),
 }
 
 
