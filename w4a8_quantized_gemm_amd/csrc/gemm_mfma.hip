@@ -595,6 +595,15 @@ MfmaPlan plan_w4a8_mfma(int M, int N, int K) {
         p.splits = s;
     }
     p.workspace = p.splits > 1 ? (size_t)p.splits * M * N * sizeof(int) : 0;
+    // Integer kernels: workgroups with at most 64 K-steps run 128-row tiles
+    // on the 16 x 16 kernel, two per CU, so one workgroup's prologue and
+    // epilogue overlap the other's main loop (measured: 2048 x 11008 x 4096
+    // 20 % faster, 1024 x 28672 x 8192 6 %, the split-K mid-M plans 1-6 %);
+    // longer ones keep 256-row tiles (the amortised switch costs less than
+    // the doubled decode per row), or the 32 x 32 kernel for 128-row plans.
+    // A 256 -> 128 switch keeps splits = 1 (the grid only grows).
+    const bool short_k = KT / p.splits <= 64;
+    p.mt16 = short_k ? 128 : (p.mt == 256 ? 256 : 0);
     return p;
 }
 
@@ -654,16 +663,20 @@ static hipError_t run_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
     return launch_splitk_reduce(part, plan.splits, M, N, sx, sw, Y, out_type, st);
 }
 
-// 256-row plans run the 16 x 16 x 64 kernel (3-6 % faster there, same
-// results bit for bit); 128-row plans this kernel, which is faster at that
-// height (the 16 x 16 slots leave less room for the decode per weight).
+// Kernel choice by plan.mt16: the 16 x 16 x 64 kernel (256-row tiles, 3-6 %
+// faster than this one there; or 128-row tiles two per CU for short K), else
+// this kernel with 128-row tiles (faster than the 16 x 16 one at that height
+// with one workgroup per CU).  Results are the same bit for bit.
 hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
                             const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
                             int out_type, int M, int N, int K, int group, const MfmaPlan& plan,
                             void* workspace, hipStream_t st) {
-    if (plan.mt == 256)
-        return launch_w4a8_mfma16(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, plan,
+    if (plan.mt16 != 0) {
+        MfmaPlan p = plan;
+        p.mt = plan.mt16;
+        return launch_w4a8_mfma16(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, p,
                                   workspace, st);
+    }
     return run_mfma<DecLQQ>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, plan,
                             workspace, st);
 }
@@ -671,8 +684,11 @@ hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
 hipError_t launch_w8a8_mfma(const int8_t* X, const float* sx, const int8_t* wq8, const float* sw,
                             void* Y, int out_type, int M, int N, int K, const MfmaPlan& plan,
                             void* workspace, hipStream_t st) {
-    if (plan.mt == 256)  // same kernel choice as the W4A8 GEMM
-        return launch_w8a8_mfma16(X, sx, wq8, sw, Y, out_type, M, N, K, plan, workspace, st);
+    if (plan.mt16 != 0) {  // same kernel choice as the W4A8 GEMM
+        MfmaPlan p = plan;
+        p.mt = plan.mt16;
+        return launch_w8a8_mfma16(X, sx, wq8, sw, Y, out_type, M, N, K, p, workspace, st);
+    }
     return run_mfma<DecW8>(X, sx, reinterpret_cast<const uint8_t*>(wq8), nullptr, nullptr, sw, Y,
                            out_type, M, N, K, 128, plan, workspace, st);
 }

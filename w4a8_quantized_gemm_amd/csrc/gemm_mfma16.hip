@@ -142,8 +142,10 @@ __device__ __forceinline__ void mfma16_drain(v4i (&acc)[RB][4]) {
 }  // namespace
 
 // W8: the W8A8 comparison on this skeleton (no decode, no parameters).
+// 128-row tiles fit two workgroups per CU (128 accumulator registers per
+// lane, at most 128 others), 256-row tiles one.
 template <int MT, int OUT, int GROUP, bool PARTIAL, bool W8>
-__global__ __launch_bounds__(256, 1) void w4a8_mfma16_kernel(
+__global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4a8_mfma16_kernel(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ s_u8, const uint8_t* __restrict__ a_u8,
     const float* __restrict__ sw, void* __restrict__ Y, int* __restrict__ part, int M, int N,
