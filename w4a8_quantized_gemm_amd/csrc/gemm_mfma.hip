@@ -597,13 +597,16 @@ MfmaPlan plan_w4a8_mfma(int M, int N, int K) {
     p.workspace = p.splits > 1 ? (size_t)p.splits * M * N * sizeof(int) : 0;
     // Integer kernels: workgroups with at most 64 K-steps run 128-row tiles
     // on the 16 x 16 kernel, two per CU, so one workgroup's prologue and
-    // epilogue overlap the other's main loop (measured: 2048 x 11008 x 4096
-    // 20 % faster, 1024 x 28672 x 8192 6 %, the split-K mid-M plans 1-6 %);
-    // longer ones keep 256-row tiles (the amortised switch costs less than
-    // the doubled decode per row), or the 32 x 32 kernel for 128-row plans.
-    // A 256 -> 128 switch keeps splits = 1 (the grid only grows).
+    // epilogue overlap the other's main loop, where 256-row tiles would make
+    // fewer than four waves (measured: 2048 x 11008 x 4096 20 % faster,
+    // 1024 x 28672 x 8192 6 %, 4096 x 8192 x 8192 2.5 %, the split-K mid-M
+    // plans 1-6 %).  With more waves (4096 x 28672 x 8192: equal time, 1.4x
+    // the HBM traffic, each weight read for twice as many row tiles) and for
+    // longer K, 256-row tiles stay; 128-row plans with long K keep the
+    // 32 x 32 kernel.  A 256 -> 128 switch keeps splits = 1.
     const bool short_k = KT / p.splits <= 64;
-    p.mt16 = short_k ? 128 : (p.mt == 256 ? 256 : 0);
+    const bool few_waves = p.mt == 128 || t256 < 4 * 256;
+    p.mt16 = (short_k && few_waves) ? 128 : (p.mt == 256 ? 256 : 0);
     return p;
 }
 
