@@ -163,9 +163,11 @@ size_t w4a8_workspace_size(int M, int N, int K, int splitk);
  * X: int8 [M][K] per-token quantised; wq, s_u8, a_u8, sw from w4a8_pack
  * (LQQ mode, same N, K, group); Y: fp16 or int32 [M][N].
  * Kernel choice is a function of the shape: M >= 64 with N % 256 == 0 runs
- * a matrix-core tile kernel (128-row workgroup tiles on 32 x 32 x 32
- * instructions, 256-row tiles on 16 x 16 x 64); otherwise the streamed-tile
- * kernel runs, with `splitk` K-slices per output tile.
+ * a matrix-core tile kernel (256-row workgroup tiles on 16 x 16 x 64
+ * instructions; 128-row tiles on 16 x 16 x 64 at two workgroups per CU when
+ * a workgroup covers at most 64 K-steps of a grid under four waves, else
+ * on 32 x 32 x 32); otherwise the streamed-tile kernel runs, with `splitk`
+ * K-slices per output tile.
  * splitk: 0 = automatic; 1, 2, 4, 8 or 16 (at most K/128) forces the
  * streamed-tile kernel with that split.  The int32 result depends on
  * neither choice.
@@ -207,8 +209,9 @@ w4a8_status_t w4a8_gemm_grouped(const int8_t* X, const float* sx,
  * the method's two ideas buy on this hardware ([LG] referee summary: the
  * ablation separating LiquidQuant from the pipeline; "What carries the
  * argument").  All three run on the 32 x 32 x 32 tile kernel (the one
- * w4a8_gemm uses for 128-row tiles; its 256-row tiles use a 16 x 16 x 64
- * kernel with the same decode), so they differ only in the decode:
+ * w4a8_gemm uses for long-K 128-row tiles; its other plans use a
+ * 16 x 16 x 64 kernel with the same decode), so they differ only in the
+ * decode:
  *   W4A8_ABL_LQQ          LiquidQuant decode interleaved with the matrix
  *                         cores (the method);
  *   W4A8_ABL_AFFINE16     same stored codes and parameters, decoded as the
