@@ -50,8 +50,9 @@ struct MfmaPlan {
     int mt;
     int splits;
     size_t workspace;  // bytes of 4-byte partials (0 when splits == 1)
-    // W4A8 / W8A8 kernel choice: tile height for the 16 x 16 x 64 kernel
-    // (128: two workgroups per CU), or 0 for the 32 x 32 x 32 kernel at mt.
+    // Integer kernels: tile height for the 16 x 16 x 64 kernel (128: two
+    // workgroups per CU), or 0 for the 32 x 32 x 32 kernel at mt.  The FP8
+    // tile kernel runs 128-row tiles (two per CU) when mt16 == 128, else mt.
     int mt16;
 };
 MfmaPlan plan_w4a8_mfma(int M, int N, int K);
