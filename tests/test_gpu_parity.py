@@ -281,6 +281,7 @@ def test_ablation_variants_bit_identical(M, N, K, g):
     ([33, 7, 0, 40], 128, 1024, 64),          # ragged, several 16-row blocks
     ([70, 0, 130, 300], 512, 640, 128),       # matrix-core tiles, odd K-steps
     ([257, 64, 1], 256, 512, 64),             # tiles; an expert with one row
+    ([1100, 0, 37, 1500], 256, 512, 128),     # >= 1024 rows: two tile workgroups per CU
 ])
 def test_grouped_gemm_parity(counts, N, K, g):
     """Each expert's rows equal w4a8_gemm of those rows against that
