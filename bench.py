@@ -31,6 +31,7 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 INT8_PEAK_TOPS = 5000.0        # MI355X dense INT8 MFMA, TOP/s
 FP8_PEAK_TFLOPS = 5000.0       # MI355X dense FP8 MFMA, TFLOP/s
 CFG = wl.LLAMA70B_SWEEP
+DOMINANT_SLOT = "upgate:M4096"  # 4096 x 28672 x 8192: the largest share of a step
 MS = (1, 16, 128, 1024, 4096)
 
 
@@ -190,10 +191,13 @@ def main():
         print(f"unknown slot {args.only}", file=sys.stderr)
         sys.exit(2)
 
-    # HIP events around a launch cost several microseconds of queue time
-    # each, so inside the timed region only the matrix-core slots (where the
-    # dominant kernel is, and where that cost is below 1 %) are bracketed.
-    evslots = [i for i, s in enumerate(slots) if s["M"] >= 1024] or list(range(len(slots)))
+    # HIP events inside the timed region bracket only the dominant slot (the
+    # largest share of the step), whose kernel the roofline reports: each
+    # further event pair cost about 6 us of step time (measured: events on
+    # the four M >= 1024 slots, 2.065 ms per step; on this slot alone, 2.047,
+    # equal to none).
+    evslots = ([i for i, s in enumerate(slots) if s["name"] == DOMINANT_SLOT]
+               or list(range(len(slots))))
     evpos = {i: j for j, i in enumerate(evslots)}
 
     def step(evs=None):
