@@ -491,6 +491,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     __syncthreads();
     constexpr int EB = SCALED ? 2 : 4;       // output element bytes
     constexpr int ROWB = 64 * EB;             // bytes per staged row
+    static_assert(kWaves * 32 * ROWB <= 3 * XB, "epilogue staging fits in the X tiles");
     uint8_t* stage = xs + wave * (32 * ROWB);
     uint8_t* out = PARTIAL ? reinterpret_cast<uint8_t*>(part + (size_t)ks * M * N)
                            : reinterpret_cast<uint8_t*>(Y);
