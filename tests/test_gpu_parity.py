@@ -167,8 +167,9 @@ def test_w4a8_gemm_parity(M, N, K, g):
     assert d.max() <= 1
 
 
-# Shapes that the dispatcher sends to the matrix-core tile kernel (N a
-# multiple of 256, M >= 64), with 128- and 256-row tiles, ragged M, and odd
+# Shapes that the dispatcher sends to the matrix-core tile kernels (N a
+# multiple of 256, M >= 64): 128-row tiles (short K: two per CU on the
+# 16 x 16 x 64 kernel), ragged M, and odd
 # K-step counts (640 = 5 steps, 896 = 7): an odd count runs one extra step of
 # zero X, and the accumulators' last writes must be complete before the
 # epilogue reads them.
@@ -192,8 +193,8 @@ def test_w4a8_gemm_mfma_parity(M, N, K, g):
 
 
 def test_mfma_tiles_full_grid():
-    """Enough workgroups for the 256-row tile and the XCD regrouping
-    (workgroup count a multiple of 8)."""
+    """A grid large enough for the XCD regrouping (workgroup count a
+    multiple of 8)."""
     M, N, K, g = 1024, 2048, 512, 64
     say(f"w4a8 mfma gemm M={M} N={N} K={K} g={g}")
     X8, sx, pk, acc, y = _small_problem(M, N, K, g, 31)
@@ -202,11 +203,13 @@ def test_mfma_tiles_full_grid():
     np.testing.assert_array_equal(host(Yi), acc)
 
 
-# 256-row tiles need at least 256 workgroups: M x N = 4096 x 4096 and more.
-# K = 384 gives an odd number of K-steps (the unrolled loop's tail step).
+# Large grids (at least 256 tiles of 256 rows: M x N = 4096 x 4096 and more)
+# with short K, which run 128-row tiles two per CU (256-row tiles, kept for
+# long K, are covered by test_256_row_tiles_long_k).  K = 384 gives an odd
+# number of K-steps (the unrolled loop's tail step).
 @pytest.mark.parametrize("M,N,K,g", [(4000, 4096, 384, 128), (4096, 4096, 512, 64)])
-def test_mfma256_tiles(M, N, K, g):
-    say(f"w4a8 mfma256 gemm M={M} N={N} K={K} g={g}")
+def test_large_grid_tiles(M, N, K, g):
+    say(f"w4a8 large-grid gemm M={M} N={N} K={K} g={g}")
     X8, sx, pk, acc, y = _small_problem(M, N, K, g, 41 + K)
     Yi = poison((M, N), torch.int32)
     w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, out=Yi)
@@ -217,12 +220,12 @@ def test_mfma256_tiles(M, N, K, g):
     assert d.max() <= 1
 
 
-# More than one wave of 256-row tiles (512, 544 and 768 tiles for 256
-# compute units): ragged M, K-step counts 2 and 4, a partial last wave.
+# Several waves of tiles (512, 544 and 768 tiles of 256 rows, run as 128-row
+# tiles two per CU): ragged M, K-step counts 2 and 4, a partial last wave.
 @pytest.mark.parametrize("M,N,K,g", [(4000, 8192, 512, 128), (4352, 8192, 256, 64),
                                      (4096, 12288, 512, 64)])
-def test_mfma256_several_waves(M, N, K, g):
-    say(f"w4a8 mfma256 gemm, several waves of tiles: M={M} N={N} K={K} g={g}")
+def test_large_grid_several_waves(M, N, K, g):
+    say(f"w4a8 gemm, several waves of tiles: M={M} N={N} K={K} g={g}")
     assert w4.workspace_size(M, N, K) == 0
     X8, sx, pk, acc, y = _small_problem(M, N, K, g, 61 + K)
     Yi = poison((M, N), torch.int32)
@@ -257,8 +260,10 @@ def test_mfma_split_k(M, N, K, g):
 def test_ablation_variants_bit_identical(M, N, K, g):
     """The conventional affine decode and the coarse pipeline produce the
     same int32 accumulators (bit-exact vs the oracle) and the same fp16 as
-    the production kernel.  Shapes the unsplit tile kernel serves: 128-row
-    tiles with one to seven K-steps, and 256-row tiles (last case)."""
+    the production kernel.  Shapes the unsplit tile kernels serve: 128-row
+    tiles with one to seven K-steps, and a grid of 256 tiles of 256 rows
+    (last case: the ablation kernels run 256-row tiles there, the product
+    path 128-row tiles two per CU)."""
     say(f"ablation variants M={M} N={N} K={K} g={g}")
     X8, sx, pk, acc, y = _small_problem(M, N, K, g, 11)
     ref16 = None
@@ -500,12 +505,12 @@ def test_w4fp8_tile_parity(M, N, K):
     assert np.all(np.abs(host(Ys) - ref) <= bound + 1e-30)
 
 
-# 256-row FP8 tiles (at least 256 of them: M x N = 4096 x 4096 and more) run
-# on the 16 x 16 x 128 kernel.  K = 384: odd K-step count (the tail step);
-# M = 4000: ragged last row tile.
+# Large FP8 grids (at least 256 tiles of 256 rows: M x N = 4096 x 4096 and
+# more) with short K, which run 128-row tiles two per CU.  K = 384: odd
+# K-step count (the tail step); M = 4000: ragged last row tile.
 @pytest.mark.parametrize("M,N,K", [(4000, 4096, 384), (4096, 4096, 512)])
-def test_w4fp8_256_row_tiles(M, N, K):
-    say(f"w4fp8 256-row tiles M={M} N={N} K={K} workspace={w4.workspace_size(M, N, K)}")
+def test_w4fp8_large_grid(M, N, K):
+    say(f"w4fp8 large grid M={M} N={N} K={K} workspace={w4.workspace_size(M, N, K)}")
     assert w4.workspace_size(M, N, K) == 0
     # integer-valued operands: exact in any summation order, bit for bit
     rng = np.random.default_rng(M + K)
@@ -568,8 +573,8 @@ def test_w8a8_pack_parity(N, K):
                                       (128, 256, 4096, 0), (100, 256, 896, 2), (257, 1024, 256, 0)])
 def test_w8a8_gemm_parity(M, N, K, sk):
     """int32 bit-exact and fp16 within 1 ulp against the oracle: streamed
-    kernel (M < 64, N % 256 != 0, or forced by splitk), tile kernel with
-    128- and 256-row tiles, ragged M, odd K-step counts and planned split-K."""
+    kernel (M < 64, N % 256 != 0, or forced by splitk), tile kernels with
+    128-row tiles, ragged M, odd K-step counts and planned split-K."""
     say(f"w8a8 gemm M={M} N={N} K={K} splitk={sk} workspace={w4.workspace_size(M, N, K, sk)}")
     W = wl.gen_weights(N, K, 1200 + M + N)
     X = wl.gen_activations(M, K, 1201 + M, 1202)
@@ -590,13 +595,14 @@ def test_w8a8_gemm_parity(M, N, K, sk):
         np.testing.assert_array_equal(host(Ys), acc)
 
 
-def test_w8a8_256_row_tiles():
-    """W8A8 on 256-row tiles (the 16 x 16 x 64 tile kernel): int32 bit-exact
+def test_w8a8_large_grid():
+    """W8A8 on a large short-K grid (128-row tiles two per CU on the
+    16 x 16 x 64 tile kernel): int32 bit-exact
     against the oracle on sampled rows and against the streamed kernel on
     every element; fp16 within 1 ulp on the sampled rows."""
     M, N, K = 4096, 4096, 384
     assert w4.workspace_size(M, N, K) == 0
-    say(f"w8a8 256-row tiles M={M} N={N} K={K}")
+    say(f"w8a8 large grid M={M} N={N} K={K}")
     W = wl.gen_weights(N, K, 1301)
     X = wl.gen_activations(M, K, 1302, 1303)
     ref = oracle.w8a8_pack(W)
@@ -701,13 +707,13 @@ def test_fp8g_gemm_parity(M, N, K, g):
     assert np.all(np.abs(host(Ys) - ref) <= bound + 1e-30)
 
 
-# Folded format on 256-row tiles (16 x 16 x 128 kernel): identity X with
-# M = K = 4096 checks every folded e4m3 weight bit for bit; realistic data
-# with ragged M and an odd K-step count against the double reference.
+# Folded format on large short-K grids (128-row tiles two per CU): identity X
+# with M = K = 4096 checks every folded e4m3 weight bit for bit; realistic
+# data with ragged M and an odd K-step count against the double reference.
 @pytest.mark.parametrize("g", [64, 128])
-def test_fp8g_256_row_tiles(g):
+def test_fp8g_large_grid(g):
     N = K = 4096
-    say(f"w4fp8g 256-row tiles identity K={K} N={N} g={g}")
+    say(f"w4fp8g large grid, identity X: K={K} N={N} g={g}")
     assert w4.workspace_size(K, N, K) == 0
     W = _fp8g_weights(N, K, g, 710 + g)
     ref = oracle.w4fp8g_pack(W, g)
@@ -720,7 +726,7 @@ def test_fp8g_256_row_tiles(g):
     np.testing.assert_array_equal(host(Y).view(np.uint32), want.astype(np.float32).view(np.uint32))
     del Y
     M, K = 4000, 384
-    say(f"w4fp8g 256-row tiles M={M} N={N} K={K} g={g}")
+    say(f"w4fp8g large grid M={M} N={N} K={K} g={g}")
     W = _fp8g_weights(N, K, g, 720 + g)
     X = wl.gen_activations(M, K, 721, 722)
     ref_pk = oracle.w4fp8g_pack(W, g)
@@ -733,6 +739,91 @@ def test_fp8g_256_row_tiles(g):
     Yb = poison((M, N), torch.bfloat16)
     w4.gemm_fp8g(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_BF16, out=Yb)
     _check_fp8_outputs(host(Yf), bf16_bits_of(Yb), ref, bound)
+
+
+def test_256_row_tiles_long_k():
+    """Plans with more than 64 K-steps per workgroup keep 256-row tiles
+    (4000 x 4096 x 8320: 65 K-steps, the odd tail step, a ragged last row
+    tile), for all four tile GEMMs.  Sampled rows against the oracle (it
+    quantises per row, so a row sample is exact): W4A8 and W8A8 int32
+    bit-exact and fp16 within 1 ulp; FP8 per-channel and folded g = 128
+    inside the FP8 bound."""
+    M, N, K, g = 4000, 4096, 8320, 128
+    assert w4.workspace_size(M, N, K) == 0
+    say(f"256-row tiles, long K: M={M} N={N} K={K}")
+    rows = np.unique(np.concatenate([[0, 255, 256, 3839, 3840, M - 1],
+                                     np.random.default_rng(17).choice(M, 10, replace=False)]))
+    W = wl.gen_weights(N, K, 1401)
+    X = wl.gen_activations(M, K, 1402, 1403)
+    # W4A8
+    ref = oracle.w4a8_pack(W, g)
+    X8, sx = oracle.quant_sym_rows(X, 127)
+    pk = {"wq": to_dev(ref["wq"]), "s_u8": to_dev(ref["s_panels"]),
+          "a_u8": to_dev(ref["a_panels"]), "sw": to_dev(ref["sw"]), "N": N, "K": K, "group": g}
+    Yi = poison((M, N), torch.int32)
+    w4.gemm(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_I32, out=Yi)
+    Yh = poison((M, N), torch.float16)
+    w4.gemm(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F16, out=Yh)
+    acc, y, _ = oracle.w4a8_gemm(X8[rows], sx[rows], ref, g)
+    np.testing.assert_array_equal(host(Yi)[rows], acc)
+    assert f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16)[rows], y).max() <= 1
+    del Yi, Yh, pk
+    # W8A8
+    ref8 = oracle.w8a8_pack(W)
+    pk8 = {"wq8": to_dev(ref8["wq8"]), "sw": to_dev(ref8["sw"]), "N": N, "K": K}
+    Yi = poison((M, N), torch.int32)
+    w4.gemm_w8a8(to_dev(X8), to_dev(sx), pk8, out_type=w4.OUT_I32, out=Yi)
+    acc8, _, _ = oracle.w8a8_gemm(X8[rows], sx[rows], ref8)
+    np.testing.assert_array_equal(host(Yi)[rows], acc8)
+    del Yi, pk8
+    # FP8, per-channel and folded
+    Xe, sxe = oracle.quant_rows_e4m3(X)
+    pf = oracle.w4fp8_pack(W)
+    pkf = {"wq": to_dev(pf["wq"]), "sw": to_dev(pf["sw"]), "N": N, "K": K}
+    Yf = poison((M, N), torch.float32)
+    w4.gemm_fp8(to_dev(Xe), to_dev(sxe), pkf, out_type=w4.OUT_F32, out=Yf)
+    reff, _ = oracle.w4fp8_ref(Xe[rows], sxe[rows], pf["q"], pf["sw"])
+    bound = _fp8_bound(Xe[rows], sxe[rows], pf["q"], pf["sw"])
+    yf = host(Yf)[rows].astype(np.float64)
+    assert np.all(np.abs(yf - reff) <= bound + 1e-30) and rel_fro(yf, reff) <= 1e-3
+    pg = oracle.w4fp8g_pack(W, g)
+    Yf = poison((M, N), torch.float32)
+    w4.gemm_fp8g(to_dev(Xe), to_dev(sxe), _fp8g_device(pg, N, K, g), out_type=w4.OUT_F32, out=Yf)
+    refg, _ = oracle.w4fp8g_ref(Xe[rows], sxe[rows], pg["w8"], pg["t"])
+    boundg = _fp8_bound_w(Xe[rows], sxe[rows], np.abs(oracle.e4m3_decode(pg["w8"])), pg["t"])
+    yg = host(Yf)[rows].astype(np.float64)
+    assert np.all(np.abs(yg - refg) <= boundg + 1e-30) and rel_fro(yg, refg) <= 1e-3
+
+
+def test_128_row_tiles_long_k():
+    """128-row plans with more than 64 K-steps per workgroup run the
+    32 x 32 x 32 tile kernel (1000 x 8192 x 8320: 256 tiles, no split, 65
+    K-steps, ragged last row tile): sampled rows, int32 bit-exact and fp16
+    within 1 ulp, for W4A8 and W8A8."""
+    M, N, K, g = 1000, 8192, 8320, 64
+    assert w4.workspace_size(M, N, K) == 0
+    say(f"128-row tiles, long K: M={M} N={N} K={K} g={g}")
+    rows = np.unique(np.concatenate([[0, 127, 128, 895, 896, M - 1],
+                                     np.random.default_rng(19).choice(M, 10, replace=False)]))
+    W = wl.gen_weights(N, K, 1501)
+    X = wl.gen_activations(M, K, 1502, 1503)
+    ref = oracle.w4a8_pack(W, g)
+    X8, sx = oracle.quant_sym_rows(X, 127)
+    pk = {"wq": to_dev(ref["wq"]), "s_u8": to_dev(ref["s_panels"]),
+          "a_u8": to_dev(ref["a_panels"]), "sw": to_dev(ref["sw"]), "N": N, "K": K, "group": g}
+    Yi = poison((M, N), torch.int32)
+    w4.gemm(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_I32, out=Yi)
+    Yh = poison((M, N), torch.float16)
+    w4.gemm(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F16, out=Yh)
+    acc, y, _ = oracle.w4a8_gemm(X8[rows], sx[rows], ref, g)
+    np.testing.assert_array_equal(host(Yi)[rows], acc)
+    assert f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16)[rows], y).max() <= 1
+    ref8 = oracle.w8a8_pack(W)
+    pk8 = {"wq8": to_dev(ref8["wq8"]), "sw": to_dev(ref8["sw"]), "N": N, "K": K}
+    Yi = poison((M, N), torch.int32)
+    w4.gemm_w8a8(to_dev(X8), to_dev(sx), pk8, out_type=w4.OUT_I32, out=Yi)
+    acc8, _, _ = oracle.w8a8_gemm(X8[rows], sx[rows], ref8)
+    np.testing.assert_array_equal(host(Yi)[rows], acc8)
 
 
 def test_fp8g_end_to_end_device_pack():
