@@ -99,8 +99,13 @@ __device__ __forceinline__ void e4m3_fold_table(float f, unsigned& lo, unsigned&
     hi = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(f6, f7, u, true);
 }
 
-// float -> IEEE binary16 bits, nearest-even (hardware conversion).
+// float -> IEEE binary16 bits, nearest-even (hardware conversion).  The
+// empty statement makes `v` a rounded float first: without it the compiler
+// may fuse the multiply that produced `v` with the conversion (one rounding
+// instead of two) in some kernels and not in others, and the epilogues of
+// the different kernels would not agree bit for bit.
 __device__ __forceinline__ unsigned short f32_to_f16_bits(float v) {
+    asm("" : "+v"(v));
     _Float16 h = (_Float16)v;
     return __builtin_bit_cast(unsigned short, h);
 }

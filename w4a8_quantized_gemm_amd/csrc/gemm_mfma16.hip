@@ -18,7 +18,10 @@
 //   A operand (row block rb, half u): X row 16 rb + r, columns
 //     32G + 16u .. +15 -- the same K columns, so A and B agree whatever the
 //     instruction's internal K order;
-//   accumulator register v: row 16 rb + 4G + v, channel 16 cb + r.
+//   the instruction takes the weights as its first operand and X as its
+//   second, so it accumulates (W X^T) blocks: accumulator register v of the
+//   lane holds row 16 rb + r, channel 16 cb + 4G + v -- four consecutive
+//   channels of one row, which the epilogue stores straight from registers.
 // One K-step (128 columns) is 8 MT/16 instructions in two groups of half
 // the slots (u = 0, 1), each walking row blocks with the four channel
 // blocks innermost.  Group 0 decodes B[*][1] of this step from the raw
@@ -308,7 +311,7 @@ __global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4a8_mfma16_kernel(
                 ring[0] = read_a(nxt, 0);
                 ring[1] = read_a(nxt, 1);
             }
-            mfma16_i8_acc(acc[rb][cb], ring[sI % 4], B[cb][u]);
+            mfma16_i8_acc(acc[rb][cb], B[cb][u], ring[sI % 4]);
             if constexpr (cb == 0 && sI + 2 < 2 * RB) ring[(sI + 2) % 4] = read_a(cur, sI + 2);
             if constexpr (s >= GS && s < GS + kLoads) w_load(kw2, s - GS, wcur);
             if constexpr (s == GS) touch_raw16(wnx);
@@ -348,19 +351,25 @@ __global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4a8_mfma16_kernel(
     __syncthreads();  // all waves done with the X tiles
 
     // ---- epilogue.  Accumulator (rb, cb) register v of lane (r, G): row
-    // 16 rb + 4G + v, channel n0 + 16 cb + r.  Two row blocks at a time go to
-    // a per-wave LDS block [32 rows][64 channels]; each row is then written
-    // as whole 16-byte pieces (final output, or this split's int32 partial).
+    // 16 rb + r, channel n0 + 16 cb + 4G + v.  Two row blocks at a time go to
+    // a per-wave LDS block [32 rows][64 channels] -- each lane writes its four
+    // consecutive channels as one 8-byte (fp16) or 16-byte (int32) piece, rows
+    // padded by 16 bytes so a write touches distinct banks -- and each row is
+    // then written to memory as whole 16-byte pieces of one 128-byte segment
+    // (final output, or this split's int32 partial).
     constexpr bool SCALED = (OUT == 0) && !PARTIAL;
     if (SCALED) sxs[tid % MT] = (m0 + tid % MT < row_hi) ? sx[m0 + tid % MT] : 0.0f;
-    float swv[4];
+    float swv[4][4];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb) swv[cb] = SCALED ? sw[n0 + 16 * cb + r] : 0.0f;
+    for (int cb = 0; cb < 4; ++cb)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) swv[cb][v] = SCALED ? sw[n0 + 16 * cb + 4 * G + v] : 0.0f;
     __syncthreads();
     constexpr int EB = SCALED ? 2 : 4;  // output element bytes
-    constexpr int ROWB = 64 * EB;       // bytes per staged row
-    static_assert(kWaves * 32 * ROWB <= 3 * XB, "epilogue staging fits in the X tiles");
-    uint8_t* stage = xs + wave * (32 * ROWB);
+    constexpr int ROWB = 64 * EB;       // bytes per row of the block
+    constexpr int RSTR = ROWB + 16;     // padded row stride in LDS
+    static_assert(kWaves * 32 * RSTR <= 3 * XB, "epilogue staging fits in the X tiles");
+    uint8_t* stage = xs + wave * (32 * RSTR);
     uint8_t* out = PARTIAL ? reinterpret_cast<uint8_t*>(part + (size_t)ks * M * N)
                            : reinterpret_cast<uint8_t*>(Y);
 #pragma unroll
@@ -368,32 +377,34 @@ __global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4a8_mfma16_kernel(
 #pragma unroll
         for (int rr = 0; rr < 2; ++rr) {
             const int rb = 2 * rp + rr;
+            uint8_t* srow = stage + (16 * rr + r) * RSTR;
+            const float sm = SCALED ? sxs[16 * rb + r] : 0.0f;
 #pragma unroll
             for (int cb = 0; cb < 4; ++cb) {
+                const int col = 16 * cb + 4 * G;
+                if constexpr (SCALED) {
+                    unsigned short h[4];
 #pragma unroll
-                for (int v = 0; v < 4; ++v) {
-                    const int row = 16 * rr + 4 * G + v;
-                    const int col = 16 * cb + r;
-                    if (!SCALED) {
-                        *reinterpret_cast<int*>(stage + row * ROWB + col * 4) = acc[rb][cb][v];
-                    } else {
-                        const float y = ((float)acc[rb][cb][v] * sxs[32 * rp + row]) * swv[cb];
-                        *reinterpret_cast<unsigned short*>(stage + row * ROWB + col * 2) =
-                            f32_to_f16_bits(y);
-                    }
+                    for (int v = 0; v < 4; ++v)
+                        h[v] = f32_to_f16_bits(((float)acc[rb][cb][v] * sm) * swv[cb][v]);
+                    uint2 pk;
+                    pk.x = h[0] | ((unsigned)h[1] << 16);
+                    pk.y = h[2] | ((unsigned)h[3] << 16);
+                    *reinterpret_cast<uint2*>(srow + col * 2) = pk;
+                } else {
+                    *reinterpret_cast<v4i*>(srow + col * 4) = acc[rb][cb];
                 }
             }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
         __builtin_amdgcn_wave_barrier();
-        constexpr int PIECES = 32 * ROWB / 16;  // 16-byte pieces per block
-        constexpr int PPR = ROWB / 16;          // pieces per row
+        constexpr int PPR = ROWB / 16;  // 16-byte pieces per row
 #pragma unroll
-        for (int w = 0; w < PIECES / 64; ++w) {
+        for (int w = 0; w < 32 * PPR / 64; ++w) {
             const int q = lane + 64 * w;
             const int row = q / PPR, piece = q % PPR;
             const int m = m0 + 32 * rp + row;
-            const v4i val = *reinterpret_cast<const v4i*>(stage + row * ROWB + piece * 16);
+            const v4i val = *reinterpret_cast<const v4i*>(stage + row * RSTR + piece * 16);
             if (m < row_hi)
                 *reinterpret_cast<v4i*>(out + ((size_t)m * N + n0) * EB + piece * 16) = val;
         }
