@@ -12,16 +12,16 @@
 // owning all MT rows and its 64 channels = packed tiles nt0 .. nt0+3, so a
 // weight is dequantised once per workgroup tile.  Lane (r = lane % 16,
 // G = lane / 16) of a 16 x 16 block:
-//   B operand (channel block cb = tile nt0 + cb, half u of the K-step): the
-//     lane's 16 packed bytes of the tile hold codes 32G .. 32G+31 of row r;
-//     decoded, codes 32G + 16u .. +15 are B[cb][u];
-//   A operand (row block rb, half u): X row 16 rb + r, columns
-//     32G + 16u .. +15 -- the same K columns, so A and B agree whatever the
+//   weight operand B[cb][u] (channel block cb = tile nt0 + cb, half u of the
+//     K-step): the lane's 16 packed bytes of the tile hold codes
+//     32G .. 32G+31 of row r; decoded, codes 32G + 16u .. +15;
+//   X operand (row block rb, half u): X row 16 rb + r, columns
+//     32G + 16u .. +15 -- the same K columns, so the two agree whatever the
 //     instruction's internal K order;
 //   the instruction takes the weights as its first operand and X as its
 //   second, so it accumulates (W X^T) blocks: accumulator register v of the
 //   lane holds row 16 rb + r, channel 16 cb + 4G + v -- four consecutive
-//   channels of one row, which the epilogue stores straight from registers.
+//   channels of one row, which the epilogue writes as one piece.
 // One K-step (128 columns) is 8 MT/16 instructions in two groups of half
 // the slots (u = 0, 1), each walking row blocks with the four channel
 // blocks innermost.  Group 0 decodes B[*][1] of this step from the raw
