@@ -440,7 +440,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
 #pragma unroll
                 for (int q = 0; q < 4; ++q) ring[q] = read_a(nxt, q);
             }
-            mfma32_i8_acc(acc[rb][cb], ring[sI % 8], B[cb][i]);
+            mfma32_i8_acc(acc[rb][cb], B[cb][i], ring[sI % 8]);
             if constexpr (cb == 1 && sI + 4 < 4 * RB) ring[(sI + 4) % 8] = read_a(cur, sI + 4);
             if constexpr (s >= GS && s < GS + DEC::kLoads) w_load(kw2, s - GS, wcur);
             // All of wnx complete here, before the X loads: the compiler's
@@ -480,48 +480,67 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));  // the last steps' X loads
     __syncthreads();  // all waves done with the X tiles
 
-    // ---- epilogue.  Accumulator (rb, cb) register v of lane (c, h): row
-    // 32rb + 8(v/4) + 4h + (v%4), channel n0 + 32cb + c.  Values go to a
-    // per-wave LDS block [32 rows][64 channels]; each row is then written as
-    // whole 16-byte pieces (final output, or this split's int32 partial).
+    // ---- epilogue.  The weights are the instruction's first operand and X
+    // its second, so it accumulates (W X^T) blocks: accumulator (rb, cb)
+    // register 4i + e of lane (c, h) holds row 32rb + c, channel
+    // n0 + 32cb + 8i + 4h + e -- runs of four consecutive channels.  Each run
+    // goes to a per-wave LDS block [32 rows][64 channels] as one 8-byte
+    // (fp16) or 16-byte (int32) piece, rows padded by 16 bytes; each row is
+    // then written as whole 16-byte pieces (final output, or this split's
+    // int32 partial).
     constexpr bool SCALED = (OUT == 0) && !PARTIAL;
     if (SCALED) sxs[tid % MT] = (m0 + tid % MT < row_hi) ? sx[m0 + tid % MT] : 0.0f;
-    const float sw0 = SCALED ? sw[n0 + c] : 0.0f;
-    const float sw1 = SCALED ? sw[n0 + 32 + c] : 0.0f;
+    float swv[2][4][4];
+#pragma unroll
+    for (int cb = 0; cb < 2; ++cb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                swv[cb][i][e] = SCALED ? sw[n0 + 32 * cb + 8 * i + 4 * h + e] : 0.0f;
     __syncthreads();
-    constexpr int EB = SCALED ? 2 : 4;       // output element bytes
-    constexpr int ROWB = 64 * EB;             // bytes per staged row
-    static_assert(kWaves * 32 * ROWB <= 3 * XB, "epilogue staging fits in the X tiles");
-    uint8_t* stage = xs + wave * (32 * ROWB);
+    constexpr int EB = SCALED ? 2 : 4;  // output element bytes
+    constexpr int ROWB = 64 * EB;       // bytes per row of the block
+    constexpr int RSTR = ROWB + 16;     // padded row stride in LDS
+    static_assert(kWaves * 32 * RSTR <= 3 * XB, "epilogue staging fits in the X tiles");
+    uint8_t* stage = xs + wave * (32 * RSTR);
     uint8_t* out = PARTIAL ? reinterpret_cast<uint8_t*>(part + (size_t)ks * M * N)
                            : reinterpret_cast<uint8_t*>(Y);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+        uint8_t* srow = stage + c * RSTR;
+        const float sm = SCALED ? sxs[32 * rb + c] : 0.0f;
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb) {
 #pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int row = 8 * (v >> 2) + 4 * h + (v & 3);
-                const int col = 32 * cb + c;
-                if (!SCALED) {
-                    *reinterpret_cast<int*>(stage + row * ROWB + col * 4) = acc[rb][cb][v];
+            for (int i = 0; i < 4; ++i) {
+                const int col = 32 * cb + 8 * i + 4 * h;
+                if constexpr (SCALED) {
+                    unsigned short hv[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        hv[e] = f32_to_f16_bits(((float)acc[rb][cb][4 * i + e] * sm) *
+                                                swv[cb][i][e]);
+                    uint2 pk;
+                    pk.x = hv[0] | ((unsigned)hv[1] << 16);
+                    pk.y = hv[2] | ((unsigned)hv[3] << 16);
+                    *reinterpret_cast<uint2*>(srow + col * 2) = pk;
                 } else {
-                    const float y = ((float)acc[rb][cb][v] * sxs[32 * rb + row]) * (cb ? sw1 : sw0);
-                    *reinterpret_cast<unsigned short*>(stage + row * ROWB + col * 2) =
-                        f32_to_f16_bits(y);
+                    *reinterpret_cast<v4i*>(srow + col * 4) =
+                        v4i{acc[rb][cb][4 * i], acc[rb][cb][4 * i + 1], acc[rb][cb][4 * i + 2],
+                            acc[rb][cb][4 * i + 3]};
                 }
             }
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
         __builtin_amdgcn_wave_barrier();
-        constexpr int PIECES = 32 * ROWB / 16;  // 16-byte pieces per block
-        constexpr int PPR = ROWB / 16;          // pieces per row
+        constexpr int PPR = ROWB / 16;  // 16-byte pieces per row
 #pragma unroll
-        for (int u = 0; u < PIECES / 64; ++u) {
+        for (int u = 0; u < 32 * PPR / 64; ++u) {
             const int q = lane + 64 * u;
             const int row = q / PPR, piece = q % PPR;
             const int m = m0 + 32 * rb + row;
-            const v4i val = *reinterpret_cast<const v4i*>(stage + row * ROWB + piece * 16);
+            const v4i val = *reinterpret_cast<const v4i*>(stage + row * RSTR + piece * 16);
             if (m < row_hi)
                 *reinterpret_cast<v4i*>(out + ((size_t)m * N + n0) * EB + piece * 16) = val;
         }
