@@ -314,7 +314,8 @@ def main():
     # ---- decode ablation on the matrix-core slots (outside the timed step):
     # the production LiquidQuant decode interleaved with the matrix cores, the
     # conventional signed affine decode, and the LiquidQuant decode done per
-    # K-step in one block.  Same codes, same results bit for bit.
+    # K-step in one block, all three on the 32 x 32 x 32 tile kernel.  Same
+    # codes, same results bit for bit.
     if not args.no_ablation:
         abl = []
         names = {w4.ABL_LQQ: "lqq", w4.ABL_AFFINE16: "affine16", w4.ABL_LQQ_COARSE: "lqq_coarse"}
@@ -323,15 +324,20 @@ def main():
             if sl["M"] < 1024:
                 continue
             row = {"slot": sl["name"]}
+            # the weight copies of every slot of this shape in turn, as in the
+            # sweep's bursts, so that no launch finds its weights in the cache
+            copies = [t["pk"] for t in slots if t["pair"] == sl["pair"]]
             for v, nm in names.items():
-                w4.gemm_ablation(v, sl["X"], sl["sx"], sl["pk"], out=sl["Y"])
-                reps = 5
+                w4.gemm_ablation(v, sl["X"], sl["sx"], copies[-1], out=sl["Y"])
+                reps = 2 * len(copies)
                 e0.record(stream)
-                for _ in range(reps):
-                    w4.gemm_ablation(v, sl["X"], sl["sx"], sl["pk"], out=sl["Y"])
+                for r in range(reps):
+                    w4.gemm_ablation(v, sl["X"], sl["sx"], copies[r % len(copies)], out=sl["Y"])
                 e1.record(stream)
                 torch.cuda.synchronize()
                 row[nm + "_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
+            # the production kernel choice for the same slot (from the sweep)
+            row["w4a8_gemm_us"] = next(r["us_mean"] for r in sweep if r["slot"] == sl["name"])
             row["affine16_vs_lqq"] = round(row["affine16_us"] / row["lqq_us"], 3)
             row["coarse_vs_lqq"] = round(row["lqq_coarse_us"] / row["lqq_us"], 3)
             abl.append(row)
