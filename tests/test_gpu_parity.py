@@ -237,6 +237,28 @@ def test_large_grid_several_waves(M, N, K, g):
     assert d.max() <= 1
 
 
+# Every width of the streamed kernel (M < 64): 4 tiles per workgroup (N =
+# 10240 and 14336 at one 16-row block, N = 4096 and 8192 at three), 7 tiles
+# (N = 28672 at three row blocks), 2 and 1.  Short K leaves waves with fewer
+# K-tiles than the load ring holds (1152 / 128 = 9 K-tiles over 4 waves, 640
+# over 8 waves with K-tile count 5).
+@pytest.mark.parametrize("M,N,K,g", [(16, 10240, 1024, 128), (1, 14336, 640, 64),
+                                     (48, 4096, 768, 64), (33, 8192, 1152, 64),
+                                     (40, 28672, 512, 128), (16, 8192, 2048, 128),
+                                     (7, 4096, 512, 64)])
+def test_stream_widths(M, N, K, g):
+    say(f"w4a8 streamed kernel widths: M={M} N={N} K={K} g={g}")
+    assert w4.workspace_size(M, N, K) == 0
+    X8, sx, pk, acc, y = _small_problem(M, N, K, g, 81 + M)
+    Yi = poison((M, N), torch.int32)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, out=Yi)
+    np.testing.assert_array_equal(host(Yi), acc)
+    Yh = poison((M, N), torch.float16)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_F16, out=Yh)
+    d = f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y)
+    assert d.max() <= 1
+
+
 # Few output tiles -> the matrix-core kernel splits K across workgroups and
 # reduces int32 partials in a second kernel (8 splits here).
 @pytest.mark.parametrize("M,N,K,g", [(128, 512, 4096, 128), (100, 256, 2048, 64)])
@@ -705,6 +727,47 @@ def test_fp8g_gemm_parity(M, N, K, g):
     Ys = poison((M, N), torch.float32)
     w4.gemm_fp8g(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F32, splitk=1, out=Ys)
     assert np.all(np.abs(host(Ys) - ref) <= bound + 1e-30)
+
+
+# The FP8 streamed kernel at 4 tiles per workgroup (N = 10240 at one 16-row
+# block) and 7 (N = 28672 at three), per-channel and folded: integer-valued
+# operands bit for bit, realistic data against the double reference.
+@pytest.mark.parametrize("M,N,K", [(16, 10240, 1024), (40, 28672, 512)])
+def test_fp8_stream_widths(M, N, K):
+    say(f"w4fp8 streamed kernel widths: M={M} N={N} K={K}")
+    rng = np.random.default_rng(M + N)
+    Xi = rng.integers(-16, 17, size=(M, K)).astype(np.float64)
+    q = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    exact = Xi.astype(np.int64) @ q.astype(np.int64).T
+    pk = {"wq": to_dev(oracle.pack_nibbles(oracle.int4_sm_codes(q))),
+          "sw": to_dev(np.ones(N, np.float32)), "N": N, "K": K}
+    Y = poison((M, N), torch.float32)
+    w4.gemm_fp8(to_dev(oracle.e4m3_encode(Xi)), to_dev(np.ones(M, np.float32)), pk,
+                out_type=w4.OUT_F32, out=Y)
+    np.testing.assert_array_equal(host(Y), exact.astype(np.float32))
+    W = wl.gen_weights(N, K, 530 + M)
+    X = wl.gen_activations(M, K, 531 + M, 532)
+    X8, sx = oracle.quant_rows_e4m3(X)
+    pk_ref = oracle.w4fp8_pack(W)
+    ref, _ = oracle.w4fp8_ref(X8, sx, pk_ref["q"], pk_ref["sw"])
+    bound = _fp8_bound(X8, sx, pk_ref["q"], pk_ref["sw"])
+    pk = {"wq": to_dev(pk_ref["wq"]), "sw": to_dev(pk_ref["sw"]), "N": N, "K": K}
+    Yf = poison((M, N), torch.float32)
+    w4.gemm_fp8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F32, out=Yf)
+    Yb = poison((M, N), torch.bfloat16)
+    w4.gemm_fp8(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_BF16, out=Yb)
+    _check_fp8_outputs(host(Yf), bf16_bits_of(Yb), ref, bound)
+    g = 128
+    Wg = _fp8g_weights(N, K, g, 540 + M)
+    ref_pk = oracle.w4fp8g_pack(Wg, g)
+    refg, _ = oracle.w4fp8g_ref(X8, sx, ref_pk["w8"], ref_pk["t"])
+    boundg = _fp8_bound_w(X8, sx, np.abs(oracle.e4m3_decode(ref_pk["w8"])), ref_pk["t"])
+    pkg = _fp8g_device(ref_pk, N, K, g)
+    Yf = poison((M, N), torch.float32)
+    w4.gemm_fp8g(to_dev(X8), to_dev(sx), pkg, out_type=w4.OUT_F32, out=Yf)
+    Yb = poison((M, N), torch.bfloat16)
+    w4.gemm_fp8g(to_dev(X8), to_dev(sx), pkg, out_type=w4.OUT_BF16, out=Yb)
+    _check_fp8_outputs(host(Yf), bf16_bits_of(Yb), refg, boundg)
 
 
 # Folded format on large short-K grids (128-row tiles two per CU): identity X

@@ -56,25 +56,31 @@ bool valid_extent(int M, int N, int K) {
 int k_tiles(int K) { return K / 128; }
 
 // Streamed kernel: NTW 16-channel tiles per workgroup, ks waves splitting K.
-// Aim for one workgroup per CU (256 CUs): NTW = tiles / 256 where that is a
-// supported width, else the widest supported NTW that divides the tile
-// count and still gives >= 256 workgroups.  K-splitting waves: eight per CU
-// in total -- ks = 8 for one workgroup per CU, fewer when the 16-row blocks
-// of M multiply the workgroups (measured 12-24 % faster at 32-48 rows than
-// keeping eight) -- and never more than K has K-tiles.
+// Width: the widest of 4, 2, 1 tiles that divides the tile count and still
+// leaves at least 160 workgroups (16-row blocks of M included).  Measured at
+// M = 16 against one workgroup per CU: 4 tiles are 8-11 % faster on
+// 28672 x 8192, 14336 x 4096, 11008 x 4096 and 10240 x 8192 although they
+// leave CUs idle on the last three, while 4 tiles at 128 workgroups (N = 8192)
+// are 25-30 % slower than 2 at 256; at M = 32 the wider tiles halve the
+// activation re-reads (8192 x 28672: 26 % faster).  Seven tiles only from
+// three 16-row blocks on and with at least 256 workgroups per row block
+// (28672 x 8192 at M = 48: 8 % faster than 4; 14336 x 4096: 15 % slower).
+// K-splitting waves: eight per workgroup, halved while the grid would hold
+// more than 2048 waves, and never more than K has K-tiles.
 w4a8::StreamCfg choose_stream(int M, int N, int K, int splitk) {
     w4a8::StreamCfg c;
     const int tiles = N / 16;
-    const int widths[5] = {7, 4, 3, 2, 1};
+    const long long rblocks = (M + 15) / 16;
+    const int widths[4] = {7, 4, 2, 1};
     c.nt_per_wave = 1;
-    for (int i = 0; i < 5; ++i) {
+    for (int i = 0; i < 4; ++i) {
         const int w = widths[i];
-        if (tiles % w == 0 && tiles / w >= 256) {
+        if (w == 7 && (rblocks < 3 || tiles / 7 < 256)) continue;
+        if (tiles % w == 0 && (tiles / w) * rblocks >= 160) {
             c.nt_per_wave = w;
             break;
         }
     }
-    // Eight K-interleaved waves per workgroup (measured best for 1..7 tiles).
     const int ks_max = 8;
     if (splitk > 0) {  // an explicit split keeps the narrowest width (fits 16 waves)
         c.nt_per_wave = 1;

@@ -380,8 +380,7 @@ hipError_t launch_w4a8_stream(const int8_t* X, const float* sx, const uint8_t* w
                                  cfg.ks, offsets, E, max_rows, st)
     switch (cfg.nt_per_wave) {
         case 7: W4A8_NTW(7, 2);
-        case 4: W4A8_NTW(4, 3);
-        case 3: W4A8_NTW(3, 3);
+        case 4: W4A8_NTW(4, 2);
         case 2: W4A8_NTW(2, 4);
         default: W4A8_NTW(1, 3);
     }
@@ -413,7 +412,6 @@ hipError_t launch_w8a8_stream(const int8_t* X, const float* sx, const int8_t* wq
     switch (cfg.nt_per_wave) {
         case 7: return w8a8_stream_ntw<7, 2>(X, sx, wq8, sw, Y, out_type, M, N, K, cfg.ks, st);
         case 4: return w8a8_stream_ntw<4, 3>(X, sx, wq8, sw, Y, out_type, M, N, K, cfg.ks, st);
-        case 3: return w8a8_stream_ntw<3, 3>(X, sx, wq8, sw, Y, out_type, M, N, K, cfg.ks, st);
         case 2: return w8a8_stream_ntw<2, 4>(X, sx, wq8, sw, Y, out_type, M, N, K, cfg.ks, st);
         default: return w8a8_stream_ntw<1, 3>(X, sx, wq8, sw, Y, out_type, M, N, K, cfg.ks, st);
     }
@@ -448,8 +446,7 @@ static hipError_t w4fp8_stream_run(const uint8_t* X, const float* sx, const uint
                                              cfg.ks, st)
     switch (cfg.nt_per_wave) {
         case 7: F8_NTW(7, 2);
-        case 4: F8_NTW(4, 3);
-        case 3: F8_NTW(3, 3);
+        case 4: F8_NTW(4, 2);
         case 2: F8_NTW(2, 4);
         default: F8_NTW(1, 3);
     }

@@ -22,7 +22,7 @@ hipError_t launch_act_e4m3(const void* X, int in_type, int M, int K, uint8_t* Xq
 // Streamed-tile GEMMs: one workgroup per (16*nt_per_wave rows of N, 16 rows
 // of M); `ks` waves split K and reduce in LDS.
 struct StreamCfg {
-    int nt_per_wave;  // 16-row weight tiles per wave (1, 2 or 4)
+    int nt_per_wave;  // 16-row weight tiles per workgroup (1, 2, 4 or 7)
     int ks;           // waves per workgroup splitting K (1..16)
 };
 
