@@ -38,8 +38,8 @@ __device__ __forceinline__ int xpiece(int R, int c) {
 }
 
 // W4A8 decode-shaped GEMM (M < 64).  One workgroup per NTW packed tiles
-// (16 channels each) and one 16-row block of X, sized so the grid is about
-// one workgroup per CU; its `ks` waves take interleaved K-tiles (wave w:
+// (16 channels each) and one 16-row block of X (NTW and ks are chosen by
+// the host from the shape); its `ks` waves take interleaved K-tiles (wave w:
 // w, w + ks, ...), so at any moment a CU reads adjacent tiles of its channel
 // rows.  Each wave keeps D K-tiles of weight loads in flight (a register
 // ring refilled as each stage is consumed); the weight stream is loaded
