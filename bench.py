@@ -61,17 +61,41 @@ def parse():
     return p.parse_args()
 
 
+def _code_only(text):
+    """C/C++ source without comments and blank space: the part of a kernel
+    source that the compiler sees (string and character literals kept)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            i = text.find("*/", i + 2)
+            i = n if i < 0 else i + 2
+        else:
+            out.append(c)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def source_digest():
-    """sha256 of the kernel sources: counter readings taken from other
-    sources no longer describe the kernels that run."""
+    """sha256 of the kernel sources without their comments: counter readings
+    taken from other code no longer describe the kernels that run."""
     import hashlib
     d = os.path.join(ROOT, "w4a8_quantized_gemm_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(d)):
         if f.endswith((".hip", ".h")):
             h.update(f.encode())
-            with open(os.path.join(d, f), "rb") as fh:
-                h.update(fh.read())
+            with open(os.path.join(d, f), encoding="utf-8") as fh:
+                h.update(_code_only(fh.read()).encode())
     return h.hexdigest()
 
 
