@@ -237,15 +237,19 @@ def test_large_grid_several_waves(M, N, K, g):
     assert d.max() <= 1
 
 
-# Every width of the streamed kernel (M < 64): 4 tiles per workgroup (N =
-# 10240 and 14336 at one 16-row block, N = 4096 and 8192 at three), 7 tiles
-# (N = 28672 at three row blocks), 2 and 1.  Short K leaves waves with fewer
-# K-tiles than the load ring holds (1152 / 128 = 9 K-tiles over 4 waves, 640
-# over 8 waves with K-tile count 5).
+# Every configuration of the streamed kernel (M < 64): one 16-row block per
+# workgroup with 4, 2 and 1 tiles (N = 10240 / 14336, 8192, 4096); two
+# blocks per workgroup with 4, 2 and 1 tiles (at 48 and 50 rows the second
+# workgroup along M holds one block partly and one wholly past M); four
+# blocks (33-63 rows) with 2 tiles.  Short K leaves
+# waves with fewer K-tiles than the load ring holds (640 / 128 = 5 K-tiles
+# over 4 waves, 1152 over 8 waves).
 @pytest.mark.parametrize("M,N,K,g", [(16, 10240, 1024, 128), (1, 14336, 640, 64),
-                                     (48, 4096, 768, 64), (33, 8192, 1152, 64),
-                                     (40, 28672, 512, 128), (16, 8192, 2048, 128),
-                                     (7, 4096, 512, 64)])
+                                     (16, 8192, 2048, 128), (7, 4096, 512, 64),
+                                     (32, 28672, 640, 128), (20, 8192, 1024, 64),
+                                     (17, 4096, 768, 128), (48, 4096, 768, 64),
+                                     (33, 8192, 1152, 64), (40, 28672, 512, 128),
+                                     (63, 11008, 512, 64), (50, 2048, 2048, 64)])
 def test_stream_widths(M, N, K, g):
     say(f"w4a8 streamed kernel widths: M={M} N={N} K={K} g={g}")
     assert w4.workspace_size(M, N, K) == 0

@@ -55,39 +55,67 @@ bool valid_extent(int M, int N, int K) {
 
 int k_tiles(int K) { return K / 128; }
 
-// Streamed kernel: NTW 16-channel tiles per workgroup, ks waves splitting K.
+// Streamed kernel: NTW 16-channel tiles per workgroup, ks waves splitting K,
+// RB 16-row blocks of M per workgroup.
 // Width: the widest of 4, 2, 1 tiles that divides the tile count and still
-// leaves at least 160 workgroups (16-row blocks of M included).  Measured at
-// M = 16 against one workgroup per CU: 4 tiles are 8-11 % faster on
-// 28672 x 8192, 14336 x 4096, 11008 x 4096 and 10240 x 8192 although they
-// leave CUs idle on the last three, while 4 tiles at 128 workgroups (N = 8192)
-// are 25-30 % slower than 2 at 256; at M = 32 the wider tiles halve the
-// activation re-reads (8192 x 28672: 26 % faster).  Seven tiles only from
-// three 16-row blocks on and with at least 256 workgroups per row block
-// (28672 x 8192 at M = 48: 8 % faster than 4; 14336 x 4096: 15 % slower).
+// leaves at least 160 workgroups.  Measured at M = 16 against one workgroup
+// per CU: 4 tiles are 8-11 % faster on 28672 x 8192, 14336 x 4096,
+// 11008 x 4096 and 10240 x 8192 although they leave CUs idle on the last
+// three, while 4 tiles at 128 workgroups (N = 8192) are 25-30 % slower than
+// 2 at 256.
+// Row blocks (W4A8 only, `row_blocks`): a workgroup takes four blocks at
+// 33-63 rows when that still allows 2 tiles or more (four blocks of four
+// tiles do not fit the registers), else two blocks from 17 rows on when
+// some width allows them, so each decoded weight feeds several blocks
+// instead of being fetched and decoded again per 16 rows (measured against
+// one block per workgroup: 28672 x 8192 at M = 32 / 48 32 % / 22 % faster,
+// 8192 x 28672 at M = 48 39 %, 11008 x 4096 at M = 32 / 48 23 % / 18 %,
+// 2048 x 4096 at M = 40 4 %).  One tile per workgroup fetches every row
+// block's activations per 16 channels: where one row block per workgroup at
+// 4 tiles leaves 160 workgroups, that is taken instead.
+// With one row block per workgroup (the FP8 and W8A8 kinds) seven tiles are
+// taken from three 16-row blocks on when they leave at least 256 workgroups
+// per block (28672 x 8192 at M = 48: 8 % faster than 4; 14336 x 4096: 15 %
+// slower).
 // K-splitting waves: eight per workgroup, halved while the grid would hold
-// more than 2048 waves, and never more than K has K-tiles.
-w4a8::StreamCfg choose_stream(int M, int N, int K, int splitk) {
+// more than 2048 waves, and never more than K has K-tiles.  An explicit
+// split keeps one tile and one row block per workgroup (up to 16 waves).
+w4a8::StreamCfg choose_stream(int M, int N, int K, int splitk, bool row_blocks = false) {
     w4a8::StreamCfg c;
     const int tiles = N / 16;
     const long long rblocks = (M + 15) / 16;
-    const int widths[4] = {7, 4, 2, 1};
-    c.nt_per_wave = 1;
-    for (int i = 0; i < 4; ++i) {
-        const int w = widths[i];
-        if (w == 7 && (rblocks < 3 || tiles / 7 < 256)) continue;
-        if (tiles % w == 0 && (tiles / w) * rblocks >= 160) {
-            c.nt_per_wave = w;
-            break;
+    // widest width leaving at least 160 workgroups with rb row blocks each
+    // (0: none does)
+    auto width_for = [&](int rb) {
+        const long long mgroups = (rblocks + rb - 1) / rb;  // workgroups along M
+        const int widths[4] = {7, 4, 2, 1};
+        for (int i = 0; i < 4; ++i) {
+            const int w = widths[i];
+            if (w == 7 && (rb > 1 || rblocks < 3 || tiles / 7 < 256)) continue;
+            if (w == 4 && rb == 4) continue;
+            if (tiles % w == 0 && (tiles / w) * mgroups >= 160) return w;
         }
+        return 0;
+    };
+    c.rb = 1;
+    if (row_blocks && splitk == 0) {
+        if (rblocks >= 3 && width_for(4) >= 2)
+            c.rb = 4;
+        else if (rblocks >= 2 && width_for(2) >= 1)
+            c.rb = 2;
+    }
+    c.nt_per_wave = width_for(c.rb) > 0 ? width_for(c.rb) : 1;
+    if (c.rb > 1 && c.nt_per_wave == 1 && width_for(1) == 4) {
+        c.rb = 1;
+        c.nt_per_wave = 4;
     }
     const int ks_max = 8;
-    if (splitk > 0) {  // an explicit split keeps the narrowest width (fits 16 waves)
+    if (splitk > 0) {
         c.nt_per_wave = 1;
         c.ks = splitk;
     } else {
         c.ks = ks_max;
-        const long long wgs = (long long)(tiles / c.nt_per_wave) * ((M + 15) / 16);
+        const long long wgs = (long long)(tiles / c.nt_per_wave) * ((rblocks + c.rb - 1) / c.rb);
         while (c.ks > 1 && wgs * c.ks > 8 * 256) c.ks /= 2;
         while (c.ks > 1 && k_tiles(K) < c.ks) c.ks /= 2;
     }
@@ -211,7 +239,8 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint
                                                  group, w4a8::plan_w4a8_mfma(M, N, K), workspace,
                                                  stream));
     return hip_status(w4a8::launch_w4a8_stream(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
-                                               group, choose_stream(M, N, K, splitk), stream));
+                                               group, choose_stream(M, N, K, splitk, true),
+                                               stream));
 }
 
 W4A8_EXPORT w4a8_status_t w4a8_gemm_grouped(const int8_t* X, const float* sx,

@@ -65,8 +65,8 @@ __device__ __forceinline__ int xpiece(int R, int c) {
 // OUT: 0 = fp16 (INT8 kinds) or bf16 (FP8 kinds), 1 = int32 or float32.
 constexpr int kWkLQQ = 0, kWkW8 = 1, kWkF8 = 2, kWkF8G = 3;
 
-template <int NTW, int D, int OUT, int GROUP, bool LDSP, int WK = kWkLQQ>
-__global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
+template <int NTW, int D, int OUT, int GROUP, bool LDSP, int WK = kWkLQQ, int RB = 1>
+__global__ __launch_bounds__(NTW == 1 && RB == 1 ? 1024 : 512) void w4a8_stream_kernel(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ s_u8, const uint8_t* __restrict__ a_u8,
     const float* __restrict__ sw, void* __restrict__ Y, int M, int N, int K, int ks,
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
         a_u8 += (size_t)e * N * (K / GROUP);
         sw += (size_t)e * N;
     }
-    const int m0 = row_lo + blockIdx.y * 16;
+    const int m0 = row_lo + blockIdx.y * (16 * RB);
     if (m0 >= row_hi) return;  // whole workgroup: no rows of this expert here
     // X through LDS pays where X is a large share of the loads (narrow
     // workgroups: 2 KB of X per K-tile against NTW KB of weights).
@@ -141,7 +141,7 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
     uint8_t* lds_s = reinterpret_cast<uint8_t*>(red);
     uint8_t* lds_a = lds_s + (size_t)np * groups * 64;
     const int pbytes = LDSP ? 2 * stream_param_span<NTW>() * groups * 64 : 0;
-    uint8_t* xslot = reinterpret_cast<uint8_t*>(red) + pbytes + wave * 2048;
+    uint8_t* xslot = reinterpret_cast<uint8_t*>(red) + pbytes + wave * (2048 * RB);
     // MFMA operand layout: lane (r, G) holds row r, columns 32G .. 32G+31.
     const int xw0 = xpiece(lane >> 3, lane & 7), xw1 = xpiece(8 + (lane >> 3), lane & 7);
     const int xr0 = xpiece(r, 2 * G), xr1 = xpiece(r, 2 * G + 1);
@@ -149,14 +149,20 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
     constexpr int WPT = W8 ? 2 : 1;  // 16-byte weight loads per lane and tile
     constexpr int NF = WK == kWkF8G ? NTW : 1;  // folded factors per stage
     struct Stage {
-        v4i x0, x1;
+        v4i x0[RB], x1[RB];
         v4i w[NTW * WPT];
         float f[NF];
     };
     auto issue = [&](int kt, Stage& st) {
         const unsigned so = (unsigned)(kt * kTileK);
-        st.x0 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xvoff, so, 0));
-        st.x1 = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xvoff8, so, 0));
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            const unsigned ro = 16u * (unsigned)rb * (unsigned)K;  // row block rb
+            st.x0[rb] = __builtin_bit_cast(
+                v4i, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xvoff + ro, so, 0));
+            st.x1[rb] = __builtin_bit_cast(
+                v4i, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, xvoff8 + ro, so, 0));
+        }
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
             if constexpr (W8) {
@@ -198,26 +204,39 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
         }
     };
 
-    Acc acc[NTW];
+    Acc acc[RB][NTW];
 #pragma unroll
-    for (int t = 0; t < NTW; ++t) acc[t] = Acc{};
+    for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int t = 0; t < NTW; ++t) acc[rb][t] = Acc{};
 
     // Multiply-accumulate of the K-tile held in stage S.
     auto consume = [&](const Stage& S, int kt) {
-        v4i x0 = S.x0, x1 = S.x1;
-        if constexpr (kXlds) {
-            // X tile -> MFMA layout through this wave's LDS slot (LDS
-            // operations of one wave complete in order).
-            *reinterpret_cast<v4i*>(xslot + xw0) = S.x0;
-            *reinterpret_cast<v4i*>(xslot + xw1) = S.x1;
-            x0 = *reinterpret_cast<const v4i*>(xslot + xr0);
-            x1 = *reinterpret_cast<const v4i*>(xslot + xr1);
+        v4i x0[RB], x1[RB];
+#pragma unroll
+        for (int rb = 0; rb < RB; ++rb) {
+            x0[rb] = S.x0[rb];
+            x1[rb] = S.x1[rb];
+            if constexpr (kXlds) {
+                // X tile -> MFMA layout through this wave's LDS slot (LDS
+                // operations of one wave complete in order).
+                uint8_t* xs = xslot + rb * 2048;
+                *reinterpret_cast<v4i*>(xs + xw0) = S.x0[rb];
+                *reinterpret_cast<v4i*>(xs + xw1) = S.x1[rb];
+                x0[rb] = *reinterpret_cast<const v4i*>(xs + xr0);
+                x1[rb] = *reinterpret_cast<const v4i*>(xs + xr1);
+            }
         }
 #pragma unroll
         for (int t = 0; t < NTW; ++t) {
             if constexpr (W8) {
-                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x0, S.w[2 * t], acc[t], 0, 0, 0);
-                acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1, S.w[2 * t + 1], acc[t], 0, 0, 0);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    acc[rb][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x0[rb], S.w[2 * t],
+                                                                       acc[rb][t], 0, 0, 0);
+                    acc[rb][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1[rb], S.w[2 * t + 1],
+                                                                       acc[rb][t], 0, 0, 0);
+                }
                 continue;
             } else if constexpr (F8) {
                 unsigned lo = kE4m3LutLo, hi = kE4m3LutHi;
@@ -227,10 +246,14 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
                                    (int)int4_to_e4m3_lo(w.y, lo, hi), (int)int4_to_e4m3_hi(w.y, lo, hi),
                                    (int)int4_to_e4m3_lo(w.z, lo, hi), (int)int4_to_e4m3_hi(w.z, lo, hi),
                                    (int)int4_to_e4m3_lo(w.w, lo, hi), (int)int4_to_e4m3_hi(w.w, lo, hi)};
-                const v8i A = v8i{x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                // formats 0/0 = e4m3 x e4m3; E8M0 scale 127 = 2^0 on both sides
-                acc[t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, Bf, acc[t], 0, 0, 0, 127,
-                                                                          0, 127);
+#pragma unroll
+                for (int rb = 0; rb < RB; ++rb) {
+                    const v8i A = v8i{x0[rb].x, x0[rb].y, x0[rb].z, x0[rb].w,
+                                      x1[rb].x, x1[rb].y, x1[rb].z, x1[rb].w};
+                    // formats 0/0 = e4m3 x e4m3; E8M0 scale 127 = 2^0 on both sides
+                    acc[rb][t] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        A, Bf, acc[rb][t], 0, 0, 0, 127, 0, 127);
+                }
                 continue;
             }
             unsigned s, a;
@@ -245,8 +268,11 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
             lqq_dequant8((unsigned)S.w[t].w, s2, a4, b[6], b[7]);
             const v4i B0 = v4i{(int)b[0], (int)b[1], (int)b[2], (int)b[3]};
             const v4i B1 = v4i{(int)b[4], (int)b[5], (int)b[6], (int)b[7]};
-            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x0, B0, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1, B1, acc[t], 0, 0, 0);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb) {
+                acc[rb][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x0[rb], B0, acc[rb][t], 0, 0, 0);
+                acc[rb][t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(x1[rb], B1, acc[rb][t], 0, 0, 0);
+            }
         }
     };
 
@@ -295,24 +321,28 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
     for (int d = 0; d < D; ++d)
         if (i + D + d < nk) consume(st[d], kt_of(i + D + d));
 
-    // Sum the ks partial tiles: element e = (t * 4 + v) * 64 + l of wave w
-    // lives at red[w * NTW * 256 + e] (reusing the parameter LDS).
+    // Sum the ks partial tiles: element e = ((rb * NTW + t) * 4 + v) * 64 + l
+    // of wave w lives at red[w * RB * NTW * 256 + e] (reusing the parameter
+    // LDS).
     // (float32 sums, for the FP8 kinds, are added in the same wave order.)
     using Sum = std::conditional_t<F8, float, int>;
     Sum* reds = reinterpret_cast<Sum*>(red);
     __syncthreads();
 #pragma unroll
-    for (int t = 0; t < NTW; ++t)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) reds[((wave * NTW + t) * 4 + v) * 64 + lane] = acc[t][v];
+        for (int t = 0; t < NTW; ++t)
+#pragma unroll
+            for (int v = 0; v < 4; ++v)
+                reds[(((wave * RB + rb) * NTW + t) * 4 + v) * 64 + lane] = acc[rb][t][v];
     __syncthreads();
-    const int nel = NTW * 256;
+    const int nel = RB * NTW * 256;
     const float tval = WK == kWkF8G ? tsc[0] : 0.0f;
     for (int e = tid; e < nel; e += blockDim.x) {
         Sum sum = reds[e];
         for (int w = 1; w < ks; ++w) sum += reds[w * nel + e];
-        const int t = e >> 8, v = (e >> 6) & 3, l = e & 63;
-        const int m = m0 + 4 * (l >> 4) + v;  // accumulator row (X row)
+        const int rb = e / (NTW * 256), t = (e >> 8) % NTW, v = (e >> 6) & 3, l = e & 63;
+        const int m = m0 + 16 * rb + 4 * (l >> 4) + v;  // accumulator row (X row)
         const int n = (nt0 + t) * kTileN + (l & 15);
         if (m < row_hi) {
             if constexpr (F8) {
@@ -332,23 +362,26 @@ __global__ __launch_bounds__(NTW == 1 ? 1024 : 512) void w4a8_stream_kernel(
 }
 
 // ----------------------------------------------------------- launchers ----
-template <int NTW, int D>
+constexpr size_t kMaxLdsBytes = 160 * 1024;  // LDS one workgroup may hold on gfx950
+
+template <int NTW, int D, int RB = 1>
 static hipError_t w4a8_stream_ntw(const int8_t* X, const float* sx, const uint8_t* wq,
                                   const uint8_t* s_u8, const uint8_t* a_u8, const float* sw,
                                   void* Y, int out_type, int M, int N, int K, int group, int ks,
                                   const int* offsets, int E, int max_rows, hipStream_t st) {
-    dim3 grid(N / (kTileN * NTW), (max_rows + 15) / 16, E);
+    dim3 grid(N / (kTileN * NTW), (max_rows + 16 * RB - 1) / (16 * RB), E);
     dim3 block(64 * ks);
     const int groups = K / group;
     const size_t pbytes = (size_t)2 * stream_param_span<NTW>() * groups * 64;
-    const size_t xbytes = (size_t)ks * 2048;  // X slots
-    const size_t rbytes = (size_t)ks * NTW * 256 * sizeof(int);
+    const size_t xbytes = (size_t)ks * 2048 * RB;  // X slots
+    const size_t rbytes = (size_t)ks * RB * NTW * 256 * sizeof(int);
     const bool ldsp = pbytes + xbytes <= 128 * 1024;
     const size_t used = (ldsp ? pbytes : 0) + xbytes;
     const size_t lds = used > rbytes ? used : rbytes;
-#define W4A8_LS(O, G, P)                                                                       \
-    hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, O, G, P>), grid, block, lds, st, X, sx, wq, \
-                       s_u8, a_u8, sw, Y, M, N, K, ks, offsets)
+    if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
+#define W4A8_LS(O, G, P)                                                                    \
+    hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, O, G, P, kWkLQQ, RB>), grid, block, lds, \
+                       st, X, sx, wq, s_u8, a_u8, sw, Y, M, N, K, ks, offsets)
     if (ldsp) {
         if (out_type == 1) {
             if (group == 64) W4A8_LS(1, 64, true); else W4A8_LS(1, 128, true);
@@ -375,14 +408,22 @@ hipError_t launch_w4a8_stream(const int8_t* X, const float* sx, const uint8_t* w
         E = 1;
         max_rows = M;
     }
-#define W4A8_NTW(W, D)                                                                      \
-    return w4a8_stream_ntw<W, D>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group,   \
-                                 cfg.ks, offsets, E, max_rows, st)
-    switch (cfg.nt_per_wave) {
-        case 7: W4A8_NTW(7, 2);
-        case 4: W4A8_NTW(4, 2);
-        case 2: W4A8_NTW(2, 4);
-        default: W4A8_NTW(1, 3);
+#define W4A8_NTW(W, D, R)                                                                    \
+    return w4a8_stream_ntw<W, D, R>(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, \
+                                    cfg.ks, offsets, E, max_rows, st)
+    // several 16-row blocks per workgroup share each decoded weight (ring
+    // of two K-tiles: the X operands of every block are held per stage;
+    // four blocks of four tiles would not fit the registers)
+    switch (cfg.nt_per_wave * 8 + cfg.rb) {
+        case 7 * 8 + 1: W4A8_NTW(7, 2, 1);
+        case 4 * 8 + 1: W4A8_NTW(4, 2, 1);
+        case 4 * 8 + 2: W4A8_NTW(4, 2, 2);
+        case 2 * 8 + 1: W4A8_NTW(2, 4, 1);
+        case 2 * 8 + 2: W4A8_NTW(2, 2, 2);
+        case 2 * 8 + 4: W4A8_NTW(2, 2, 4);
+        case 1 * 8 + 1: W4A8_NTW(1, 3, 1);
+        case 1 * 8 + 2: W4A8_NTW(1, 2, 2);
+        default: return hipErrorInvalidValue;
     }
 #undef W4A8_NTW
 }
