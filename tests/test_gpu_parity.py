@@ -310,6 +310,7 @@ def test_ablation_variants_bit_identical(M, N, K, g):
     ([5, 0, 16, 19], 256, 512, 64),          # streamed kernel; an empty expert
     ([1, 1, 1, 1, 1, 1, 1, 1], 512, 640, 128),  # one row each (decode, top-1)
     ([33, 7, 0, 40], 128, 1024, 64),          # ragged, several 16-row blocks
+    ([20, 3, 17, 0, 9, 31, 2, 18], 1280, 512, 128),  # streamed, 4 tiles, two row blocks
     ([70, 0, 130, 300], 512, 640, 128),       # matrix-core tiles, odd K-steps
     ([257, 64, 1], 256, 512, 64),             # tiles; an expert with one row
     ([1100, 0, 37, 1500], 256, 512, 128),     # >= 1024 rows: two tile workgroups per CU

@@ -273,13 +273,17 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm_grouped(const int8_t* X, const float* sx,
     // streamed tiles: the width rule of the dense problem applied to all
     // experts' tiles together; four K-splitting waves (most experts hold
     // fewer rows than max_rows, so the padded grid overstates the active
-    // workgroups; four measured best at 16 and 64 tokens on Mixtral shapes)
+    // workgroups; four measured best at 16 and 64 tokens on Mixtral shapes);
+    // two 16-row blocks per workgroup above 16 rows per expert (Mixtral
+    // expert shapes at 64 / 96 tokens: 16-17 % / 25-28 % faster; four
+    // blocks were slower)
     w4a8::StreamCfg c = choose_stream(16, N * E, K, 0);
     while (c.nt_per_wave > 1 && (N / 16) % c.nt_per_wave != 0) {
         c.nt_per_wave = c.nt_per_wave == 7 ? 4 : c.nt_per_wave == 4 ? 2 : 1;
     }
     c.ks = 4;
     while (c.ks > 1 && k_tiles(K) < c.ks) c.ks /= 2;
+    if (rows > 16 && c.nt_per_wave != 7) c.rb = 2;
     return hip_status(w4a8::launch_w4a8_stream(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
                                                group, c, stream, offsets, E, rows));
 }
