@@ -734,10 +734,13 @@ def test_fp8g_gemm_parity(M, N, K, g):
     assert np.all(np.abs(host(Ys) - ref) <= bound + 1e-30)
 
 
-# The FP8 streamed kernel at 4 tiles per workgroup (N = 10240 at one 16-row
-# block) and 7 (N = 28672 at three), per-channel and folded: integer-valued
+# The FP8 streamed kernel at 4 tiles per workgroup (N = 10240, one 16-row
+# block per workgroup), two row blocks at 4, 2 and 1 tiles (the last with a
+# second workgroup along M whose blocks lie partly and wholly past M) and
+# four row blocks at 2 tiles, per-channel and folded: integer-valued
 # operands bit for bit, realistic data against the double reference.
-@pytest.mark.parametrize("M,N,K", [(16, 10240, 1024), (40, 28672, 512)])
+@pytest.mark.parametrize("M,N,K", [(16, 10240, 1024), (20, 10240, 640), (24, 8192, 1024),
+                                   (48, 2048, 1024), (40, 28672, 512)])
 def test_fp8_stream_widths(M, N, K):
     say(f"w4fp8 streamed kernel widths: M={M} N={N} K={K}")
     rng = np.random.default_rng(M + N)

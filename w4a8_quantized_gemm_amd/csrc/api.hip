@@ -63,7 +63,7 @@ int k_tiles(int K) { return K / 128; }
 // 11008 x 4096 and 10240 x 8192 although they leave CUs idle on the last
 // three, while 4 tiles at 128 workgroups (N = 8192) are 25-30 % slower than
 // 2 at 256.
-// Row blocks (W4A8 only, `row_blocks`): a workgroup takes four blocks at
+// Row blocks (W4A8 and FP8, `row_blocks`): a workgroup takes four blocks at
 // 33-63 rows when that still allows 2 tiles or more (four blocks of four
 // tiles do not fit the registers), else two blocks from 17 rows on when
 // some width allows them, so each decoded weight feeds several blocks
@@ -73,7 +73,7 @@ int k_tiles(int K) { return K / 128; }
 // 2048 x 4096 at M = 40 4 %).  One tile per workgroup fetches every row
 // block's activations per 16 channels: where one row block per workgroup at
 // 4 tiles leaves 160 workgroups, that is taken instead.
-// With one row block per workgroup (the FP8 and W8A8 kinds) seven tiles are
+// With one row block per workgroup (the W8A8 comparison) seven tiles are
 // taken from three 16-row blocks on when they leave at least 256 workgroups
 // per block (28672 x 8192 at M = 48: 8 % faster than 4; 14336 x 4096: 15 %
 // slower).
@@ -335,7 +335,7 @@ W4A8_EXPORT w4a8_status_t w4fp8_gemm(const uint8_t* X_e4m3, const float* sx, con
                                                   w4a8::plan_w4a8_mfma(M, N, K), workspace,
                                                   stream));
     return hip_status(w4a8::launch_w4fp8_stream(X_e4m3, sx, wq, sw, Y, out_type, M, N, K,
-                                                choose_stream(M, N, K, splitk), stream));
+                                                choose_stream(M, N, K, splitk, true), stream));
 }
 
 W4A8_EXPORT w4a8_status_t w4fp8g_pack(const float* W, int N, int K, int group, uint8_t* wq,
@@ -376,7 +376,7 @@ W4A8_EXPORT w4a8_status_t w4fp8g_gemm(const uint8_t* X_e4m3, const float* sx, co
                                                    K, group, w4a8::plan_w4a8_mfma(M, N, K),
                                                    workspace, stream));
     return hip_status(w4a8::launch_w4fp8g_stream(X_e4m3, sx, wq, fsc, tscale, Y, out_type, M, N,
-                                                 K, group, choose_stream(M, N, K, splitk),
+                                                 K, group, choose_stream(M, N, K, splitk, true),
                                                  stream));
 }
 

@@ -458,22 +458,23 @@ hipError_t launch_w8a8_stream(const int8_t* X, const float* sx, const int8_t* wq
     }
 }
 
-template <int NTW, int D, int WK, int GROUP>
+template <int NTW, int D, int WK, int GROUP, int RB = 1>
 static hipError_t w4fp8_stream_ntw(const uint8_t* X, const float* sx, const uint8_t* wq,
                                    const float* sw, const float* fsc, const float* tsc, void* Y,
                                    int out_type, int M, int N, int K, int ks, hipStream_t st) {
-    dim3 grid(N / (kTileN * NTW), (M + 15) / 16, 1);
+    dim3 grid(N / (kTileN * NTW), (M + 16 * RB - 1) / (16 * RB), 1);
     dim3 block(64 * ks);
-    const size_t xbytes = (size_t)ks * 2048;
-    const size_t rbytes = (size_t)ks * NTW * 256 * sizeof(float);
+    const size_t xbytes = (size_t)ks * 2048 * RB;
+    const size_t rbytes = (size_t)ks * RB * NTW * 256 * sizeof(float);
     const size_t lds = xbytes > rbytes ? xbytes : rbytes;
+    if (lds > kMaxLdsBytes) return hipErrorInvalidConfiguration;
     const int8_t* Xb = reinterpret_cast<const int8_t*>(X);
     if (out_type == 1)
-        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, 1, GROUP, false, WK>), grid, block, lds, st,
-                           Xb, sx, wq, nullptr, nullptr, sw, Y, M, N, K, ks, nullptr, fsc, tsc);
+        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, 1, GROUP, false, WK, RB>), grid, block, lds,
+                           st, Xb, sx, wq, nullptr, nullptr, sw, Y, M, N, K, ks, nullptr, fsc, tsc);
     else
-        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, 0, GROUP, false, WK>), grid, block, lds, st,
-                           Xb, sx, wq, nullptr, nullptr, sw, Y, M, N, K, ks, nullptr, fsc, tsc);
+        hipLaunchKernelGGL((w4a8_stream_kernel<NTW, D, 0, GROUP, false, WK, RB>), grid, block, lds,
+                           st, Xb, sx, wq, nullptr, nullptr, sw, Y, M, N, K, ks, nullptr, fsc, tsc);
     return hipGetLastError();
 }
 
@@ -482,14 +483,19 @@ static hipError_t w4fp8_stream_run(const uint8_t* X, const float* sx, const uint
                                    const float* sw, const float* fsc, const float* tsc, void* Y,
                                    int out_type, int M, int N, int K, StreamCfg cfg,
                                    hipStream_t st) {
-#define F8_NTW(W, D)                                                                          \
-    return w4fp8_stream_ntw<W, D, WK, GROUP>(X, sx, wq, sw, fsc, tsc, Y, out_type, M, N, K, \
-                                             cfg.ks, st)
-    switch (cfg.nt_per_wave) {
-        case 7: F8_NTW(7, 2);
-        case 4: F8_NTW(4, 2);
-        case 2: F8_NTW(2, 4);
-        default: F8_NTW(1, 3);
+#define F8_NTW(W, D, R)                                                                          \
+    return w4fp8_stream_ntw<W, D, WK, GROUP, R>(X, sx, wq, sw, fsc, tsc, Y, out_type, M, N, K, \
+                                                cfg.ks, st)
+    switch (cfg.nt_per_wave * 8 + cfg.rb) {
+        case 7 * 8 + 1: F8_NTW(7, 2, 1);
+        case 4 * 8 + 1: F8_NTW(4, 2, 1);
+        case 4 * 8 + 2: F8_NTW(4, 2, 2);
+        case 2 * 8 + 1: F8_NTW(2, 4, 1);
+        case 2 * 8 + 2: F8_NTW(2, 2, 2);
+        case 2 * 8 + 4: F8_NTW(2, 2, 4);
+        case 1 * 8 + 1: F8_NTW(1, 3, 1);
+        case 1 * 8 + 2: F8_NTW(1, 2, 2);
+        default: return hipErrorInvalidValue;
     }
 #undef F8_NTW
 }

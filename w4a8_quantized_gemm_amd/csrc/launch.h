@@ -24,7 +24,7 @@ hipError_t launch_act_e4m3(const void* X, int in_type, int M, int K, uint8_t* Xq
 struct StreamCfg {
     int nt_per_wave;  // 16-row weight tiles per workgroup (1, 2, 4 or 7)
     int ks;           // waves per workgroup splitting K (1..16)
-    int rb = 1;       // 16-row blocks of M per workgroup (1, 2 or 4; W4A8 only)
+    int rb = 1;       // 16-row blocks of M per workgroup (1, 2 or 4; not W8A8)
 };
 
 // offsets != nullptr: grouped problem of E experts (rows offsets[e] ..
