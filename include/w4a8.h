@@ -166,8 +166,9 @@ size_t w4a8_workspace_size(int M, int N, int K, int splitk);
  * a matrix-core tile kernel (256-row workgroup tiles on 16 x 16 x 64
  * instructions; 128-row tiles on 16 x 16 x 64 at two workgroups per CU when
  * a workgroup covers at most 64 K-steps of a grid under four waves, else
- * on 32 x 32 x 32); otherwise the streamed-tile kernel runs, with `splitk`
- * K-slices per output tile.
+ * on 32 x 32 x 32); otherwise the streamed-tile kernel runs (one, two or
+ * four 16-row blocks of X per workgroup sharing each decoded weight), with
+ * `splitk` K-slices per output tile.
  * splitk: 0 = automatic; 1, 2, 4, 8 or 16 (at most K/128) forces the
  * streamed-tile kernel with that split.  The int32 result depends on
  * neither choice.
