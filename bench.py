@@ -503,6 +503,44 @@ def main():
                               "results": res}
         del pk8, pk8g, cps8, cps8g, X8
 
+    # ---- per-token activation quantisation, the step before every GEMM:
+    # fp16 X -> INT8 codes (W4A8) or e4m3 codes (W4FP8) plus float32 row
+    # scales, at the sweep's activation shapes.  HBM bound: 2 bytes read and
+    # 1 written per value; copies of X used in turn past 512 MB in total
+    # where that fits, so the large shapes stream from HBM (the 16-row ones
+    # are a few hundred KB and launch bound whatever the copies).
+    if not args.no_ablation and not args.only:
+        qres = []
+        for (M, K) in ((16, 8192), (16, 28672), (4096, 8192), (4096, 28672)):
+            ncp = max(2, min(8, int(512e6 // (M * K * 2)) + 1))
+            Xs = [torch.randn((M, K), device=dev).to(torch.float16) for _ in range(ncp)]
+            Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+            Xe = torch.empty((M, K), dtype=torch.uint8, device=dev)
+            sq = torch.empty(M, dtype=torch.float32, device=dev)
+            row = {"M": M, "K": K, "x_copies": ncp}
+            for tag, fn in (("int8", lambda r: w4.quant_act(Xs[r % ncp], out=(Xq, sq))),
+                            ("e4m3", lambda r: w4.quant_act_fp8(Xs[r % ncp], out=(Xe, sq)))):
+                for r in range(3):
+                    fn(r)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 20
+                e0.record(stream)
+                for r in range(reps):
+                    fn(r)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                us = e0.elapsed_time(e1) * 1e3 / reps
+                ab = 3 * M * K + 4 * M
+                row[tag + "_us"] = round(us, 2)
+                row[tag + "_gbs"] = round(ab / (us * 1e-6) / 1e9, 1)
+                row[tag + "_hbm_frac"] = round(ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+            qres.append(row)
+            del Xs, Xq, Xe, sq
+        out["variant_quant_act"] = {"workload": "fp16 activations -> per-token INT8 / e4m3 + "
+                                                "float32 scales; events over 20 back-to-back "
+                                                "launches rotating x_copies copies of X",
+                                    "results": qres}
+
     if not args.no_cpu_baseline and not args.only:
         desc = [(s["name"], s["M"], s["N"], s["K"], g, s["pair"]) for s in slots]
         out["cpu_baseline"] = cpu_baseline(desc, args.cpu_sample_cols)

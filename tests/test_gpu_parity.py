@@ -89,7 +89,11 @@ def test_pack_int4_parity(N, K):
 
 
 # ------------------------------------------------- activation quant --------
-@pytest.mark.parametrize("M,K", [(1, 512), (16, 4096), (33, 1024)])
+# Rows of up to 32768 elements are held in registers (2, 4, 8 or 16 pieces
+# of eight per thread: K = 1024 .. 4096, 8192, 16384, 28672); longer rows
+# (33024) take the two-pass kernels.
+@pytest.mark.parametrize("M,K", [(1, 512), (16, 4096), (33, 1024), (3, 8192), (5, 16384),
+                                 (2, 28672), (3, 33024)])
 def test_quant_act_parity(M, K):
     say(f"quant act M={M} K={K}")
     X = wl.gen_activations(M, K, 300 + M, 301)
@@ -106,7 +110,8 @@ def test_quant_act_parity(M, K):
 
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
-@pytest.mark.parametrize("M,K", [(1, 512), (16, 4096), (37, 1040)])
+@pytest.mark.parametrize("M,K", [(1, 512), (16, 4096), (37, 1040), (4, 8192), (4, 28672),
+                                 (4, 33024)])
 def test_quant_act_typed_parity(dt, M, K):
     """fp16 / bf16 activations: the device widens to float32 and quantises;
     the oracle widens the same bit patterns (exact) and quantises.  Rows:

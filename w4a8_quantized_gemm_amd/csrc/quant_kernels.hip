@@ -227,18 +227,34 @@ struct Row8 {  // eight consecutive elements of a row, widened to float32
 };
 
 template <int IN>
-__device__ __forceinline__ Row8<IN> load_row8(const void* row, int i) {  // elements 8i..8i+7
+struct Raw8 {  // the same eight elements as stored (32 bytes float32, 16 otherwise)
+    v4i w[IN == 0 ? 2 : 1];
+};
+
+template <int IN>
+__device__ __forceinline__ Raw8<IN> load_raw8(const void* row, int i) {  // elements 8i..8i+7
+    Raw8<IN> r;
+    const v4i* p = reinterpret_cast<const v4i*>(row) + (IN == 0 ? 2 * i : i);
+    r.w[0] = p[0];
+    if constexpr (IN == 0) r.w[1] = p[1];
+    return r;
+}
+
+template <int IN>
+__device__ __forceinline__ Row8<IN> widen8(const Raw8<IN>& w) {
     Row8<IN> r;
     if constexpr (IN == 0) {
-        const float4* p = reinterpret_cast<const float4*>(row) + 2 * i;
-        const float4 a = p[0], b = p[1];
-        r.v[0] = a.x; r.v[1] = a.y; r.v[2] = a.z; r.v[3] = a.w;
-        r.v[4] = b.x; r.v[5] = b.y; r.v[6] = b.z; r.v[7] = b.w;
-    } else {
-        const v4i w = reinterpret_cast<const v4i*>(row)[i];
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            const unsigned h = ((unsigned)w[j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
+            // through a scalar: a bit cast of the vector element itself
+            // reads lane 0 of the vector with this compiler
+            const int x = w.w[j >> 2][j & 3];
+            r.v[j] = __builtin_bit_cast(float, x);
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const unsigned h = ((unsigned)w.w[0][j >> 1] >> (16 * (j & 1))) & 0xFFFFu;
             if constexpr (IN == 1)
                 r.v[j] = (float)__builtin_bit_cast(_Float16, (unsigned short)h);
             else
@@ -249,13 +265,12 @@ __device__ __forceinline__ Row8<IN> load_row8(const void* row, int i) {  // elem
 }
 
 template <int IN>
-__device__ __forceinline__ float row_absmax(const void* row, int K) {
-    float m = 0.0f;
-    for (int i = threadIdx.x; i < K / 8; i += 256) {
-        const Row8<IN> r = load_row8<IN>(row, i);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(r.v[j]));
-    }
+__device__ __forceinline__ Row8<IN> load_row8(const void* row, int i) {
+    return widen8<IN>(load_raw8<IN>(row, i));
+}
+
+// Largest of the 256 threads' values.
+__device__ __forceinline__ float block_max256(float m) {
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
     __shared__ float part[4];
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
@@ -263,6 +278,17 @@ __device__ __forceinline__ float row_absmax(const void* row, int K) {
     m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
     __syncthreads();
     return m;
+}
+
+template <int IN>
+__device__ __forceinline__ float row_absmax(const void* row, int K) {
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < K / 8; i += 256) {
+        const Row8<IN> r = load_row8<IN>(row, i);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(r.v[j]));
+    }
+    return block_max256(m);
 }
 
 template <int IN>
@@ -330,6 +356,65 @@ __global__ __launch_bounds__(256) void act_e4m3_kernel(const void* __restrict__ 
     }
 }
 
+// The same two quantisers with the row held in registers between the
+// absolute maximum and the quantisation (rows of at most 2048 CH elements):
+// the row is read from memory once instead of twice.  Q: 0 = INT8 (qmax
+// 127), 1 = e4m3; arithmetic identical to the kernels above.
+template <int IN, int Q, int CH>
+__global__ __launch_bounds__(256) void act_quant_regs_kernel(const void* __restrict__ X, int K,
+                                                             uint8_t* __restrict__ Xq,
+                                                             float* __restrict__ sx) {
+    const void* row = row_ptr<IN>(X, K);
+    const int n8 = K / 8;
+    Raw8<IN> c[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        c[j] = i < n8 ? load_raw8<IN>(row, i) : Raw8<IN>{};
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const Row8<IN> r = widen8<IN>(c[j]);  // zeros past the row end
+#pragma unroll
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(r.v[e]));
+    }
+    const float s = scale_of(block_max256(m), Q == 0 ? 127.0f : 448.0f);
+    if (threadIdx.x == 0) sx[blockIdx.x] = s;
+    uint2* out = reinterpret_cast<uint2*>(Xq + (size_t)blockIdx.x * K);
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+        const int i = threadIdx.x + 256 * j;
+        if (i >= n8) continue;
+        const Row8<IN> r = widen8<IN>(c[j]);
+        unsigned b[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            b[e] = Q == 0 ? (unsigned)(quant_sym(r.v[e], s, 127.0f) & 0xFF)
+                          : f32_to_e4m3(__fdiv_rn(r.v[e], s));
+        out[i] = uint2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                       b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+    }
+}
+
+template <int IN, int Q>
+static bool launch_act_regs(const void* X, int M, int K, uint8_t* Xq, float* sx,
+                            hipStream_t st) {
+    const int n8 = K / 8;
+#define ACT_REGS(CH)                                                                           \
+    if (n8 <= 256 * CH) {                                                                      \
+        hipLaunchKernelGGL((act_quant_regs_kernel<IN, Q, CH>), dim3(M), dim3(256), 0, st, X, K, \
+                           Xq, sx);                                                            \
+        return true;                                                                           \
+    }
+    ACT_REGS(2)
+    ACT_REGS(4)
+    ACT_REGS(8)
+    ACT_REGS(16)
+#undef ACT_REGS
+    return false;  // longer rows: the two-pass kernels
+}
+
 // ----------------------------------------------------------- launchers ----
 hipError_t launch_pack_lqq(const float* W, int N, int K, int group, int qmax, uint8_t* wq,
                            uint8_t* s_u8, uint8_t* a_u8, float* sw, hipStream_t st) {
@@ -373,7 +458,13 @@ hipError_t launch_pack_fp8g(const float* W, int N, int K, int group, uint8_t* wq
 
 hipError_t launch_act_int8(const void* X, int in_type, int M, int K, int8_t* Xq, float* sx,
                            hipStream_t st) {
-    if (in_type == 1)
+    uint8_t* Xb = reinterpret_cast<uint8_t*>(Xq);
+    const bool regs = in_type == 1   ? launch_act_regs<1, 0>(X, M, K, Xb, sx, st)
+                      : in_type == 2 ? launch_act_regs<2, 0>(X, M, K, Xb, sx, st)
+                                     : launch_act_regs<0, 0>(X, M, K, Xb, sx, st);
+    if (regs)
+        ;
+    else if (in_type == 1)
         hipLaunchKernelGGL(act_int8_kernel<1>, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
     else if (in_type == 2)
         hipLaunchKernelGGL(act_int8_kernel<2>, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
@@ -384,7 +475,12 @@ hipError_t launch_act_int8(const void* X, int in_type, int M, int K, int8_t* Xq,
 
 hipError_t launch_act_e4m3(const void* X, int in_type, int M, int K, uint8_t* Xq, float* sx,
                            hipStream_t st) {
-    if (in_type == 1)
+    const bool regs = in_type == 1   ? launch_act_regs<1, 1>(X, M, K, Xq, sx, st)
+                      : in_type == 2 ? launch_act_regs<2, 1>(X, M, K, Xq, sx, st)
+                                     : launch_act_regs<0, 1>(X, M, K, Xq, sx, st);
+    if (regs)
+        ;
+    else if (in_type == 1)
         hipLaunchKernelGGL(act_e4m3_kernel<1>, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
     else if (in_type == 2)
         hipLaunchKernelGGL(act_e4m3_kernel<2>, dim3(M), dim3(256), 0, st, X, K, Xq, sx);
