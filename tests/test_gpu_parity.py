@@ -89,11 +89,14 @@ def test_pack_int4_parity(N, K):
 
 
 # ------------------------------------------------- activation quant --------
-# Rows of up to 32768 elements are held in registers (2, 4, 8 or 16 pieces
-# of eight per thread: K = 1024 .. 4096, 8192, 16384, 28672); longer rows
-# (33024) take the two-pass kernels.
+# Rows of up to 32768 elements are held in registers: with fewer than 256
+# rows 1024 threads per row hold 1, 2 or 4 pieces of eight each (K up to
+# 8192, 16384, 28672), from 256 rows on 256 threads hold 2, 4, 8 or 16
+# (K = 2048, 8192, 16384, 28672); longer rows (33024) take the two-pass
+# kernels.
 @pytest.mark.parametrize("M,K", [(1, 512), (16, 4096), (33, 1024), (3, 8192), (5, 16384),
-                                 (2, 28672), (3, 33024)])
+                                 (2, 28672), (3, 33024), (300, 2048), (256, 8192),
+                                 (257, 16384), (256, 28672), (256, 33024)])
 def test_quant_act_parity(M, K):
     say(f"quant act M={M} K={K}")
     X = wl.gen_activations(M, K, 300 + M, 301)
@@ -111,7 +114,7 @@ def test_quant_act_parity(M, K):
 
 @pytest.mark.parametrize("dt", ["f16", "bf16"])
 @pytest.mark.parametrize("M,K", [(1, 512), (16, 4096), (37, 1040), (4, 8192), (4, 28672),
-                                 (4, 33024)])
+                                 (4, 33024), (260, 4096), (256, 28672)])
 def test_quant_act_typed_parity(dt, M, K):
     """fp16 / bf16 activations: the device widens to float32 and quantises;
     the oracle widens the same bit patterns (exact) and quantises.  Rows:

@@ -269,13 +269,16 @@ __device__ __forceinline__ Row8<IN> load_row8(const void* row, int i) {
     return widen8<IN>(load_raw8<IN>(row, i));
 }
 
-// Largest of the 256 threads' values.
-__device__ __forceinline__ float block_max256(float m) {
+// Largest of the TPB threads' values.
+template <int TPB = 256>
+__device__ __forceinline__ float block_max(float m) {
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    __shared__ float part[4];
+    __shared__ float part[TPB / 64];
     if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = m;
     __syncthreads();
-    m = fmaxf(fmaxf(part[0], part[1]), fmaxf(part[2], part[3]));
+    m = part[0];
+#pragma unroll
+    for (int w = 1; w < TPB / 64; ++w) m = fmaxf(m, part[w]);
     __syncthreads();
     return m;
 }
@@ -288,7 +291,7 @@ __device__ __forceinline__ float row_absmax(const void* row, int K) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) m = fmaxf(m, fabsf(r.v[j]));
     }
-    return block_max256(m);
+    return block_max(m);
 }
 
 template <int IN>
@@ -357,11 +360,13 @@ __global__ __launch_bounds__(256) void act_e4m3_kernel(const void* __restrict__ 
 }
 
 // The same two quantisers with the row held in registers between the
-// absolute maximum and the quantisation (rows of at most 2048 CH elements):
-// the row is read from memory once instead of twice.  Q: 0 = INT8 (qmax
-// 127), 1 = e4m3; arithmetic identical to the kernels above.
-template <int IN, int Q, int CH>
-__global__ __launch_bounds__(256) void act_quant_regs_kernel(const void* __restrict__ X, int K,
+// absolute maximum and the quantisation (rows of at most 8 TPB CH
+// elements): the row is read from memory once instead of twice.  Q: 0 =
+// INT8 (qmax 127), 1 = e4m3; arithmetic identical to the kernels above.
+// TPB threads per row: 1024 when there are fewer rows than CUs, so that
+// each thread converts fewer elements.
+template <int IN, int Q, int CH, int TPB>
+__global__ __launch_bounds__(TPB) void act_quant_regs_kernel(const void* __restrict__ X, int K,
                                                              uint8_t* __restrict__ Xq,
                                                              float* __restrict__ sx) {
     const void* row = row_ptr<IN>(X, K);
@@ -369,7 +374,7 @@ __global__ __launch_bounds__(256) void act_quant_regs_kernel(const void* __restr
     Raw8<IN> c[CH];
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-        const int i = threadIdx.x + 256 * j;
+        const int i = threadIdx.x + TPB * j;
         c[j] = i < n8 ? load_raw8<IN>(row, i) : Raw8<IN>{};
     }
     float m = 0.0f;
@@ -379,12 +384,12 @@ __global__ __launch_bounds__(256) void act_quant_regs_kernel(const void* __restr
 #pragma unroll
         for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(r.v[e]));
     }
-    const float s = scale_of(block_max256(m), Q == 0 ? 127.0f : 448.0f);
+    const float s = scale_of(block_max<TPB>(m), Q == 0 ? 127.0f : 448.0f);
     if (threadIdx.x == 0) sx[blockIdx.x] = s;
     uint2* out = reinterpret_cast<uint2*>(Xq + (size_t)blockIdx.x * K);
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
-        const int i = threadIdx.x + 256 * j;
+        const int i = threadIdx.x + TPB * j;
         if (i >= n8) continue;
         const Row8<IN> r = widen8<IN>(c[j]);
         unsigned b[8];
@@ -401,16 +406,22 @@ template <int IN, int Q>
 static bool launch_act_regs(const void* X, int M, int K, uint8_t* Xq, float* sx,
                             hipStream_t st) {
     const int n8 = K / 8;
-#define ACT_REGS(CH)                                                                           \
-    if (n8 <= 256 * CH) {                                                                      \
-        hipLaunchKernelGGL((act_quant_regs_kernel<IN, Q, CH>), dim3(M), dim3(256), 0, st, X, K, \
-                           Xq, sx);                                                            \
-        return true;                                                                           \
+#define ACT_REGS(CH, TPB)                                                                   \
+    if (n8 <= TPB * CH) {                                                                   \
+        hipLaunchKernelGGL((act_quant_regs_kernel<IN, Q, CH, TPB>), dim3(M), dim3(TPB), 0, st, \
+                           X, K, Xq, sx);                                                   \
+        return true;                                                                        \
     }
-    ACT_REGS(2)
-    ACT_REGS(4)
-    ACT_REGS(8)
-    ACT_REGS(16)
+    if (M < 256) {
+        ACT_REGS(1, 1024)
+        ACT_REGS(2, 1024)
+        ACT_REGS(4, 1024)
+    } else {
+        ACT_REGS(2, 256)
+        ACT_REGS(4, 256)
+        ACT_REGS(8, 256)
+        ACT_REGS(16, 256)
+    }
 #undef ACT_REGS
     return false;  // longer rows: the two-pass kernels
 }
