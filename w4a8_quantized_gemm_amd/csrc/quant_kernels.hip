@@ -392,13 +392,32 @@ __global__ __launch_bounds__(TPB) void act_quant_regs_kernel(const void* __restr
         const int i = threadIdx.x + TPB * j;
         if (i >= n8) continue;
         const Row8<IN> r = widen8<IN>(c[j]);
-        unsigned b[8];
+        if constexpr (Q == 0) {
+            unsigned b[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            b[e] = Q == 0 ? (unsigned)(quant_sym(r.v[e], s, 127.0f) & 0xFF)
-                          : f32_to_e4m3(__fdiv_rn(r.v[e], s));
-        out[i] = uint2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
-                       b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+            for (int e = 0; e < 8; ++e) b[e] = (unsigned)(quant_sym(r.v[e], s, 127.0f) & 0xFF);
+            out[i] = uint2{b[0] | (b[1] << 8) | (b[2] << 16) | (b[3] << 24),
+                           b[4] | (b[5] << 8) | (b[6] << 16) | (b[7] << 24)};
+        } else {
+            // |x / s| <= 448 (1 + 2^-23) here, where the hardware conversion
+            // (nearest even) gives f32_to_e4m3's codes; a NaN quotient (NaN
+            // input) gets f32_to_e4m3's 0x7F whatever its sign
+            float t[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) t[e] = __fdiv_rn(r.v[e], s);
+            unsigned w[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int l = __builtin_amdgcn_cvt_pk_fp8_f32(t[4 * h], t[4 * h + 1], 0, false);
+                w[h] = (unsigned)__builtin_amdgcn_cvt_pk_fp8_f32(t[4 * h + 2], t[4 * h + 3], l,
+                                                                  true);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (t[4 * h + e] != t[4 * h + e])
+                        w[h] = (w[h] & ~(0xFFu << (8 * e))) | (0x7Fu << (8 * e));
+            }
+            out[i] = uint2{w[0], w[1]};
+        }
     }
 }
 
