@@ -127,3 +127,25 @@ def test_graph_fp8_and_grouped():
              lambda: w4.gemm_fp8g(X8[:16], sx8[:16], pkg, out_type=w4.OUT_F32, out=Yg),
              lambda: w4.gemm_grouped(Xqe, sxe, offs, pke, max(counts), out=Ye)]
     _replay_and_check(calls, [Yb, Yg, Ye])
+
+
+def test_graph_row_blocks_and_quant():
+    """Streamed calls with two and four 16-row blocks per workgroup, and both
+    activation quantisers at both thread counts per row (fewer / more rows
+    than CUs)."""
+    calls, outs = [], []
+    for (M, N, K, g, seed) in ((24, 8192, 1024, 64, 51), (40, 8192, 1024, 128, 52)):
+        X8, sx, pk = _w4a8_case(M, N, K, g, seed)
+        Yh = torch.empty((M, N), dtype=torch.float16, device=DEV)
+        calls.append(lambda X8=X8, sx=sx, pk=pk, Yh=Yh: w4.gemm(X8, sx, pk, out=Yh))
+        outs.append(Yh)
+    for (M, K, seed) in ((16, 4096, 53), (300, 2048, 54)):
+        Xh = torch.from_numpy(wl.gen_activations(M, K, seed, seed + 1)).to(DEV).to(torch.float16)
+        q8 = torch.empty((M, K), dtype=torch.int8, device=DEV)
+        s8 = torch.empty(M, dtype=torch.float32, device=DEV)
+        qe = torch.empty((M, K), dtype=torch.uint8, device=DEV)
+        se = torch.empty(M, dtype=torch.float32, device=DEV)
+        calls.append(lambda Xh=Xh, q8=q8, s8=s8: w4.quant_act(Xh, out=(q8, s8)))
+        calls.append(lambda Xh=Xh, qe=qe, se=se: w4.quant_act_fp8(Xh, out=(qe, se)))
+        outs += [q8, s8, qe, se]
+    _replay_and_check(calls, outs)
