@@ -605,11 +605,14 @@ def test_w8a8_pack_parity(N, K):
 @pytest.mark.parametrize("M,N,K,sk", [(1, 128, 640, 0), (5, 64, 512, 0), (16, 448, 1024, 0),
                                       (33, 256, 512, 0), (64, 256, 640, 0), (100, 512, 1024, 0),
                                       (300, 512, 1152, 0), (513, 256, 512, 0),
-                                      (128, 256, 4096, 0), (100, 256, 896, 2), (257, 1024, 256, 0)])
+                                      (128, 256, 4096, 0), (100, 256, 896, 2), (257, 1024, 256, 0),
+                                      (16, 10240, 1024, 0), (16, 8192, 512, 0),
+                                      (40, 28672, 512, 0)])
 def test_w8a8_gemm_parity(M, N, K, sk):
     """int32 bit-exact and fp16 within 1 ulp against the oracle: streamed
-    kernel (M < 64, N % 256 != 0, or forced by splitk), tile kernels with
-    128-row tiles, ragged M, odd K-step counts and planned split-K."""
+    kernel (M < 64, N % 256 != 0, or forced by splitk; 1, 2, 4 and 7 tiles
+    per workgroup), tile kernels with 128-row tiles, ragged M, odd K-step
+    counts and planned split-K."""
     say(f"w8a8 gemm M={M} N={N} K={K} splitk={sk} workspace={w4.workspace_size(M, N, K, sk)}")
     W = wl.gen_weights(N, K, 1200 + M + N)
     X = wl.gen_activations(M, K, 1201 + M, 1202)
