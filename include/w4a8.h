@@ -30,10 +30,14 @@
  *     valid the call returns W4A8_OK without checking pointers (nothing is
  *     read or written) and launches nothing.
  *   - Shape constraints: K a positive multiple of 128, N a multiple of 64,
- *     group in {64, 128}; every device pointer 16-byte aligned.  For every
- *     GEMM: M*K < 2^31 and N*K < 2^32 (the kernels address operands with
- *     32-bit buffer ranges); larger problems return W4A8_ERR_SHAPE (split M
- *     across calls).
+ *     group in {64, 128}.  For every GEMM: M*K < 2^31 and N*K < 2^32 (the
+ *     kernels address operands with 32-bit buffer ranges); larger problems
+ *     return W4A8_ERR_SHAPE (split M across calls).
+ *   - Alignment (W4A8_ERR_ALIGNMENT otherwise): the byte and element
+ *     arrays -- W, X, Xq, wq, wq8, s_u8, a_u8, Y and any workspace -- start
+ *     on a 16-byte boundary (the kernels move them in 16-byte pieces); the
+ *     float32 / int32 vectors -- sx, sw, offsets, fsc, tscale -- on a 4-byte
+ *     boundary.
  *
  * Packed 4-bit weight layout (W4A8_LAYOUT_VERSION 1), wq = N*K/2 bytes:
  *   the [N][K] matrix of 4-bit codes is cut into tiles of 16 rows x 128 K.
@@ -68,7 +72,7 @@ typedef enum {
     W4A8_OK = 0,
     W4A8_ERR_NULL_PTR = 1,    /* a required pointer is NULL                     */
     W4A8_ERR_SHAPE = 2,       /* negative size, K % 128, N % 64, group, qmax     */
-    W4A8_ERR_ALIGNMENT = 3,   /* a device pointer is not 16-byte aligned         */
+    W4A8_ERR_ALIGNMENT = 3,   /* a pointer breaks the alignment rule above       */
     W4A8_ERR_WORKSPACE = 4,   /* workspace smaller than w4a8_workspace_size()    */
     W4A8_ERR_UNSUPPORTED = 5, /* device is not gfx950, or a bad mode/flag value  */
     W4A8_ERR_HIP = 6          /* a HIP call failed; see w4a8_last_hip_error()    */

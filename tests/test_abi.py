@@ -247,3 +247,80 @@ def test_valid_call_without_gpu_reports_hip_error():
     assert st in (HIP, UNSUP)
     if st == HIP:
         assert lib.w4a8_last_hip_error() != 0
+
+
+def test_alignment_rule():
+    """Byte arrays (including the group parameters, which the streamed
+    kernel copies in 16-byte pieces) need 16-byte alignment; the float32 /
+    int32 vectors need 4.  A misaligned pointer is rejected before any HIP
+    call; a 4-byte-aligned scale vector passes the alignment check."""
+    assert gemm(s=A + 4) == ALIGN
+    assert gemm(a=A + 8) == ALIGN
+    assert gemm(sw=A + 2) == ALIGN
+    assert gemm(sw=A + 4) != ALIGN and gemm(sx=A + 4) != ALIGN
+    assert pack(s=A + 4) == ALIGN
+    assert pack(a=A + 2) == ALIGN
+    assert pack(mode=1, s=A + 4, a=A + 2, g=0, qmax=0) != ALIGN  # INT4: s/a unused
+    assert lib.w4a8_gemm_ablation(0, A, A, A, A + 4, A, A, A, 0, 256, 256, 512, 128,
+                                  None) == ALIGN
+    assert lib.w4a8_gemm_grouped(A, A, A, 4, A, A, A + 8, A, A, 0, 64, 256, 512, 64, 16,
+                                 None) == ALIGN
+    assert lib.w4a8_gemm_grouped(A, A, A + 4, 4, A, A, A, A, A, 0, 64, 256, 512, 64, 16,
+                                 None) != ALIGN
+
+
+def test_binding_checks_sizes_before_any_launch():
+    """The Python binding compares every operand's size with the call's
+    M, N, K (and group) before a pointer reaches the library, so a wrongly
+    sized output, scale vector or packed array cannot be read or written
+    past its end.  CPU tensors of the right sizes get past these checks and
+    stop at the device check, so nothing here launches anything."""
+    torch = pytest.importorskip("torch")
+    M, N, K, g = 16, 256, 512, 64
+    X = torch.zeros((M, K), dtype=torch.int8)
+    sx = torch.ones(M)
+    pk = {"wq": torch.zeros(N * K // 2, dtype=torch.uint8),
+          "s_u8": torch.ones(N * K // g, dtype=torch.uint8),
+          "a_u8": torch.ones(N * K // g, dtype=torch.uint8),
+          "sw": torch.ones(N), "N": N, "K": K, "group": g}
+    for fn in (w4.gemm, lambda *a, **k: w4.gemm_ablation(w4.ABL_LQQ, *a, **k)):
+        with pytest.raises(ValueError, match="out"):
+            fn(X, sx, pk, out=torch.empty((M, N - 64), dtype=torch.float16))
+        with pytest.raises(ValueError, match="sx"):
+            fn(X, sx[:M - 1], pk)
+        for key in ("wq", "s_u8", "a_u8", "sw"):
+            with pytest.raises(ValueError, match=key):
+                fn(X, sx, dict(pk, **{key: pk[key][:-16]}))
+        with pytest.raises(ValueError, match="GPU"):
+            fn(X, sx, pk)
+    with pytest.raises(ValueError, match="K of X"):
+        w4.gemm(torch.zeros((M, K + 128), dtype=torch.int8), sx, pk)
+    # grouped: E experts' arrays end to end
+    E = 2
+    pke = {k: (torch.cat([v, v]) if torch.is_tensor(v) else v) for k, v in pk.items()}
+    pke["E"] = E
+    offs = torch.tensor([0, 8, M], dtype=torch.int32)
+    with pytest.raises(ValueError, match="out"):
+        w4.gemm_grouped(X, sx, offs, pke, 8, out=torch.empty((M + 1, N), dtype=torch.float16))
+    with pytest.raises(ValueError, match="wq"):
+        w4.gemm_grouped(X, sx, offs, dict(pke, wq=pk["wq"]), 8)
+    with pytest.raises(ValueError, match="GPU"):
+        w4.gemm_grouped(X, sx, offs, pke, 8)
+    # FP8 per-channel and folded, W8A8
+    Xe = torch.zeros((M, K), dtype=torch.uint8)
+    pf = {"wq": pk["wq"], "sw": pk["sw"], "N": N, "K": K}
+    with pytest.raises(ValueError, match="out"):
+        w4.gemm_fp8(Xe, sx, pf, out=torch.empty((M, N), dtype=torch.bfloat16)[:, :128])
+    with pytest.raises(ValueError, match="sw"):
+        w4.gemm_fp8(Xe, sx, dict(pf, sw=pk["sw"][:-1]))
+    pg = {"wq": pk["wq"], "fsc": torch.ones((K // g, N)), "tscale": torch.ones(1),
+          "N": N, "K": K, "group": g}
+    with pytest.raises(ValueError, match="fsc"):
+        w4.gemm_fp8g(Xe, sx, dict(pg, fsc=torch.ones((K // g, N - 64))))
+    with pytest.raises(ValueError, match="GPU"):
+        w4.gemm_fp8g(Xe, sx, pg)
+    p8 = {"wq8": torch.zeros(N * K, dtype=torch.int8), "sw": pk["sw"], "N": N, "K": K}
+    with pytest.raises(ValueError, match="wq8"):
+        w4.gemm_w8a8(X, sx, dict(p8, wq8=pk["wq"]))
+    with pytest.raises(ValueError, match="sx"):
+        w4.gemm_w8a8(X, torch.ones(M + 3), p8)

@@ -877,6 +877,59 @@ def test_256_row_tiles_long_k():
     assert np.all(np.abs(yg - refg) <= boundg + 1e-30) and rel_fro(yg, refg) <= 1e-3
 
 
+# The 256-row plan of the 16 x 16 x 64 kernel (the one the M = 4096 Llama-2-70B
+# shapes run), every output element against the oracle, outputs poisoned:
+# short K with an even (2) and odd (3) K-step count on a grid of 1024 tiles
+# (four waves, so 256-row tiles stay), and long K with 65 (odd, the padding
+# step) and 66 (even) K-steps; 4000 rows leave a ragged last row tile.  The
+# W8A8 comparison runs the same plan.  These are the cases where a missed
+# wait state in the hand-placed matrix-core schedule would show.
+_PLAN256 = [(4096, 16384, 256, 64, True), (4096, 16384, 384, 128, True),
+            (4000, 4096, 8320, 128, True), (4096, 4096, 8448, 64, False)]
+
+
+@pytest.mark.parametrize("M,N,K,g,w8", _PLAN256)
+def test_256_row_plan_every_element(M, N, K, g, w8):
+    assert w4.workspace_size(M, N, K) == 0
+    say(f"256-row 16x16x64 plan, every element: M={M} N={N} K={K} g={g}")
+    X8, sx, pk, acc, y = _small_problem(M, N, K, g, 1600 + K)
+    Yi = poison((M, N), torch.int32)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, out=Yi)
+    np.testing.assert_array_equal(host(Yi), acc)
+    del Yi
+    Yh = poison((M, N), torch.float16)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_F16, out=Yh)
+    assert f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y).max() <= 1
+    del Yh
+    if w8:
+        W = wl.gen_weights(N, K, 1600 + K)
+        ref8 = oracle.w8a8_pack(W)
+        acc8, y8, _ = oracle.w8a8_gemm(host(X8), host(sx), ref8)
+        pk8 = {"wq8": to_dev(ref8["wq8"]), "sw": to_dev(ref8["sw"]), "N": N, "K": K}
+        Yi = poison((M, N), torch.int32)
+        w4.gemm_w8a8(X8, sx, pk8, out_type=w4.OUT_I32, out=Yi)
+        np.testing.assert_array_equal(host(Yi), acc8)
+        Yh = poison((M, N), torch.float16)
+        w4.gemm_w8a8(X8, sx, pk8, out_type=w4.OUT_F16, out=Yh)
+        assert f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y8).max() <= 1
+
+
+def test_stream_params_from_global():
+    """The streamed kernel reads the group parameters from global memory
+    (byte loads per tile) when the parameter panels and X slots exceed its
+    LDS budget: 20 x 4096 x 28672 with g = 64 runs two row blocks per
+    workgroup, one tile, eight K-splitting waves, parameters not in LDS."""
+    M, N, K, g = 20, 4096, 28672, 64
+    say(f"streamed kernel, parameters from global memory: M={M} N={N} K={K} g={g}")
+    X8, sx, pk, acc, y = _small_problem(M, N, K, g, 1701)
+    Yi = poison((M, N), torch.int32)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, out=Yi)
+    np.testing.assert_array_equal(host(Yi), acc)
+    Yh = poison((M, N), torch.float16)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_F16, out=Yh)
+    assert f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y).max() <= 1
+
+
 def test_128_row_tiles_long_k():
     """128-row plans with more than 64 K-steps per workgroup run the
     32 x 32 x 32 tile kernel (1000 x 8192 x 8320: 256 tiles, no split, 65
@@ -947,8 +1000,10 @@ def test_llama_shapes_sampled(cfg, sh):
     W, pk = _device_packed(cfg, sh)
     X = wl.gen_activations(sh.M, sh.K, wl.seed_x(cfg, sh.M), wl.seed_outliers(cfg))
     Xq, sx = w4.quant_act(to_dev(X))
-    Yh = w4.gemm(Xq, sx, pk, out_type=w4.OUT_F16)
-    Yi = w4.gemm(Xq, sx, pk, out_type=w4.OUT_I32)
+    Yh = poison((sh.M, sh.N), torch.float16)
+    w4.gemm(Xq, sx, pk, out_type=w4.OUT_F16, out=Yh)
+    Yi = poison((sh.M, sh.N), torch.int32)
+    w4.gemm(Xq, sx, pk, out_type=w4.OUT_I32, out=Yi)
     torch.cuda.synchronize()
     rng = np.random.default_rng(sh.M * 7 + sh.N)
     nsel = np.sort(rng.choice(sh.N, 48, replace=False))

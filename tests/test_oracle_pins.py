@@ -322,6 +322,88 @@ def test_quant_rows_e4m3_scale():
     assert np.median(rel) < 0.04
 
 
+def _e4m3_magnitudes():
+    """The 127 finite non-negative OCP e4m3 values, code 0x00 .. 0x7E, from
+    the format definition (bias 7; exponent field 0 is subnormal, m/8 *
+    2^-6), written here independently of the oracle's decoder."""
+    vals = []
+    for b in range(0x7F):
+        e, m = b >> 3, b & 7
+        vals.append(m / 8.0 * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7))
+    return np.array(vals, np.float64)
+
+
+def _e4m3_codes_brute(quot):
+    """Nearest finite e4m3 code of each float32 quotient by exhaustive search
+    over all 127 magnitudes; ties go to the even code; magnitudes above 448
+    saturate to 448 (0x7E); the sign bit is copied (zeros keep it)."""
+    vals = _e4m3_magnitudes()
+    a = np.abs(quot.astype(np.float64)).ravel()
+    d = np.abs(a[:, None] - vals[None, :])
+    best = d.min(axis=1, keepdims=True)
+    cand = d == best
+    # among equally near codes (at most two, adjacent), take the even one
+    even = cand & (np.arange(0x7F)[None, :] % 2 == 0)
+    code = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+    code = code.astype(np.uint8) | np.where(np.signbit(quot.ravel()), 0x80, 0).astype(np.uint8)
+    return code.reshape(quot.shape)
+
+
+def test_quant_rows_e4m3_every_code():
+    """Per-token e4m3 codes element by element ([FQ] abstract: FP8
+    activations; the reading: scale = max|x| / 448 in float32, codes =
+    e4m3 of the float32 quotient x / scale, nearest with ties to even,
+    saturating).  The expected codes come from numpy's float32 quotient
+    and an exhaustive nearest search over the format's values, on rows
+    whose scales are not powers of two.  Each row also holds quotients
+    placed exactly on midpoints between neighbouring e4m3 values, where a
+    quotient formed another way (in double precision, or as x times the
+    reciprocal 448 / max) would round to the other neighbour."""
+    rng = np.random.default_rng(31)
+    vals = _e4m3_magnitudes()
+    mids = (vals[:-1] + vals[1:]) / 2
+    rows, cols = 12, 1024
+    x = (rng.standard_normal((rows, cols)) * 3.0).astype(np.float32)
+    x[:, rng.choice(cols, 10, replace=False)] *= np.float32(20.0)
+    x[:, 5] = 0.0
+    x[:, 6] = -0.0
+    n_ties = 0
+    for r in range(rows):
+        amax = np.float32(rng.uniform(3.0, 90.0))  # never a power of two
+        while float(amax) == 2.0 ** np.round(np.log2(float(amax))):
+            amax = np.float32(rng.uniform(3.0, 90.0))
+        row = np.clip(x[r], -amax, amax)
+        row[0] = amax
+        s = np.float32(amax) / np.float32(448.0)
+        # midpoint quotients: x = the float32 nearest s * mid, nudged one ulp
+        # either way until the float32 quotient x / s is the midpoint itself
+        placed = 0
+        for i, mdp in enumerate(mids[::3]):
+            xv = np.float32(mdp * float(s))
+            for cand in (xv, np.nextafter(xv, np.float32(np.inf)),
+                         np.nextafter(xv, np.float32(-np.inf))):
+                if float(np.float32(cand) / s) == mdp and abs(cand) <= amax:
+                    sign = np.float32(-1.0) if i % 2 else np.float32(1.0)
+                    row[16 + placed] = sign * cand
+                    placed += 1
+                    break
+        n_ties += placed
+        x[r] = row
+    q, s = oracle.quant_rows_e4m3(x)
+    want_s = (np.abs(x).max(axis=1) / np.float32(448.0)).astype(np.float32)
+    np.testing.assert_array_equal(s, want_s)
+    quot = (x / want_s[:, None]).astype(np.float32)  # numpy: float32 IEEE division
+    want = _e4m3_codes_brute(quot)
+    np.testing.assert_array_equal(q, want)
+    assert n_ties > 20 * rows  # the midpoint cases are really there
+    # the reading's alternatives differ from it on those rows
+    recip = (x * (np.float32(448.0) / np.abs(x).max(axis=1))[:, None]).astype(np.float32)
+    assert not np.array_equal(_e4m3_codes_brute(recip), want)
+    dq = x.astype(np.float64) / want_s[:, None].astype(np.float64)
+    dcode = _e4m3_codes_brute(dq)
+    assert not np.array_equal(dcode, want)
+
+
 # ------------------------------------------------------ per-row quant ------
 def test_quant_sym_rows_properties():
     rng = np.random.default_rng(12)

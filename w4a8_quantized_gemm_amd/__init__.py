@@ -116,6 +116,41 @@ def _need(t, dtype, name):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _numel_is(t, n, name):
+    """Shape checks run before the dtype / device checks, so a caller's
+    wrongly sized tensor is named before any pointer reaches the library
+    (whose kernels read and write exactly the sizes the shape implies)."""
+    if t is not None and t.numel() != n:
+        raise ValueError(f"{name} must hold {n} elements, got {t.numel()} "
+                         f"(shape {tuple(t.shape)})")
+
+
+def _shape_is(t, shape, name):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _gemm_shapes(X, sx, packed, out, keys, group=None, E=1):
+    """M, N, K of a GEMM call after checking every operand's size against
+    them: X [M][K], sx [M], out [M][N], the packed weight arrays of E
+    experts (codes, group parameters, channel scales) and K against the
+    packed K."""
+    if X.dim() != 2:
+        raise ValueError("X must be a 2-D tensor [M][K]")
+    M, K = X.shape
+    N = packed["N"]
+    if packed["K"] != K:
+        raise ValueError("K of X and of the packed weights differ")
+    _numel_is(sx, M, "sx")
+    _shape_is(out, (M, N), "out")
+    sizes = {"wq": N * K // 2, "wq8": N * K, "sw": N, "tscale": 1}
+    if group:
+        sizes.update(s_u8=N * K // group, a_u8=N * K // group, fsc=N * K // group)
+    for k in keys:
+        _numel_is(packed.get(k), E * sizes[k], k)
+    return M, N, K
+
+
 # ------------------------------------------------------------------ API ----
 
 def pack(W, group: int = 64, qmax: int = 127, mode: int = PACK_LQQ, stream=None):
@@ -202,12 +237,10 @@ def gemm(Xq, sx, packed, out_type: int = OUT_F16, splitk: int = 0, out=None,
     `workspace` (uint8 device tensor of at least workspace_size() bytes) is
     allocated here when not given and the shape needs one."""
     torch = _torch()
+    M, N, K = _gemm_shapes(Xq, sx, packed, out, ("wq", "s_u8", "a_u8", "sw"),
+                           packed["group"])
     _need(Xq, torch.int8, "Xq")
-    M, K = Xq.shape
-    N = packed["N"]
-    if packed["K"] != K:
-        raise ValueError("K of X and of the packed weights differ")
-    if out_type == OUT_F16:
+    if out_type == OUT_F16 or sx is not None:
         _need(sx, torch.float32, "sx")
     ydt = torch.float16 if out_type == OUT_F16 else torch.int32
     Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
@@ -239,15 +272,14 @@ def gemm_grouped(Xq, sx, offsets, packed, max_rows: int, out_type: int = OUT_F16
     """w4a8_gemm_grouped: rows offsets[e]..offsets[e+1]-1 of Xq use expert e
     of `packed` (from pack_experts); offsets is a device int32 [E+1] tensor."""
     torch = _torch()
-    _need(Xq, torch.int8, "Xq")
-    _need(offsets, torch.int32, "offsets")
-    M, K = Xq.shape
-    N, E = packed["N"], packed["E"]
-    if packed["K"] != K:
-        raise ValueError("K of X and of the packed weights differ")
+    E = packed["E"]
+    M, N, K = _gemm_shapes(Xq, sx, packed, out, ("wq", "s_u8", "a_u8", "sw"),
+                           packed["group"], E)
     if offsets.numel() != E + 1:
         raise ValueError("offsets must hold E + 1 entries")
-    if out_type == OUT_F16:
+    _need(Xq, torch.int8, "Xq")
+    _need(offsets, torch.int32, "offsets")
+    if out_type == OUT_F16 or sx is not None:
         _need(sx, torch.float32, "sx")
     ydt = torch.float16 if out_type == OUT_F16 else torch.int32
     Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
@@ -265,12 +297,10 @@ def gemm_ablation(variant: int, Xq, sx, packed, out_type: int = OUT_F16, out=Non
     ABL_LQQ (production), ABL_AFFINE16 (conventional signed 16-bit-lane
     decode) or ABL_LQQ_COARSE (decode not interleaved with the matrix core)."""
     torch = _torch()
+    M, N, K = _gemm_shapes(Xq, sx, packed, out, ("wq", "s_u8", "a_u8", "sw"),
+                           packed["group"])
     _need(Xq, torch.int8, "Xq")
-    M, K = Xq.shape
-    N = packed["N"]
-    if packed["K"] != K:
-        raise ValueError("K of X and of the packed weights differ")
-    if out_type == OUT_F16:
+    if out_type == OUT_F16 or sx is not None:
         _need(sx, torch.float32, "sx")
     ydt = torch.float16 if out_type == OUT_F16 else torch.int32
     Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
@@ -288,12 +318,9 @@ def gemm_fp8(Xq, sx, packed, out_type: int = OUT_BF16, splitk: int = 0, out=None
 
     `workspace` as for gemm() (same size: float32 split-K partials)."""
     torch = _torch()
+    M, N, K = _gemm_shapes(Xq, sx, packed, out, ("wq", "sw"))
     _need(Xq, torch.uint8, "Xq")
     _need(sx, torch.float32, "sx")
-    M, K = Xq.shape
-    N = packed["N"]
-    if packed["K"] != K:
-        raise ValueError("K of X and of the packed weights differ")
     ydt = torch.bfloat16 if out_type == OUT_BF16 else torch.float32
     Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
     _need(Y, ydt, "out")
@@ -329,12 +356,9 @@ def gemm_fp8g(Xq, sx, packed, out_type: int = OUT_BF16, splitk: int = 0, out=Non
               workspace=None, stream=None):
     """w4fp8g_gemm on pack_fp8g output: Y [M][N] bfloat16 or float32."""
     torch = _torch()
+    M, N, K = _gemm_shapes(Xq, sx, packed, out, ("wq", "fsc", "tscale"), packed["group"])
     _need(Xq, torch.uint8, "Xq")
     _need(sx, torch.float32, "sx")
-    M, K = Xq.shape
-    N = packed["N"]
-    if packed["K"] != K:
-        raise ValueError("K of X and of the packed weights differ")
     ydt = torch.bfloat16 if out_type == OUT_BF16 else torch.float32
     Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
     _need(Y, ydt, "out")
@@ -367,11 +391,10 @@ def gemm_w8a8(Xq, sx, packed, out_type: int = OUT_F16, splitk: int = 0, out=None
               workspace=None, stream=None):
     """w8a8_gemm on pack_w8 output: Y [M][N] fp16 (OUT_F16) or int32 (OUT_I32)."""
     torch = _torch()
+    M, N, K = _gemm_shapes(Xq, sx, packed, out, ("wq8", "sw"))
     _need(Xq, torch.int8, "Xq")
-    M, K = Xq.shape
-    N = packed["N"]
-    if packed["K"] != K:
-        raise ValueError("K of X and of the packed weights differ")
+    if out_type == OUT_F16 or sx is not None:
+        _need(sx, torch.float32, "sx")
     ydt = torch.float16 if out_type == OUT_F16 else torch.int32
     Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
     _need(Y, ydt, "out")

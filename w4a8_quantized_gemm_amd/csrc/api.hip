@@ -142,7 +142,7 @@ W4A8_EXPORT const char* w4a8_status_str(w4a8_status_t s) {
         case W4A8_OK: return "ok";
         case W4A8_ERR_NULL_PTR: return "a required pointer is NULL";
         case W4A8_ERR_SHAPE: return "invalid shape, group, qmax or split factor";
-        case W4A8_ERR_ALIGNMENT: return "a device pointer is not 16-byte aligned";
+        case W4A8_ERR_ALIGNMENT: return "a device pointer is misaligned (16 bytes for arrays, 4 for scale vectors)";
         case W4A8_ERR_WORKSPACE: return "workspace is smaller than w4a8_workspace_size()";
         case W4A8_ERR_UNSUPPORTED: return "unsupported device, mode or output type";
         case W4A8_ERR_HIP: return "HIP runtime error (see w4a8_last_hip_error)";
@@ -171,6 +171,7 @@ W4A8_EXPORT w4a8_status_t w4a8_pack(const float* W, int N, int K, int group, int
     if (!W || !wq || !sw) return W4A8_ERR_NULL_PTR;
     if (mode == W4A8_PACK_LQQ && (!s_u8 || !a_u8)) return W4A8_ERR_NULL_PTR;
     if (!aligned16(W) || !aligned16(wq) || !aligned4(sw)) return W4A8_ERR_ALIGNMENT;
+    if (mode == W4A8_PACK_LQQ && (!aligned16(s_u8) || !aligned16(a_u8))) return W4A8_ERR_ALIGNMENT;
     w4a8_status_t d = check_device();
     if (d != W4A8_OK) return d;
     if (mode == W4A8_PACK_LQQ)
@@ -227,6 +228,7 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint
     if (!X || !wq || !s_u8 || !a_u8 || !Y) return W4A8_ERR_NULL_PTR;
     if (out_type == W4A8_OUT_F16 && (!sx || !sw)) return W4A8_ERR_NULL_PTR;
     if (!aligned16(X) || !aligned16(wq) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
+    if (!aligned16(s_u8) || !aligned16(a_u8)) return W4A8_ERR_ALIGNMENT;
     if ((sx && !aligned4(sx)) || (sw && !aligned4(sw))) return W4A8_ERR_ALIGNMENT;
     const size_t need = w4a8_workspace_size(M, N, K, splitk);
     if (workspace_bytes < need) return W4A8_ERR_WORKSPACE;
@@ -256,6 +258,7 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm_grouped(const int8_t* X, const float* sx,
     if (!X || !offsets || !wq || !s_u8 || !a_u8 || !Y) return W4A8_ERR_NULL_PTR;
     if (out_type == W4A8_OUT_F16 && (!sx || !sw)) return W4A8_ERR_NULL_PTR;
     if (!aligned16(X) || !aligned16(wq) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
+    if (!aligned16(s_u8) || !aligned16(a_u8)) return W4A8_ERR_ALIGNMENT;
     if (!aligned4(offsets) || (sx && !aligned4(sx)) || (sw && !aligned4(sw)))
         return W4A8_ERR_ALIGNMENT;
     w4a8_status_t d = check_device();
@@ -305,6 +308,7 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm_ablation(int variant, const int8_t* X, const
     if (!X || !wq || !s_u8 || !a_u8 || !Y) return W4A8_ERR_NULL_PTR;
     if (out_type == W4A8_OUT_F16 && (!sx || !sw)) return W4A8_ERR_NULL_PTR;
     if (!aligned16(X) || !aligned16(wq) || !aligned16(Y)) return W4A8_ERR_ALIGNMENT;
+    if (!aligned16(s_u8) || !aligned16(a_u8)) return W4A8_ERR_ALIGNMENT;
     if ((sx && !aligned4(sx)) || (sw && !aligned4(sw))) return W4A8_ERR_ALIGNMENT;
     w4a8_status_t d = check_device();
     if (d != W4A8_OK) return d;
