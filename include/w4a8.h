@@ -18,7 +18,8 @@
  * Conventions for every entry point:
  *   - All array arguments are DEVICE pointers, owned by the caller.  The
  *     library never allocates or frees device memory and keeps no state
- *     besides a per-device cache of the device architecture check.
+ *     besides a per-device cache of the device architecture check and, for
+ *     w4a8_gemm_noalloc, one static device array per GPU (below).
  *   - Work is enqueued on `stream` (NULL = the default stream) and the call
  *     returns without synchronising.  Faults inside kernels surface at the
  *     caller's next synchronisation, as usual in HIP.
@@ -182,6 +183,28 @@ w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint8_t* wq,
                         const float* sw, void* Y, int out_type, int M, int N,
                         int K, int group, int splitk, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * w4a8_gemm for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Arguments, results and errors are those of w4a8_gemm (same kernels, same
+ * bits), without the workspace: the split-K partials go to a static device
+ * array of this library, W4A8_NOALLOC_SCRATCH_BYTES long, one per GPU,
+ * held until the process ends.  Every problem size w4a8_gemm accepts needs
+ * at most 32 MiB of partials (at most 256 workgroups of 128 x 256 int32
+ * each); a problem whose w4a8_workspace_size(M, N, K, splitk) exceeded the
+ * array would return W4A8_ERR_WORKSPACE.  No call allocates or frees
+ * memory.  All calls on one GPU share its array: calls that may overlap in
+ * time on one GPU (different streams, no ordering between them) race and
+ * must not be issued.  Calls ordered on one stream are safe, and so are
+ * calls on different GPUs.
+ */
+#define W4A8_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+w4a8_status_t w4a8_gemm_noalloc(const int8_t* X, const float* sx,
+                                const uint8_t* wq, const uint8_t* s_u8,
+                                const uint8_t* a_u8, const float* sw, void* Y,
+                                int out_type, int M, int N, int K, int group,
+                                int splitk, hipStream_t stream);
 
 /*
  * Grouped W4A8 GEMM for mixture-of-experts layers (the pages evaluate

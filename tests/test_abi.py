@@ -324,3 +324,20 @@ def test_binding_checks_sizes_before_any_launch():
         w4.gemm_w8a8(X, sx, dict(p8, wq8=pk["wq"]))
     with pytest.raises(ValueError, match="sx"):
         w4.gemm_w8a8(X, torch.ones(M + 3), p8)
+
+
+def test_gemm_noalloc_validation():
+    """w4a8_gemm_noalloc validates exactly as w4a8_gemm does, before any HIP
+    call (no workspace argument: the library's static scratch stands in)."""
+    def na(X=A, sx=A, wq=A, s=A, a=A, sw=A, Y=A, out=0, M=16, N=64, K=256, g=64, splitk=0):
+        return lib.w4a8_gemm_noalloc(X, sx, wq, s, a, sw, Y, out, M, N, K, g, splitk, None)
+    assert na(X=None) == NULL
+    assert na(sx=None) == NULL
+    assert na(out=5) == UNSUP
+    assert na(K=192) == SHAPE
+    assert na(splitk=3) == SHAPE
+    assert na(s=A + 4) == ALIGN
+    assert na(M=0, X=None, Y=None) == OK
+    # a split-K shape: needs partials, none are passed, still not a NULL error
+    assert lib.w4a8_workspace_size(128, 512, 8192, 0) > 0
+    assert na(M=128, N=512, K=8192) in (HIP, UNSUP)

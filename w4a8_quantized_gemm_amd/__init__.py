@@ -42,6 +42,7 @@ LAYOUT_VERSION = 1
 
 EXPORTS = ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act",
            "w4a8_quant_act_ex", "w4fp8_quant_act_ex", "w4a8_workspace_size", "w4a8_gemm",
+           "w4a8_gemm_noalloc",
            "w4a8_gemm_ablation", "w4a8_gemm_grouped", "w4fp8_gemm", "w4fp8g_pack",
            "w4fp8g_gemm", "w8a8_pack", "w8a8_gemm",
            "w4a8_status_str", "w4a8_last_hip_error", "w4a8_layout_version")
@@ -55,6 +56,7 @@ lib.w4fp8_quant_act_ex.argtypes = [_P, _I, _I, _I, _P, _P, _P]
 lib.w4a8_workspace_size.argtypes = [_I, _I, _I, _I]
 lib.w4a8_workspace_size.restype = _Z
 lib.w4a8_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]
+lib.w4a8_gemm_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
 lib.w4fp8_gemm.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P, _Z, _P]
 lib.w4a8_gemm_ablation.argtypes = [_I, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _P]
 lib.w4a8_gemm_grouped.argtypes = [_P, _P, _P, _I, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
@@ -67,7 +69,7 @@ lib.w4a8_status_str.restype = ctypes.c_char_p
 lib.w4a8_last_hip_error.restype = _I
 lib.w4a8_layout_version.restype = _I
 for _n in ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act", "w4a8_quant_act_ex",
-           "w4fp8_quant_act_ex", "w4a8_gemm", "w4a8_gemm_ablation", "w4a8_gemm_grouped",
+           "w4fp8_quant_act_ex", "w4a8_gemm", "w4a8_gemm_noalloc", "w4a8_gemm_ablation", "w4a8_gemm_grouped",
            "w4fp8_gemm", "w4fp8g_pack", "w4fp8g_gemm", "w8a8_pack", "w8a8_gemm"):
     getattr(lib, _n).restype = _I
 
@@ -254,6 +256,27 @@ def gemm(Xq, sx, packed, out_type: int = OUT_F16, splitk: int = 0, out=None,
                          _ptr(packed["a_u8"]), _ptr(packed["sw"]), _ptr(Y), out_type, M, N,
                          K, packed["group"], splitk, _ptr(workspace), ws_bytes,
                          _stream(stream)), "w4a8_gemm")
+    return Y
+
+
+def gemm_noalloc(Xq, sx, packed, out_type: int = OUT_F16, splitk: int = 0, out=None,
+                 stream=None):
+    """w4a8_gemm_noalloc: w4a8_gemm with the library's static scratch as the
+    split-K workspace (the library allocates nothing; `out` given, nothing
+    is allocated here either)."""
+    torch = _torch()
+    M, N, K = _gemm_shapes(Xq, sx, packed, out, ("wq", "s_u8", "a_u8", "sw"),
+                           packed["group"])
+    _need(Xq, torch.int8, "Xq")
+    if out_type == OUT_F16 or sx is not None:
+        _need(sx, torch.float32, "sx")
+    ydt = torch.float16 if out_type == OUT_F16 else torch.int32
+    Y = out if out is not None else torch.empty((M, N), dtype=ydt, device=Xq.device)
+    _need(Y, ydt, "out")
+    _check(lib.w4a8_gemm_noalloc(_ptr(Xq), _ptr(sx), _ptr(packed["wq"]), _ptr(packed["s_u8"]),
+                                 _ptr(packed["a_u8"]), _ptr(packed["sw"]), _ptr(Y), out_type,
+                                 M, N, K, packed["group"], splitk, _stream(stream)),
+           "w4a8_gemm_noalloc")
     return Y
 
 

@@ -215,11 +215,16 @@ W4A8_EXPORT w4a8_status_t w4fp8_quant_act(const float* X, int M, int K, uint8_t*
     return w4fp8_quant_act_ex(X, W4A8_IN_F32, M, K, Xq, sx, stream);
 }
 
-W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint8_t* wq,
-                                    const uint8_t* s_u8, const uint8_t* a_u8, const float* sw,
-                                    void* Y, int out_type, int M, int N, int K, int group,
-                                    int splitk, void* workspace, size_t workspace_bytes,
-                                    hipStream_t stream) {
+namespace w4a8 {
+
+// w4a8_gemm's validation and dispatch.  use_scratch: the workspace is this
+// library's static device scratch (w4a8_gemm_noalloc), workspace_bytes its
+// capacity; its address is looked up only once the arguments are valid.
+w4a8_status_t gemm_entry(const int8_t* X, const float* sx, const uint8_t* wq,
+                         const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
+                         int out_type, int M, int N, int K, int group, int splitk,
+                         void* workspace, size_t workspace_bytes, bool use_scratch,
+                         hipStream_t stream) {
     if (out_type != W4A8_OUT_F16 && out_type != W4A8_OUT_I32) return W4A8_ERR_UNSUPPORTED;
     if (M < 0 || !valid_nk(N, K) || !valid_group(group) || !valid_splitk(splitk, K))
         return W4A8_ERR_SHAPE;
@@ -232,10 +237,17 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint
     if ((sx && !aligned4(sx)) || (sw && !aligned4(sw))) return W4A8_ERR_ALIGNMENT;
     const size_t need = w4a8_workspace_size(M, N, K, splitk);
     if (workspace_bytes < need) return W4A8_ERR_WORKSPACE;
-    if (need > 0 && !workspace) return W4A8_ERR_NULL_PTR;
-    if (need > 0 && !aligned16(workspace)) return W4A8_ERR_ALIGNMENT;
+    if (!use_scratch && need > 0 && !workspace) return W4A8_ERR_NULL_PTR;
+    if (!use_scratch && need > 0 && !aligned16(workspace)) return W4A8_ERR_ALIGNMENT;
     w4a8_status_t d = check_device();
     if (d != W4A8_OK) return d;
+    if (use_scratch) {
+        workspace = nullptr;
+        if (need > 0) {
+            const hipError_t e = noalloc_scratch(&workspace);
+            if (e != hipSuccess) return hip_status(e);
+        }
+    }
     if (splitk == 0 && use_mfma_tiles(M, N, K))
         return hip_status(w4a8::launch_w4a8_mfma(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
                                                  group, w4a8::plan_w4a8_mfma(M, N, K), workspace,
@@ -243,6 +255,17 @@ W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint
     return hip_status(w4a8::launch_w4a8_stream(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
                                                group, choose_stream(M, N, K, splitk, true),
                                                stream));
+}
+
+}  // namespace w4a8
+
+W4A8_EXPORT w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint8_t* wq,
+                                    const uint8_t* s_u8, const uint8_t* a_u8, const float* sw,
+                                    void* Y, int out_type, int M, int N, int K, int group,
+                                    int splitk, void* workspace, size_t workspace_bytes,
+                                    hipStream_t stream) {
+    return w4a8::gemm_entry(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K, group, splitk,
+                            workspace, workspace_bytes, false, stream);
 }
 
 W4A8_EXPORT w4a8_status_t w4a8_gemm_grouped(const int8_t* X, const float* sx,

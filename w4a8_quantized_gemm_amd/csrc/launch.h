@@ -119,4 +119,8 @@ hipError_t launch_w4fp8g_stream(const uint8_t* X, const float* sx, const uint8_t
                                 const float* fsc, const float* tsc, void* Y, int out_type, int M,
                                 int N, int K, int group, StreamCfg cfg, hipStream_t st);
 
+// Device address of this library's static scratch array on the current
+// device (looked up once per device); W4A8_NOALLOC_SCRATCH_BYTES long.
+hipError_t noalloc_scratch(void** ptr);
+
 }  // namespace w4a8
