@@ -282,7 +282,13 @@ def test_mfma_split_k(M, N, K, g):
     w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, out=Yi)
     np.testing.assert_array_equal(host(Yi), acc)
     Yh = poison((M, N), torch.float16)
+    # a poisoned workspace (scratch: its contents on entry are ignored), then
+    # the same workspace again
     ws = poison((w4.workspace_size(M, N, K),), torch.uint8)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_F16, out=Yh, workspace=ws)
+    d = f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y)
+    assert d.max() <= 1
+    Yh = poison((M, N), torch.float16)
     w4.gemm(X8, sx, pk, out_type=w4.OUT_F16, out=Yh, workspace=ws)
     d = f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y)
     assert d.max() <= 1
@@ -381,6 +387,39 @@ def test_split_counts_any_integer(M, N, K, splits):
     Ys = poison((M, N), torch.int32)
     w4.gemm(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_I32, splitk=1, out=Ys)
     np.testing.assert_array_equal(got, host(Ys))
+
+
+def test_workspace_shared_across_split_calls():
+    """One workspace serves a sequence of split-K calls of different shapes
+    and kinds (W4A8, FP8, W8A8) ordered on one stream: whatever one call
+    leaves in it does not reach the next call's results."""
+    shapes = [(128, 512, 4096, 128), (100, 256, 2048, 64), (200, 1024, 8192, 128)]
+    need = max(w4.workspace_size(M, N, K) for M, N, K, _ in shapes)
+    ws = poison((need,), torch.uint8)
+    for i, (M, N, K, g) in enumerate(shapes):
+        say(f"shared workspace, call {i}: M={M} N={N} K={K} g={g}")
+        assert w4.workspace_size(M, N, K) > 0
+        X8, sx, pk, acc, y = _small_problem(M, N, K, g, 3300 + i)
+        Yi = poison((M, N), torch.int32)
+        w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, out=Yi, workspace=ws)
+        np.testing.assert_array_equal(host(Yi), acc)
+        # FP8 split call on the same workspace
+        W = wl.gen_weights(N, K, 3300 + i)
+        Xf = wl.gen_activations(M, K, 3301 + i, 3302 + i)
+        Xe, sxe = oracle.quant_rows_e4m3(Xf)
+        pf = oracle.w4fp8_pack(W)
+        pkf = {"wq": to_dev(pf["wq"]), "sw": to_dev(pf["sw"]), "N": N, "K": K}
+        Yf = poison((M, N), torch.float32)
+        w4.gemm_fp8(to_dev(Xe), to_dev(sxe), pkf, out_type=w4.OUT_F32, out=Yf, workspace=ws)
+        ref, _ = oracle.w4fp8_ref(Xe, sxe, pf["q"], pf["sw"])
+        assert rel_fro(host(Yf), ref) <= 1e-3
+        # W8A8 split call
+        ref8 = oracle.w8a8_pack(W)
+        acc8, _, _ = oracle.w8a8_gemm(host(X8), host(sx), ref8)
+        pk8 = {"wq8": to_dev(ref8["wq8"]), "sw": to_dev(ref8["sw"]), "N": N, "K": K}
+        Yi = poison((M, N), torch.int32)
+        w4.gemm_w8a8(X8, sx, pk8, out_type=w4.OUT_I32, out=Yi, workspace=ws)
+        np.testing.assert_array_equal(host(Yi), acc8)
 
 
 def test_workspace_too_small_is_rejected():
