@@ -54,7 +54,15 @@ def parse():
     p.add_argument("--no-fp8", action="store_true")
     p.add_argument("--no-ablation", action="store_true")
     p.add_argument("--no-moe", action="store_true")
-    p.add_argument("--cpu-sample-cols", type=int, default=256)
+    p.add_argument("--no-7b", action="store_true")
+    p.add_argument("--cpu-sample-cols", type=int, default=4096,
+                   help="output channels per slot in the all-core oracle sample")
+    p.add_argument("--cpu-sample-cols-1core", type=int, default=256,
+                   help="output channels per slot in the one-core oracle sample")
+    p.add_argument("--cpu-baseline-only", action="store_true",
+                   help="only time the oracle sample (no GPU) and print its JSON")
+    p.add_argument("--bursts", type=int, default=5,
+                   help="bursts of 20 back-to-back launches per slot outside the timed step")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run plain 256 MiB device-to-device copies (the known-size "
                         "kernel that scales the HBM byte counters)")
@@ -104,7 +112,21 @@ def profiled_traffic(slot_name):
     counter summary (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by
     what the same counter reads for a copy of known size), or None when no
     summary exists or the kernel sources changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{slot_name.replace(':', '_')}.txt")
+    kv = _profile_kv(f"traffic_{slot_name.replace(':', '_')}.txt")
+    if kv is None:
+        return None
+    try:
+        fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"])
+        write = float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"])
+    except (KeyError, ValueError):
+        return None
+    return round((fetch + write) * 1024.0)
+
+
+def _profile_kv(name):
+    """key: value lines of profiles/<name>.txt, or None when the file is
+    missing or its counters were taken from other kernel code."""
+    path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -113,14 +135,30 @@ def profiled_traffic(slot_name):
             if ":" in line and not line.startswith("#"):
                 k, v = line.split(":", 1)
                 kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != source_digest():
+        return None
+    return kv
+
+
+def profiled_mfma(slot_name, M, N, K, us_per_launch):
+    """Matrix-core counters per launch of `slot_name`'s kernel from the
+    committed summary: INT8 matrix-core operations counted (MOPS x 512)
+    against the algorithmic 2*M*N*K, the fraction of SIMD cycles the matrix
+    core was busy, and the shader clock the busy cycles imply."""
+    kv = _profile_kv(f"mfma_{slot_name.replace(':', '_')}.txt")
+    if kv is None:
+        return None
     try:
-        if kv.get("source_sha256") != source_digest():
-            return None
-        fetch = float(kv["fetch_kib_per_dispatch"]) * float(kv["fetch_scale"])
-        write = float(kv["write_kib_per_dispatch"]) * float(kv["write_scale"])
+        mops = float(kv["mfma_mops_i8_per_dispatch"])
+        busy = float(kv["mfma_busy_cycles_per_dispatch"])
+        gui = float(kv["grbm_gui_active_per_dispatch"])
+        simds = float(kv["simds"])
     except (KeyError, ValueError):
         return None
-    return round((fetch + write) * 1024.0)
+    return {"int8_ops_counted": mops * 512.0, "int8_ops_algorithmic": 2.0 * M * N * K,
+            "busy_frac": round(busy / (gui * simds), 4),
+            "gui_active_cycles": gui,
+            "clock_ghz_implied": round(gui / (us_per_launch * 1e3), 3)}
 
 
 def calibrate_copy():
@@ -136,21 +174,28 @@ def calibrate_copy():
     print(json.dumps({"calibrate_copy_bytes": n, "dispatches": 4}), flush=True)
 
 
+def sweep_desc():
+    """(name, M, N, K, group, pair) of every slot of the sweep (no GPU)."""
+    pairs = wl.nk_pairs(CFG)
+    tags = {pairs[0]: "upgate", pairs[1]: "down"}
+    return [(f"{tags[(N, K)]}:M{M}", M, N, K, 128, pi)
+            for pi, (N, K) in enumerate(pairs) for M in MS]
+
+
 def cpu_baseline(slots_desc, ncols):
     """Oracle (test infrastructure) timed on the host cores: identity decode,
     int32 GEMM and fp16 epilogue for every slot of the sweep, restricted to
     `ncols` output channels per slot; scaled to the full step."""
-    import numpy as np
     import oracle
-    import workloads as wl
     total_ops_full = 0.0
     t_scaled = 0.0
+    t_real = 0.0
     per_pair = {}
     for (tag, M, N, K, g, pair) in slots_desc:
         if pair not in per_pair:
             # numpy draws row-major: a smaller draw with the same seed is
             # exactly the leading rows of the full matrices the GPU uses
-            W = wl.gen_weights(ncols, K, wl.seed_w(CFG, pair))
+            W = wl.gen_weights(min(ncols, N), K, wl.seed_w(CFG, pair))
             X = wl.gen_activations(max(MS), K, wl.seed_x(CFG, max(MS)),
                                    wl.seed_outliers(CFG))
             X8_all, sx_all = oracle.quant_sym_rows(X, 127)
@@ -160,14 +205,27 @@ def cpu_baseline(slots_desc, ncols):
         t0 = time.perf_counter()
         oracle.w4a8_gemm(X8, sx, pk, g)
         dt = time.perf_counter() - t0
-        t_scaled += dt * (N / ncols)
+        t_real += dt
+        t_scaled += dt * (N / min(ncols, N))
         total_ops_full += 2.0 * M * N * K
     threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or len(os.sched_getaffinity(0))
-    return {"value": total_ops_full / t_scaled / 1e12, "unit": "TOPS", "cores": threads,
+    return {"value": round(total_ops_full / t_scaled / 1e12, 5), "unit": "TOPS", "cores": threads,
             "kind": "oracle",
             "sample": f"each of the 10 GEMMs of the sweep on {ncols} of its N output "
-                      f"channels (decode + int32 GEMM + fp16 epilogue), time scaled by "
-                      f"N/{ncols}; {t_scaled:.1f} s projected for one full step"}
+                      f"channels (decode + int32 GEMM + fp16 epilogue): {t_real:.1f} s of "
+                      f"oracle time, scaled by N/{ncols} to {t_scaled:.1f} s for one full step"}
+
+
+def cpu_baseline_one_core(ncols):
+    """The same oracle sample in a child process limited to one thread."""
+    import subprocess
+    env = dict(os.environ, OMP_NUM_THREADS="1")
+    res = subprocess.run([sys.executable, os.path.abspath(__file__), "--cpu-baseline-only",
+                          "--cpu-sample-cols", str(ncols)], env=env, capture_output=True,
+                         text=True, timeout=600)
+    if res.returncode != 0:
+        return {"error": res.stderr[-300:]}
+    return json.loads(res.stdout.strip().splitlines()[-1])
 
 
 def main():
@@ -178,6 +236,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.cpu_baseline_only:
+        print(json.dumps(cpu_baseline(sweep_desc(), args.cpu_sample_cols)), flush=True)
         return
 
     import numpy as np
@@ -205,9 +266,14 @@ def main():
             name = f"{tags[(N, K)]}:M{M}"
             if args.only and args.only != name:
                 continue
-            copy = {k: (v.clone() if torch.is_tensor(v) else v) for k, v in pk.items()}
+            # one weight copy per slot; a slot run alone (--only) rotates
+            # through copies past 512 MB so that, as in the full step, no
+            # launch finds its weights in the 256 MB Infinity Cache
+            ncp = 1 if not args.only else -(-600_000_000 // weight_bytes(N, K, g))
+            copies = [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in pk.items()}
+                      for _ in range(ncp)]
             Y = torch.empty((M, N), dtype=torch.float16, device=dev)
-            slots.append({"name": name, "M": M, "N": N, "K": K, "pair": pi, "pk": copy,
+            slots.append({"name": name, "M": M, "N": N, "K": K, "pair": pi, "pks": copies,
                           "X": Xq[:M], "sx": sx[:M], "Y": Y})
         del pk
     torch.cuda.synchronize()
@@ -224,17 +290,17 @@ def main():
                or list(range(len(slots))))
     evpos = {i: j for j, i in enumerate(evslots)}
 
-    def step(evs=None):
+    def step(k, evs=None):
         for i, s in enumerate(slots):
             ev = evs is not None and i in evpos
             if ev:
                 evs[evpos[i]][0].record(stream)
-            w4.gemm(s["X"], s["sx"], s["pk"], out=s["Y"])
+            w4.gemm(s["X"], s["sx"], s["pks"][k % len(s["pks"])], out=s["Y"])
             if ev:
                 evs[evpos[i]][1].record(stream)
 
-    for _ in range(args.warmup):
-        step()
+    for k in range(args.warmup):
+        step(k)
     torch.cuda.synchronize()
 
     evs = [[[torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)]
@@ -242,7 +308,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        step(evs[k])
+        step(k, evs[k])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
@@ -257,44 +323,89 @@ def main():
     # slots of the same shape (5 x 121 MB, more than the 256 MB Infinity
     # Cache), so a launch never finds its weights cached; events bracket the
     # burst only, so a launch's figure includes the gap to the next dispatch.
+    # Several bursts per slot give the median and the spread.
+    reps = 20
+
+    def bursts(launch, pool, n):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for r in range(2):
+            launch(pool[r % len(pool)])
+        out_us = []
+        for _ in range(n):
+            e0.record(stream)
+            for r in range(reps):
+                launch(pool[r % len(pool)])
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out_us.append(e0.elapsed_time(e1) * 1e3 / reps)
+        return np.array(out_us)
+
+    def graph_bursts(launch, pool, Yout, n):
+        """As bursts(), but the `reps` launches are captured once in a HIP
+        graph and replayed, so a launch's figure is the GPU's (kernel plus
+        dispatch gap) even where a Python launch takes longer than the
+        kernel; every replay is checked against the eager result."""
+        launch(pool[(reps - 1) % len(pool)])
+        torch.cuda.synchronize()
+        want = Yout.clone()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for r in range(3):
+                launch(pool[r % len(pool)])
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for r in range(reps):
+                launch(pool[r % len(pool)])
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        out_us = []
+        for _ in range(n):
+            e0.record(stream)
+            graph.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            if not torch.equal(Yout, want):
+                raise RuntimeError("graph replay differs from the eager result")
+            out_us.append(e0.elapsed_time(e1) * 1e3 / reps)
+        del graph
+        return np.array(out_us)
+
     burst_us = {}
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     for i, s in enumerate(slots):
         if i in ev_us:
             continue
-        copies = [t["pk"] for t in slots if t["pair"] == s["pair"]]
-        reps = 20
-        for r in range(2):
-            w4.gemm(s["X"], s["sx"], copies[r % len(copies)], out=s["Y"])
-        e0.record(stream)
-        for r in range(reps):
-            w4.gemm(s["X"], s["sx"], copies[r % len(copies)], out=s["Y"])
-        e1.record(stream)
-        torch.cuda.synchronize()
-        burst_us[i] = e0.elapsed_time(e1) * 1e3 / reps
+        pool = [pk for t in slots if t["pair"] == s["pair"] for pk in t["pks"]]
+        burst_us[i] = bursts(lambda pk, s=s: w4.gemm(s["X"], s["sx"], pk, out=s["Y"]), pool,
+                             args.bursts)
 
     sweep = []
     total_ops = 0.0
     kern_ms_sum = 0.0
     for i, s in enumerate(slots):
         M, N, K = s["M"], s["N"], s["K"]
-        us = float(np.mean(ev_us[i])) if i in ev_us else burst_us[i]
+        ts = ev_us[i] if i in ev_us else burst_us[i]
+        # events in the timed region: the mean launch time; bursts: the median burst
+        us = float(np.mean(ts)) if i in ev_us else float(np.median(ts))
         ops = 2.0 * M * N * K
         total_ops += ops
         kern_ms_sum += us / 1e3
         wgbs = weight_bytes(N, K, g) / (us * 1e-6) / 1e9
         row = {"slot": s["name"], "M": M, "N": N, "K": K, "group": g,
-               "us_mean": round(us, 2),
-               "timing": "events in timed region" if i in ev_us else "back-to-back burst",
+               "us": round(us, 2),
+               "timing": "events in timed region" if i in ev_us else "back-to-back bursts",
+               "us_median": round(float(np.median(ts)), 2),
+               "us_min": round(float(ts.min()), 2), "us_max": round(float(ts.max()), 2),
                "tops": round(ops / (us * 1e-6) / 1e12, 2),
                "weight_stream_gbs": round(wgbs, 1),
                "hbm_frac_algo": round(algo_bytes(M, N, K, g) / (us * 1e-6) / 1e9
                                       / HBM_PEAK_GBS, 4),
                "mfma_frac": round(ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS, 4)}
         if i in ev_us:
-            row["us_min"] = round(float(ev_us[i].min()), 2)
+            row["launches"] = len(ts)
         else:
-            row["launches_per_burst"] = 20
+            row["bursts"] = len(ts)
+            row["launches_per_burst"] = reps
         sweep.append(row)
 
     value = total_ops / (ms_per_step * 1e-3) / 1e12
@@ -304,20 +415,22 @@ def main():
         if e is None:
             return None
         if bound == "mfma":
-            a = 2.0 * e["M"] * e["N"] * e["K"] / (e["us_mean"] * 1e-6) / 1e12
+            a = 2.0 * e["M"] * e["N"] * e["K"] / (e["us"] * 1e-6) / 1e12
             return {"bound": "mfma", "achieved": round(a, 2), "peak": INT8_PEAK_TOPS,
                     "unit": "TFLOP/s", "frac": round(a / INT8_PEAK_TOPS, 4),
-                    "traffic": profiled_traffic(slot_name), "kernel_slot": slot_name,
-                    "us_per_launch": e["us_mean"], "timing": e["timing"]}
-        a = algo_bytes(e["M"], e["N"], e["K"], g) / (e["us_mean"] * 1e-6) / 1e9
+                    "traffic": profiled_traffic(slot_name),
+                    "mfma_counters": profiled_mfma(slot_name, e["M"], e["N"], e["K"], e["us"]),
+                    "kernel_slot": slot_name,
+                    "us_per_launch": e["us"], "timing": e["timing"]}
+        a = algo_bytes(e["M"], e["N"], e["K"], g) / (e["us"] * 1e-6) / 1e9
         return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(a / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(slot_name),
                 "kernel_slot": slot_name,
-                "us_per_launch": e["us_mean"], "timing": e["timing"]}
+                "us_per_launch": e["us"], "timing": e["timing"]}
 
     # dominant kernel: the slot with the largest share of the step (among
     # those timed with events inside the timed region)
-    dom = max((sweep[i] for i in evslots), key=lambda e: e["us_mean"])
+    dom = max((sweep[i] for i in evslots), key=lambda e: e["us"])
     dom_bound = "mfma" if dom["M"] >= 1024 else "hbm"
     out = {
         "metric": METRIC, "value": round(value, 3), "unit": "TOPS", "n_gpus": 1,
@@ -335,6 +448,57 @@ def main():
         "sweep": sweep,
     }
 
+    # ---- Llama-2-7B shapes, reported beside the 70B sweep (not part of the
+    # timed step): attention-projection decode (M = 1, 4, 16 on 4096 x 4096)
+    # and MLP prefill (2048 tokens on 11008 x 4096 and 4096 x 11008), group
+    # 64.  Each shape rotates through weight copies past 600 MB (68 copies of
+    # the 8.9 MB decode weights), so no launch finds its weights in the
+    # 256 MB Infinity Cache; several bursts of back-to-back launches each.
+    if not args.no_7b and not args.only:
+        rows7 = []
+        for cfg in (wl.LLAMA7B_DECODE, wl.LLAMA7B_PREFILL):
+            for pi, (N, K) in enumerate(wl.nk_pairs(cfg)):
+                g7 = 64
+                Wf = torch.from_numpy(wl.gen_weights(N, K, wl.seed_w(cfg, pi))).to(dev)
+                pk7 = w4.pack(Wf, group=g7)
+                del Wf
+                ncp = -(-600_000_000 // weight_bytes(N, K, g7))
+                pool = [pk7] + [{k: (v.clone() if torch.is_tensor(v) else v)
+                                 for k, v in pk7.items()} for _ in range(ncp - 1)]
+                for sh in wl.CONFIGS[cfg].shapes:
+                    if (sh.N, sh.K) != (N, K):
+                        continue
+                    M = sh.M
+                    Xf = torch.from_numpy(wl.gen_activations(M, K, wl.seed_x(cfg, M),
+                                                             wl.seed_outliers(cfg))).to(dev)
+                    X7, sx7 = w4.quant_act(Xf)
+                    del Xf
+                    Y7 = torch.empty((M, N), dtype=torch.float16, device=dev)
+                    ts = graph_bursts(lambda pk, X7=X7, sx7=sx7, Y7=Y7:
+                                      w4.gemm(X7, sx7, pk, out=Y7), pool, Y7, args.bursts)
+                    us = float(np.median(ts))
+                    ops = 2.0 * M * N * K
+                    ab = algo_bytes(M, N, K, g7)
+                    bound = "hbm" if M <= 16 else "mfma"
+                    frac = (ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBS if bound == "hbm"
+                            else ops / (us * 1e-6) / 1e12 / INT8_PEAK_TOPS)
+                    rows7.append({"shape": sh.name, "M": M, "N": N, "K": K, "group": g7,
+                                  "us_median": round(us, 2), "us_min": round(float(ts.min()), 2),
+                                  "us_max": round(float(ts.max()), 2),
+                                  "tops": round(ops / (us * 1e-6) / 1e12, 2),
+                                  "weight_stream_gbs": round(weight_bytes(N, K, g7)
+                                                             / (us * 1e-6) / 1e9, 1),
+                                  "bound": bound, "frac_of_peak": round(frac, 4),
+                                  "weight_copies": ncp})
+                del pool, pk7
+        out["llama7b"] = {"workload": "llama2-7b linear shapes (W4A8, group 64), fp16 out; "
+                                      "median over replays of a HIP graph of 20 launches "
+                                      "rotating weight copies past 600 MB (a Python launch "
+                                      "takes longer than the decode kernels); decode rows "
+                                      "against 8 TB/s (algorithmic bytes), prefill rows "
+                                      "against 5 POP/s",
+                          "results": rows7}
+
     # ---- decode ablation on the matrix-core slots (outside the timed step):
     # the production LiquidQuant decode interleaved with the matrix cores, the
     # conventional signed affine decode, and the LiquidQuant decode done per
@@ -350,7 +514,7 @@ def main():
             row = {"slot": sl["name"]}
             # the weight copies of every slot of this shape in turn, as in the
             # sweep's bursts, so that no launch finds its weights in the cache
-            copies = [t["pk"] for t in slots if t["pair"] == sl["pair"]]
+            copies = [pk for t in slots if t["pair"] == sl["pair"] for pk in t["pks"]]
             for v, nm in names.items():
                 w4.gemm_ablation(v, sl["X"], sl["sx"], copies[-1], out=sl["Y"])
                 reps = 2 * len(copies)
@@ -361,7 +525,7 @@ def main():
                 torch.cuda.synchronize()
                 row[nm + "_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
             # the production kernel choice for the same slot (from the sweep)
-            row["w4a8_gemm_us"] = next(r["us_mean"] for r in sweep if r["slot"] == sl["name"])
+            row["w4a8_gemm_us"] = next(r["us"] for r in sweep if r["slot"] == sl["name"])
             row["affine16_vs_lqq"] = round(row["affine16_us"] / row["lqq_us"], 3)
             row["coarse_vs_lqq"] = round(row["lqq_coarse_us"] / row["lqq_us"], 3)
             abl.append(row)
@@ -393,7 +557,7 @@ def main():
                 e1.record(stream)
                 torch.cuda.synchronize()
                 us8 = e0.elapsed_time(e1) * 1e3 / reps
-                w4us = next(x["us_mean"] for x in sweep if x["slot"] == sl["name"])
+                w4us = next(x["us"] for x in sweep if x["slot"] == sl["name"])
                 cmp_rows.append({"slot": sl["name"], "w8a8_us": round(us8, 2), "w4a8_us": w4us,
                                  "w8a8_vs_w4a8": round(us8 / w4us, 3)})
             del pk8, pk8b
@@ -561,8 +725,8 @@ def main():
                                     "results": qres}
 
     if not args.no_cpu_baseline and not args.only:
-        desc = [(s["name"], s["M"], s["N"], s["K"], g, s["pair"]) for s in slots]
-        out["cpu_baseline"] = cpu_baseline(desc, args.cpu_sample_cols)
+        out["cpu_baseline"] = cpu_baseline(sweep_desc(), args.cpu_sample_cols)
+        out["cpu_baseline"]["one_core"] = cpu_baseline_one_core(args.cpu_sample_cols_1core)
 
     print(json.dumps(out), flush=True)
 
