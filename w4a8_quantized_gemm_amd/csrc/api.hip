@@ -138,7 +138,13 @@ bool valid_splitk(int splitk, int K) {
 }  // namespace
 
 W4A8_EXPORT const char* w4a8_status_str(w4a8_status_t s) {
-    switch (s) {
+    // A C caller may pass any int (an unknown or future code): read the
+    // argument's bits as an int, since a value outside the enumerators'
+    // range may not be read through the enum type in C++.
+    int code;
+    std::memcpy(&code, &s, sizeof code);
+    static_assert(sizeof(w4a8_status_t) == sizeof(int), "status codes travel as int");
+    switch (code) {
         case W4A8_OK: return "ok";
         case W4A8_ERR_NULL_PTR: return "a required pointer is NULL";
         case W4A8_ERR_SHAPE: return "invalid shape, group, qmax or split factor";
