@@ -60,51 +60,71 @@ __device__ __forceinline__ size_t packed_dword_offset(int nt, int kt, int KT, in
     return ((size_t)nt * KT + kt) * kTileBytes + (size_t)(16 * G + r) * 16 + 4 * d;
 }
 
-// LiquidQuant second level.  One thread per (row n, group j): a first pass
-// finds min/max of the INT8 values of its group, a second pass writes the
-// UINT4 codes (as whole packed dwords: 8 consecutive columns) plus s_u8/a_u8.
+// LiquidQuant second level.  One thread per packed dword (8 consecutive
+// columns of one row, read as two float4): it forms the 8 INT8 values once,
+// the GW = group / 8 threads of a group (aligned lanes of one wave) combine
+// their minima and maxima by XOR shuffles, and each thread then writes its
+// dword of UINT4 codes; the group's first thread writes s_u8 / a_u8.  The
+// arithmetic is per element and in the same order as a serial loop, so the
+// codes do not depend on the thread layout.
+template <int GW>
 __global__ __launch_bounds__(256) void lqq_group_kernel(const float* __restrict__ W,
                                                         const float* __restrict__ sw, int N, int K,
-                                                        int group, float qmax,
-                                                        uint8_t* __restrict__ wq,
+                                                        float qmax, uint8_t* __restrict__ wq,
                                                         uint8_t* __restrict__ s_u8,
                                                         uint8_t* __restrict__ a_u8) {
-    const int groups = K / group;
     const long long tid = (long long)blockIdx.x * 256 + threadIdx.x;
-    if (tid >= (long long)N * groups) return;
-    const int n = (int)(tid / groups);
-    const int j = (int)(tid % groups);
+    const long long per_row = K / 8;
+    // N * K / 8 is a multiple of GW and groups are lane-aligned, so a group's
+    // threads are all in range or all out of range; out-of-range threads
+    // still take part in the shuffles (on row 0) and write nothing
+    const bool live = tid < (long long)N * per_row;
+    const long long t = live ? tid : 0;
+    const int n = (int)(t / per_row);
+    const int k = (int)(t % per_row) * 8;
     const float s_ch = sw[n];
-    const float* w = W + (size_t)n * K + (size_t)j * group;
+    const float4* w4 = reinterpret_cast<const float4*>(W + (size_t)n * K + k);
+    const float4 v0 = w4[0], v1 = w4[1];
+    const float v[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    int q8[8];
     int mn = 127, mx = -128;
-    for (int t = 0; t < group; ++t) {
-        int q = quant_sym(w[t], s_ch, qmax);
-        mn = min(mn, q);
-        mx = max(mx, q);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        q8[e] = quant_sym(v[e], s_ch, qmax);
+        mn = min(mn, q8[e]);
+        mx = max(mx, q8[e]);
     }
+#pragma unroll
+    for (int off = GW / 2; off > 0; off >>= 1) {
+        mn = min(mn, __shfl_xor(mn, off, 64));
+        mx = max(mx, __shfl_xor(mx, off, 64));
+    }
+    if (!live) return;
     const int R = mx - mn;
     int s = (R + 14) / 15;
     s = s < 1 ? 1 : s;
     const int a = 128 + mn;
     const int cap = (127 - mn) / s;
-    s_u8[param_offset(n, j, groups)] = (uint8_t)s;
-    a_u8[param_offset(n, j, groups)] = (uint8_t)a;
-    const int KT = K / kTileK, nt = n / kTileN, r = n % kTileN;
-    for (int c8 = 0; c8 < group; c8 += 8) {
-        unsigned word = 0;
-        for (int e = 0; e < 8; ++e) {
-            int u = quant_sym(w[c8 + e], s_ch, qmax) - mn;
-            int q = (2 * u + s) / (2 * s);
-            q = min(q, cap);
-            q = min(q, 15);
-            // column +e -> byte (e & 3), low nibble for e < 4, high for e >= 4
-            word |= (unsigned)q << (8 * (e & 3) + 4 * (e >> 2));
-        }
-        const int k = j * group + c8;
-        const int kt = k / kTileK, kk = k % kTileK;
-        size_t off = packed_dword_offset(nt, kt, KT, kk / 32, r, (kk % 32) / 8);
-        *reinterpret_cast<unsigned*>(wq + off) = word;
+    const int groups = K / (8 * GW);
+    const int j = k / (8 * GW);
+    if ((threadIdx.x & (GW - 1)) == 0) {
+        s_u8[param_offset(n, j, groups)] = (uint8_t)s;
+        a_u8[param_offset(n, j, groups)] = (uint8_t)a;
     }
+    unsigned word = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const int u = q8[e] - mn;
+        int q = (2 * u + s) / (2 * s);
+        q = min(q, cap);
+        q = min(q, 15);
+        // column +e -> byte (e & 3), low nibble for e < 4, high for e >= 4
+        word |= (unsigned)q << (8 * (e & 3) + 4 * (e >> 2));
+    }
+    const int KT = K / kTileK, nt = n / kTileN, r = n % kTileN;
+    const int kt = k / kTileK, kk = k % kTileK;
+    const size_t off = packed_dword_offset(nt, kt, KT, kk / 32, r, (kk % 32) / 8);
+    *reinterpret_cast<unsigned*>(wq + off) = word;
 }
 
 // INT4 symmetric sign-magnitude nibbles.  One thread per packed dword
@@ -449,10 +469,14 @@ static bool launch_act_regs(const void* X, int M, int K, uint8_t* Xq, float* sx,
 hipError_t launch_pack_lqq(const float* W, int N, int K, int group, int qmax, uint8_t* wq,
                            uint8_t* s_u8, uint8_t* a_u8, float* sw, hipStream_t st) {
     hipLaunchKernelGGL(row_scale_kernel, dim3(N), dim3(256), 0, st, W, K, (float)qmax, sw);
-    long long threads = (long long)N * (K / group);
-    unsigned blocks = (unsigned)((threads + 255) / 256);
-    hipLaunchKernelGGL(lqq_group_kernel, dim3(blocks), dim3(256), 0, st, W, sw, N, K, group,
-                       (float)qmax, wq, s_u8, a_u8);
+    const long long threads = (long long)N * (K / 8);  // one per packed dword
+    const unsigned blocks = (unsigned)((threads + 255) / 256);
+    if (group == 64)
+        hipLaunchKernelGGL((lqq_group_kernel<8>), dim3(blocks), dim3(256), 0, st, W, sw, N, K,
+                           (float)qmax, wq, s_u8, a_u8);
+    else
+        hipLaunchKernelGGL((lqq_group_kernel<16>), dim3(blocks), dim3(256), 0, st, W, sw, N, K,
+                           (float)qmax, wq, s_u8, a_u8);
     return hipGetLastError();
 }
 
