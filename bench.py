@@ -228,6 +228,59 @@ def cpu_baseline_one_core(ncols):
     return json.loads(res.stdout.strip().splitlines()[-1])
 
 
+def _smi_sample():
+    """One `amd-smi metric --clock --power --json` reading: mean shader clock
+    over the XCDs, memory clock (MHz) and socket power (W)."""
+    import shutil
+    import subprocess
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    res = subprocess.run([exe, "metric", "--clock", "--power", "--json"], capture_output=True,
+                         text=True, timeout=30)
+    d = json.loads(res.stdout)
+    g = (d["gpu_data"] if isinstance(d, dict) else d)[0]
+    gfx = [v["clk"]["value"] for k, v in g["clock"].items()
+           if k.startswith("gfx") and isinstance(v.get("clk"), dict)]
+    mem = g["clock"]["mem_0"]["clk"]["value"]
+    power = g["power"]["socket_power"]["value"]
+    return {"gfx_mhz": sum(gfx) / len(gfx), "mem_mhz": mem, "socket_power_w": power}
+
+
+def clocks_under_load(launch, n_samples=4, limit_s=20.0):
+    """Clocks and power read by amd-smi while `launch` (one GEMM) runs back
+    to back: a sampler thread takes readings after a settling pause while
+    this thread keeps the GPU queue full."""
+    import threading
+    import torch
+    samples, errors = [], []
+
+    def sampler():
+        time.sleep(0.5)
+        while len(samples) < n_samples and len(errors) < 2:
+            try:
+                samples.append(_smi_sample())
+            except Exception as e:  # the tool is optional on a host
+                errors.append(repr(e)[:200])
+
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.time()
+    th.start()
+    launches = 0
+    while th.is_alive() and time.time() - t0 < limit_s:
+        for _ in range(20):
+            launch()
+        launches += 20
+        torch.cuda.synchronize()
+    th.join(timeout=1.0)
+    if not samples:
+        return {"error": errors[0] if errors else "no reading"}
+    mean = lambda k: round(sum(x[k] for x in samples) / len(samples), 1)
+    return {"gfx_mhz_mean": mean("gfx_mhz"),
+            "gfx_mhz_min": round(min(x["gfx_mhz"] for x in samples), 1),
+            "mem_mhz": mean("mem_mhz"), "socket_power_w_mean": mean("socket_power_w"),
+            "socket_power_w_max": max(x["socket_power_w"] for x in samples),
+            "samples": len(samples), "launches": launches}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -447,6 +500,15 @@ def main():
         "kernel_ms_per_step": round(kern_ms_sum, 4),
         "sweep": sweep,
     }
+
+    # ---- shader / memory clock and socket power while the dominant slot's
+    # GEMM runs back to back (amd-smi readings; the clock the chip holds
+    # under this load is what bounds the matrix-core kernels)
+    if not args.only:
+        ds = next(s for s in slots if s["name"] == DOMINANT_SLOT)
+        out["clocks_under_load"] = dict(
+            clocks_under_load(lambda: w4.gemm(ds["X"], ds["sx"], ds["pks"][0], out=ds["Y"])),
+            slot=DOMINANT_SLOT)
 
     # ---- Llama-2-7B shapes, reported beside the 70B sweep (not part of the
     # timed step): attention-projection decode (M = 1, 4, 16 on 4096 x 4096)

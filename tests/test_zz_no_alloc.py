@@ -88,3 +88,41 @@ def test_noalloc_matches_gemm_two_calls():
                 np.testing.assert_array_equal(b, acc)
             else:
                 assert _ulp(b.view(np.uint16), y).max() <= 1
+
+
+def test_noalloc_in_captured_graph():
+    """The callers this entry point is for capture it in a HIP graph: three
+    split-K calls of different shapes sharing the static scratch, captured
+    once and replayed three times with eager work in between; every replay
+    equals eager w4a8_gemm bit for bit."""
+    cases = [(128, 4096, 8192, 128), (100, 2048, 4096, 64), (192, 1024, 8192, 128)]
+    probs = [_problem(M, N, K, g, 4200 + i) for i, (M, N, K, g) in enumerate(cases)]
+    outs = [_poison((M, N), torch.float16) for (M, N, K, g) in cases]
+    want = []
+    for (X8, sx, pk, acc, y), (M, N, K, g) in zip(probs, cases):
+        assert w4.workspace_size(M, N, K) > 0
+        ref = _poison((M, N), torch.float16)
+        w4.gemm(X8, sx, pk, out_type=w4.OUT_F16, out=ref)
+        want.append(ref)
+    for (X8, sx, pk, _, _), Y in zip(probs, outs):  # first call on the device: eager
+        _noalloc(X8, sx, pk, Y, w4.OUT_F16)
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for (X8, sx, pk, _, _), Y in zip(probs, outs):
+                _noalloc(X8, sx, pk, Y, w4.OUT_F16)
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        for Y in outs:
+            Y.view(torch.uint8).fill_(0xAB)
+        X8, sx, pk, _, _ = probs[0]
+        w4.gemm(X8, sx, pk, out_type=w4.OUT_I32)  # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for Y, ref in zip(outs, want):
+            np.testing.assert_array_equal(Y.cpu().numpy().view(np.uint16),
+                                          ref.cpu().numpy().view(np.uint16))
