@@ -151,11 +151,13 @@ w4a8_status_t w4fp8_quant_act_ex(const void* X, int in_type, int M, int K,
  * when the matrix-core kernel has too few output tiles to fill the GPU it
  * splits K across workgroups, writes partial tiles (splits x M x N x 4
  * bytes: int32 for w4a8_gemm, float32 for w4fp8_gemm) and sums them in split
- * order in a second kernel (deterministic; exact for int32).  Returns 0 when
- * no split is used and when splitk != 0 (streamed kernel, which reduces on
- * chip).  The workspace is scratch: its contents on entry are ignored and
- * undefined on return; calls that share a workspace must be ordered on one
- * stream.
+ * order in a second kernel (deterministic; exact for int32).  w4a8_gemm and
+ * w8a8_gemm may instead split K between the wave pairs of a workgroup and
+ * need half of it, or none; the size returned covers every entry point.
+ * Returns 0 when no split is used and when splitk != 0 (streamed kernel,
+ * which reduces on chip).  The workspace is scratch: its contents on entry
+ * are ignored and undefined on return; calls that share a workspace must be
+ * ordered on one stream.
  */
 size_t w4a8_workspace_size(int M, int N, int K, int splitk);
 
@@ -171,7 +173,9 @@ size_t w4a8_workspace_size(int M, int N, int K, int splitk);
  * a matrix-core tile kernel (256-row workgroup tiles on 16 x 16 x 64
  * instructions; 128-row tiles on 16 x 16 x 64 at two workgroups per CU when
  * a workgroup covers at most 64 K-steps of a grid under four waves, else
- * on 32 x 32 x 32); otherwise the streamed-tile kernel runs (one, two or
+ * on 32 x 32 x 32; with too few tiles to fill the GPU, K is split across
+ * workgroups, or between the two wave pairs of 128-channel workgroups);
+ * otherwise the streamed-tile kernel runs (one, two or
  * four 16-row blocks of X per workgroup sharing each decoded weight), with
  * `splitk` K-slices per output tile.
  * splitk: 0 = automatic; 1, 2, 4, 8 or 16 (at most K/128) forces the

@@ -272,7 +272,9 @@ def test_stream_widths(M, N, K, g):
 
 
 # Few output tiles -> the matrix-core kernel splits K across workgroups and
-# reduces int32 partials in a second kernel (8 splits here).
+# reduces int32 partials in a second kernel (128 x 512 x 4096: two splits of
+# two K parts each; 100 x 256 x 2048: one workgroup per 128 channels, two K
+# parts, no partials).
 @pytest.mark.parametrize("M,N,K,g", [(128, 512, 4096, 128), (100, 256, 2048, 64)])
 def test_mfma_split_k(M, N, K, g):
     say(f"w4a8 mfma split-K gemm M={M} N={N} K={K} g={g} ws={w4.workspace_size(M, N, K)}")
@@ -950,6 +952,54 @@ def test_256_row_plan_every_element(M, N, K, g, w8):
         np.testing.assert_array_equal(host(Yi), acc8)
         Yh = poison((M, N), torch.float16)
         w4.gemm_w8a8(X8, sx, pk8, out_type=w4.OUT_F16, out=Yh)
+        assert f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y8).max() <= 1
+
+
+# 128-row plans that split K across two workgroups (or, when the extra X
+# reads cost no more than the partials, an even number of them) run K parts
+# instead: workgroups of 128 channels whose wave pairs take the two halves of
+# the split's K range and add their int32 sums through LDS, with half the
+# splits.  Every output element against the oracle, outputs and workspace
+# poisoned (the same workspace twice):
+#   128 x 2048 x 2816: 22 K-steps, two halves of 11 (odd: a padding step
+#     each), no partials;
+#   100 x 4096 x 2944: 23 K-steps, halves of 11 and 12 (the shorter runs one
+#     X tile of zeros), ragged rows, group 64;
+#   128 x 2048 x 4096: 32 K-steps, two splits of two parts of 8, reduced
+#     from int32 partials;
+#   128 x 512 x 4096: the same plan on two channel tiles, group 64;
+#   128 x 3840 x 2048: 30 channel tiles (not a multiple of 8: the plain tile
+#     order), no partials;
+#   64 x 1024 x 8960: eight splits stay (X read again would cost more than
+#     the partials), K-steps 8 or 9 per split.
+# The W8A8 comparison runs the same plans.
+_KPARTS = [(128, 2048, 2816, 128, True), (100, 4096, 2944, 64, True),
+           (128, 2048, 4096, 128, True), (128, 512, 4096, 64, False),
+           (128, 3840, 2048, 128, False), (64, 1024, 8960, 128, True)]
+
+
+@pytest.mark.parametrize("M,N,K,g,w8", _KPARTS)
+def test_k_parts_every_element(M, N, K, g, w8):
+    say(f"K parts in the workgroup, every element: M={M} N={N} K={K} g={g}")
+    X8, sx, pk, acc, y = _small_problem(M, N, K, g, 1800 + K)
+    ws = poison((max(w4.workspace_size(M, N, K), 16),), torch.uint8)
+    for _ in range(2):
+        Yi = poison((M, N), torch.int32)
+        w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, out=Yi, workspace=ws)
+        np.testing.assert_array_equal(host(Yi), acc)
+        Yh = poison((M, N), torch.float16)
+        w4.gemm(X8, sx, pk, out_type=w4.OUT_F16, out=Yh, workspace=ws)
+        assert f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y).max() <= 1
+    if w8:
+        W = wl.gen_weights(N, K, 1800 + K)
+        ref8 = oracle.w8a8_pack(W)
+        acc8, y8, _ = oracle.w8a8_gemm(host(X8), host(sx), ref8)
+        pk8 = {"wq8": to_dev(ref8["wq8"]), "sw": to_dev(ref8["sw"]), "N": N, "K": K}
+        Yi = poison((M, N), torch.int32)
+        w4.gemm_w8a8(X8, sx, pk8, out_type=w4.OUT_I32, out=Yi, workspace=ws)
+        np.testing.assert_array_equal(host(Yi), acc8)
+        Yh = poison((M, N), torch.float16)
+        w4.gemm_w8a8(X8, sx, pk8, out_type=w4.OUT_F16, out=Yh, workspace=ws)
         assert f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y8).max() <= 1
 
 

@@ -256,7 +256,7 @@ w4a8_status_t gemm_entry(const int8_t* X, const float* sx, const uint8_t* wq,
     }
     if (splitk == 0 && use_mfma_tiles(M, N, K))
         return hip_status(w4a8::launch_w4a8_mfma(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
-                                                 group, w4a8::plan_w4a8_mfma(M, N, K), workspace,
+                                                 group, w4a8::plan_w4a8_mfma(M, N, K, true), workspace,
                                                  stream));
     return hip_status(w4a8::launch_w4a8_stream(X, sx, wq, s_u8, a_u8, sw, Y, out_type, M, N, K,
                                                group, choose_stream(M, N, K, splitk, true),
@@ -446,7 +446,7 @@ W4A8_EXPORT w4a8_status_t w8a8_gemm(const int8_t* X, const float* sx, const int8
     if (d != W4A8_OK) return d;
     if (splitk == 0 && use_mfma_tiles(M, N, K))
         return hip_status(w4a8::launch_w8a8_mfma(X, sx, wq8, sw, Y, out_type, M, N, K,
-                                                 w4a8::plan_w4a8_mfma(M, N, K), workspace,
+                                                 w4a8::plan_w4a8_mfma(M, N, K, true), workspace,
                                                  stream));
     return hip_status(w4a8::launch_w8a8_stream(X, sx, wq8, sw, Y, out_type, M, N, K,
                                                choose_stream(M, N, K, splitk), stream));

@@ -591,7 +591,7 @@ hipError_t launch_splitk_reduce(const int* part, int splits, int M, int N, const
 }
 
 // Workgroup tile height and K split for the matrix-core kernel.
-MfmaPlan plan_w4a8_mfma(int M, int N, int K) {
+MfmaPlan plan_w4a8_mfma(int M, int N, int K, bool k_parts) {
     MfmaPlan p;
     const int KT = K / kTileK;
     const long long t256 = (long long)(N / kNT) * ((M + 255) / 256);
@@ -627,6 +627,28 @@ MfmaPlan plan_w4a8_mfma(int M, int N, int K) {
     const bool short_k = KT / p.splits <= 64;
     const bool few_waves = p.mt == 128 || t256 < 4 * 256;
     p.mt16 = (short_k && few_waves) ? 128 : (p.mt == 256 ? 256 : 0);
+    // Integer 16 x 16 kernel with an even split count: workgroups of 128
+    // channels whose two wave pairs take the two K halves (exact int32 sums
+    // through LDS) cover the same grid with half the splits -- the same
+    // K-steps per wave and half the partials, but every workgroup reads X
+    // for half as many channels, so X is read once more per 256 channels.
+    // Taken when that removes the partials and the second launch (two
+    // splits), or when the X bytes it adds are at most the partial bytes it
+    // saves (written once and read once).  Measured, alternating launches on
+    // one GPU: 128 x 28672 x 8192 48.0 -> 42.6 us, 64 x 28672 x 8192 42.1 ->
+    // 38.2, 128 x 4096 x 4096 (four splits) 17.6 -> 16.1; not taken at
+    // 128 x 8192 x 28672 (eight splits: 48.1 -> 50.1) or 256 x 8192 x 8192
+    // (four: 30.7 -> 31.1).
+    p.kin = 1;
+    if (k_parts && p.mt16 == 128 && p.mt == 128 && p.splits % 2 == 0) {
+        const long long x_extra = (long long)(N / kNT) * (((M + 127) / 128) * 128LL) * K;
+        const long long saved = (long long)p.splits * M * N * (long long)sizeof(int);
+        if (p.splits == 2 || x_extra <= saved) {
+            p.kin = 2;
+            p.splits /= 2;
+            p.workspace = p.splits > 1 ? (size_t)p.splits * M * N * sizeof(int) : 0;
+        }
+    }
     return p;
 }
 

@@ -28,6 +28,14 @@
 // weights `wcur`; group 1 loads the step after next into `wcur` and decodes
 // the next step's parameters and B[*][0] from `wnx`.  X goes global -> LDS
 // directly (three rotating tiles), as in the 32 x 32 kernel.
+//
+// K parts (KIN = 2, 128-row tiles): the workgroup covers 128 channels, and
+// waves 0-1 and 2-3 take the two halves of its K range, each pair with its
+// own X tiles; at the end each wave hands its partner the sums of the rows
+// the partner writes (exact int32 adds through LDS).  For the shapes that
+// would otherwise split K across workgroups, the same grid then needs half
+// as many splits and no partials when it was two: the partial tiles' store
+// and second read cost a third of the time at 128 x 28672 x 8192.
 #include <type_traits>
 
 #include "launch.h"
@@ -146,15 +154,18 @@ __device__ __forceinline__ void mfma16_drain(v4i (&acc)[RB][4]) {
 
 // W8: the W8A8 comparison on this skeleton (no decode, no parameters).
 // 128-row tiles fit two workgroups per CU (128 accumulator registers per
-// lane, at most 128 others), 256-row tiles one.
-template <int MT, int OUT, int GROUP, bool PARTIAL, bool W8>
-__global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4a8_mfma16_kernel(
+// lane, at most 128 others), 256-row tiles one; with K parts (KIN = 2) the
+// X tiles take 96 KiB of LDS, one workgroup per CU.
+template <int MT, int OUT, int GROUP, bool PARTIAL, bool W8, int KIN>
+__global__ __launch_bounds__(256, (MT == 128 && KIN == 1) ? 2 : 1) void w4a8_mfma16_kernel(
     const int8_t* __restrict__ X, const float* __restrict__ sx, const uint8_t* __restrict__ wq,
     const uint8_t* __restrict__ s_u8, const uint8_t* __restrict__ a_u8,
     const float* __restrict__ sw, void* __restrict__ Y, int* __restrict__ part, int M, int N,
     int K, int tiles_n, int tiles_m, int splits, const int* __restrict__ offsets) {
+    static_assert(KIN == 1 || (KIN == 2 && MT == 128), "K parts: 128-row tiles only");
     constexpr int RB = MT / 16;        // 16-row blocks per wave
-    constexpr int CPT = MT / 32;       // X loads (1 KiB per wave) per K-step
+    constexpr int NWX = kWaves / KIN;  // waves per K part (sharing its X tiles)
+    constexpr int CPT = MT / (8 * NWX);  // X loads (1 KiB per wave) per K-step
     constexpr int SLOTS = 8 * RB;      // matrix-core instructions per wave per K-step
     constexpr int GS = SLOTS / 2;      // slots per group u
     constexpr int kLoads = W8 ? 8 : 6;  // raw loads per K-step: 4 tiles, s, a (W8: 8 halves)
@@ -163,14 +174,17 @@ __global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4a8_mfma16_kernel(
     constexpr int DQ0 = (NOPS + GS - 1) / GS;         // group-0 decode steps per slot
     constexpr int DQ1 = (NPAR + NOPS + GS - 1) / GS;  // group-1 parameter + decode steps per slot
     using Raw = std::conditional_t<W8, WRaw8x16, WRaw16>;
-    constexpr unsigned XB = MT * 128;  // bytes of one X tile
-    __shared__ __attribute__((aligned(1024))) uint8_t xs[3 * XB];
+    constexpr unsigned XB = MT * 128;     // bytes of one X tile
+    constexpr unsigned XSTEP = KIN * XB;  // one K-step's X tiles, one per K part
+    __shared__ __attribute__((aligned(1024))) uint8_t xs[3 * XSTEP];
     __shared__ float sxs[MT];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 15, G = lane >> 4;
+    const int kp = wave / NWX;  // K part of this wave
+    const int wc = wave % NWX;  // its 64-channel panel within the workgroup
 
     const TileCoord tc = tile_coord(blockIdx.x, tiles_m, tiles_n, splits);
     const int ks = tc.ks;
@@ -189,32 +203,46 @@ __global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4a8_mfma16_kernel(
     }
     const int m0 = row_lo + tc.tm * MT;
     if (m0 >= row_hi) return;  // whole workgroup: no rows of this expert here
-    const int n0 = tc.tn * kNT + wave * kColsPerWave;
+    const int n0 = tc.tn * (kNT / KIN) + wc * kColsPerWave;
     const int KTall = K / kTileK;
-    const int kt0 = (int)((long long)KTall * ks / splits);
-    const int KT = (int)((long long)KTall * (ks + 1) / splits) - kt0;  // >= 1
-    // K-steps run in pairs with a single loop exit; an odd count gets one
-    // more step whose X tile reads as zero (its weights are the last real
-    // step's, so no load leaves this split's K range).
-    const int KTe = KT + (KT & 1);
+    // K is cut into splits * KIN parts; this wave takes part ks * KIN + kp
+    const int parts = splits * KIN;
+    const int pidx = ks * KIN + kp;
+    const int kt0 = (int)((long long)KTall * pidx / parts);
+    const int KT = (int)((long long)KTall * (pidx + 1) / parts) - kt0;  // >= 1
+    // Every wave of the workgroup runs the same number of K-steps (one
+    // barrier per step): the longest part's, in pairs with a single loop
+    // exit.  Steps past a wave's own part read an X tile of zeros (their
+    // weights are the part's last real step's, so no load leaves the part's
+    // K range).
+    int KTmax = KT;
+    if constexpr (KIN == 2) {
+        const int q0 = ks * KIN;
+        const int a0 = (int)((long long)KTall * q0 / parts);
+        const int a1 = (int)((long long)KTall * (q0 + 1) / parts);
+        const int a2 = (int)((long long)KTall * (q0 + 2) / parts);
+        KTmax = max(a1 - a0, a2 - a1);
+    }
+    const int KTe = KTmax + (KTmax & 1);
     const int groups = K / GROUP;
 
     // ---- X straight into LDS (same tile format and load mapping as the
-    // 32 x 32 kernel): wave w's load p fills rows 32p + 8w .. +7; lane l
-    // writes slot l % 8 of row 32p + 8w + l / 8 and fetches that row's chunk
+    // 32 x 32 kernel): the X tile of K part kp is filled by its NWX waves;
+    // load p of panel wave wc fills rows 8 (NWX p + wc) .. +7, lane l writing
+    // slot l % 8 of row 8 (NWX p + wc) + l / 8 from that row's chunk
     // (l % 8) ^ xswz(row & 15).
     const __amdgpu_buffer_rsrc_t xr_rsrc = buf_rsrc(X, (unsigned)M * (unsigned)K);
-    const int xr = 8 * wave + (lane >> 3);
+    const int xr = 8 * wc + (lane >> 3);
     const int xc = (lane & 7) ^ xswz(xr & 15);
     const unsigned xvoff =
         (unsigned)(m0 + xr) * (unsigned)K + (unsigned)(xc * 16) + (unsigned)(kt0 * kTileK);
-    const unsigned xrowstep = 32u * (unsigned)K;
-    const unsigned xsbase = lds_addr(xs);
+    const unsigned xrowstep = 8u * NWX * (unsigned)K;
+    const unsigned xsbase = lds_addr(xs) + (unsigned)kp * XB;
     auto x_load = [&](int kt, int p, unsigned buf) {
         const bool live = kt < KT;  // kt >= KT: offset past the buffer, reads 0
         const unsigned vo = live ? xvoff + (unsigned)p * xrowstep : 0xFFFFFFF0u;
         const unsigned so = live ? (unsigned)(kt * kTileK) : 0u;
-        buf_load16_lds(xr_rsrc, vo, so, xsbase + buf + (unsigned)(4 * p + wave) * 1024u);
+        buf_load16_lds(xr_rsrc, vo, so, xsbase + buf + (unsigned)(NWX * p + wc) * 1024u);
     };
     // A operand (row block rb, half u): row 16 rb + r, chunk 2G + u.
     int aoff[2];
@@ -259,7 +287,7 @@ __global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4a8_mfma16_kernel(
     v4i B[4][2];
     v4i ring[4];
     const int k1 = min(1, KTe - 1), kw1 = min(1, KT - 1);
-    unsigned bc = 0, bn = XB, bd = 2 * XB;  // LDS tiles of X(kt), X(kt+1), X(kt+2)
+    unsigned bc = 0, bn = XSTEP, bd = 2 * XSTEP;  // LDS tiles of X(kt), X(kt+1), X(kt+2)
 #pragma unroll
     for (int p = 0; p < CPT; ++p) x_load(0, p, bc);
 #pragma unroll
@@ -278,8 +306,9 @@ __global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4a8_mfma16_kernel(
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(kLoads, 0));  // X(0), X(1), W(0) complete
     __syncthreads();
+    const uint8_t* xsk = xs + kp * XB;  // this K part's X tiles
     auto read_a = [&](unsigned buf, int sI) {  // sI = RB*u + rb
-        return *reinterpret_cast<const v4i*>(xs + buf + (sI % RB) * 2048 + aoff[sI / RB]);
+        return *reinterpret_cast<const v4i*>(xsk + buf + (sI % RB) * 2048 + aoff[sI / RB]);
     };
     ring[0] = read_a(bc, 0);
     ring[1] = read_a(bc, 1);
@@ -364,71 +393,117 @@ __global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4a8_mfma16_kernel(
     for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int v = 0; v < 4; ++v) swv[cb][v] = SCALED ? sw[n0 + 16 * cb + 4 * G + v] : 0.0f;
-    __syncthreads();
+    // K parts: the two waves of a channel panel hold sums over the two K
+    // halves.  Part kp writes row blocks [kp HB, kp HB + HB): each wave first
+    // stores its sums of the other half's row blocks to LDS (block (receiving
+    // part, panel, row block, channel block) of 64 lanes x 16 bytes), then,
+    // after the barrier, adds its partner's sums of its own.
+    constexpr int HB = RB / 2;
+    if constexpr (KIN == 2) {
+        static_assert(KIN * NWX * HB * 4 * 1024 <= 3 * XSTEP, "K-part exchange fits in LDS");
+        v4i* xch = reinterpret_cast<v4i*>(xs);
+        auto xidx = [&](int d, int i, int cb) {
+            return ((d * NWX + wc) * HB * 4 + i * 4 + cb) * 64 + lane;
+        };
+        auto give = [&](auto mec) {
+            constexpr int me = decltype(mec)::value;
+            static_for<HB>([&](auto ic) {
+                static_for<4>([&](auto cc) {
+                    constexpr int i = decltype(ic)::value, cb = decltype(cc)::value;
+                    xch[xidx(1 - me, i, cb)] = acc[(1 - me) * HB + i][cb];
+                });
+            });
+        };
+        auto take = [&](auto mec) {
+            constexpr int me = decltype(mec)::value;
+            static_for<HB>([&](auto ic) {
+                static_for<4>([&](auto cc) {
+                    constexpr int i = decltype(ic)::value, cb = decltype(cc)::value;
+                    acc[me * HB + i][cb] += xch[xidx(me, i, cb)];
+                });
+            });
+        };
+        if (kp == 0) give(std::integral_constant<int, 0>{});
+        else give(std::integral_constant<int, 1>{});
+        __syncthreads();
+        if (kp == 0) take(std::integral_constant<int, 0>{});
+        else take(std::integral_constant<int, 1>{});
+    }
+    __syncthreads();  // sxs written; the exchange blocks read before staging reuses them
     constexpr int EB = SCALED ? 2 : 4;  // output element bytes
     constexpr int ROWB = 64 * EB;       // bytes per row of the block
     constexpr int RSTR = ROWB + 16;     // padded row stride in LDS
-    static_assert(kWaves * 32 * RSTR <= 3 * XB, "epilogue staging fits in the X tiles");
+    static_assert(kWaves * 32 * RSTR <= 3 * XSTEP, "epilogue staging fits in the X tiles");
     uint8_t* stage = xs + wave * (32 * RSTR);
     uint8_t* out = PARTIAL ? reinterpret_cast<uint8_t*>(part + (size_t)ks * M * N)
                            : reinterpret_cast<uint8_t*>(Y);
+    // row-block pairs rp0 .. rp0 + NP - 1
+    auto epi = [&](auto rp0c, auto npc) {
+        constexpr int rp0 = decltype(rp0c)::value, NP = decltype(npc)::value;
+        static_for<NP>([&](auto rpc) {
+            constexpr int rp = rp0 + decltype(rpc)::value;
 #pragma unroll
-    for (int rp = 0; rp < RB / 2; ++rp) {
+            for (int rr = 0; rr < 2; ++rr) {
+                const int rb = 2 * rp + rr;
+                uint8_t* srow = stage + (16 * rr + r) * RSTR;
+                const float sm = SCALED ? sxs[16 * rb + r] : 0.0f;
 #pragma unroll
-        for (int rr = 0; rr < 2; ++rr) {
-            const int rb = 2 * rp + rr;
-            uint8_t* srow = stage + (16 * rr + r) * RSTR;
-            const float sm = SCALED ? sxs[16 * rb + r] : 0.0f;
+                for (int cb = 0; cb < 4; ++cb) {
+                    const int col = 16 * cb + 4 * G;
+                    if constexpr (SCALED) {
+                        unsigned short h[4];
 #pragma unroll
-            for (int cb = 0; cb < 4; ++cb) {
-                const int col = 16 * cb + 4 * G;
-                if constexpr (SCALED) {
-                    unsigned short h[4];
-#pragma unroll
-                    for (int v = 0; v < 4; ++v)
-                        h[v] = f32_to_f16_bits(((float)acc[rb][cb][v] * sm) * swv[cb][v]);
-                    uint2 pk;
-                    pk.x = h[0] | ((unsigned)h[1] << 16);
-                    pk.y = h[2] | ((unsigned)h[3] << 16);
-                    *reinterpret_cast<uint2*>(srow + col * 2) = pk;
-                } else {
-                    *reinterpret_cast<v4i*>(srow + col * 4) = acc[rb][cb];
+                        for (int v = 0; v < 4; ++v)
+                            h[v] = f32_to_f16_bits(((float)acc[rb][cb][v] * sm) * swv[cb][v]);
+                        uint2 pk;
+                        pk.x = h[0] | ((unsigned)h[1] << 16);
+                        pk.y = h[2] | ((unsigned)h[3] << 16);
+                        *reinterpret_cast<uint2*>(srow + col * 2) = pk;
+                    } else {
+                        *reinterpret_cast<v4i*>(srow + col * 4) = acc[rb][cb];
+                    }
                 }
             }
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
-        __builtin_amdgcn_wave_barrier();
-        constexpr int PPR = ROWB / 16;  // 16-byte pieces per row
+            __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes done
+            __builtin_amdgcn_wave_barrier();
+            constexpr int PPR = ROWB / 16;  // 16-byte pieces per row
 #pragma unroll
-        for (int w = 0; w < 32 * PPR / 64; ++w) {
-            const int q = lane + 64 * w;
-            const int row = q / PPR, piece = q % PPR;
-            const int m = m0 + 32 * rp + row;
-            const v4i val = *reinterpret_cast<const v4i*>(stage + row * RSTR + piece * 16);
-            if (m < row_hi)
-                *reinterpret_cast<v4i*>(out + ((size_t)m * N + n0) * EB + piece * 16) = val;
-        }
-        __builtin_amdgcn_s_waitcnt(0xc07f);
-        __builtin_amdgcn_wave_barrier();
+            for (int w = 0; w < 32 * PPR / 64; ++w) {
+                const int q = lane + 64 * w;
+                const int row = q / PPR, piece = q % PPR;
+                const int m = m0 + 32 * rp + row;
+                const v4i val = *reinterpret_cast<const v4i*>(stage + row * RSTR + piece * 16);
+                if (m < row_hi)
+                    *reinterpret_cast<v4i*>(out + ((size_t)m * N + n0) * EB + piece * 16) = val;
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+        });
+    };
+    if constexpr (KIN == 1) {
+        epi(std::integral_constant<int, 0>{}, std::integral_constant<int, RB / 2>{});
+    } else {
+        if (kp == 0) epi(std::integral_constant<int, 0>{}, std::integral_constant<int, HB / 2>{});
+        else epi(std::integral_constant<int, HB / 2>{}, std::integral_constant<int, HB / 2>{});
     }
 }
 
-template <int MT, int OUT, bool PARTIAL, bool W8>
+template <int MT, int OUT, bool PARTIAL, bool W8, int KIN = 1>
 static void launch_tile16(const int8_t* X, const float* sx, const uint8_t* wq,
                           const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
                           int* part, int M, int N, int K, int group, int splits, hipStream_t st,
                           const int* offsets, int E, int max_rows) {
-    const int tiles_n = N / kNT;
+    const int tiles_n = N / (kNT / KIN);
     const int tiles_m = ((offsets ? max_rows : M) + MT - 1) / MT;
     dim3 grid(tiles_n * tiles_m * splits, offsets ? E : 1), block(256);
     if (group == 64 && !W8)
-        hipLaunchKernelGGL((w4a8_mfma16_kernel<MT, OUT, 64, PARTIAL, W8>), grid, block, 0, st, X,
-                           sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, tiles_n, tiles_m, splits,
-                           offsets);
+        hipLaunchKernelGGL((w4a8_mfma16_kernel<MT, OUT, 64, PARTIAL, W8, KIN>), grid, block, 0,
+                           st, X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, tiles_n, tiles_m,
+                           splits, offsets);
     else
-        hipLaunchKernelGGL((w4a8_mfma16_kernel<MT, OUT, 128, PARTIAL, W8>), grid, block, 0, st,
-                           X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, tiles_n, tiles_m, splits,
-                           offsets);
+        hipLaunchKernelGGL((w4a8_mfma16_kernel<MT, OUT, 128, PARTIAL, W8, KIN>), grid, block, 0,
+                           st, X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, tiles_n, tiles_m,
+                           splits, offsets);
 }
 
 template <bool W8>
@@ -438,6 +513,20 @@ static hipError_t run_mfma16(const int8_t* X, const float* sx, const uint8_t* wq
                              void* workspace, hipStream_t st, const int* offsets, int E,
                              int max_rows) {
     int* part = reinterpret_cast<int*>(workspace);
+    if (plan.kin == 2) {  // 128-row tiles, no grouped problems
+        if (plan.splits == 1) {
+            if (out_type == 1)
+                launch_tile16<128, 1, false, W8, 2>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K,
+                                                    group, 1, st, nullptr, 1, 0);
+            else
+                launch_tile16<128, 0, false, W8, 2>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K,
+                                                    group, 1, st, nullptr, 1, 0);
+            return hipGetLastError();
+        }
+        launch_tile16<128, 1, true, W8, 2>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group,
+                                           plan.splits, st, nullptr, 1, 0);
+        return launch_splitk_reduce(part, plan.splits, M, N, sx, sw, Y, out_type, st);
+    }
     if (plan.splits == 1) {
 #define T16(MT_, O_) \
     launch_tile16<MT_, O_, false, W8>(X, sx, wq, s_u8, a_u8, sw, Y, part, M, N, K, group, 1, st, \

@@ -55,8 +55,14 @@ struct MfmaPlan {
     // workgroups per CU), or 0 for the 32 x 32 x 32 kernel at mt.  The FP8
     // tile kernel runs 128-row tiles (two per CU) when mt16 == 128, else mt.
     int mt16;
+    // K parts per workgroup of the integer 16 x 16 kernel: 2 = workgroups of
+    // 128 channels whose wave pairs take the two halves of the split's K
+    // range (only with mt16 == 128; splits then counts workgroups per tile).
+    int kin = 1;
 };
-MfmaPlan plan_w4a8_mfma(int M, int N, int K);
+// k_parts: the caller runs the integer 16 x 16 kernel, which can take K
+// parts; the workspace of such a plan is at most that of the plan without.
+MfmaPlan plan_w4a8_mfma(int M, int N, int K, bool k_parts = false);
 hipError_t launch_w4a8_mfma(const int8_t* X, const float* sx, const uint8_t* wq,
                             const uint8_t* s_u8, const uint8_t* a_u8, const float* sw, void* Y,
                             int out_type, int M, int N, int K, int group, const MfmaPlan& plan,
