@@ -971,11 +971,13 @@ def test_256_row_plan_every_element(M, N, K, g, w8):
 #   128 x 3840 x 2048: 30 channel tiles (not a multiple of 8: the plain tile
 #     order), no partials;
 #   64 x 1024 x 8960: eight splits stay (X read again would cost more than
-#     the partials), K-steps 8 or 9 per split.
+#     the partials), K-steps 8 or 9 per split;
+#   128 x 2048 x 2560: halves of 10 K-steps.
 # The W8A8 comparison runs the same plans.
 _KPARTS = [(128, 2048, 2816, 128, True), (100, 4096, 2944, 64, True),
            (128, 2048, 4096, 128, True), (128, 512, 4096, 64, False),
-           (128, 3840, 2048, 128, False), (64, 1024, 8960, 128, True)]
+           (128, 3840, 2048, 128, False), (64, 1024, 8960, 128, True),
+           (128, 2048, 2560, 64, True)]
 
 
 @pytest.mark.parametrize("M,N,K,g,w8", _KPARTS)
