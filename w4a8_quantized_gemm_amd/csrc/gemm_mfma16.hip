@@ -397,37 +397,30 @@ __global__ __launch_bounds__(256, (MT == 128 && KIN == 1) ? 2 : 1) void w4a8_mfm
     // halves.  Part kp writes row blocks [kp HB, kp HB + HB): each wave first
     // stores its sums of the other half's row blocks to LDS (block (receiving
     // part, panel, row block, channel block) of 64 lanes x 16 bytes), then,
-    // after the barrier, adds its partner's sums of its own.
+    // after the barrier, adds its partner's sums of its own into `fin`.  Row
+    // blocks are chosen by a select on kp (uniform), so every accumulator
+    // index stays a constant and both parts share one code path.
     constexpr int HB = RB / 2;
+    constexpr int FB = KIN == 2 ? HB : 1;
+    v4i fin[FB][4];
     if constexpr (KIN == 2) {
         static_assert(KIN * NWX * HB * 4 * 1024 <= 3 * XSTEP, "K-part exchange fits in LDS");
         v4i* xch = reinterpret_cast<v4i*>(xs);
         auto xidx = [&](int d, int i, int cb) {
             return ((d * NWX + wc) * HB * 4 + i * 4 + cb) * 64 + lane;
         };
-        auto give = [&](auto mec) {
-            constexpr int me = decltype(mec)::value;
-            static_for<HB>([&](auto ic) {
-                static_for<4>([&](auto cc) {
-                    constexpr int i = decltype(ic)::value, cb = decltype(cc)::value;
-                    xch[xidx(1 - me, i, cb)] = acc[(1 - me) * HB + i][cb];
-                });
-            });
-        };
-        auto take = [&](auto mec) {
-            constexpr int me = decltype(mec)::value;
-            static_for<HB>([&](auto ic) {
-                static_for<4>([&](auto cc) {
-                    constexpr int i = decltype(ic)::value, cb = decltype(cc)::value;
-                    acc[me * HB + i][cb] += xch[xidx(me, i, cb)];
-                });
-            });
-        };
-        if (kp == 0) give(std::integral_constant<int, 0>{});
-        else give(std::integral_constant<int, 1>{});
+        const bool hi = kp != 0;
+#pragma unroll
+        for (int i = 0; i < HB; ++i)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+                xch[xidx(1 - kp, i, cb)] = hi ? acc[i][cb] : acc[HB + i][cb];
         __syncthreads();
-        if (kp == 0) take(std::integral_constant<int, 0>{});
-        else take(std::integral_constant<int, 1>{});
+#pragma unroll
+        for (int i = 0; i < HB; ++i)
+#pragma unroll
+            for (int cb = 0; cb < 4; ++cb)
+                fin[i][cb] = (hi ? acc[HB + i][cb] : acc[i][cb]) + xch[xidx(kp, i, cb)];
     }
     __syncthreads();  // sxs written; the exchange blocks read before staging reuses them
     constexpr int EB = SCALED ? 2 : 4;  // output element bytes
@@ -437,30 +430,32 @@ __global__ __launch_bounds__(256, (MT == 128 && KIN == 1) ? 2 : 1) void w4a8_mfm
     uint8_t* stage = xs + wave * (32 * RSTR);
     uint8_t* out = PARTIAL ? reinterpret_cast<uint8_t*>(part + (size_t)ks * M * N)
                            : reinterpret_cast<uint8_t*>(Y);
-    // row-block pairs rp0 .. rp0 + NP - 1
-    auto epi = [&](auto rp0c, auto npc) {
-        constexpr int rp0 = decltype(rp0c)::value, NP = decltype(npc)::value;
-        static_for<NP>([&](auto rpc) {
-            constexpr int rp = rp0 + decltype(rpc)::value;
+    // Row-block pairs 0 .. NP-1 from row r0 of the tile on; value(rb, cb) is
+    // the sum of local row block rb, channel block cb.
+    auto epi = [&](auto npc, int r0, auto value) {
+        constexpr int NP = decltype(npc)::value;
+#pragma unroll
+        for (int rp = 0; rp < NP; ++rp) {
 #pragma unroll
             for (int rr = 0; rr < 2; ++rr) {
                 const int rb = 2 * rp + rr;
                 uint8_t* srow = stage + (16 * rr + r) * RSTR;
-                const float sm = SCALED ? sxs[16 * rb + r] : 0.0f;
+                const float sm = SCALED ? sxs[r0 + 16 * rb + r] : 0.0f;
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) {
                     const int col = 16 * cb + 4 * G;
+                    const v4i a = value(rb, cb);
                     if constexpr (SCALED) {
                         unsigned short h[4];
 #pragma unroll
                         for (int v = 0; v < 4; ++v)
-                            h[v] = f32_to_f16_bits(((float)acc[rb][cb][v] * sm) * swv[cb][v]);
+                            h[v] = f32_to_f16_bits(((float)a[v] * sm) * swv[cb][v]);
                         uint2 pk;
                         pk.x = h[0] | ((unsigned)h[1] << 16);
                         pk.y = h[2] | ((unsigned)h[3] << 16);
                         *reinterpret_cast<uint2*>(srow + col * 2) = pk;
                     } else {
-                        *reinterpret_cast<v4i*>(srow + col * 4) = acc[rb][cb];
+                        *reinterpret_cast<v4i*>(srow + col * 4) = a;
                     }
                 }
             }
@@ -471,21 +466,21 @@ __global__ __launch_bounds__(256, (MT == 128 && KIN == 1) ? 2 : 1) void w4a8_mfm
             for (int w = 0; w < 32 * PPR / 64; ++w) {
                 const int q = lane + 64 * w;
                 const int row = q / PPR, piece = q % PPR;
-                const int m = m0 + 32 * rp + row;
+                const int m = m0 + r0 + 32 * rp + row;
                 const v4i val = *reinterpret_cast<const v4i*>(stage + row * RSTR + piece * 16);
                 if (m < row_hi)
                     *reinterpret_cast<v4i*>(out + ((size_t)m * N + n0) * EB + piece * 16) = val;
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
-        });
+        }
     };
-    if constexpr (KIN == 1) {
-        epi(std::integral_constant<int, 0>{}, std::integral_constant<int, RB / 2>{});
-    } else {
-        if (kp == 0) epi(std::integral_constant<int, 0>{}, std::integral_constant<int, HB / 2>{});
-        else epi(std::integral_constant<int, HB / 2>{}, std::integral_constant<int, HB / 2>{});
-    }
+    if constexpr (KIN == 1)
+        epi(std::integral_constant<int, RB / 2>{}, 0,
+            [&](int rb, int cb) { return acc[rb][cb]; });
+    else
+        epi(std::integral_constant<int, HB / 2>{}, 16 * HB * kp,
+            [&](int rb, int cb) { return fin[rb][cb]; });
 }
 
 template <int MT, int OUT, bool PARTIAL, bool W8, int KIN = 1>
