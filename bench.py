@@ -281,6 +281,15 @@ def clocks_under_load(launch, n_samples=4, limit_s=20.0):
             "samples": len(samples), "launches": launches}
 
 
+def decode_target(sweep, target=0.70):
+    """Fraction of the 8 TB/s HBM peak (algorithmic bytes) that each slot
+    with M <= 16 reaches back to back, against the 70 % target."""
+    fr = {e["slot"]: e["hbm_frac_algo"] for e in sweep
+          if int(e["slot"].split(":M")[1]) <= 16 and e.get("hbm_frac_algo") is not None}
+    return {"target_hbm_frac": target, "slots": fr,
+            "met": bool(fr) and all(v >= target for v in fr.values())}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -497,6 +506,9 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof(dom["slot"], dom_bound),
         "roofline_decode": roof("upgate:M16", "hbm") or roof("down:M16", "hbm"),
+        # the decode target (70 % of HBM bandwidth at M <= 16), judged on
+        # the back-to-back figures, launch gaps included
+        "decode_target": decode_target(sweep),
         "kernel_ms_per_step": round(kern_ms_sum, 4),
         "sweep": sweep,
     }
