@@ -364,12 +364,18 @@ def test_grouped_gemm_parity(counts, N, K, g):
 
 
 @pytest.mark.parametrize("M,N,K,splits", [(600, 4352, 3072, 3), (300, 4352, 5120, 5),
-                                           (500, 2304, 7168, 7), (100, 256, 16384, 16)])
+                                           (500, 2304, 7168, 7), (100, 256, 16384, 16),
+                                           (640, 2048, 6272, 6), (100, 6912, 9216, 9),
+                                           (128, 6144, 10368, 10), (64, 5632, 11264, 11),
+                                           (128, 5120, 12416, 12), (128, 4864, 13312, 13),
+                                           (128, 4608, 14464, 14), (128, 4352, 15360, 15)])
 def test_split_counts_any_integer(M, N, K, splits):
-    """The split-K plan fills one wave of CUs with any integer split count:
-    int32 results bit-exact against the oracle on sampled rows (the oracle
-    quantises per row, so a row sample is exact) and against the streamed
-    kernel on every element."""
+    """The split-K plan fills one wave of CUs with any integer split count
+    (the reduction is built once per count, 2 to 16; the even counts here
+    keep their splits, since K parts would read X again for more bytes than
+    the partials): int32 results bit-exact against the oracle on sampled
+    rows (the oracle quantises per row, so a row sample is exact) and
+    against the streamed kernel on every element."""
     assert w4.workspace_size(M, N, K) == splits * M * N * 4
     g = 128
     say(f"w4a8 split-K {splits} M={M} N={N} K={K}")
@@ -553,11 +559,13 @@ def test_w4fp8_integer_valued_exact(M, N, K):
 
 # Matrix-core tile path (M >= 64, N % 256 == 0): ragged M, several tiles in
 # both directions, one and two K-steps per split, and planned split-K with
-# float32 partials (M=128, K=4096: one tile, four splits).
+# float32 partials (M=128, K=4096: one tile, four splits; then 16, 9, 13 and
+# 6 splits, each count a reduction of its own).
 @pytest.mark.parametrize("M,N,K", [(64, 256, 640), (512, 1024, 896), (300, 512, 1152),
                                    (64, 256, 1024), (100, 256, 1024), (256, 512, 2048),
                                    (300, 512, 1024), (513, 256, 2048), (128, 256, 4096),
-                                   (100, 512, 2048), (1024, 1024, 256)])
+                                   (100, 512, 2048), (1024, 1024, 256), (100, 256, 16384),
+                                   (100, 6912, 9216), (128, 4864, 13312), (640, 2048, 6272)])
 def test_w4fp8_tile_parity(M, N, K):
     say(f"w4fp8 tile gemm M={M} N={N} K={K} workspace={w4.workspace_size(M, N, K)}")
     W = wl.gen_weights(N, K, 500 + M + N)

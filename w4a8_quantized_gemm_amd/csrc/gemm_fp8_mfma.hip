@@ -372,18 +372,24 @@ __global__ __launch_bounds__(256, MT == 128 ? 2 : 1) void w4fp8_mfma_kernel(
 
 // Sum of the split-K float32 partial tiles in split order, then the
 // per-token x per-channel scale (or, with `tsc`, the per-tensor scale) to
-// bf16 or float32.  Each thread handles four consecutive channels of one row.
-template <int OUT>
+// bf16 or float32.  Workgroup (x, y) covers 1024 channels of row y; each
+// thread four consecutive channels, its S partial loads all in flight
+// before the first add (the adds keep split order).
+template <int OUT, int S>
 __global__ __launch_bounds__(256) void splitk_reduce_f32_kernel(
-    const float* __restrict__ part, int splits, int M, int N, const float* __restrict__ sx,
+    const float* __restrict__ part, int M, int N, const float* __restrict__ sx,
     const float* __restrict__ sw, const float* __restrict__ tsc, void* __restrict__ Y) {
-    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (n >= N) return;
+    const int m = blockIdx.y;
     const size_t MN = (size_t)M * N;
-    if (q * 4 >= MN) return;
-    const size_t e = q * 4;
-    v4f acc = *reinterpret_cast<const v4f*>(part + e);
-    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const v4f*>(part + s * MN + e);
-    const int m = (int)(e / N), n = (int)(e % N);
+    const size_t e = (size_t)m * N + n;
+    v4f v[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) v[s] = *reinterpret_cast<const v4f*>(part + s * MN + e);
+    v4f acc = v[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) acc += v[s];
     const float sm = sx[m];
     float y[4];
 #pragma unroll
@@ -395,6 +401,23 @@ __global__ __launch_bounds__(256) void splitk_reduce_f32_kernel(
         pk.x = f32_to_bf16_bits(y[0]) | ((unsigned)f32_to_bf16_bits(y[1]) << 16);
         pk.y = f32_to_bf16_bits(y[2]) | ((unsigned)f32_to_bf16_bits(y[3]) << 16);
         *reinterpret_cast<uint2*>(reinterpret_cast<unsigned short*>(Y) + e) = pk;
+    }
+}
+
+// splits in 2 .. 16 (the plans' range), one instantiation each.
+template <int OUT, int S = 2>
+static hipError_t splitk_reduce_f32_run(const float* part, int splits, int M, int N,
+                                        const float* sx, const float* sw, const float* tsc,
+                                        void* Y, hipStream_t st) {
+    if constexpr (S > 16) {
+        return hipErrorInvalidValue;
+    } else {
+        if (splits != S)
+            return splitk_reduce_f32_run<OUT, S + 1>(part, splits, M, N, sx, sw, tsc, Y, st);
+        const dim3 grid((unsigned)((N / 4 + 255) / 256), (unsigned)M);
+        hipLaunchKernelGGL((splitk_reduce_f32_kernel<OUT, S>), grid, dim3(256), 0, st, part, M,
+                           N, sx, sw, tsc, Y);
+        return hipGetLastError();
     }
 }
 
@@ -435,15 +458,10 @@ static hipError_t w4fp8_mfma_group(const uint8_t* X, const float* sx, const uint
     if (mt == 256) FP8_TILE(256, 1, true, plan.splits);
     else FP8_TILE(128, 1, true, plan.splits);
 #undef FP8_TILE
-    const size_t quads = ((size_t)M * N) / 4;
-    const unsigned blocks = (unsigned)((quads + 255) / 256);
+    if (M == 0) return hipGetLastError();
     if (out_type == 1)
-        hipLaunchKernelGGL((splitk_reduce_f32_kernel<1>), dim3(blocks), dim3(256), 0, st, part,
-                           plan.splits, M, N, sx, sw, tsc, Y);
-    else
-        hipLaunchKernelGGL((splitk_reduce_f32_kernel<0>), dim3(blocks), dim3(256), 0, st, part,
-                           plan.splits, M, N, sx, sw, tsc, Y);
-    return hipGetLastError();
+        return splitk_reduce_f32_run<1>(part, plan.splits, M, N, sx, sw, tsc, Y, st);
+    return splitk_reduce_f32_run<0>(part, plan.splits, M, N, sx, sw, tsc, Y, st);
 }
 
 hipError_t launch_w4fp8_mfma(const uint8_t* X, const float* sx, const uint8_t* wq,

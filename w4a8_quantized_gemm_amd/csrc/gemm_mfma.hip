@@ -550,22 +550,28 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
 }
 
 // Sum of the split-K partial tiles in split order (exact int32), then the
-// per-token x per-channel scale to fp16, or the raw int32 sums.  Each thread
-// handles four consecutive channels of one row.
-template <int OUT>
+// per-token x per-channel scale to fp16, or the raw int32 sums.  Workgroup
+// (x, y) covers 1024 channels of row y; each thread four consecutive
+// channels.  The split count is a template argument, so a thread's S partial
+// loads are all in flight before the first add.
+template <int OUT, int S>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(
-    const int* __restrict__ part, int splits, int M, int N, const float* __restrict__ sx,
+    const int* __restrict__ part, int M, int N, const float* __restrict__ sx,
     const float* __restrict__ sw, void* __restrict__ Y) {
-    const size_t q = (size_t)blockIdx.x * 256 + threadIdx.x;
+    const int n = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (n >= N) return;
+    const int m = blockIdx.y;
     const size_t MN = (size_t)M * N;
-    if (q * 4 >= MN) return;
-    const size_t e = q * 4;
-    v4i acc = *reinterpret_cast<const v4i*>(part + e);
-    for (int s = 1; s < splits; ++s) acc += *reinterpret_cast<const v4i*>(part + s * MN + e);
+    const size_t e = (size_t)m * N + n;
+    v4i v[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) v[s] = *reinterpret_cast<const v4i*>(part + s * MN + e);
+    v4i acc = v[0];
+#pragma unroll
+    for (int s = 1; s < S; ++s) acc += v[s];
     if (OUT == 1) {
         *reinterpret_cast<v4i*>(reinterpret_cast<int*>(Y) + e) = acc;
     } else {
-        const int m = (int)(e / N), n = (int)(e % N);
         const float sm = sx[m];
         unsigned short hv[4];
 #pragma unroll
@@ -577,17 +583,27 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(
     }
 }
 
+// splits in 2 .. 16 (the plans' range), one instantiation each.
+template <int OUT, int S = 2>
+static hipError_t splitk_reduce_run(const int* part, int splits, int M, int N, const float* sx,
+                                    const float* sw, void* Y, hipStream_t st) {
+    if constexpr (S > 16) {
+        return hipErrorInvalidValue;
+    } else {
+        if (splits != S)
+            return splitk_reduce_run<OUT, S + 1>(part, splits, M, N, sx, sw, Y, st);
+        const dim3 grid((unsigned)((N / 4 + 255) / 256), (unsigned)M);
+        hipLaunchKernelGGL((splitk_reduce_kernel<OUT, S>), grid, dim3(256), 0, st, part, M, N,
+                           sx, sw, Y);
+        return hipGetLastError();
+    }
+}
+
 hipError_t launch_splitk_reduce(const int* part, int splits, int M, int N, const float* sx,
                                 const float* sw, void* Y, int out_type, hipStream_t st) {
-    const size_t quads = ((size_t)M * N) / 4;
-    const unsigned blocks = (unsigned)((quads + 255) / 256);
-    if (out_type == 1)
-        hipLaunchKernelGGL((splitk_reduce_kernel<1>), dim3(blocks), dim3(256), 0, st, part,
-                           splits, M, N, sx, sw, Y);
-    else
-        hipLaunchKernelGGL((splitk_reduce_kernel<0>), dim3(blocks), dim3(256), 0, st, part,
-                           splits, M, N, sx, sw, Y);
-    return hipGetLastError();
+    if (M == 0) return hipSuccess;
+    if (out_type == 1) return splitk_reduce_run<1>(part, splits, M, N, sx, sw, Y, st);
+    return splitk_reduce_run<0>(part, splits, M, N, sx, sw, Y, st);
 }
 
 // Workgroup tile height and K split for the matrix-core kernel.
