@@ -24,6 +24,16 @@ __device__ __forceinline__ v4i load16(const void* p) {
     return *reinterpret_cast<const v4i*>(p);
 }
 
+// 16-byte store of a tile kernel's result: non-temporal for the final
+// output, which nothing reads back, so it does not displace the panels other
+// workgroups are reading from L2 (4096 x 28672 x 8192: 704 -> 696 us); split-K
+// partials, which the reduction reads next, keep the plain store.
+template <bool KEEP>
+__device__ __forceinline__ void store16_result(void* p, v4i v) {
+    if constexpr (KEEP) *reinterpret_cast<v4i*>(p) = v;
+    else __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(p));
+}
+
 // LiquidQuant dequantisation of four codes held one per byte of `c`
 // (LiquidGEMM, Pith review of arXiv 2509.01229, "What carries the
 // argument" / paper Eq. 12): byte = (q*s + a) XOR 0x80.  The multiply-add

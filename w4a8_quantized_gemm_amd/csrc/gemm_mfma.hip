@@ -542,7 +542,7 @@ __global__ __launch_bounds__(256, 1) void w4a8_mfma_kernel(
             const int m = m0 + 32 * rb + row;
             const v4i val = *reinterpret_cast<const v4i*>(stage + row * RSTR + piece * 16);
             if (m < row_hi)
-                *reinterpret_cast<v4i*>(out + ((size_t)m * N + n0) * EB + piece * 16) = val;
+                store16_result<PARTIAL>(out + ((size_t)m * N + n0) * EB + piece * 16, val);
         }
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_wave_barrier();
