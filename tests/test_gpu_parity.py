@@ -932,9 +932,12 @@ def test_256_row_tiles_long_k():
 # (four waves, so 256-row tiles stay), and long K with 65 (odd, the padding
 # step) and 66 (even) K-steps; 4000 rows leave a ragged last row tile.  The
 # W8A8 comparison runs the same plan.  These are the cases where a missed
-# wait state in the hand-placed matrix-core schedule would show.
+# wait state in the hand-placed matrix-core schedule would show.  Two more
+# long-K cases with rows past M in the last row tile: 304 tiles (66 K-steps)
+# and 512 tiles (65 K-steps).
 _PLAN256 = [(4096, 16384, 256, 64, True), (4096, 16384, 384, 128, True),
-            (4000, 4096, 8320, 128, True), (4096, 4096, 8448, 64, False)]
+            (4000, 4096, 8320, 128, True), (4096, 4096, 8448, 64, False),
+            (4000, 4864, 8448, 128, True), (4000, 8192, 8320, 64, False)]
 
 
 @pytest.mark.parametrize("M,N,K,g,w8", _PLAN256)
