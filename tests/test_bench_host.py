@@ -1,7 +1,7 @@
 """Host-side logic of bench.py, on the CPU: the one-GPU rule, the byte
 counts behind the roofline figures, the source digest that decides whether
 committed counter summaries still describe the kernels, and the decode
-target's verdict."""
+target's outcome."""
 import os
 import subprocess
 import sys
@@ -45,7 +45,7 @@ def test_source_digest_is_stable():
     assert len(bench.source_digest()) == 64
 
 
-def test_decode_target_verdict():
+def test_decode_target_outcome():
     sweep = [{"slot": "upgate:M1", "hbm_frac_algo": 0.71},
              {"slot": "upgate:M16", "hbm_frac_algo": 0.70},
              {"slot": "down:M16", "hbm_frac_algo": 0.69},

@@ -1,4 +1,4 @@
-"""The decode's instruction count in this build's own gfx950 code.
+"""The decode's instruction count in the library's own gfx950 code.
 
 LiquidGEMM (Pith review of arXiv 2509.01229, minor comment 1, paper Sec. 5.3)
 counts 2 instructions per 4 weights for the dequantisation, 7 per 8 with the
