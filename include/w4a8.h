@@ -189,6 +189,29 @@ w4a8_status_t w4a8_gemm(const int8_t* X, const float* sx, const uint8_t* wq,
                         size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * The kernel plan w4a8_gemm takes for a shape (a pure function of M, N, K
+ * and splitk, computed on the host; group does not enter it), for callers
+ * that size launches or check a configuration.  Outputs:
+ *   *kernel         0 = streamed-tile kernel, 1 = tile kernel on
+ *                   16 x 16 x 64 instructions, 2 = tile kernel on
+ *                   32 x 32 x 32 instructions;
+ *   *tile_rows      rows of X per workgroup (16, 32 or 64 streamed; 128 or
+ *                   256 for the tile kernels);
+ *   *tile_channels  output channels per workgroup;
+ *   *splits         workgroups sharing one output tile's K range (int32
+ *                   partials in the workspace when > 1);
+ *   *k_parts        groups of waves of one workgroup splitting its K range
+ *                   (streamed: K-splitting waves; tile kernels: 1 or 2).
+ * An empty problem (M or N = 0), for which w4a8_gemm launches nothing,
+ * reports the streamed kernel's plan.  W4A8_ERR_NULL_PTR if an output
+ * pointer is NULL; W4A8_ERR_SHAPE for a shape or splitk that w4a8_gemm
+ * rejects.
+ */
+w4a8_status_t w4a8_gemm_plan(int M, int N, int K, int splitk, int* kernel,
+                             int* tile_rows, int* tile_channels, int* splits,
+                             int* k_parts);
+
+/*
  * w4a8_gemm for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc.
  * Arguments, results and errors are those of w4a8_gemm (same kernels, same

@@ -55,8 +55,27 @@ int main() {
                     const size_t w = w4a8_workspace_size(m, n, k, sk);
                     if (w > W4A8_NOALLOC_SCRATCH_BYTES) ++fails;  // every plan fits the static scratch
                     total += w;
+                    // the plan query over the same shapes: a valid shape gets a
+                    // plan whose split count and K parts fit its K-steps
+                    int kern = -1, rows = 0, chans = 0, splits = 0, parts = 0;
+                    const w4a8_status_t st =
+                        w4a8_gemm_plan(m, n, k, sk, &kern, &rows, &chans, &splits, &parts);
+                    if (st == W4A8_OK) {
+                        if (kern < 0 || kern > 2 || rows <= 0 || chans <= 0 || splits < 1 ||
+                            parts < 1 || splits * parts > k / 128)
+                            ++fails;
+                        total += (size_t)(kern + rows + chans + splits + parts);
+                    } else if (st != W4A8_ERR_SHAPE) {
+                        ++fails;
+                    }
                 }
     EXPECT(w4a8_workspace_size(-5, 256, 128, 0), 0);
+    {
+        int v[5];
+        EXPECT(w4a8_gemm_plan(16, 256, 128, 0, nullptr, v + 1, v + 2, v + 3, v + 4),
+               W4A8_ERR_NULL_PTR);
+        EXPECT(w4a8_gemm_plan(-1, 256, 128, 0, v, v + 1, v + 2, v + 3, v + 4), W4A8_ERR_SHAPE);
+    }
 
     // pack
     EXPECT(w4a8_pack(nullptr, 64, 256, 64, 127, 0, b, b, b, f, nullptr), W4A8_ERR_NULL_PTR);

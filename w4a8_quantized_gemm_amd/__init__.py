@@ -42,7 +42,7 @@ LAYOUT_VERSION = 1
 
 EXPORTS = ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act",
            "w4a8_quant_act_ex", "w4fp8_quant_act_ex", "w4a8_workspace_size", "w4a8_gemm",
-           "w4a8_gemm_noalloc",
+           "w4a8_gemm_noalloc", "w4a8_gemm_plan",
            "w4a8_gemm_ablation", "w4a8_gemm_grouped", "w4fp8_gemm", "w4fp8g_pack",
            "w4fp8g_gemm", "w8a8_pack", "w8a8_gemm",
            "w4a8_status_str", "w4a8_last_hip_error", "w4a8_layout_version")
@@ -54,6 +54,7 @@ lib.w4fp8_quant_act.argtypes = [_P, _I, _I, _P, _P, _P]
 lib.w4a8_quant_act_ex.argtypes = [_P, _I, _I, _I, _P, _P, _P]
 lib.w4fp8_quant_act_ex.argtypes = [_P, _I, _I, _I, _P, _P, _P]
 lib.w4a8_workspace_size.argtypes = [_I, _I, _I, _I]
+lib.w4a8_gemm_plan.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P]
 lib.w4a8_workspace_size.restype = _Z
 lib.w4a8_gemm.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _Z, _P]
 lib.w4a8_gemm_noalloc.argtypes = [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
@@ -70,7 +71,8 @@ lib.w4a8_last_hip_error.restype = _I
 lib.w4a8_layout_version.restype = _I
 for _n in ("w4a8_pack", "w4a8_quant_act", "w4fp8_quant_act", "w4a8_quant_act_ex",
            "w4fp8_quant_act_ex", "w4a8_gemm", "w4a8_gemm_noalloc", "w4a8_gemm_ablation", "w4a8_gemm_grouped",
-           "w4fp8_gemm", "w4fp8g_pack", "w4fp8g_gemm", "w8a8_pack", "w8a8_gemm"):
+           "w4fp8_gemm", "w4fp8g_pack", "w4fp8g_gemm", "w8a8_pack", "w8a8_gemm",
+           "w4a8_gemm_plan"):
     getattr(lib, _n).restype = _I
 
 assert lib.w4a8_layout_version() == LAYOUT_VERSION
@@ -230,6 +232,16 @@ def quant_act_fp8(X, stream=None, out=None):
 
 def workspace_size(M: int, N: int, K: int, splitk: int = 0) -> int:
     return int(lib.w4a8_workspace_size(M, N, K, splitk))
+
+
+def gemm_plan(M: int, N: int, K: int, splitk: int = 0) -> dict:
+    """The kernel plan w4a8_gemm takes for this shape (host-side, no GPU)."""
+    vals = [ctypes.c_int(0) for _ in range(5)]
+    _check(lib.w4a8_gemm_plan(M, N, K, splitk, *[ctypes.addressof(v) for v in vals]),
+           "w4a8_gemm_plan")
+    kernel, rows, chans, splits, parts = (v.value for v in vals)
+    return {"kernel": ("stream", "tile16", "tile32")[kernel], "tile_rows": rows,
+            "tile_channels": chans, "splits": splits, "k_parts": parts}
 
 
 def gemm(Xq, sx, packed, out_type: int = OUT_F16, splitk: int = 0, out=None,

@@ -8,6 +8,7 @@
 #include <cstring>
 
 #include "launch.h"
+#include "mfma_common.h"
 #include "w4a8.h"
 
 #define W4A8_EXPORT extern "C" __attribute__((visibility("default")))
@@ -159,6 +160,31 @@ W4A8_EXPORT const char* w4a8_status_str(w4a8_status_t s) {
 W4A8_EXPORT int w4a8_last_hip_error(void) { return g_last_hip_error; }
 
 W4A8_EXPORT int w4a8_layout_version(void) { return W4A8_LAYOUT_VERSION; }
+
+W4A8_EXPORT w4a8_status_t w4a8_gemm_plan(int M, int N, int K, int splitk, int* kernel,
+                                         int* tile_rows, int* tile_channels, int* splits,
+                                         int* k_parts) {
+    if (!kernel || !tile_rows || !tile_channels || !splits || !k_parts) return W4A8_ERR_NULL_PTR;
+    if (M < 0 || !valid_nk(N, K) || !valid_splitk(splitk, K)) return W4A8_ERR_SHAPE;
+    // (an empty problem, M or N = 0, launches nothing; it reports the
+    // streamed kernel's plan and never reaches the tile plan's arithmetic)
+    if (splitk == 0 && M > 0 && N > 0 && use_mfma_tiles(M, N, K)) {  // as launch_w4a8_mfma
+        const w4a8::MfmaPlan p = w4a8::plan_w4a8_mfma(M, N, K, true);
+        *kernel = p.mt16 != 0 ? 1 : 2;
+        *tile_rows = p.mt16 != 0 ? p.mt16 : p.mt;
+        *tile_channels = w4a8::kNT / p.kin;
+        *splits = p.splits;
+        *k_parts = p.kin;
+    } else {
+        const w4a8::StreamCfg c = choose_stream(M, N, K, splitk, true);
+        *kernel = 0;
+        *tile_rows = 16 * c.rb;
+        *tile_channels = 16 * c.nt_per_wave;
+        *splits = 1;
+        *k_parts = c.ks;
+    }
+    return W4A8_OK;
+}
 
 W4A8_EXPORT size_t w4a8_workspace_size(int M, int N, int K, int splitk) {
     if (M <= 0 || !valid_nk(N, K) || N == 0 || splitk != 0) return 0;
