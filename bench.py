@@ -506,7 +506,7 @@ def main():
                    "parallelism": "single GPU"},
         "roofline": roof(dom["slot"], dom_bound),
         "roofline_decode": roof("upgate:M16", "hbm") or roof("down:M16", "hbm"),
-        # the decode target (70 % of HBM bandwidth at M <= 16), judged on
+        # the decode target (70 % of HBM bandwidth at M <= 16), assessed on
         # the back-to-back figures, launch gaps included
         "decode_target": decode_target(sweep),
         "kernel_ms_per_step": round(kern_ms_sum, 4),
