@@ -49,7 +49,8 @@ def parse():
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
-    p.add_argument("--only", default="", help="run one slot, e.g. upgate:M4096")
+    p.add_argument("--only", default="",
+                   help="run one slot, e.g. upgate:M4096, or fp8 for the FP8 variant alone")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true")
     p.add_argument("--no-ablation", action="store_true")
@@ -290,6 +291,115 @@ def decode_target(sweep, target=0.70):
             "met": bool(fr) and all(v >= target for v in fr.values())}
 
 
+def sustain(torch, stream, launch, pool, ms=100.0):
+    """About `ms` milliseconds of untimed back-to-back launches
+    (launch(pool[r % len(pool)])), so that what is timed next runs at the
+    clock the chip holds under sustained load.  Measured on one box: after
+    50 ms idle, 20 back-to-back launches of 4096 x 28672 x 8192 took 823 us
+    each, 714 us after 100 ms of load; at 16 x 8192 x 28672, 27.0 against
+    24.1 us."""
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    launch(pool[0])
+    t1.record(stream)
+    torch.cuda.synchronize()
+    for r in range(min(5000, int(ms / max(t0.elapsed_time(t1), 1e-3)) + 1)):
+        launch(pool[r % len(pool)])
+
+
+def graph_bursts(torch, stream, launch, pool, Yout, n, reps=20):
+    """Per-launch microseconds of `reps` launches (launch(pool[r % len(pool)]))
+    captured once in a HIP graph, so a launch's figure is the GPU's (kernel
+    plus dispatch gap) even where a Python launch takes longer than the
+    kernel.  Two replays, each followed by a synchronisation, are first
+    checked against the eager result; then, after about 100 ms of untimed
+    replays, n replays run back to back on `stream` (the GPU kept busy, as in
+    the sweep: this part is power-bound, and idle gaps would raise its
+    clock), each bracketed by events, and the output of the last is checked
+    again."""
+    import numpy as np
+    launch(pool[(reps - 1) % len(pool)])
+    torch.cuda.synchronize()
+    want = Yout.clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for r in range(3):
+            launch(pool[r % len(pool)])
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for r in range(reps):
+            launch(pool[r % len(pool)])
+    for _ in range(2):
+        Yout.zero_()
+        graph.replay()
+        torch.cuda.synchronize()
+        if not torch.equal(Yout, want):
+            raise RuntimeError("graph replay differs from the eager result")
+    sustain(torch, stream, lambda _: graph.replay(), [None])
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    evs[0].record(stream)
+    for i in range(n):
+        graph.replay()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    if not torch.equal(Yout, want):
+        raise RuntimeError("graph replay differs from the eager result")
+    out_us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 / reps for i in range(n)]
+    del graph
+    return np.array(out_us)
+
+
+def fp8_variant(w4, wl, torch, dev, stream, n=5):
+    """FP8 variants (INT4 weights x e4m3 activations), reported alongside the
+    W4A8 sweep: per-channel scales, and per-group scales folded into the FP8
+    weights with a per-tensor rescale; the prefill shape and a 16-token
+    decode shape."""
+    import numpy as np
+    sh = wl.CONFIGS[wl.FP8_VARIANT].shapes[0]
+    Wf = torch.from_numpy(wl.gen_weights(sh.N, sh.K, wl.seed_w(wl.FP8_VARIANT))).to(dev)
+    pk8 = w4.pack(Wf, mode=w4.PACK_INT4_SYM)
+    pk8g = w4.pack_fp8g(Wf, group=128)
+    del Wf
+    # weight copies used in turn, more bytes than the 256 MB Infinity
+    # Cache, so no launch finds its weights cached from the previous use
+    ncp = int(300e6 // (sh.N * sh.K // 2)) + 1
+    cps8 = [pk8] + [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in pk8.items()}
+                    for _ in range(ncp - 1)]
+    cps8g = [pk8g] + [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in pk8g.items()}
+                      for _ in range(ncp - 1)]
+    Xf = torch.from_numpy(wl.gen_activations(sh.M, sh.K, wl.seed_x(wl.FP8_VARIANT),
+                                             wl.seed_outliers(wl.FP8_VARIANT))).to(dev)
+    X8, sx8 = w4.quant_act_fp8(Xf)
+    del Xf
+
+    res = {}
+    for M in (sh.M, 16):
+        Yb = torch.empty((M, sh.N), dtype=torch.bfloat16, device=dev)
+        Xm, sxm = X8[:M], sx8[:M]
+        for tag, fn, pool in (("per_channel",
+                               lambda pk: w4.gemm_fp8(Xm, sxm, pk, out=Yb), cps8),
+                              ("group128_folded",
+                               lambda pk: w4.gemm_fp8g(Xm, sxm, pk, out=Yb), cps8g)):
+            ts = graph_bursts(torch, stream, fn, pool, Yb, n)
+            us = float(np.median(ts))
+            tf = 2.0 * M * sh.N * sh.K / (us * 1e-6) / 1e12
+            wb = sh.N * sh.K / 2 + (sh.N * 4 if tag == "per_channel"
+                                    else sh.N * sh.K // 128 * 4 + 4)
+            ab = wb + M * sh.K + M * 4 + M * sh.N * 2
+            res[f"{tag}_M{M}"] = {"us": round(us, 2), "us_min": round(float(ts.min()), 2),
+                                  "us_max": round(float(ts.max()), 2), "tflops": round(tf, 2),
+                                  "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4),
+                                  "hbm_frac_algo": round(ab / (us * 1e-6) / 1e9
+                                                         / HBM_PEAK_GBS, 4)}
+    return {"workload": f"int4-fp8 N={sh.N} K={sh.K}, M={sh.M} and 16, bf16 out; median over "
+                        f"{n} back-to-back replays of a HIP graph of 20 launches rotating {ncp} "
+                        "weight copies (a Python launch takes longer than the 16-row kernels), "
+                        "the output checked against the eager result",
+            "results": res}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -310,6 +420,11 @@ def main():
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
+    if args.only == "fp8":
+        # the FP8 variant alone, for the profiler
+        print(json.dumps({"variant_fp8": fp8_variant(w4, wl, torch, dev, stream, args.bursts)}),
+              flush=True)
+        return
     pairs = wl.nk_pairs(CFG)           # [(28672, 8192), (8192, 28672)]
     tags = {pairs[0]: "upgate", pairs[1]: "down"}
     g = 128
@@ -390,8 +505,7 @@ def main():
 
     def bursts(launch, pool, n):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        for r in range(2):
-            launch(pool[r % len(pool)])
+        sustain(torch, stream, launch, pool)
         out_us = []
         for _ in range(n):
             e0.record(stream)
@@ -400,37 +514,6 @@ def main():
             e1.record(stream)
             torch.cuda.synchronize()
             out_us.append(e0.elapsed_time(e1) * 1e3 / reps)
-        return np.array(out_us)
-
-    def graph_bursts(launch, pool, Yout, n):
-        """As bursts(), but the `reps` launches are captured once in a HIP
-        graph and replayed, so a launch's figure is the GPU's (kernel plus
-        dispatch gap) even where a Python launch takes longer than the
-        kernel; every replay is checked against the eager result."""
-        launch(pool[(reps - 1) % len(pool)])
-        torch.cuda.synchronize()
-        want = Yout.clone()
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            for r in range(3):
-                launch(pool[r % len(pool)])
-        torch.cuda.current_stream().wait_stream(side)
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            for r in range(reps):
-                launch(pool[r % len(pool)])
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        out_us = []
-        for _ in range(n):
-            e0.record(stream)
-            graph.replay()
-            e1.record(stream)
-            torch.cuda.synchronize()
-            if not torch.equal(Yout, want):
-                raise RuntimeError("graph replay differs from the eager result")
-            out_us.append(e0.elapsed_time(e1) * 1e3 / reps)
-        del graph
         return np.array(out_us)
 
     burst_us = {}
@@ -548,7 +631,7 @@ def main():
                     X7, sx7 = w4.quant_act(Xf)
                     del Xf
                     Y7 = torch.empty((M, N), dtype=torch.float16, device=dev)
-                    ts = graph_bursts(lambda pk, X7=X7, sx7=sx7, Y7=Y7:
+                    ts = graph_bursts(torch, stream, lambda pk, X7=X7, sx7=sx7, Y7=Y7:
                                       w4.gemm(X7, sx7, pk, out=Y7), pool, Y7, args.bursts)
                     us = float(np.median(ts))
                     ops = 2.0 * M * N * K
@@ -566,9 +649,9 @@ def main():
                                   "weight_copies": ncp})
                 del pool, pk7
         out["llama7b"] = {"workload": "llama2-7b linear shapes (W4A8, group 64), fp16 out; "
-                                      "median over replays of a HIP graph of 20 launches "
-                                      "rotating weight copies past 600 MB (a Python launch "
-                                      "takes longer than the decode kernels); decode rows "
+                                      "median over back-to-back replays of a HIP graph of 20 "
+                                      "launches rotating weight copies past 600 MB (a Python "
+                                      "launch takes longer than the decode kernels); decode rows "
                                       "against 8 TB/s (algorithmic bytes), prefill rows "
                                       "against 5 POP/s",
                           "results": rows7}
@@ -585,21 +668,30 @@ def main():
         for sl in slots:
             if sl["M"] < 1024:
                 continue
-            row = {"slot": sl["name"]}
             # the weight copies of every slot of this shape in turn, as in the
             # sweep's bursts, so that no launch finds its weights in the cache
             copies = [pk for t in slots if t["pair"] == sl["pair"] for pk in t["pks"]]
-            for v, nm in names.items():
-                w4.gemm_ablation(v, sl["X"], sl["sx"], copies[-1], out=sl["Y"])
-                reps = 2 * len(copies)
-                e0.record(stream)
-                for r in range(reps):
-                    w4.gemm_ablation(v, sl["X"], sl["sx"], copies[r % len(copies)], out=sl["Y"])
-                e1.record(stream)
-                torch.cuda.synchronize()
-                row[nm + "_us"] = round(e0.elapsed_time(e1) * 1e3 / reps, 2)
-            # the production kernel choice for the same slot (from the sweep)
-            row["w4a8_gemm_us"] = next(r["us"] for r in sweep if r["slot"] == sl["name"])
+            fns = {nm: (lambda pk, v=v, sl=sl: w4.gemm_ablation(v, sl["X"], sl["sx"], pk,
+                                                                 out=sl["Y"]))
+                   for v, nm in names.items()}
+            # the production kernel choice for the same slot, in the same loop
+            fns["w4a8_gemm"] = lambda pk, sl=sl: w4.gemm(sl["X"], sl["sx"], pk, out=sl["Y"])
+            reps = 2 * len(copies)
+            sustain(torch, stream, fns["lqq"], copies)
+            times = {nm: [] for nm in fns}
+            # the variants interleaved, one burst each per round, medians over
+            # the rounds, so that drift of the clock affects them alike
+            for _ in range(args.bursts):
+                for nm, fn in fns.items():
+                    e0.record(stream)
+                    for r in range(reps):
+                        fn(copies[r % len(copies)])
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    times[nm].append(e0.elapsed_time(e1) * 1e3 / reps)
+            row = {"slot": sl["name"]}
+            for nm, v in times.items():
+                row[nm + "_us"] = round(float(np.median(v)), 2)
             row["affine16_vs_lqq"] = round(row["affine16_us"] / row["lqq_us"], 3)
             row["coarse_vs_lqq"] = round(row["lqq_coarse_us"] / row["lqq_us"], 3)
             abl.append(row)
@@ -622,22 +714,31 @@ def main():
             for sl in slots:
                 if sl["pair"] != pi:
                     continue
-                for _ in range(3):
-                    w4.gemm_w8a8(sl["X"], sl["sx"], pk8, out=sl["Y"])
+                pool4 = [pk for t in slots if t["pair"] == pi for pk in t["pks"]]
+                f8 = lambda r, sl=sl: w4.gemm_w8a8(sl["X"], sl["sx"], pk8 if r % 2 == 0 else pk8b,
+                                                   out=sl["Y"])
+                f4 = lambda r, sl=sl, pool4=pool4: w4.gemm(sl["X"], sl["sx"],
+                                                          pool4[r % len(pool4)], out=sl["Y"])
+                sustain(torch, stream, f8, [0, 1])
                 reps = 10 if sl["M"] >= 1024 else 20
-                e0.record(stream)
-                for r in range(reps):
-                    w4.gemm_w8a8(sl["X"], sl["sx"], pk8 if r % 2 == 0 else pk8b, out=sl["Y"])
-                e1.record(stream)
-                torch.cuda.synchronize()
-                us8 = e0.elapsed_time(e1) * 1e3 / reps
-                w4us = next(x["us"] for x in sweep if x["slot"] == sl["name"])
-                cmp_rows.append({"slot": sl["name"], "w8a8_us": round(us8, 2), "w4a8_us": w4us,
-                                 "w8a8_vs_w4a8": round(us8 / w4us, 3)})
+                t8, t4 = [], []
+                # W8A8 and W4A8 bursts interleaved, medians over the rounds
+                for _ in range(args.bursts):
+                    for fn, acc in ((f8, t8), (f4, t4)):
+                        e0.record(stream)
+                        for r in range(reps):
+                            fn(r)
+                        e1.record(stream)
+                        torch.cuda.synchronize()
+                        acc.append(e0.elapsed_time(e1) * 1e3 / reps)
+                us8, us4 = float(np.median(t8)), float(np.median(t4))
+                cmp_rows.append({"slot": sl["name"], "w8a8_us": round(us8, 2),
+                                 "w4a8_us": round(us4, 2), "w8a8_vs_w4a8": round(us8 / us4, 3)})
             del pk8, pk8b
-        out["w8a8_compare"] = {"note": "W8A8 timed back-to-back alternating two weight "
-                                       "copies (events over 10-20 launches); W4A8 from the "
-                                       "sweep (rotating weight copies)",
+        out["w8a8_compare"] = {"note": "medians over rounds of interleaved bursts of 10-20 "
+                                       "back-to-back launches: W8A8 alternating two weight "
+                                       "copies, W4A8 rotating the sweep's weight copies of the "
+                                       "same shape",
                                "results": cmp_rows}
 
     # ---- grouped (mixture-of-experts) GEMM: Mixtral-8x7B expert layers, 8
@@ -662,8 +763,8 @@ def main():
                 Xq_m, sx_m = w4.quant_act(Xm)
                 Ym = torch.empty((Mm, Nm), dtype=torch.float16, device=dev)
                 mr = int(counts.max())
-                for r in range(3):
-                    w4.gemm_grouped(Xq_m, sx_m, offs, pkms[r % 2], mr, out=Ym)
+                sustain(torch, stream, lambda pk: w4.gemm_grouped(Xq_m, sx_m, offs, pk, mr,
+                                                                   out=Ym), pkms)
                 reps = 10
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
@@ -686,60 +787,8 @@ def main():
                                           "launches alternating two copies of the expert weights",
                               "results": moe}
 
-    # ---- FP8 variants (INT4 weights x e4m3 activations), reported alongside:
-    # per-channel scales, and per-group scales folded into the FP8 weights
-    # with a per-tensor rescale; prefill shape and a 16-token decode shape
     if not args.no_fp8 and not args.only:
-        sh = wl.CONFIGS[wl.FP8_VARIANT].shapes[0]
-        Wf = torch.from_numpy(wl.gen_weights(sh.N, sh.K, wl.seed_w(wl.FP8_VARIANT))).to(dev)
-        pk8 = w4.pack(Wf, mode=w4.PACK_INT4_SYM)
-        pk8g = w4.pack_fp8g(Wf, group=128)
-        del Wf
-        # weight copies used in turn, more bytes than the 256 MB Infinity
-        # Cache, so no launch finds its weights cached from the previous use
-        ncp = int(300e6 // (sh.N * sh.K // 2)) + 1
-        cps8 = [pk8] + [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in pk8.items()}
-                        for _ in range(ncp - 1)]
-        cps8g = [pk8g] + [{k: (v.clone() if torch.is_tensor(v) else v) for k, v in pk8g.items()}
-                          for _ in range(ncp - 1)]
-        Xf = torch.from_numpy(wl.gen_activations(sh.M, sh.K, wl.seed_x(wl.FP8_VARIANT),
-                                                 wl.seed_outliers(wl.FP8_VARIANT))).to(dev)
-        X8, sx8 = w4.quant_act_fp8(Xf)
-        del Xf
-
-        def timed(fn, reps):
-            for r in range(3):
-                fn(r)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for r in range(reps):
-                fn(r)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            return e0.elapsed_time(e1) * 1e3 / reps
-
-        res = {}
-        for M in (sh.M, 16):
-            Yb = torch.empty((M, sh.N), dtype=torch.bfloat16, device=dev)
-            Xm, sxm = X8[:M], sx8[:M]
-            for tag, fn in (("per_channel",
-                             lambda r: w4.gemm_fp8(Xm, sxm, cps8[r % ncp], out=Yb)),
-                            ("group128_folded",
-                             lambda r: w4.gemm_fp8g(Xm, sxm, cps8g[r % ncp], out=Yb))):
-                us = timed(fn, 20)
-                tf = 2.0 * M * sh.N * sh.K / (us * 1e-6) / 1e12
-                wb = sh.N * sh.K / 2 + (sh.N * 4 if tag == "per_channel"
-                                        else sh.N * sh.K // 128 * 4 + 4)
-                ab = wb + M * sh.K + M * 4 + M * sh.N * 2
-                res[f"{tag}_M{M}"] = {"us": round(us, 2), "tflops": round(tf, 2),
-                                      "mfma_frac": round(tf / FP8_PEAK_TFLOPS, 4),
-                                      "hbm_frac_algo": round(ab / (us * 1e-6) / 1e9
-                                                             / HBM_PEAK_GBS, 4)}
-        out["variant_fp8"] = {"workload": f"int4-fp8 N={sh.N} K={sh.K}, M={sh.M} and 16, "
-                                          "bf16 out; events over 20 back-to-back launches "
-                                          f"rotating {ncp} weight copies",
-                              "results": res}
-        del pk8, pk8g, cps8, cps8g, X8
+        out["variant_fp8"] = fp8_variant(w4, wl, torch, dev, stream, args.bursts)
 
     # ---- per-token activation quantisation, the step before every GEMM:
     # fp16 X -> INT8 codes (W4A8) or e4m3 codes (W4FP8) plus float32 row
@@ -756,36 +805,12 @@ def main():
             Xe = torch.empty((M, K), dtype=torch.uint8, device=dev)
             sq = torch.empty(M, dtype=torch.float32, device=dev)
             row = {"M": M, "K": K, "x_copies": ncp}
-            for tag, fn, Yq in (("int8", lambda r: w4.quant_act(Xs[r % ncp], out=(Xq, sq)), Xq),
-                                ("e4m3", lambda r: w4.quant_act_fp8(Xs[r % ncp], out=(Xe, sq)),
-                                 Xe)):
+            for tag, fn, Yq in (("int8", lambda i: w4.quant_act(Xs[i], out=(Xq, sq)), Xq),
+                                ("e4m3", lambda i: w4.quant_act_fp8(Xs[i], out=(Xe, sq)), Xe)):
                 # the launches are captured in a HIP graph and replayed: the
                 # 16-row kernels take less time than a launch from Python
-                reps = 20
-                fn(reps - 1)
-                torch.cuda.synchronize()
-                want = Yq.clone()
-                side = torch.cuda.Stream()
-                side.wait_stream(torch.cuda.current_stream())
-                with torch.cuda.stream(side):
-                    for r in range(3):
-                        fn(r)
-                torch.cuda.current_stream().wait_stream(side)
-                graph = torch.cuda.CUDAGraph()
-                with torch.cuda.graph(graph):
-                    for r in range(reps):
-                        fn(r)
-                graph.replay()
-                torch.cuda.synchronize()
-                if not torch.equal(Yq, want):
-                    raise RuntimeError(f"quant_act {tag} {M}x{K}: graph replay differs")
-                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                graph.replay()
-                e1.record(stream)
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / reps
-                del graph
+                ts = graph_bursts(torch, stream, fn, list(range(ncp)), Yq, args.bursts)
+                us = float(np.median(ts))
                 ab = 3 * M * K + 4 * M
                 row[tag + "_us"] = round(us, 2)
                 row[tag + "_gbs"] = round(ab / (us * 1e-6) / 1e9, 1)
@@ -793,9 +818,9 @@ def main():
             qres.append(row)
             del Xs, Xq, Xe, sq
         out["variant_quant_act"] = {"workload": "fp16 activations -> per-token INT8 / e4m3 + "
-                                                "float32 scales; events around one replay of a "
-                                                "HIP graph of 20 launches rotating x_copies "
-                                                "copies of X",
+                                                "float32 scales; median over back-to-back "
+                                                "replays of a HIP graph of 20 launches rotating "
+                                                "x_copies copies of X",
                                     "results": qres}
 
     if not args.no_cpu_baseline and not args.only:
