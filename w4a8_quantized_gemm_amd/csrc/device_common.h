@@ -24,14 +24,25 @@ __device__ __forceinline__ v4i load16(const void* p) {
     return *reinterpret_cast<const v4i*>(p);
 }
 
-// 16-byte store of a tile kernel's result: non-temporal for the final
-// output, which nothing reads back, so it does not displace the panels other
-// workgroups are reading from L2 (4096 x 28672 x 8192: 704 -> 696 us); split-K
-// partials, which the reduction reads next, keep the plain store.
+// 16-byte store of a tile kernel's result.
+//   Final output: non-temporal.  Nothing reads it back, so it does not
+//   displace the panels other workgroups are reading from L2
+//   (4096 x 28672 x 8192: 704 -> 696 us).
+//   Split-K partials (KEEP): device scope (sc1).  The reduction launch reads
+//   them on every XCD, and each XCD has its own L2, so they have to reach
+//   memory anyway.  A device-scope store writes them through during the
+//   kernel, instead of leaving tens of MB dirty in L2 for the end-of-kernel
+//   writeback that the next launch waits on (128 x 8192 x 28672, eight
+//   splits: 45.5 -> 43.2 us; 256 x 8192 x 8192: 30.7 -> 29.5; plans without
+//   partials unchanged).  The store comes from inline assembly because no
+//   builtin gives a plain 16-byte vector store a scope; it has no outputs,
+//   and a load-counter wait the compiler places after it only waits longer.
 template <bool KEEP>
 __device__ __forceinline__ void store16_result(void* p, v4i v) {
-    if constexpr (KEEP) *reinterpret_cast<v4i*>(p) = v;
-    else __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(p));
+    if constexpr (KEEP)
+        asm volatile("global_store_dwordx4 %0, %1, off sc1" : : "v"(p), "v"(v) : "memory");
+    else
+        __builtin_nontemporal_store(v, reinterpret_cast<v4i*>(p));
 }
 
 // LiquidQuant dequantisation of four codes held one per byte of `c`
