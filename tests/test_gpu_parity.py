@@ -162,7 +162,7 @@ def _small_problem(M, N, K, g, seed):
 
 
 @pytest.mark.parametrize("M", list(range(1, 18)) + [33, 100])
-@pytest.mark.parametrize("N,K,g", [(128, 640, 64), (64, 512, 128)])
+@pytest.mark.parametrize("N,K,g", [(128, 640, 64), (64, 512, 128), (128, 128, 64)])
 def test_w4a8_gemm_parity(M, N, K, g):
     say(f"w4a8 gemm M={M} N={N} K={K} g={g}")
     X8, sx, pk, acc, y = _small_problem(M, N, K, g, 1000 + M)
@@ -180,10 +180,11 @@ def test_w4a8_gemm_parity(M, N, K, g):
 # 16 x 16 x 64 kernel), ragged M, and odd
 # K-step counts (640 = 5 steps, 896 = 7): an odd count runs one extra step of
 # zero X, and the accumulators' last writes must be complete before the
-# epilogue reads them.
+# epilogue reads them.  K = 128 is a single K-step (the loop's second step is
+# all zero X).
 @pytest.mark.parametrize("M", [64, 65, 100, 128, 129, 200, 256, 257, 300, 513, 777])
 @pytest.mark.parametrize("N,K,g", [(256, 512, 64), (512, 1024, 128), (1024, 640, 128),
-                                   (512, 896, 64)])
+                                   (512, 896, 64), (256, 128, 64), (512, 128, 128)])
 def test_w4a8_gemm_mfma_parity(M, N, K, g):
     say(f"w4a8 mfma gemm M={M} N={N} K={K} g={g}")
     X8, sx, pk, acc, y = _small_problem(M, N, K, g, 2000 + M)
@@ -196,7 +197,7 @@ def test_w4a8_gemm_mfma_parity(M, N, K, g):
     assert d.max() <= 1
     # the streamed-tile kernel (forced by an explicit split) agrees
     Ys = poison((M, N), torch.int32)
-    w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, splitk=2, out=Ys)
+    w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, splitk=2 if K >= 256 else 1, out=Ys)
     np.testing.assert_array_equal(host(Ys), acc)
 
 
@@ -534,7 +535,8 @@ def _check_fp8_outputs(yf, yb_bits, ref, bound):
 
 
 @pytest.mark.parametrize("M,N,K", [(16, 128, 1024), (100, 256, 1024), (300, 512, 2048),
-                                   (128, 256, 4096), (100, 256, 640), (300, 512, 1152)])
+                                   (128, 256, 4096), (100, 256, 640), (300, 512, 1152),
+                                   (16, 128, 128), (100, 256, 128)])
 def test_w4fp8_integer_valued_exact(M, N, K):
     """Integer activations in [-16, 16] (exact in e4m3) times |q| <= 7: every
     product is an integer <= 112 and every partial sum an integer below
@@ -656,7 +658,8 @@ def test_w8a8_pack_parity(N, K):
                                       (300, 512, 1152, 0), (513, 256, 512, 0),
                                       (128, 256, 4096, 0), (100, 256, 896, 2), (257, 1024, 256, 0),
                                       (16, 10240, 1024, 0), (16, 8192, 512, 0),
-                                      (40, 28672, 512, 0)])
+                                      (40, 28672, 512, 0), (16, 256, 128, 0),
+                                      (128, 512, 128, 0), (300, 256, 128, 0)])
 def test_w8a8_gemm_parity(M, N, K, sk):
     """int32 bit-exact and fp16 within 1 ulp against the oracle: streamed
     kernel (M < 64, N % 256 != 0, or forced by splitk; 1, 2, 4 and 7 tiles
