@@ -1080,6 +1080,106 @@ def test_fp8g_end_to_end_device_pack():
     np.testing.assert_array_equal(host(a).view(np.uint32), host(b).view(np.uint32))
 
 
+# ---------------------------------------------- largest accepted sizes ----
+def test_largest_activation_extent():
+    """M * K just below 2^31, the largest activation extent the entry points
+    accept: the kernels address X with 32-bit buffer offsets, so the last
+    rows sit at offsets near the top of that range.  16256 x 256 x 131072
+    runs the 32 x 32 tile kernel with two K splits (int32 partials in the
+    workspace); an explicit split factor runs the streamed kernel over all
+    1016 row blocks.  Sampled rows, the first and the last among them, match
+    the oracle: int32 exactly, fp16 within 1 ulp."""
+    M, N, K, g = 16256, 256, 131072, 128
+    assert M * K < (1 << 31) <= (M + 128) * K  # one more 128-row tile would not fit
+    plan = w4.gemm_plan(M, N, K)
+    assert (plan["kernel"], plan["splits"]) == ("tile32", 2), plan
+    say(f"largest activation extent M={M} N={N} K={K} plan={plan}")
+    W = wl.gen_weights(N, K, 4242)
+    pk_ref = oracle.w4a8_pack(W, g)
+    pk = {"wq": to_dev(pk_ref["wq"]), "s_u8": to_dev(pk_ref["s_panels"]),
+          "a_u8": to_dev(pk_ref["a_panels"]), "sw": to_dev(pk_ref["sw"]),
+          "N": N, "K": K, "group": g}
+    del W
+    rng = np.random.default_rng(4243)
+    X8 = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+    sx = rng.uniform(1e-3, 2e-2, size=M).astype(np.float32)
+    rows = np.array([0, 1, 2, M // 2, M - 129, M - 17, M - 2, M - 1])
+    acc, y, _ = oracle.w4a8_gemm(X8[rows], sx[rows], pk_ref, g)
+    Xd, sxd = to_dev(X8), to_dev(sx)
+    del X8
+    for sk in (0, 1):
+        say(f"  splitk={sk}")
+        Yi = poison((M, N), torch.int32)
+        w4.gemm(Xd, sxd, pk, out_type=w4.OUT_I32, splitk=sk, out=Yi)
+        np.testing.assert_array_equal(host(Yi[to_dev(rows)]), acc)
+        del Yi
+        Yh = poison((M, N), torch.float16)
+        w4.gemm(Xd, sxd, pk, out_type=w4.OUT_F16, splitk=sk, out=Yh)
+        d = f16_ulp_diff(host(Yh[to_dev(rows)].view(torch.int16)).view(np.uint16), y)
+        assert d.max() <= 1
+        del Yh
+    del Xd
+
+
+def test_largest_weight_extent():
+    """N * K just below 2^32 codes, the largest weight extent the entry points
+    accept: 2 GiB of packed codes, addressed with 32-bit buffer offsets.
+    Random codes and valid group parameters (s in 1..16, a <= 255 - 15 s, so
+    q*s + a stays a byte), built directly in the packed layout; the oracle
+    decodes sampled channels, the last ones among them, from their own 16-channel
+    slabs.  M = 16 runs the streamed kernel, M = 128 the 128-row tile kernel;
+    the FP8 kernels read the same codes as sign-magnitude INT4 (integer
+    activations, unit scales: exact float32 sums)."""
+    N, K, g = 524032, 8192, 128
+    assert N * K < (1 << 32) <= (N + 256) * K  # one more 256-channel tile would not fit
+    KT, G = K // 128, K // g
+    rng = np.random.default_rng(4244)
+    wq = rng.integers(0, 256, size=N * K // 2, dtype=np.uint8)
+    s_rm = rng.integers(1, 17, size=(N, G), dtype=np.uint8)
+    a_rm = (1 + rng.integers(0, 1 << 16, size=(N, G)) % (255 - 15 * s_rm.astype(np.int64))
+            ).astype(np.uint8)
+    sw = rng.uniform(1e-4, 1e-3, size=N).astype(np.float32)
+    chans = np.array([0, 1, 255, N // 2 + 7, N - 257, N - 17, N - 2, N - 1])
+
+    def codes_of(n):  # the 16-channel slab of channel n holds all its K-tiles
+        slab = wq[(n // 16) * KT * 1024:(n // 16 + 1) * KT * 1024]
+        return oracle.unpack_nibbles(slab, 16, K)[n % 16]
+
+    codes = np.stack([codes_of(n) for n in chans])
+    sub = {"codes": codes, "s_u8": s_rm[chans], "a_u8": a_rm[chans], "sw": sw[chans]}
+    pk = {"wq": to_dev(wq), "s_u8": to_dev(oracle.params_to_panels(s_rm)),
+          "a_u8": to_dev(oracle.params_to_panels(a_rm)), "sw": to_dev(sw),
+          "N": N, "K": K, "group": g}
+    del wq
+    cidx = to_dev(chans)
+    for M in (16, 128):
+        plan = w4.gemm_plan(M, N, K)
+        say(f"largest weight extent M={M} N={N} K={K} plan={plan}")
+        X8 = rng.integers(-127, 128, size=(M, K), dtype=np.int8)
+        sx = rng.uniform(1e-3, 2e-2, size=M).astype(np.float32)
+        acc, y, _ = oracle.w4a8_gemm(X8, sx, sub, g)
+        Yi = poison((M, N), torch.int32)
+        w4.gemm(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_I32, out=Yi)
+        np.testing.assert_array_equal(host(Yi[:, cidx]), acc)
+        del Yi
+        Yh = poison((M, N), torch.float16)
+        w4.gemm(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F16, out=Yh)
+        d = f16_ulp_diff(host(Yh[:, cidx].view(torch.int16)).view(np.uint16), y)
+        assert d.max() <= 1
+        del Yh
+        # FP8 kernels: integer activations in [-16, 16] (exact in e4m3)
+        Xi = rng.integers(-16, 17, size=(M, K)).astype(np.float64)
+        Xe = oracle.e4m3_encode(Xi)
+        q = oracle.int4_sm_values(codes).astype(np.int64)
+        exact = (Xi.astype(np.int64) @ q.T).astype(np.float32)
+        pk8 = {"wq": pk["wq"], "sw": to_dev(np.ones(N, np.float32)), "N": N, "K": K}
+        Yf = poison((M, N), torch.float32)
+        w4.gemm_fp8(to_dev(Xe), to_dev(np.ones(M, np.float32)), pk8, out_type=w4.OUT_F32,
+                    out=Yf)
+        np.testing.assert_array_equal(host(Yf[:, cidx]), exact)
+        del Yf
+
+
 # ------------------------------------------- Llama-shaped workloads --------
 _FULL = [(c, sh) for c in (wl.LLAMA7B_DECODE, wl.LLAMA7B_PREFILL, wl.LLAMA70B_SWEEP)
          for sh in wl.CONFIGS[c].shapes]
