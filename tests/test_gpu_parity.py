@@ -175,6 +175,51 @@ def test_w4a8_gemm_parity(M, N, K, g):
     assert d.max() <= 1
 
 
+# Degenerate inputs of the method through the GEMM kernels: channels whose
+# groups have zero range (all zero, constant: s = 1, q = 0, decode = min),
+# alternate +-max|w| (every group spans the full INT8 range: the saturation
+# branch), a narrow range (R <= 15: lossless), one outlier per group, and the
+# largest and smallest per-channel scales side by side; activation rows all
+# zero (scale 1, codes 0), at +-qmax everywhere, and alternating signs.
+@pytest.mark.parametrize("M", [7, 100])
+@pytest.mark.parametrize("g", [64, 128])
+def test_degenerate_weights_and_rows(M, g):
+    N, K = 256, 1024
+    say(f"degenerate weights and rows M={M} g={g}")
+    W = wl.gen_weights(N, K, 5100 + g)
+    W[0] = 0.0
+    W[1] = 0.5
+    W[2] = np.where(np.arange(K) % 2 == 0, 1.0, -1.0)
+    W[3] = 0.01 + 1e-4 * (np.arange(K) % 7)
+    W[4, ::g] = 3.0
+    W[5] *= 1e-30
+    W[6] *= 1e6
+    X = wl.gen_activations(M, K, 5200 + M, 5201)
+    X[0] = 0.0
+    X[1] = 2.0
+    X[2] = np.where(np.arange(K) % 3 == 0, -1.5, 1.5)
+    X[3, :g] = 0.0
+    pk_ref = oracle.w4a8_pack(W, g)
+    X8, sx = oracle.quant_sym_rows(X, 127)
+    acc, y, _ = oracle.w4a8_gemm(X8, sx, pk_ref, g)
+    pk = {"wq": to_dev(pk_ref["wq"]), "s_u8": to_dev(pk_ref["s_panels"]),
+          "a_u8": to_dev(pk_ref["a_panels"]), "sw": to_dev(pk_ref["sw"]),
+          "N": N, "K": K, "group": g}
+    for sk in (0, 1):
+        Yi = poison((M, N), torch.int32)
+        w4.gemm(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_I32, splitk=sk, out=Yi)
+        np.testing.assert_array_equal(host(Yi), acc)
+        Yh = poison((M, N), torch.float16)
+        w4.gemm(to_dev(X8), to_dev(sx), pk, out_type=w4.OUT_F16, splitk=sk, out=Yh)
+        d = f16_ulp_diff(host(Yh.view(torch.int16)).view(np.uint16), y)
+        assert d.max() <= 1
+    # the device pack of the same weights gives the same codes
+    dpk = w4.pack(to_dev(W), group=g)
+    np.testing.assert_array_equal(host(dpk["wq"]), pk_ref["wq"])
+    np.testing.assert_array_equal(host(dpk["s_u8"]), pk_ref["s_panels"])
+    np.testing.assert_array_equal(host(dpk["a_u8"]), pk_ref["a_panels"])
+
+
 # Shapes that the dispatcher sends to the matrix-core tile kernels (N a
 # multiple of 256, M >= 64): 128-row tiles (short K: two per CU on the
 # 16 x 16 x 64 kernel), ragged M, and odd
