@@ -409,6 +409,34 @@ def test_grouped_gemm_parity(counts, N, K, g):
     assert np.all(yi[offs[-1]:].view(np.uint32) == 0xABABABAB)   # untouched
 
 
+@pytest.mark.parametrize("N", [128, 256])   # streamed kernel / 128-row tiles
+def test_grouped_bad_offsets_clamped(N):
+    """Offsets out of order, negative and past M: each expert's rows are
+    clamped to [0, M] (lo = clamp(off[e]), hi = clamp(max(off[e+1], lo))), as
+    the header states, so bad offsets only leave rows unwritten.  Here expert
+    0 and 3 come out empty, experts 1 and 2 own rows 5..59 and 60..99, and
+    rows 0..4 stay untouched."""
+    M, K, g, E = 100, 512, 128, 4
+    offs = np.array([10, 5, 60, 200, -3], np.int32)
+    owned = {1: (5, 60), 2: (60, 100)}
+    say(f"grouped gemm, bad offsets {offs.tolist()} M={M} N={N}")
+    X = wl.gen_activations(M, K, 700, 701)
+    X8, sx = oracle.quant_sym_rows(X, 127)
+    refs = [oracle.w4a8_pack(wl.gen_weights(N, K, 710 + e), g) for e in range(E)]
+    pk = {"wq": to_dev(np.concatenate([r["wq"].ravel() for r in refs])),
+          "s_u8": to_dev(np.concatenate([r["s_panels"] for r in refs])),
+          "a_u8": to_dev(np.concatenate([r["a_panels"] for r in refs])),
+          "sw": to_dev(np.concatenate([r["sw"] for r in refs])),
+          "N": N, "K": K, "group": g, "E": E}
+    Yi = poison((M, N), torch.int32)
+    w4.gemm_grouped(to_dev(X8), to_dev(sx), to_dev(offs), pk, M, out_type=w4.OUT_I32, out=Yi)
+    yi = host(Yi)
+    for e, (r0, r1) in owned.items():
+        acc, _, _ = oracle.w4a8_gemm(X8[r0:r1], sx[r0:r1], refs[e], g)
+        np.testing.assert_array_equal(yi[r0:r1], acc)
+    assert np.all(yi[:5].view(np.uint32) == 0xABABABAB)   # no expert owns rows 0..4
+
+
 @pytest.mark.parametrize("M,N,K,splits", [(600, 4352, 3072, 3), (300, 4352, 5120, 5),
                                            (500, 2304, 7168, 7), (100, 256, 16384, 16),
                                            (640, 2048, 6272, 6), (100, 6912, 9216, 9),
