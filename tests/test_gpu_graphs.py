@@ -5,7 +5,8 @@ The library allocates nothing and issues no memset or copy, so a captured
 call is just its kernel launches.  Each graph is replayed several times
 with eager work in between (the outputs are overwritten eagerly before
 every replay), and every replay must reproduce the eager result bit for
-bit.
+bit.  The last test runs calls on several streams at once: the entry points
+share no state, so overlapping calls give the serial results.
 """
 import numpy as np
 import pytest
@@ -149,3 +150,46 @@ def test_graph_row_blocks_and_quant():
         calls.append(lambda Xh=Xh, qe=qe, se=se: w4.quant_act_fp8(Xh, out=(qe, se)))
         outs += [q8, s8, qe, se]
     _replay_and_check(calls, outs)
+
+
+def test_concurrent_streams():
+    """Calls share no state: several GEMMs (streamed, tile, split-K with a
+    workspace each, and the FP8 tile kernel) enqueued on four streams, so
+    their kernels overlap on the GPU, give the same bits as the same calls
+    run one after another on one stream."""
+    cases = [(16, 1024, 2048, 128, 31), (512, 512, 1024, 64, 32), (128, 256, 4096, 128, 33),
+             (200, 1024, 8192, 128, 34)]
+    calls, outs = [], []
+    for (M, N, K, g, seed) in cases:
+        X8, sx, pk = _w4a8_case(M, N, K, g, seed)
+        ws = torch.empty(max(w4.workspace_size(M, N, K), 16), dtype=torch.uint8, device=DEV)
+        Y = torch.empty((M, N), dtype=torch.int32, device=DEV)
+        calls.append(lambda X8=X8, sx=sx, pk=pk, ws=ws, Y=Y:
+                     w4.gemm(X8, sx, pk, out_type=w4.OUT_I32, out=Y, workspace=ws))
+        outs.append(Y)
+    M, N, K = 300, 512, 2048
+    rng = np.random.default_rng(35)
+    q = rng.integers(-7, 8, size=(N, K)).astype(np.int8)
+    X8f = oracle.e4m3_encode(rng.integers(-16, 17, size=(M, K)).astype(np.float64))
+    pk8 = {"wq": to_dev(oracle.pack_nibbles(oracle.int4_sm_codes(q))),
+           "sw": to_dev(np.ones(N, np.float32)), "N": N, "K": K}
+    X8d, ones = to_dev(X8f), to_dev(np.ones(M, np.float32))
+    Yf = torch.empty((M, N), dtype=torch.float32, device=DEV)
+    calls.append(lambda: w4.gemm_fp8(X8d, ones, pk8, out_type=w4.OUT_F32, out=Yf))
+    outs.append(Yf)
+    assert w4.workspace_size(128, 256, 4096) > 0 and w4.workspace_size(200, 1024, 8192) > 0
+    for fn in calls:  # one after another on the current stream
+        fn()
+    torch.cuda.synchronize()
+    ref = [o.clone() for o in outs]
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    for r in range(3):
+        for o in outs:
+            o.view(torch.uint8).fill_(0x5A + r)
+        torch.cuda.synchronize()
+        for i, fn in enumerate(calls):
+            with torch.cuda.stream(streams[i % 4]):
+                fn()
+        torch.cuda.synchronize()
+        for o, e in zip(outs, ref):
+            assert torch.equal(o.view(torch.uint8), e.view(torch.uint8)), f"round {r}"
