@@ -50,7 +50,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--only", default="",
-                   help="run one slot, e.g. upgate:M4096, or fp8 for the FP8 variant alone")
+                   help="run one slot, e.g. upgate:M4096, or fp8 / moe / quant for that "
+                        "variant alone")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true")
     p.add_argument("--no-ablation", action="store_true")
@@ -295,19 +296,20 @@ def decode_target(sweep, target=0.70):
 
 
 def sustain(torch, stream, launch, pool, ms=100.0):
-    """About `ms` milliseconds of untimed back-to-back launches
-    (launch(pool[r % len(pool)])), so that what is timed next runs at the
-    clock the chip holds under sustained load.  Measured on one box: after
-    50 ms idle, 20 back-to-back launches of 4096 x 28672 x 8192 took 823 us
-    each, 714 us after 100 ms of load; at 16 x 8192 x 28672, 27.0 against
-    24.1 us."""
-    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0.record(stream)
-    launch(pool[0])
-    t1.record(stream)
-    torch.cuda.synchronize()
-    for r in range(min(5000, int(ms / max(t0.elapsed_time(t1), 1e-3)) + 1)):
-        launch(pool[r % len(pool)])
+    """About `ms` milliseconds (wall clock) of untimed back-to-back launches
+    (launch(pool[r % len(pool)]), eight between synchronisations), so that
+    what is timed next runs at the clock the chip holds under sustained
+    load.  Measured on one box: after 50 ms idle, 20 back-to-back launches of
+    4096 x 28672 x 8192 took 823 us each, 714 us after 100 ms of load; at
+    16 x 8192 x 28672, 27.0 against 24.1 us.  `stream` is where the launches
+    go (torch's current stream)."""
+    t_start = time.perf_counter()
+    r = 0
+    while r < 20000 and (time.perf_counter() - t_start) * 1e3 < ms:
+        for _ in range(8):
+            launch(pool[r % len(pool)])
+            r += 1
+        torch.cuda.synchronize()
 
 
 def graph_bursts(torch, stream, launch, pool, Yout, n, reps=20):
@@ -352,6 +354,95 @@ def graph_bursts(torch, stream, launch, pool, Yout, n, reps=20):
     out_us = [evs[i].elapsed_time(evs[i + 1]) * 1e3 / reps for i in range(n)]
     del graph
     return np.array(out_us)
+
+
+def moe_variant(w4, wl, torch, dev, stream, n=5):
+    """Grouped (mixture-of-experts) GEMM: Mixtral-8x7B expert layers, 8
+    experts with top-2 routing drawn from a seeded generator (each token to
+    two distinct experts), synthetic weights and activations of those
+    shapes, at 16 and 2048 tokens."""
+    import numpy as np
+    rng = np.random.default_rng(8)
+    E, g_moe = 8, 128
+    moe = []
+    for (Nm, Km, tag) in ((14336, 4096, "up"), (4096, 14336, "down")):
+        Ws = torch.from_numpy(np.stack([wl.gen_weights(Nm, Km, 800 + e) for e in range(E)]))
+        pkm = w4.pack_experts(Ws.to(dev), group=g_moe)
+        del Ws
+        # two copies of the expert weights used in turn (2 x 240 MB)
+        pkms = [pkm, {k: (v.clone() if torch.is_tensor(v) else v) for k, v in pkm.items()}]
+        for T in (16, 2048):
+            picks = np.stack([rng.choice(E, 2, replace=False) for _ in range(T)])
+            counts = np.bincount(picks.ravel(), minlength=E)
+            offs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+                                    ).to(dev)
+            Mm = int(counts.sum())
+            Xm = torch.from_numpy(wl.gen_activations(Mm, Km, 900 + T, 901)).to(dev)
+            Xq_m, sx_m = w4.quant_act(Xm)
+            Ym = torch.empty((Mm, Nm), dtype=torch.float16, device=dev)
+            mr = int(counts.max())
+            launch = (lambda pk, Xq_m=Xq_m, sx_m=sx_m, offs=offs, mr=mr, Ym=Ym:
+                      w4.gemm_grouped(Xq_m, sx_m, offs, pk, mr, out=Ym))
+            sustain(torch, stream, launch, pkms)
+            reps = 10
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            ts = []
+            for _ in range(n):
+                e0.record(stream)
+                for r in range(reps):
+                    launch(pkms[r % 2])
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3 / reps)
+            us = float(np.median(ts))
+            active = int((counts > 0).sum())
+            wbytes = active * weight_bytes(Nm, Km, g_moe)
+            moe.append({"layer": tag, "N": Nm, "K": Km, "tokens": T, "rows": Mm,
+                        "max_rows_per_expert": mr, "active_experts": active,
+                        "us": round(us, 2), "us_min": round(min(ts), 2),
+                        "us_max": round(max(ts), 2),
+                        "tops": round(2.0 * Mm * Nm * Km / (us * 1e-6) / 1e12, 2),
+                        "weight_stream_gbs": round(wbytes / (us * 1e-6) / 1e9, 1)})
+        del pkm, pkms
+    return {"workload": "Mixtral-8x7B expert layers, 8 experts top-2, W4A8 group 128, fp16 "
+                        f"out; median over {n} bursts of 10 back-to-back launches alternating "
+                        "two copies of the expert weights",
+            "results": moe}
+
+
+def quant_variant(w4, torch, dev, stream, n=5):
+    """Per-token activation quantisation, the step before every GEMM: fp16 X
+    -> INT8 codes (W4A8) or e4m3 codes (W4FP8) plus float32 row scales, at
+    the sweep's activation shapes.  HBM bound: 2 bytes read and 1 written
+    per value; copies of X used in turn past 512 MB in total where that
+    fits, so the large shapes stream from HBM (the 16-row ones are a few
+    hundred KB and launch bound whatever the copies)."""
+    import numpy as np
+    qres = []
+    for (M, K) in ((16, 8192), (16, 28672), (4096, 8192), (4096, 28672)):
+        ncp = max(2, min(8, int(512e6 // (M * K * 2)) + 1))
+        Xs = [torch.randn((M, K), device=dev).to(torch.float16) for _ in range(ncp)]
+        Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
+        Xe = torch.empty((M, K), dtype=torch.uint8, device=dev)
+        sq = torch.empty(M, dtype=torch.float32, device=dev)
+        row = {"M": M, "K": K, "x_copies": ncp}
+        for tag, fn, Yq in (("int8", lambda i: w4.quant_act(Xs[i], out=(Xq, sq)), Xq),
+                            ("e4m3", lambda i: w4.quant_act_fp8(Xs[i], out=(Xe, sq)), Xe)):
+            # the launches are captured in a HIP graph and replayed: the
+            # 16-row kernels take less time than a launch from Python
+            ts = graph_bursts(torch, stream, fn, list(range(ncp)), Yq, n)
+            us = float(np.median(ts))
+            ab = 3 * M * K + 4 * M
+            row[tag + "_us"] = round(us, 2)
+            row[tag + "_gbs"] = round(ab / (us * 1e-6) / 1e9, 1)
+            row[tag + "_hbm_frac"] = round(ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+        qres.append(row)
+        del Xs, Xq, Xe, sq
+    return {"workload": "fp16 activations -> per-token INT8 / e4m3 + float32 scales; median "
+                        "over back-to-back replays of a HIP graph of 20 launches rotating "
+                        "x_copies copies of X",
+            "results": qres}
 
 
 def fp8_variant(w4, wl, torch, dev, stream, n=5):
@@ -426,6 +517,16 @@ def main():
     if args.only == "fp8":
         # the FP8 variant alone, for the profiler
         print(json.dumps({"variant_fp8": fp8_variant(w4, wl, torch, dev, stream, args.bursts)}),
+              flush=True)
+        return
+    if args.only == "quant":
+        # the activation quantisation alone, for the profiler
+        print(json.dumps({"variant_quant_act": quant_variant(w4, torch, dev, stream,
+                                                             args.bursts)}), flush=True)
+        return
+    if args.only == "moe":
+        # the grouped GEMM alone, for the profiler
+        print(json.dumps({"variant_moe": moe_variant(w4, wl, torch, dev, stream, args.bursts)}),
               flush=True)
         return
     pairs = wl.nk_pairs(CFG)           # [(28672, 8192), (8192, 28672)]
@@ -759,87 +860,16 @@ def main():
                                        "same shape",
                                "results": cmp_rows}
 
-    # ---- grouped (mixture-of-experts) GEMM: Mixtral-8x7B expert layers, 8
-    # experts with top-2 routing drawn from a seeded generator (each token to
-    # two distinct experts), synthetic weights and activations of those shapes
+    # ---- grouped (mixture-of-experts) GEMM, Mixtral-8x7B expert layers
     if not args.no_moe and not args.only:
-        rng = np.random.default_rng(8)
-        E, g_moe = 8, 128
-        moe = []
-        for (Nm, Km, tag) in ((14336, 4096, "up"), (4096, 14336, "down")):
-            Ws = torch.from_numpy(np.stack([wl.gen_weights(Nm, Km, 800 + e) for e in range(E)]))
-            pkm = w4.pack_experts(Ws.to(dev), group=g_moe)
-            del Ws
-            # two copies of the expert weights used in turn (2 x 240 MB)
-            pkms = [pkm, {k: (v.clone() if torch.is_tensor(v) else v) for k, v in pkm.items()}]
-            for T in (16, 2048):
-                picks = np.stack([rng.choice(E, 2, replace=False) for _ in range(T)])
-                counts = np.bincount(picks.ravel(), minlength=E)
-                offs = torch.from_numpy(np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)).to(dev)
-                Mm = int(counts.sum())
-                Xm = torch.from_numpy(wl.gen_activations(Mm, Km, 900 + T, 901)).to(dev)
-                Xq_m, sx_m = w4.quant_act(Xm)
-                Ym = torch.empty((Mm, Nm), dtype=torch.float16, device=dev)
-                mr = int(counts.max())
-                sustain(torch, stream, lambda pk: w4.gemm_grouped(Xq_m, sx_m, offs, pk, mr,
-                                                                   out=Ym), pkms)
-                reps = 10
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
-                e0.record(stream)
-                for r in range(reps):
-                    w4.gemm_grouped(Xq_m, sx_m, offs, pkms[r % 2], mr, out=Ym)
-                e1.record(stream)
-                torch.cuda.synchronize()
-                us = e0.elapsed_time(e1) * 1e3 / reps
-                active = int((counts > 0).sum())
-                wbytes = active * weight_bytes(Nm, Km, g_moe)
-                moe.append({"layer": tag, "N": Nm, "K": Km, "tokens": T, "rows": Mm,
-                            "max_rows_per_expert": mr, "active_experts": active,
-                            "us": round(us, 2),
-                            "tops": round(2.0 * Mm * Nm * Km / (us * 1e-6) / 1e12, 2),
-                            "weight_stream_gbs": round(wbytes / (us * 1e-6) / 1e9, 1)})
-            del pkm, pkms
-        out["variant_moe"] = {"workload": "Mixtral-8x7B expert layers, 8 experts top-2, "
-                                          "W4A8 group 128, fp16 out; events over 10 back-to-back "
-                                          "launches alternating two copies of the expert weights",
-                              "results": moe}
+        out["variant_moe"] = moe_variant(w4, wl, torch, dev, stream, args.bursts)
 
     if not args.no_fp8 and not args.only:
         out["variant_fp8"] = fp8_variant(w4, wl, torch, dev, stream, args.bursts)
 
-    # ---- per-token activation quantisation, the step before every GEMM:
-    # fp16 X -> INT8 codes (W4A8) or e4m3 codes (W4FP8) plus float32 row
-    # scales, at the sweep's activation shapes.  HBM bound: 2 bytes read and
-    # 1 written per value; copies of X used in turn past 512 MB in total
-    # where that fits, so the large shapes stream from HBM (the 16-row ones
-    # are a few hundred KB and launch bound whatever the copies).
+    # ---- per-token activation quantisation, the step before every GEMM
     if not args.no_ablation and not args.only:
-        qres = []
-        for (M, K) in ((16, 8192), (16, 28672), (4096, 8192), (4096, 28672)):
-            ncp = max(2, min(8, int(512e6 // (M * K * 2)) + 1))
-            Xs = [torch.randn((M, K), device=dev).to(torch.float16) for _ in range(ncp)]
-            Xq = torch.empty((M, K), dtype=torch.int8, device=dev)
-            Xe = torch.empty((M, K), dtype=torch.uint8, device=dev)
-            sq = torch.empty(M, dtype=torch.float32, device=dev)
-            row = {"M": M, "K": K, "x_copies": ncp}
-            for tag, fn, Yq in (("int8", lambda i: w4.quant_act(Xs[i], out=(Xq, sq)), Xq),
-                                ("e4m3", lambda i: w4.quant_act_fp8(Xs[i], out=(Xe, sq)), Xe)):
-                # the launches are captured in a HIP graph and replayed: the
-                # 16-row kernels take less time than a launch from Python
-                ts = graph_bursts(torch, stream, fn, list(range(ncp)), Yq, args.bursts)
-                us = float(np.median(ts))
-                ab = 3 * M * K + 4 * M
-                row[tag + "_us"] = round(us, 2)
-                row[tag + "_gbs"] = round(ab / (us * 1e-6) / 1e9, 1)
-                row[tag + "_hbm_frac"] = round(ab / (us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
-            qres.append(row)
-            del Xs, Xq, Xe, sq
-        out["variant_quant_act"] = {"workload": "fp16 activations -> per-token INT8 / e4m3 + "
-                                                "float32 scales; median over back-to-back "
-                                                "replays of a HIP graph of 20 launches rotating "
-                                                "x_copies copies of X",
-                                    "results": qres}
+        out["variant_quant_act"] = quant_variant(w4, torch, dev, stream, args.bursts)
 
     if not args.no_cpu_baseline and not args.only:
         out["cpu_baseline"] = cpu_baseline(sweep_desc(), args.cpu_sample_cols)
