@@ -155,9 +155,12 @@ w4a8_status_t w4fp8_quant_act_ex(const void* X, int in_type, int M, int K,
  * w8a8_gemm may instead split K between the wave pairs of a workgroup and
  * need half of it, or none; the size returned covers every entry point.
  * Returns 0 when no split is used and when splitk != 0 (streamed kernel,
- * which reduces on chip).  The workspace is scratch: its contents on entry
- * are ignored and undefined on return; calls that share a workspace must be
- * ordered on one stream.
+ * which reduces on chip).  The size does not depend on the group size
+ * (partials are per output element), so the call takes the split factor in
+ * its place: an explicit split selects the streamed kernel, which needs no
+ * workspace.  The workspace is scratch: its contents on entry are ignored
+ * and undefined on return; calls that share a workspace must be ordered on
+ * one stream.
  */
 size_t w4a8_workspace_size(int M, int N, int K, int splitk);
 
