@@ -297,13 +297,18 @@ def test_large_grid_several_waves(M, N, K, g):
 # workgroup along M holds one block partly and one wholly past M); four
 # blocks (33-63 rows) with 2 tiles.  Short K leaves
 # waves with fewer K-tiles than the load ring holds (640 / 128 = 5 K-tiles
-# over 4 waves, 1152 over 8 waves).
+# over 4 waves, 1152 over 8 waves).  The last case holds too many group
+# parameters for LDS (512 groups per channel row: parameter panels plus X
+# slots past 128 KiB), so each tile reads its scale and offset bytes from
+# memory with one row block and 128-wide groups (test_stream_params_from_global
+# covers two row blocks and 64-wide groups).
 @pytest.mark.parametrize("M,N,K,g", [(16, 10240, 1024, 128), (1, 14336, 640, 64),
                                      (16, 8192, 2048, 128), (7, 4096, 512, 64),
                                      (32, 28672, 640, 128), (20, 8192, 1024, 64),
                                      (17, 4096, 768, 128), (48, 4096, 768, 64),
                                      (33, 8192, 1152, 64), (40, 28672, 512, 128),
-                                     (63, 11008, 512, 64), (50, 2048, 2048, 64)])
+                                     (63, 11008, 512, 64), (50, 2048, 2048, 64),
+                                     (20, 2048, 65536, 128)])
 def test_stream_widths(M, N, K, g):
     say(f"w4a8 streamed kernel widths: M={M} N={N} K={K} g={g}")
     assert w4.workspace_size(M, N, K) == 0

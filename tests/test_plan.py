@@ -64,6 +64,7 @@ PARITY = {
     (100, 256, 16384): (T16, 128, 256, 16, 1),
     # streamed: parameters from global memory (two row blocks, one tile)
     (20, 4096, 28672): (ST, 32, 16, 1, 8),
+    (20, 2048, 65536): (ST, 16, 16, 1, 8),        # one row block, g = 128
     # a single K-step on either kernel
     (16, 128, 128): (ST, 16, 16, 1, 1),
     (128, 512, 128): (T16, 128, 256, 1, 1),
