@@ -374,6 +374,7 @@ __global__ __launch_bounds__(256, (MT == 128 && KIN == 1) ? 2 : 1) void w4a8_mfm
         bc = bd;
         bd = bn;
         bn = t0;
+        if (kt + 2 >= KTe) mfma_loop_exit_wait();  // the iteration that leaves the loop
     }
     mfma16_drain(acc);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));  // the last steps' X loads

@@ -89,6 +89,22 @@ __device__ __forceinline__ void mfma32_drain(ACC (&acc)[RB][2]) {
     __builtin_amdgcn_sched_barrier(0);
 }
 
+// Wait states at the bottom of the main loop's last iteration, after its
+// last matrix-core instruction (called under a uniform branch on the loop
+// counter).  The register allocator may split an accumulator's live range at
+// the loop exit and copy it out of its AGPR there, before the drain that
+// follows the loop: neither the scheduling barriers nor the drain's
+// redefinitions constrain where it puts such copies.  With these wait states
+// inside the loop, every path out of it is far enough from the last write.
+// An XDL write of a register and a vector read of it need passes + 3 wait
+// states on CDNA3, one more on gfx950: at most 20 for the 16-pass
+// instructions used here.  Waiting in every iteration instead cost 0.2-1.0 %
+// on the 70B shapes.  A CPU test checks the distance on every path in this
+// build's assembly.
+__device__ __forceinline__ void mfma_loop_exit_wait() {
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 3");
+}
+
 // Workgroup -> (output tile, K split).  Workgroups are dealt round-robin to
 // the 8 XCDs (each with its own L2); regroup so each XCD walks a contiguous
 // run of tiles, and order the tiles in 4 (M) x 8 (channel panel) blocks so
