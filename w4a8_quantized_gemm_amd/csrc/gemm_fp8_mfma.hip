@@ -51,8 +51,8 @@ struct F8Lut {
     unsigned lo[2], hi[2];
 };
 
-struct F8Tmp {
-    unsigned m, e, s;
+struct F8Tmp {  // the two dwords converted together (index h)
+    unsigned m[2], e[2], s[2];
 };
 
 // Producing operand B[cb][j] of a K-step is 32 single-instruction steps:
@@ -61,34 +61,38 @@ struct F8Tmp {
 //   B[2d] = (s << 4) | e                               (low nibbles)
 //   t = w >> 4; m = t & 0x07070707; e = perm(table, m);
 //   B[2d+1] = (w & 0x80808080) | e                      (high nibbles)
+// Dwords go in pairs (d = 2 (q / 16) + h) whose steps alternate, so no
+// step reads the result of the one just before it (the compiler puts a wait
+// state between two dependent assembly statements, not knowing what they
+// are).
 template <int J, int OP>
 __device__ __forceinline__ void f8_step(F8Tmp& t, const F8Step& w, const F8Lut& lut,
                                         unsigned sgn, v8i (&B)[2][2]) {
-    constexpr int cb = OP / 32, q = OP % 32, d = q / 8, st = q % 8;
+    constexpr int cb = OP / 32, q = OP % 32, h = q % 2, d = 2 * (q / 16) + h, st = (q % 16) / 2;
     const unsigned wd = (unsigned)w.w[cb][J][d];
     if constexpr (st == 0) {
-        asm volatile("v_and_b32 %0, 0x07070707, %1" : "=v"(t.m) : "v"(wd));
+        asm volatile("v_and_b32 %0, 0x07070707, %1" : "=v"(t.m[h]) : "v"(wd));
     } else if constexpr (st == 1) {
         asm volatile("v_perm_b32 %0, %1, %2, %3"
-                     : "=v"(t.e)
-                     : "v"(lut.hi[cb]), "v"(lut.lo[cb]), "v"(t.m));
+                     : "=v"(t.e[h])
+                     : "v"(lut.hi[cb]), "v"(lut.lo[cb]), "v"(t.m[h]));
     } else if constexpr (st == 2) {
-        asm volatile("v_and_b32 %0, 0x08080808, %1" : "=v"(t.s) : "v"(wd));
+        asm volatile("v_and_b32 %0, 0x08080808, %1" : "=v"(t.s[h]) : "v"(wd));
     } else if constexpr (st == 3) {
         unsigned x;
-        asm volatile("v_lshl_or_b32 %0, %1, 4, %2" : "=v"(x) : "v"(t.s), "v"(t.e));
+        asm volatile("v_lshl_or_b32 %0, %1, 4, %2" : "=v"(x) : "v"(t.s[h]), "v"(t.e[h]));
         B[cb][J][2 * d] = (int)x;
     } else if constexpr (st == 4) {
-        asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(t.m) : "v"(wd));
+        asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(t.m[h]) : "v"(wd));
     } else if constexpr (st == 5) {
-        asm volatile("v_and_b32 %0, 0x07070707, %1" : "=v"(t.m) : "v"(t.m));
+        asm volatile("v_and_b32 %0, 0x07070707, %1" : "=v"(t.m[h]) : "v"(t.m[h]));
     } else if constexpr (st == 6) {
         asm volatile("v_perm_b32 %0, %1, %2, %3"
-                     : "=v"(t.e)
-                     : "v"(lut.hi[cb]), "v"(lut.lo[cb]), "v"(t.m));
+                     : "=v"(t.e[h])
+                     : "v"(lut.hi[cb]), "v"(lut.lo[cb]), "v"(t.m[h]));
     } else {
         unsigned x;
-        asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(x) : "v"(wd), "v"(sgn), "v"(t.e));
+        asm volatile("v_and_or_b32 %0, %1, %2, %3" : "=v"(x) : "v"(wd), "v"(sgn), "v"(t.e[h]));
         B[cb][J][2 * d + 1] = (int)x;
     }
 }

@@ -79,8 +79,8 @@ struct DecLQQ {
     struct Params {
         unsigned s2[2], a4[2];  // scale pair, offset quad per channel block
     };
-    struct Tmp {
-        unsigned lo, t, hi;
+    struct Tmp {  // the two dwords decoded together (index dd)
+        unsigned lo[2], t[2], hi[2];
     };
     static constexpr int kParamOps = 4;
     static constexpr int kOps = 28;
@@ -98,32 +98,34 @@ struct DecLQQ {
         }
     }
 
-    // Instruction group I takes dwords d = 2(I%2), 2(I%2)+1 of slot e = I/2.
+    // Instruction group I takes dwords d = 2(I%2), 2(I%2)+1 of slot e = I/2;
+    // their steps alternate (dd = q % 2), so no step reads the result of the
+    // one just before it.
     template <int I, int OP>
     __device__ __forceinline__ static void step(Tmp& tmp, const WStep32& w, const Params& p,
                                                 v4i (&B)[2][4]) {
-        constexpr int cb = OP / 14, q = OP % 14, dd = q / 7, st = q % 7;
+        constexpr int cb = OP / 14, q = OP % 14, dd = q % 2, st = q / 2;
         constexpr int e = I / 2, d = 2 * (I % 2) + dd;
         const unsigned wd = (unsigned)w.w[cb][e][d];
         if constexpr (st == 0) {
-            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.lo) : "v"(wd));
+            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.lo[dd]) : "v"(wd));
         } else if constexpr (st == 1) {
-            asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(tmp.t) : "v"(wd));
+            asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(tmp.t[dd]) : "v"(wd));
         } else if constexpr (st == 2) {
-            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.hi) : "v"(tmp.t));
+            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.hi[dd]) : "v"(tmp.t[dd]));
         } else if constexpr (st == 3) {
             asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
-                         : "=v"(tmp.lo) : "v"(tmp.lo), "v"(p.s2[cb]), "v"(p.a4[cb]));
+                         : "=v"(tmp.lo[dd]) : "v"(tmp.lo[dd]), "v"(p.s2[cb]), "v"(p.a4[cb]));
         } else if constexpr (st == 4) {
             asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
-                         : "=v"(tmp.hi) : "v"(tmp.hi), "v"(p.s2[cb]), "v"(p.a4[cb]));
+                         : "=v"(tmp.hi[dd]) : "v"(tmp.hi[dd]), "v"(p.s2[cb]), "v"(p.a4[cb]));
         } else if constexpr (st == 5) {
             unsigned x;
-            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(tmp.lo));
+            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(tmp.lo[dd]));
             B[cb][I][2 * dd] = (int)x;
         } else {
             unsigned x;
-            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(tmp.hi));
+            asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(tmp.hi[dd]));
             B[cb][I][2 * dd + 1] = (int)x;
         }
     }
@@ -145,8 +147,8 @@ struct DecAffine16 {
     struct Params {
         unsigned s2[2], m2[2];  // scale, min in both 16-bit lanes
     };
-    struct Tmp {
-        unsigned lo, t, hi, e0, e1;
+    struct Tmp {  // the two dwords decoded together (index dd)
+        unsigned lo[2], t[2], hi[2], e0[2], e1[2];
     };
     static constexpr int kParamOps = 6;
     static constexpr int kOps = 52;
@@ -168,31 +170,31 @@ struct DecAffine16 {
     template <int I, int OP>
     __device__ __forceinline__ static void step(Tmp& tmp, const WStep32& w, const Params& p,
                                                 v4i (&B)[2][4]) {
-        constexpr int cb = OP / 26, q = OP % 26, dd = q / 13, st = q % 13;
+        constexpr int cb = OP / 26, q = OP % 26, dd = q % 2, st = q / 2;  // dwords alternate
         constexpr int e = I / 2, d = 2 * (I % 2) + dd;
         const unsigned wd = (unsigned)w.w[cb][e][d];
         constexpr unsigned kEven = 0x0C020C00u, kOdd = 0x0C030C01u, kGather = 0x06020400u;
         if constexpr (st == 0) {
-            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.lo) : "v"(wd));
+            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.lo[dd]) : "v"(wd));
         } else if constexpr (st == 1) {
-            asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(tmp.t) : "v"(wd));
+            asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(tmp.t[dd]) : "v"(wd));
         } else if constexpr (st == 2) {
-            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.hi) : "v"(tmp.t));
+            asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(tmp.hi[dd]) : "v"(tmp.t[dd]));
         } else if constexpr (st == 3 || st == 8) {
-            const unsigned src = st == 3 ? tmp.lo : tmp.hi;
-            asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(tmp.e0) : "v"(src), "s"(kEven));
+            const unsigned src = st == 3 ? tmp.lo[dd] : tmp.hi[dd];
+            asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(tmp.e0[dd]) : "v"(src), "s"(kEven));
         } else if constexpr (st == 4 || st == 9) {
-            const unsigned src = st == 4 ? tmp.lo : tmp.hi;
-            asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(tmp.e1) : "v"(src), "s"(kOdd));
+            const unsigned src = st == 4 ? tmp.lo[dd] : tmp.hi[dd];
+            asm volatile("v_perm_b32 %0, 0, %1, %2" : "=v"(tmp.e1[dd]) : "v"(src), "s"(kOdd));
         } else if constexpr (st == 5 || st == 10) {
             asm volatile("v_pk_mad_i16 %0, %1, %2, %3"
-                         : "=v"(tmp.e0) : "v"(tmp.e0), "v"(p.s2[cb]), "v"(p.m2[cb]));
+                         : "=v"(tmp.e0[dd]) : "v"(tmp.e0[dd]), "v"(p.s2[cb]), "v"(p.m2[cb]));
         } else if constexpr (st == 6 || st == 11) {
             asm volatile("v_pk_mad_i16 %0, %1, %2, %3"
-                         : "=v"(tmp.e1) : "v"(tmp.e1), "v"(p.s2[cb]), "v"(p.m2[cb]));
+                         : "=v"(tmp.e1[dd]) : "v"(tmp.e1[dd]), "v"(p.s2[cb]), "v"(p.m2[cb]));
         } else {
             unsigned x;
-            asm volatile("v_perm_b32 %0, %1, %2, %3" : "=v"(x) : "v"(tmp.e1), "v"(tmp.e0), "s"(kGather));
+            asm volatile("v_perm_b32 %0, %1, %2, %3" : "=v"(x) : "v"(tmp.e1[dd]), "v"(tmp.e0[dd]), "s"(kGather));
             B[cb][I][2 * dd + (st == 12 ? 1 : 0)] = (int)x;
         }
     }

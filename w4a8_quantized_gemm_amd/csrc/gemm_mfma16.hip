@@ -87,8 +87,9 @@ struct Par16 {
     unsigned s2[4], a4[4];  // per channel block: scale pair, offset quad
 };
 
+// Temporaries of the two packed dwords decoded together (index dd).
 struct Tmp16 {
-    unsigned lo, t, hi;
+    unsigned lo[2], t[2], hi[2];
 };
 
 // Parameter step K_ (0..7): scale pair (even) or offset quad (odd) of
@@ -106,35 +107,39 @@ __device__ __forceinline__ void par16_step(const WRaw16& w, Par16& p) {
 }
 
 // Decode step OP (0..55) producing B[*][U]: channel block cb = OP / 14,
-// packed dword d = 2U + (OP % 14) / 7, instruction st = OP % 7:
+// packed dword d = 2U + dd with dd = (OP % 14) % 2, instruction
+// st = (OP % 14) / 2:
 //   lo = w & 0x0F0F0F0F; t = w >> 4; hi = t & 0x0F0F0F0F;
 //   lo = lo*s + a; hi = hi*s + a (two codes per 16-bit lane);
 //   B[cb][U] dwords 2dd, 2dd+1 = lo ^ 0x80808080, hi ^ 0x80808080
+// The two dwords' steps alternate, so no step reads the result of the one
+// just before it (the compiler puts a wait state between two dependent
+// assembly statements, not knowing what they are).
 template <int U, int OP>
 __device__ __forceinline__ void dec16_step(Tmp16& t, const WRaw16& w, const Par16& p,
                                            v4i (&B)[4][2]) {
-    constexpr int cb = OP / 14, q = OP % 14, dd = q / 7, st = q % 7;
+    constexpr int cb = OP / 14, q = OP % 14, dd = q % 2, st = q / 2;
     constexpr int d = 2 * U + dd;
     const unsigned wd = (unsigned)w.w[cb][d];
     if constexpr (st == 0) {
-        asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(t.lo) : "v"(wd));
+        asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(t.lo[dd]) : "v"(wd));
     } else if constexpr (st == 1) {
-        asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(t.t) : "v"(wd));
+        asm volatile("v_lshrrev_b32 %0, 4, %1" : "=v"(t.t[dd]) : "v"(wd));
     } else if constexpr (st == 2) {
-        asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(t.hi) : "v"(t.t));
+        asm volatile("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(t.hi[dd]) : "v"(t.t[dd]));
     } else if constexpr (st == 3) {
         asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
-                     : "=v"(t.lo) : "v"(t.lo), "v"(p.s2[cb]), "v"(p.a4[cb]));
+                     : "=v"(t.lo[dd]) : "v"(t.lo[dd]), "v"(p.s2[cb]), "v"(p.a4[cb]));
     } else if constexpr (st == 4) {
         asm volatile("v_pk_mad_u16 %0, %1, %2, %3"
-                     : "=v"(t.hi) : "v"(t.hi), "v"(p.s2[cb]), "v"(p.a4[cb]));
+                     : "=v"(t.hi[dd]) : "v"(t.hi[dd]), "v"(p.s2[cb]), "v"(p.a4[cb]));
     } else if constexpr (st == 5) {
         unsigned x;
-        asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(t.lo));
+        asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(t.lo[dd]));
         B[cb][U][2 * dd] = (int)x;
     } else {
         unsigned x;
-        asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(t.hi));
+        asm volatile("v_xor_b32 %0, 0x80808080, %1" : "=v"(x) : "v"(t.hi[dd]));
         B[cb][U][2 * dd + 1] = (int)x;
     }
 }
