@@ -82,7 +82,8 @@ def _functions(asm):
 
 
 def _blocks(items):
-    """Basic blocks: list of (instructions, successor block indices)."""
+    """Basic blocks and their successor indices.  A label maps to the next
+    block that has instructions (consecutive labels share it)."""
     blocks, cur, labels = [], [], {}
     for mn, ops, hand, label in items:
         if label is not None:
@@ -106,7 +107,6 @@ def _blocks(items):
         if not mn.startswith(("s_branch", "s_endpgm", "s_setpc")) and i + 1 < len(blocks):
             s.append(i + 1)
         succ.append(s)
-    # a label that starts an empty run maps to the next block
     return blocks, succ
 
 
@@ -114,10 +114,6 @@ def _check(items):
     """Fewest wait states between a hand-issued matrix-core write of an AGPR
     and a later access of it; returns (minimum, list of violations)."""
     blocks, succ = _blocks(items)
-    pred = [[] for _ in blocks]
-    for i, ss in enumerate(succ):
-        for j in ss:
-            pred[j].append(i)
     entry = [dict() for _ in blocks]  # AGPR -> wait states since its pending write
     done = [False] * len(blocks)
     seen_min, bad = CAP, []
